@@ -1,0 +1,379 @@
+"""Plain fp64 CPU oracle for GPTQ layer-wise second-order weight quantization.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously-correct
+reference that the GPU library is checked against.  Only the test suite, the
+smoke check and the CPU-baseline leg of the benchmark may import it; the
+library itself never does, and this module imports nothing from the library.
+
+Everything is float64 numpy/scipy, written to be read against the pages that
+describe the method.  Short names used in the citations below:
+
+  [OBQ]     "Part 2: Adaptive Rounding: Optimal Brain Quantizer (OBQ)"
+            (feed.roma.co.ke)
+  [GPTQ]    "Part 3: Adaptive Rounding: GPTQ" (hello-fri-end.github.io)
+  [SOQ]     the English blog post on GPTQ second-order quantization
+            (hungho77.github.io, /hung/blog/gptq-second-order-quantization/)
+  [SOQ-vi]  the Vietnamese edition of that post (/hung/vi/blog/...)
+
+Readings taken where the pages are silent or disagree (each is also listed in
+the design notes):
+
+  R1  H = 2 X X^T, unnormalised ([SOQ] "The objective is layer output";
+      [SOQ-vi] "Objective").  Codes do not depend on this scale because the
+      damping is relative.
+  R2  lambda = damp * mean(diag H) of the undamped H, added once to every
+      diagonal entry ([SOQ] "3. Cholesky reformulation").
+  R3  The factor read row by row is the UPPER U with H_d^{-1} = U^T U; row p of
+      U covers columns >= p, which is what compensating later columns needs
+      ([GPTQ] "Observation 3"; [SOQ-vi] writes the flush as E R[B, B:]).
+  R4  Signs: e_p = (v_p - what_p) / U_pp and V <- V - e U[p, :].  This is the
+      loss-minimising update of [GPTQ] "Observation 3" / [OBQ] "Generalized
+      Weight Update" written with U; the flush in [GPTQ] "Algorithm GPTQ"
+      stores the opposite sign in E, which taken literally pushes weights the
+      wrong way.
+  R5  Quantizer ([GPTQ] summary table "Asymmetric uniform"; [SOQ]
+      "Group-wise quantization"): x_lo = min(0, min v), x_hi = max(0, max v),
+      s = (x_hi - x_lo) / maxq, z = rint(-x_lo / s), q = clip(rint(v/s) + z,
+      0, maxq), what = s (q - z).  A group whose values are all zero (empty
+      range) uses x_hi = 1 (s = 1/maxq, z = 0), so its codes are exact zeros.
+  R6  Rounding is round-half-to-even (IEEE rint).
+  R7  Group parameters are taken when the sweep reaches the group's first
+      column, from the current (already compensated) values of that group;
+      per-row parameters (group <= 0) come from the original row.
+  R8  Columns are swept left to right ([GPTQ] "Observation 1").
+  R9  Block size and group size must nest (group % block == 0 or
+      block % group == 0); the last block and group may be short.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional, Tuple
+
+import numpy as np
+import scipy.linalg
+from scipy.linalg import lapack
+
+
+# ----------------------------------------------------------------------------- Hessian and damping
+
+def hessian(chunks: Iterable[np.ndarray]) -> np.ndarray:
+    """H = 2 X X^T with X the [n x tokens] calibration inputs, given here as
+    token-major chunks [tokens_c x n] ([SOQ] "The objective is layer output":
+    the Hessian of ||WX - What X||^2 is 2XX^T; [OBQ] "Goal": the input
+    covariance stands in for the true Hessian).  fp64, both triangles."""
+    H = None
+    for c in chunks:
+        c = np.asarray(c, dtype=np.float64)
+        G = c.T @ c
+        H = G if H is None else H + G
+    return 2.0 * H
+
+
+def damp(H: np.ndarray, rel: float) -> Tuple[np.ndarray, float]:
+    """H_d = H + lambda I with lambda = rel * mean(diag H) ([SOQ] "3. Cholesky
+    reformulation": about one percent of the average Hessian diagonal;
+    [GPTQ] "Algorithm GPTQ": H = XX^T + lambda I)."""
+    lam = float(rel) * float(np.mean(np.diag(H)))
+    Hd = np.array(H, dtype=np.float64, copy=True)
+    Hd[np.diag_indices_from(Hd)] += lam
+    return Hd, lam
+
+
+# ----------------------------------------------------------------------------- inverse-Hessian factor
+
+def inverse_cholesky_upper(Hd: np.ndarray) -> Tuple[Optional[np.ndarray], int]:
+    """U upper-triangular with H_d^{-1} = U^T U ([GPTQ] "Observation 3": factor
+    the inverse once, then read its rows; reading R3).
+
+    Steps as stated: Cholesky of H_d, the inverse from that factor, then the
+    Cholesky of the inverse.  Returns (U, 0), or (None, k) when the k-th
+    (1-based) leading minor of H_d is not positive definite."""
+    L, info = lapack.dpotrf(np.asarray(Hd, dtype=np.float64), lower=1, clean=1)
+    if info != 0:
+        return None, int(info)
+    G, info = lapack.dpotri(L, lower=1)
+    if info != 0:
+        return None, int(info)
+    G = np.tril(G) + np.tril(G, -1).T
+    U, info = lapack.dpotrf(G, lower=0, clean=1)
+    if info != 0:
+        return None, int(info)
+    return np.triu(U), 0
+
+
+# ----------------------------------------------------------------------------- quantizer
+
+def maxq_of(bits: int) -> int:
+    return (1 << int(bits)) - 1
+
+
+def quant_params(v: np.ndarray, bits: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Asymmetric min/max scale and integer zero point per row of v [rows x k]
+    (reading R5).  Returns s [rows] (float64) and z [rows] (float64 holding
+    integers)."""
+    v = np.asarray(v, dtype=np.float64)
+    maxq = maxq_of(bits)
+    lo = np.minimum(v.min(axis=1), 0.0)
+    hi = np.maximum(v.max(axis=1), 0.0)
+    empty = hi == lo
+    hi = np.where(empty, 1.0, hi)
+    lo = np.where(empty, 0.0, lo)
+    s = (hi - lo) / maxq
+    z = np.rint(-lo / s)
+    return s, z
+
+
+def quantize(v: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int) -> np.ndarray:
+    """q = clip(rint(v/s) + z, 0, maxq) (reading R5, R6); integer codes."""
+    t = np.asarray(v, dtype=np.float64) / s
+    return np.clip(np.rint(t) + z, 0, maxq_of(bits)).astype(np.int64)
+
+
+def dequantize(q: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    return s * (np.asarray(q, dtype=np.float64) - z)
+
+
+def n_groups(n: int, group: int) -> int:
+    return 1 if group <= 0 else (n + group - 1) // group
+
+
+def check_schedule(n: int, group: int, block: int) -> None:
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    if group > 0 and not (group % block == 0 or block % group == 0):
+        raise ValueError("group and block sizes must nest (reading R9)")
+
+
+# ----------------------------------------------------------------------------- the sweep
+
+def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group: int, block: Optional[int]) -> Dict[str, np.ndarray]:
+    """GPTQ's column sweep over one layer ([GPTQ] "Algorithm GPTQ"; [SOQ-vi]
+    "Lazy batch update").
+
+    block=None runs the definition: after each column every later column is
+    compensated at once.  block=B runs the pages' lazy schedule: within a
+    block of B columns the compensation touches only the block, and the
+    accumulated scaled errors E are flushed to all later columns by one
+    matrix product V[:, i2:] -= E U[i:i2, i2:] when the block ends.  Both give
+    the same result up to the order of floating-point sums.
+
+    Per column p (readings R3-R8):
+      at a group start: (s, z) from the current V[:, p:p+group]
+      q = clip(rint(V_p / s) + z, 0, maxq);  what = s (q - z)
+      e = (V_p - what) / U_pp                   (the scaled error kept in E)
+      V[:, later] -= e U[p, later]              ([OBQ] "Generalized Weight Update":
+                                                 delta_rem = delta_p (H^-1)_{p,rem}/(H^-1)_pp,
+                                                 read from row p of U)
+
+    Returns q [m x n] int64, s and z [m x G], E [m x n], What [m x n],
+    t [m x n] = V_p / s (pre-rounding value in steps) and tz [m x G] = -x_lo/s
+    (pre-rounding zero point), err_sq [m] = sum_p e_p^2."""
+    V = np.array(W, dtype=np.float64, copy=True)
+    m, n = V.shape
+    if U.shape != (n, n):
+        raise ValueError("U must be n x n")
+    B = n if block is None else int(block)
+    if block is not None:
+        check_schedule(n, group, B)
+    G = n_groups(n, group)
+    q = np.zeros((m, n), dtype=np.int64)
+    E = np.zeros((m, n))
+    T = np.zeros((m, n))
+    S = np.zeros((m, G))
+    Z = np.zeros((m, G))
+    TZ = np.zeros((m, G))
+    maxq = maxq_of(bits)
+
+    def take_params(p: int, g_idx: int, vals: np.ndarray):
+        s, z = quant_params(vals, bits)
+        S[:, g_idx], Z[:, g_idx] = s, z
+        lo = np.minimum(vals.min(axis=1), 0.0)
+        TZ[:, g_idx] = -lo / s
+
+    if group <= 0:
+        take_params(0, 0, V)
+    for i in range(0, n, B):
+        i2 = min(i + B, n)
+        for p in range(i, i2):
+            if group > 0 and p % group == 0:
+                take_params(p, p // group, V[:, p:min(p + group, n)])
+            gi = 0 if group <= 0 else p // group
+            s, z = S[:, gi], Z[:, gi]
+            T[:, p] = V[:, p] / s
+            q[:, p] = np.clip(np.rint(T[:, p]) + z, 0, maxq).astype(np.int64)
+            what = s * (q[:, p] - z)
+            e = (V[:, p] - what) / U[p, p]
+            E[:, p] = e
+            end = n if block is None else i2
+            V[:, p + 1:end] -= np.outer(e, U[p, p + 1:end])
+        if block is not None and i2 < n:
+            V[:, i2:] -= E[:, i:i2] @ U[i:i2, i2:]
+    gidx = np.zeros(n, dtype=np.int64) if group <= 0 else np.arange(n) // group
+    What = S[:, gidx] * (q - Z[:, gidx])
+    return {"q": q, "s": S, "z": Z, "E": E, "What": What, "t": T, "tz": TZ,
+            "err_sq": np.sum(E * E, axis=1)}
+
+
+def obs_step(v_row: np.ndarray, U: np.ndarray, p: int, what_p: float) -> np.ndarray:
+    """One compensation step on a single row: fix column p to what_p and move
+    the later columns by the optimal amount ([OBQ] "Generalized Weight
+    Update"), using row p of U (reading R3/R4).  Returns the new row."""
+    v = np.array(v_row, dtype=np.float64, copy=True)
+    e = (v[p] - what_p) / U[p, p]
+    v[p] = what_p
+    v[p + 1:] -= e * U[p, p + 1:]
+    return v
+
+
+# ----------------------------------------------------------------------------- two slower routes to the same sweep (cross-checks)
+
+def gptq_quantize_obs(W: np.ndarray, Hd: np.ndarray, bits: int, group: int) -> Dict[str, np.ndarray]:
+    """The same fixed-order sweep driven by an explicit inverse Hessian and its
+    rank-one downdate after each column ([OBQ] "The OBS / GPTQ Trick";
+    [GPTQ] "Observation 3": H^-1_{-p} = H^-1 - H^-1_{:,p} H^-1_{p,:} / (H^-1)_pp),
+    with the update delta_rem = delta_p (H^-1)_{p,rem} / (H^-1)_pp.
+    O(n^3); for small n only."""
+    V = np.array(W, dtype=np.float64, copy=True)
+    m, n = V.shape
+    Hinv = np.linalg.inv(np.asarray(Hd, dtype=np.float64))
+    q = np.zeros((m, n), dtype=np.int64)
+    G = n_groups(n, group)
+    S = np.zeros((m, G))
+    Z = np.zeros((m, G))
+    if group <= 0:
+        S[:, 0], Z[:, 0] = quant_params(V, bits)
+    for p in range(n):
+        if group > 0 and p % group == 0:
+            S[:, p // group], Z[:, p // group] = quant_params(V[:, p:p + group], bits)
+        gi = 0 if group <= 0 else p // group
+        q[:, p] = quantize(V[:, p], S[:, gi], Z[:, gi], bits)
+        delta = dequantize(q[:, p], S[:, gi], Z[:, gi]) - V[:, p]     # what_p - w_p
+        V[:, p + 1:] += np.outer(delta, Hinv[p, p + 1:] / Hinv[p, p])
+        V[:, p] += delta
+        Hinv = Hinv - np.outer(Hinv[:, p], Hinv[p, :]) / Hinv[p, p]
+    return {"q": q, "s": S, "z": Z, "V": V}
+
+
+def gptq_quantize_naive(W: np.ndarray, Hd: np.ndarray, bits: int, group: int) -> Dict[str, np.ndarray]:
+    """The same sweep re-inverting the Hessian of the not-yet-quantized
+    columns at every step (the naive procedure of [OBQ] "The OBS / GPTQ
+    Trick").  O(n^4); for tiny n only."""
+    V = np.array(W, dtype=np.float64, copy=True)
+    m, n = V.shape
+    q = np.zeros((m, n), dtype=np.int64)
+    G = n_groups(n, group)
+    S = np.zeros((m, G))
+    Z = np.zeros((m, G))
+    if group <= 0:
+        S[:, 0], Z[:, 0] = quant_params(V, bits)
+    for p in range(n):
+        if group > 0 and p % group == 0:
+            S[:, p // group], Z[:, p // group] = quant_params(V[:, p:p + group], bits)
+        gi = 0 if group <= 0 else p // group
+        q[:, p] = quantize(V[:, p], S[:, gi], Z[:, gi], bits)
+        delta = dequantize(q[:, p], S[:, gi], Z[:, gi]) - V[:, p]
+        Ginv = np.linalg.inv(np.asarray(Hd, dtype=np.float64)[p:, p:])
+        V[:, p + 1:] += np.outer(delta, Ginv[0, 1:] / Ginv[0, 0])
+        V[:, p] += delta
+    return {"q": q, "s": S, "z": Z, "V": V}
+
+
+# ----------------------------------------------------------------------------- comparators and measures
+
+def rtn(W: np.ndarray, bits: int, group: int) -> Dict[str, np.ndarray]:
+    """Round-to-nearest with the same quantizer and parameters taken from the
+    original weights, no compensation ([SOQ] "GPTQ in the method landscape")."""
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    G = n_groups(n, group)
+    S = np.zeros((m, G))
+    Z = np.zeros((m, G))
+    if group <= 0:
+        S[:, 0], Z[:, 0] = quant_params(W, bits)
+    else:
+        for g in range(G):
+            S[:, g], Z[:, g] = quant_params(W[:, g * group:(g + 1) * group], bits)
+    gidx = np.zeros(n, dtype=np.int64) if group <= 0 else np.arange(n) // group
+    q = np.clip(np.rint(W / S[:, gidx]) + Z[:, gidx], 0, maxq_of(bits)).astype(np.int64)
+    return {"q": q, "s": S, "z": Z, "What": S[:, gidx] * (q - Z[:, gidx])}
+
+
+def dequant_from(q: np.ndarray, s: np.ndarray, z: np.ndarray, group: int) -> np.ndarray:
+    n = q.shape[1]
+    gidx = np.zeros(n, dtype=np.int64) if group <= 0 else np.arange(n) // group
+    return np.asarray(s, np.float64)[:, gidx] * (q.astype(np.float64) - np.asarray(z, np.float64)[:, gidx])
+
+
+def layer_loss(W: np.ndarray, What: np.ndarray, H: np.ndarray) -> float:
+    """||W X - What X||_F^2 ([SOQ] "The objective is layer output"), evaluated
+    as 1/2 tr(dW H dW^T) with the undamped H = 2 X X^T."""
+    D = np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)
+    return 0.5 * float(np.sum((D @ np.asarray(H, dtype=np.float64)) * D))
+
+
+def layer_loss_direct(W: np.ndarray, What: np.ndarray, X_tokens: np.ndarray) -> float:
+    """||(W - What) X||_F^2 with X given token-major [tokens x n]."""
+    D = np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)
+    Y = np.asarray(X_tokens, dtype=np.float64) @ D.T
+    return float(np.sum(Y * Y))
+
+
+# ----------------------------------------------------------------------------- packed code layout
+
+def packed_words(n: int, bits: int) -> int:
+    return (n * bits + 31) // 32
+
+
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """Per row, a little-endian bit-stream of b-bit codes: code j occupies bits
+    [j*b, (j+1)*b) counted from bit 0 of the row's first uint32 word; a code
+    may straddle two words."""
+    q = np.asarray(q, dtype=np.uint64)
+    m, n = q.shape
+    W = packed_words(n, bits)
+    acc = np.zeros((m, W + 1), dtype=np.uint64)
+    for j in range(n):
+        bit = j * bits
+        w, off = divmod(bit, 32)
+        acc[:, w] |= (q[:, j] << np.uint64(off))
+    lo = acc & np.uint64(0xFFFFFFFF)
+    carry = acc >> np.uint64(32)
+    lo[:, 1:] |= carry[:, :-1]
+    return lo[:, :W].astype(np.uint32)
+
+
+def unpack_codes(words: np.ndarray, bits: int, n: int) -> np.ndarray:
+    """Inverse of pack_codes: [m x words] uint32 -> [m x n] int64 codes."""
+    words = np.asarray(words, dtype=np.uint64)
+    m = words.shape[0]
+    ext = np.concatenate([words, np.zeros((m, 1), dtype=np.uint64)], axis=1)
+    mask = np.uint64((1 << bits) - 1)
+    out = np.zeros((m, n), dtype=np.int64)
+    for j in range(n):
+        bit = j * bits
+        w, off = divmod(bit, 32)
+        both = ext[:, w] | (ext[:, w + 1] << np.uint64(32))
+        out[:, j] = ((both >> np.uint64(off)) & mask).astype(np.int64)
+    return out
+
+
+# ----------------------------------------------------------------------------- whole layer
+
+def quantize_layer_from_x(W: np.ndarray, x_chunks: Iterable[np.ndarray], bits: int, group: int, block: int,
+                          rel_damp: float = 0.01) -> Dict[str, object]:
+    """The per-layer pipeline of [GPTQ] "Algorithm GPTQ" for one layer:
+    H from X, damping, the inverse factor, then the blocked sweep."""
+    H = hessian(x_chunks)
+    Hd, lam = damp(H, rel_damp)
+    U, info = inverse_cholesky_upper(Hd)
+    if info != 0:
+        raise np.linalg.LinAlgError(f"damped Hessian not positive definite at column {info}")
+    out = gptq_quantize(W, U, bits, group, block)
+    out.update({"H": H, "lam": lam, "U": U})
+    return out
+
+
+def boundary_distance(t: np.ndarray) -> np.ndarray:
+    """Distance (in quantization steps) of a pre-rounding value to the nearest
+    rounding boundary k + 1/2."""
+    return np.abs(t - (np.floor(t) + 0.5))
