@@ -1,0 +1,162 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ layer-quantization library.
+ *
+ * GPTQ quantizes one linear layer at a time with second-order error
+ * compensation.  The three calls below are its three stages:
+ *
+ *   gptq_hessian_accumulate  H += 2 X X^T from calibration activations
+ *   gptq_prepare_hinv        damp H and take the upper Cholesky factor U of
+ *                            the damped inverse
+ *   gptq_quantize_layer      sweep the columns of W in blocks, rounding each
+ *                            column, compensating later columns from the rows
+ *                            of U, and emitting packed codes, scales and zeros
+ *
+ * Sources (web pages describing the method):
+ *   [OBQ]    "Part 2: Adaptive Rounding: Optimal Brain Quantizer (OBQ)"
+ *   [GPTQ]   "Part 3: Adaptive Rounding: GPTQ"
+ *   [SOQ]    the English post on GPTQ second-order quantization
+ *            (hungho77.github.io) and [SOQ-vi], its Vietnamese edition.
+ *
+ * Conventions for every call:
+ *   - Array arguments are DEVICE pointers owned by the caller; the library
+ *     allocates no memory and keeps no state between calls.  Scratch memory
+ *     is passed in as `workspace`, sized by the matching *_workspace_bytes().
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it and return without synchronizing.
+ *   - Matrices are row-major with an explicit leading dimension.
+ *   - Argument errors are detected on the host, before any HIP call, and
+ *     returned synchronously; nothing is enqueued then.  Launch failures
+ *     return GPTQ_ERR_HIP.  Numerical failure of the factorization is
+ *     reported through the device-side `info` word (see gptq_prepare_hinv).
+ *   - Concurrent calls on distinct buffers and workspaces are safe.
+ *   - NaN or Inf inputs give unspecified (but memory-safe) outputs.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = 1,  /* bad size, pointer, dtype, bits, group/block */
+  GPTQ_ERR_UNSUPPORTED = 2,  /* valid request this build cannot run        */
+  GPTQ_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required     */
+  GPTQ_ERR_HIP = 4           /* a HIP launch or runtime call failed         */
+} gptq_status;
+
+typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* gptq_status_string(int32_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t gptq_version(void);
+
+/* ------------------------------------------------------------------------
+ * Stage 1: Hessian accumulation.
+ *
+ * Defines H = 2 X X^T, the Hessian of the layer objective ||WX - What X||^2
+ * ([SOQ] "The objective is layer output, not weight distance"; [OBQ]
+ * "Goal": the input covariance is the proxy Hessian).
+ *
+ *   H        [n x n] float32, row-major, leading dimension n.  In/out:
+ *            H <- H + 2 * sum_t x_t x_t^T over the `tokens` rows of X.
+ *            The caller zeroes H before the first call and may call again
+ *            for further token chunks; both triangles are valid (and exactly
+ *            symmetric) after every call.
+ *   X        [tokens x n] activations, token-major (one token per row),
+ *            leading dimension ldx >= n, element type x_dtype (fp16, bf16 or
+ *            fp32).  Products of fp16/bf16 inputs are exact in fp32; sums
+ *            are fp32 in a fixed order, so results are deterministic.
+ *   tokens   >= 0 (0 is a no-op).
+ *   workspace, ws_bytes: at least gptq_hessian_workspace_bytes(n, tokens).
+ * Errors: n < 1, ldx < n, tokens < 0, NULL H/X (tokens > 0), unknown dtype
+ * -> GPTQ_ERR_INVALID_ARG; short workspace -> GPTQ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens);
+gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int32_t x_dtype,
+                                    int64_t tokens, int64_t ldx,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 2+3: damping and the inverse-Hessian factor.
+ *
+ * lambda = damp * mean(diag H) ([SOQ] "3. Cholesky reformulation": about one
+ * percent of the average Hessian diagonal; [GPTQ] "Algorithm GPTQ":
+ * H + lambda I), then U upper-triangular with (H + lambda I)^{-1} = U^T U
+ * ([GPTQ] "Observation 3: The Cholesky Reformulation": factor the inverse
+ * once and read its rows; [SOQ-vi] writes the flush with rows R[B, B:] of
+ * this upper factor).
+ *
+ *   H          [n x n] float32 symmetric (both triangles read), leading
+ *              dimension n.  Not modified unless U == H (in-place allowed).
+ *   damp       relative damping (>= 0), 0.01 for the usual one percent.
+ *   U          [n x n] float32 out, leading dimension n; strictly lower part
+ *              written as 0.
+ *   info       device int32 out: 0 on success; k > 0 if H + lambda I is not
+ *              positive definite (numerically), k being the 1-based column
+ *              at which the factorization (which runs from the last column
+ *              towards the first) broke down.  U is undefined when k > 0.
+ *   lambda_out device float32 out: the lambda used.
+ *   workspace, ws_bytes: at least gptq_prepare_workspace_bytes(n).
+ * Errors: n < 1, damp < 0 or not finite, NULL pointers ->
+ * GPTQ_ERR_INVALID_ARG; short workspace -> GPTQ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t gptq_prepare_workspace_bytes(int64_t n);
+gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp, float* U,
+                              int32_t* info, float* lambda_out,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 4: the blocked column sweep with lazy trailing updates.
+ *
+ * [GPTQ] "Algorithm GPTQ" and "Observation 2: Lazy Batch Updates";
+ * [SOQ-vi] "Lazy batch update".  Columns are swept left to right
+ * ([GPTQ] "Observation 1").  For each column p, all rows at once:
+ *   at the first column of a group: s, z from the current values of the
+ *     group: x_lo = min(0, min), x_hi = max(0, max) (x_hi = 1 if both are 0),
+ *     s = (x_hi - x_lo)/maxq, z = rint(-x_lo/s), maxq = 2^bits - 1;
+ *     per-row mode takes them once from the original row;
+ *   q = clamp(rint(v/s) + z, 0, maxq), what = s (q - z);
+ *   e = (v - what)/U[p][p];  later columns of the block v_j -= e U[p][j];
+ * and after each block [i, i2): V[:, i2:] -= E U[i:i2, i2:] (one GEMM).
+ *
+ *   W          [m x n] weights, leading dimension ldw >= n, type w_dtype.
+ *              Read; if write_dequant != 0, overwritten by what = s(q - z)
+ *              (rounded to w_dtype).
+ *   U          [n x n] float32 from gptq_prepare_hinv (only the upper
+ *              triangle is read), leading dimension n.
+ *   bits       2..8.
+ *   group_size <= 0: one (s, z) per row; else g >= 1 with
+ *              g % block_size == 0 or block_size % g == 0.
+ *   block_size 1..128 (B).  Results do not depend on B except through the
+ *              order of floating-point sums.
+ *   qcodes     [m x ceil(n*bits/32)] uint32 out: per row a little-endian
+ *              bit-stream, code j at bits [j*bits, (j+1)*bits) from bit 0 of
+ *              the row's first word (a code may straddle two words; unused
+ *              high bits of the last word are 0).
+ *   scales     [m x G] float32 out, zeros [m x G] int32 out, G = 1 per-row,
+ *              else ceil(n / group_size).
+ *   err_sq     optional [m] float32 out (NULL to skip): sum_p e_p^2 per row.
+ *   workspace, ws_bytes: at least gptq_quantize_workspace_bytes(m, n).
+ * Errors: m < 1, n < 1, ldw < n, bits outside 2..8, block_size outside
+ * 1..128, group/block not nesting, NULL required pointers, unknown dtype ->
+ * GPTQ_ERR_INVALID_ARG; short workspace -> GPTQ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n);
+gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, int64_t ldw,
+                                const float* U, int32_t bits, int64_t group_size,
+                                int64_t block_size, uint32_t* qcodes, float* scales,
+                                int32_t* zeros, float* err_sq, int32_t write_dequant,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

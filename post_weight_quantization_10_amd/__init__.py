@@ -1,0 +1,208 @@
+"""GPTQ layer-wise second-order weight quantization on AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libgptq_mi355x.so`` (C ABI in include/gptq.h).
+The functions below only marshal arguments: every stage runs in the
+library's HIP kernels.  PyTorch supplies device memory (outputs and
+workspaces) and the current HIP stream.  If the shared library is missing the
+import of the binding raises; there is no fallback path.
+
+Stages (same names as the C ABI):
+    hessian_accumulate(H, X)                    H += 2 X^T X   (X token-major)
+    prepare_hinv(H, damp)                       -> U, lambda, info
+    quantize_layer(W, U, bits, group, block)    -> packed codes, scales, zeros
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgptq_mi355x.so")
+
+GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_UNSUPPORTED, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP = range(5)
+F16, BF16, F32 = 0, 1, 2
+_DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+
+_lib = None
+
+
+class GPTQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run post_weight_quantization_10_amd.build.build() "
+                          "(hipcc, --offload-arch=gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, sz, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    f32 = ctypes.c_float
+    L.gptq_status_string.argtypes = [i32]
+    L.gptq_status_string.restype = ctypes.c_char_p
+    L.gptq_version.argtypes = []
+    L.gptq_version.restype = i32
+    L.gptq_hessian_workspace_bytes.argtypes = [i64, i64]
+    L.gptq_hessian_workspace_bytes.restype = sz
+    L.gptq_hessian_accumulate.argtypes = [vp, i64, vp, i32, i64, i64, vp, sz, vp]
+    L.gptq_hessian_accumulate.restype = i32
+    L.gptq_prepare_workspace_bytes.argtypes = [i64]
+    L.gptq_prepare_workspace_bytes.restype = sz
+    L.gptq_prepare_hinv.argtypes = [vp, i64, f32, vp, vp, vp, vp, sz, vp]
+    L.gptq_prepare_hinv.restype = i32
+    L.gptq_quantize_workspace_bytes.argtypes = [i64, i64]
+    L.gptq_quantize_workspace_bytes.restype = sz
+    L.gptq_quantize_layer.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.gptq_quantize_layer.restype = i32
+    _lib = L
+    return L
+
+
+def lib() -> ctypes.CDLL:
+    return _load()
+
+
+def status_string(status: int) -> str:
+    return _load().gptq_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(_load().gptq_version())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(fn: str, st: int) -> None:
+    if st != GPTQ_OK:
+        raise GPTQError(fn, st)
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _workspace(nbytes: int, dev: torch.device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
+# ----------------------------------------------------------------------------- workspace sizes
+
+def hessian_workspace_bytes(n: int, tokens: int) -> int:
+    return int(_load().gptq_hessian_workspace_bytes(int(n), int(tokens)))
+
+
+def prepare_workspace_bytes(n: int) -> int:
+    return int(_load().gptq_prepare_workspace_bytes(int(n)))
+
+
+def quantize_workspace_bytes(m: int, n: int) -> int:
+    return int(_load().gptq_quantize_workspace_bytes(int(m), int(n)))
+
+
+# ----------------------------------------------------------------------------- the three stages
+
+def hessian_accumulate(H: torch.Tensor, X: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """H += 2 * X^T X for token-major activations X [tokens x n] (fp16, bf16 or
+    fp32, rows may be strided).  H is [n x n] float32 contiguous; returns H."""
+    _require(H.is_cuda and X.is_cuda and H.device == X.device, "H and X must be on the same GPU")
+    _require(H.dtype == torch.float32 and H.dim() == 2 and H.shape[0] == H.shape[1] and H.is_contiguous(),
+             "H must be a contiguous float32 [n, n] tensor")
+    _require(X.dim() == 2 and X.shape[1] == H.shape[0] and X.stride(1) == 1, "X must be [tokens, n] with unit column stride")
+    _require(X.dtype in _DT, f"unsupported activation dtype {X.dtype}")
+    n, T = H.shape[0], X.shape[0]
+    need = hessian_workspace_bytes(n, T)
+    ws = workspace if workspace is not None else _workspace(need, H.device)
+    st = _load().gptq_hessian_accumulate(H.data_ptr(), n, X.data_ptr() if T else None, _DT[X.dtype], T,
+                                         max(X.stride(0), n), ws.data_ptr(), ws.numel(), _stream(H.device))
+    _check("gptq_hessian_accumulate", st)
+    return H
+
+
+def prepare_hinv(H: torch.Tensor, damp: float = 0.01, U: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """U upper with (H + lambda I)^-1 = U^T U, lambda = damp * mean(diag H).
+    Returns (U, lambda [1] float32, info [1] int32) as device tensors; read
+    info after a synchronize (0 = success)."""
+    _require(H.is_cuda and H.dtype == torch.float32 and H.dim() == 2 and H.shape[0] == H.shape[1]
+             and H.is_contiguous(), "H must be a contiguous float32 [n, n] CUDA tensor")
+    n = H.shape[0]
+    if U is None:
+        U = torch.empty_like(H)
+    _require(U.shape == H.shape and U.dtype == torch.float32 and U.is_contiguous() and U.device == H.device,
+             "U must match H")
+    lam = torch.empty(1, dtype=torch.float32, device=H.device)
+    info = torch.empty(1, dtype=torch.int32, device=H.device)
+    ws = workspace if workspace is not None else _workspace(prepare_workspace_bytes(n), H.device)
+    st = _load().gptq_prepare_hinv(H.data_ptr(), n, float(damp), U.data_ptr(), info.data_ptr(), lam.data_ptr(),
+                                   ws.data_ptr(), ws.numel(), _stream(H.device))
+    _check("gptq_prepare_hinv", st)
+    return U, lam, info
+
+
+def n_groups(n: int, group_size: int) -> int:
+    return 1 if group_size <= 0 else (n + group_size - 1) // group_size
+
+
+def packed_words(n: int, bits: int) -> int:
+    return (n * bits + 31) // 32
+
+
+def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, group_size: int, block_size: int = 128,
+                   write_dequant: bool = True, err_sq: bool = True,
+                   workspace: Optional[torch.Tensor] = None,
+                   out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """Blocked GPTQ sweep of W [m x n] (fp16 / bf16 / fp32, row stride >= n)
+    against the factor U.  Returns {'qcodes' [m x words] int32 (uint32 bit
+    patterns), 'scales' [m x G] float32, 'zeros' [m x G] int32, 'err_sq' [m]}.
+    With write_dequant, W is overwritten in place by s (q - z)."""
+    _require(W.is_cuda and U.is_cuda and W.device == U.device, "W and U must be on the same GPU")
+    _require(W.dim() == 2 and W.stride(1) == 1 and W.dtype in _DT, "W must be [m, n] fp16/bf16/fp32, unit column stride")
+    m, n = W.shape
+    _require(U.shape == (n, n) and U.dtype == torch.float32 and U.is_contiguous(), "U must be contiguous float32 [n, n]")
+    G = n_groups(n, group_size)
+    dev = W.device
+    o = dict(out or {})
+    if "qcodes" not in o:
+        o["qcodes"] = torch.empty((m, packed_words(n, bits)), dtype=torch.int32, device=dev)
+    if "scales" not in o:
+        o["scales"] = torch.empty((m, G), dtype=torch.float32, device=dev)
+    if "zeros" not in o:
+        o["zeros"] = torch.empty((m, G), dtype=torch.int32, device=dev)
+    if err_sq and "err_sq" not in o:
+        o["err_sq"] = torch.empty((m,), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else _workspace(quantize_workspace_bytes(m, n), dev)
+    st = _load().gptq_quantize_layer(W.data_ptr(), _DT[W.dtype], m, n, max(W.stride(0), n), U.data_ptr(), int(bits),
+                                     int(group_size), int(block_size), o["qcodes"].data_ptr(), o["scales"].data_ptr(),
+                                     o["zeros"].data_ptr(), _ptr(o.get("err_sq")) if err_sq else None,
+                                     1 if write_dequant else 0, ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("gptq_quantize_layer", st)
+    return o
+
+
+def gptq_layer(W: torch.Tensor, X: torch.Tensor, bits: int, group_size: int, block_size: int = 128,
+               damp: float = 0.01, write_dequant: bool = True) -> Dict[str, torch.Tensor]:
+    """All three stages for one layer: H from X, the damped inverse factor,
+    then the sweep.  Raises if the damped Hessian is not positive definite."""
+    n = W.shape[1]
+    H = torch.zeros((n, n), dtype=torch.float32, device=W.device)
+    hessian_accumulate(H, X)
+    U, lam, info = prepare_hinv(H, damp)
+    res = quantize_layer(W, U, bits, group_size, block_size, write_dequant=write_dequant)
+    if int(info.item()) != 0:
+        raise GPTQError("gptq_prepare_hinv (damped Hessian not positive definite)", GPTQ_ERR_INVALID_ARG)
+    res.update({"H": H, "U": U, "lambda": lam, "info": info})
+    return res

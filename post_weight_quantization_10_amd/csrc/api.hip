@@ -1,0 +1,90 @@
+// C ABI of the library: argument validation on the host, then the launch
+// sequences of the three GPTQ stages (declared in include/gptq.h).
+#include <cmath>
+
+#include "../../include/gptq.h"
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace gptq {
+size_t syrk_workspace_bytes(int64_t n, int64_t tokens, int dtype);
+hipError_t syrk_accumulate(float* H, int64_t n, const void* X, int dtype, int64_t tokens, int64_t ldx, void* ws,
+                           hipStream_t stream);
+size_t prepare_workspace_bytes(int64_t n);
+hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t* info, float* lambda_out, void* ws,
+                        hipStream_t s);
+size_t quantize_workspace_bytes(int64_t m, int64_t n);
+hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, const float* U, int bits, int64_t group,
+                          int64_t B, uint32_t* qcodes, float* S, int32_t* Z, float* err_sq, int write_dequant,
+                          void* ws, hipStream_t st);
+}  // namespace gptq
+
+namespace {
+constexpr int64_t kMaxDim = 65535;  // grid-dimension limit of the per-row launches
+inline bool dtype_ok(int32_t d) { return d == GPTQ_F16 || d == GPTQ_BF16 || d == GPTQ_F32; }
+}  // namespace
+
+extern "C" {
+
+const char* gptq_status_string(int32_t s) {
+  switch (s) {
+    case GPTQ_OK: return "GPTQ_OK";
+    case GPTQ_ERR_INVALID_ARG: return "GPTQ_ERR_INVALID_ARG";
+    case GPTQ_ERR_UNSUPPORTED: return "GPTQ_ERR_UNSUPPORTED";
+    case GPTQ_ERR_WORKSPACE: return "GPTQ_ERR_WORKSPACE";
+    case GPTQ_ERR_HIP: return "GPTQ_ERR_HIP";
+    default: return "GPTQ_UNKNOWN_STATUS";
+  }
+}
+
+int32_t gptq_version(void) { return 100; }
+
+size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens) {
+  // the fp32 path stages fewer tokens per step and may use more splits
+  const size_t a = gptq::syrk_workspace_bytes(n, tokens, GPTQ_F16);
+  const size_t b = gptq::syrk_workspace_bytes(n, tokens, GPTQ_F32);
+  return a > b ? a : b;
+}
+
+gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  if (n < 1 || n > kMaxDim || tokens < 0 || ldx < n || !dtype_ok(x_dtype) || H == nullptr) return GPTQ_ERR_INVALID_ARG;
+  if (tokens == 0) return GPTQ_OK;
+  if (X == nullptr) return GPTQ_ERR_INVALID_ARG;
+  const size_t need = gptq::syrk_workspace_bytes(n, tokens, x_dtype);
+  if (workspace == nullptr || ws_bytes < need) return GPTQ_ERR_WORKSPACE;
+  hipError_t e = gptq::syrk_accumulate(H, n, X, x_dtype, tokens, ldx, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+}
+
+size_t gptq_prepare_workspace_bytes(int64_t n) { return gptq::prepare_workspace_bytes(n); }
+
+gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t* info, float* lambda_out,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (n < 1 || n > kMaxDim || !(damp >= 0.f) || !std::isfinite(damp) || H == nullptr || U == nullptr ||
+      info == nullptr || lambda_out == nullptr)
+    return GPTQ_ERR_INVALID_ARG;
+  if (workspace == nullptr || ws_bytes < gptq::prepare_workspace_bytes(n)) return GPTQ_ERR_WORKSPACE;
+  hipError_t e = gptq::prepare_hinv(H, n, damp, U, info, lambda_out, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+}
+
+size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n) { return gptq::quantize_workspace_bytes(m, n); }
+
+gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, int64_t ldw, const float* U,
+                                int32_t bits, int64_t group_size, int64_t block_size, uint32_t* qcodes, float* scales,
+                                int32_t* zeros, float* err_sq, int32_t write_dequant, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  if (m < 1 || n < 1 || n > kMaxDim || ldw < n || !dtype_ok(w_dtype) || bits < 2 || bits > 8 || block_size < 1 ||
+      block_size > 128)
+    return GPTQ_ERR_INVALID_ARG;
+  if (group_size > 0 && !(group_size % block_size == 0 || block_size % group_size == 0)) return GPTQ_ERR_INVALID_ARG;
+  if (W == nullptr || U == nullptr || qcodes == nullptr || scales == nullptr || zeros == nullptr)
+    return GPTQ_ERR_INVALID_ARG;
+  if (workspace == nullptr || ws_bytes < gptq::quantize_workspace_bytes(m, n)) return GPTQ_ERR_WORKSPACE;
+  hipError_t e = gptq::quantize_layer(W, w_dtype, m, n, ldw, U, bits, group_size, block_size, qcodes, scales, zeros,
+                                      err_sq, write_dequant, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+}
+
+}  // extern "C"

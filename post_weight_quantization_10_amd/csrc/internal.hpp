@@ -1,0 +1,34 @@
+// Internal launchers shared between the HIP translation units of the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptq {
+
+// Flags for gemm_f32.
+enum : int {
+  GEMM_LOWER_TILES = 1,  // C square; only 128x128 tiles on or below the diagonal are computed
+  GEMM_A_LOWER = 2,      // op(A)[i][k] == 0 for k > i (skip those K chunks)
+  GEMM_B_LOWER = 4,      // op(B)[k][j] == 0 for k < j (skip those K chunks)
+};
+
+struct GemmDesc {
+  const float* A;
+  const float* B;
+  float* C;
+  int64_t lda, ldb, ldc;
+  int64_t strideA, strideB, strideC;  // per batch entry (blockIdx.z)
+  int M, N, K, batch;
+  float alpha, beta;
+  int flags;
+  const int32_t* info;  // if non-null and *info != 0 the kernel does nothing
+};
+
+// C = alpha * op(A) * op(B) + beta * C in fp32 on the MFMA pipe.
+// op(A) is M x K: A[i*lda + k] (transA = false) or A[k*lda + i] (true).
+// op(B) is K x N: B[k*ldb + j] (transB = false) or B[j*ldb + k] (true).
+// beta == 0 never reads C.  C may alias A only when N <= 128 (each tile row
+// then reads all of its A rows before writing them).
+hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s);
+
+}  // namespace gptq

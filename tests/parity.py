@@ -1,0 +1,85 @@
+"""Comparison helpers between GPU outputs and the fp64 oracle.
+
+Tolerances:
+  * H: ||H_gpu - H_oracle||_F / ||H_oracle||_F <= 1e-5.
+  * Codes: bit-exact, except that a row's first mismatch must sit where the
+    oracle's pre-rounding value (v/s, or the zero point -x_lo/s of that
+    column's group) lies within 1e-4 of a rounding boundary; after such a
+    near-tie a row may legitimately diverge (every later value in the row
+    depends on it), and overall >= 99.9 % of codes must be identical.
+  * Scales: relative 1e-5 on every group that starts at or before the row's
+    first code mismatch.
+  * Layer loss ||(W - What) X||^2 (one fp64 evaluator for both sides): within
+    1e-3 relative.
+"""
+from __future__ import annotations
+
+import sys
+from typing import Dict
+
+import numpy as np
+
+import oracle as O
+
+H_RTOL = 1e-5
+TIE = 1e-4
+SAME_FRAC = 0.999
+SCALE_RTOL = 1e-5
+LOSS_RTOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def h_rel_err(H_gpu: np.ndarray, H_ref: np.ndarray) -> float:
+    return float(np.linalg.norm(H_gpu.astype(np.float64) - H_ref) / np.linalg.norm(H_ref))
+
+
+def group_index(n: int, group: int) -> np.ndarray:
+    return np.zeros(n, dtype=np.int64) if group <= 0 else np.arange(n) // group
+
+
+def compare_codes(q_gpu: np.ndarray, s_gpu: np.ndarray, z_gpu: np.ndarray, ref: Dict[str, np.ndarray],
+                  group: int) -> Dict[str, float]:
+    q_o, t, tz = ref["q"], ref["t"], ref["tz"]
+    m, n = q_o.shape
+    gidx = group_index(n, group)
+    mism = q_gpu != q_o
+    rows = np.where(mism.any(axis=1))[0]
+    first = np.full(m, n, dtype=np.int64)
+    unexcused = []
+    for r in rows:
+        p = int(np.argmax(mism[r]))
+        first[r] = p
+        near = O.boundary_distance(np.array([t[r, p]]))[0] < TIE or \
+            O.boundary_distance(np.array([tz[r, gidx[p]]]))[0] < TIE
+        if not near:
+            unexcused.append((int(r), p, float(t[r, p]), int(q_gpu[r, p]), int(q_o[r, p])))
+    # scales of groups starting at or before the first mismatch
+    G = s_gpu.shape[1]
+    gstart = np.zeros(G, dtype=np.int64) if group <= 0 else np.arange(G) * group
+    ok_mask = gstart[None, :] <= first[:, None]
+    srel = np.abs(s_gpu.astype(np.float64) - ref["s"]) / np.abs(ref["s"])
+    zdiff = (z_gpu.astype(np.int64) != ref["z"].astype(np.int64))
+    return {
+        "same_frac": 1.0 - float(mism.mean()),
+        "rows_diverged": int(len(rows)),
+        "unexcused": unexcused,
+        "scale_rel_max": float(srel[ok_mask].max()) if ok_mask.any() else 0.0,
+        "zero_mismatch": int(zdiff[ok_mask].sum()),
+    }
+
+
+def assert_codes(rep: Dict[str, float], label: str = "") -> None:
+    assert not rep["unexcused"], f"{label}: first mismatch not at a near-tie: {rep['unexcused'][:5]}"
+    assert rep["same_frac"] >= SAME_FRAC, f"{label}: only {rep['same_frac']:.5f} of codes identical"
+    assert rep["scale_rel_max"] <= SCALE_RTOL, f"{label}: scale rel err {rep['scale_rel_max']:.3e}"
+
+
+def loss_rel(W: np.ndarray, H: np.ndarray, q_gpu, s_gpu, z_gpu, ref, group) -> float:
+    Wh_gpu = O.dequant_from(q_gpu, s_gpu, z_gpu, group)
+    l_gpu = O.layer_loss(W, Wh_gpu, H)
+    l_ora = O.layer_loss(W, ref["What"], H)
+    return abs(l_gpu - l_ora) / l_ora
