@@ -1,0 +1,187 @@
+"""Benchmark: one GPTQ layer (H from calibration tokens, damping, inverse
+factor, blocked sweep) on one MI355X.
+
+Default workload: the attention-projection layer (W 4096x4096 fp16 with 0.1 %
+outliers x10; X = 262144 tokens x 4096 fp16, lognormal channel scales, 8
+outlier channels x20; 4-bit, group 128, block 128, damp 0.01), inputs drawn by
+synth/ and resident in HBM before timing.  A step is the whole path:
+restore W, zero H, gptq_hessian_accumulate, gptq_prepare_hinv,
+gptq_quantize_layer (with the dequantized weights written back).
+
+Prints one JSON line (rank 0).  Multi-GPU runs are not supported.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TF16 = 2500.0     # MI355X dense fp16 MFMA, TFLOP/s
+PEAK_TF32 = 157.3      # MI355X fp32 MFMA, TFLOP/s
+PEAK_HBM = 8000.0      # GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="attn", choices=["attn", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_attn_4096x262144_traffic.json"),
+                    help="JSON with rocprofv3 FETCH/WRITE bytes per SYRK launch (optional)")
+    return ap.parse_args()
+
+
+def cpu_baseline(W16, X16, job, U_gpu):
+    """The fp64 oracle timed on a bounded sample of the same layer, scaled to
+    one full layer: H over 8 of the 128 token chunks (x16), the inverse factor
+    at full size (x1), the sweep over 256 of the 4096 rows (x16)."""
+    import numpy as np
+
+    import oracle as O
+    T = X16.shape[0]
+    n = W16.shape[1]
+    m = W16.shape[0]
+    tok = min(T, 8 * 2048)
+    rows = min(m, 256)
+    t0 = time.perf_counter()
+    H = O.hessian([X16[c:c + 2048] for c in range(0, tok, 2048)])
+    t1 = time.perf_counter()
+    Hd, _ = O.damp(H * (T / tok), job.damp)
+    U, info = O.inverse_cholesky_upper(Hd)
+    t2 = time.perf_counter()
+    Ug = U_gpu.astype(np.float64)
+    O.gptq_quantize(W16[:rows].astype(np.float64), Ug, job.bits, job.group, job.block)
+    t3 = time.perf_counter()
+    est = (t1 - t0) * (T / tok) + (t2 - t1) + (t3 - t2) * (m / rows)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(est * 1e3, 1), "unit": "ms per layer (estimated from the sample)", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle: Hessian over {tok} of {T} tokens (x{T // tok}), full {n}x{n} inverse factor, "
+                      f"sweep of {rows} of {m} rows (x{m // rows}); stage seconds "
+                      f"{t1 - t0:.2f}/{t2 - t1:.2f}/{t3 - t2:.2f}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the quantizer's data-parallel path here is a single-GPU build "
+              "(multi-GPU sharding is a design note, not implemented)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_10_amd as pw
+    import synth
+
+    dev = torch.device("cuda:0")
+    wl = synth.workloads()[args.workload]
+    job = wl.jobs[0]
+    t_gen = time.perf_counter()
+    W_np = synth.stacked_weight(job, wl.seed, wl.wid)
+    X_np = synth.x_full(job.x, wl.seed, wl.wid)
+    t_gen = time.perf_counter() - t_gen
+    m, n = W_np.shape
+    T = X_np.shape[0]
+    W0 = torch.from_numpy(W_np).to(dev)
+    X = torch.from_numpy(X_np).to(dev)
+    Wk = W0.clone()
+    H = torch.zeros((n, n), dtype=torch.float32, device=dev)
+    U = torch.empty_like(H)
+    hws = torch.empty(max(pw.hessian_workspace_bytes(n, T), 1), dtype=torch.uint8, device=dev)
+    pws = torch.empty(pw.prepare_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    qws = torch.empty(pw.quantize_workspace_bytes(m, n), dtype=torch.uint8, device=dev)
+    out = {
+        "qcodes": torch.empty((m, pw.packed_words(n, job.bits)), dtype=torch.int32, device=dev),
+        "scales": torch.empty((m, pw.n_groups(n, job.group)), dtype=torch.float32, device=dev),
+        "zeros": torch.empty((m, pw.n_groups(n, job.group)), dtype=torch.int32, device=dev),
+        "err_sq": torch.empty((m,), dtype=torch.float32, device=dev),
+    }
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    phase = {"hessian": [], "prepare": [], "quantize": []}
+    info_t = None
+
+    def step(record: bool):
+        nonlocal info_t
+        Wk.copy_(W0)
+        H.zero_()
+        ev[0].record()
+        pw.hessian_accumulate(H, X, workspace=hws)
+        ev[1].record()
+        _, _, info_t = pw.prepare_hinv(H, job.damp, U=U, workspace=pws)
+        ev[2].record()
+        pw.quantize_layer(Wk, U, job.bits, job.group, job.block, write_dequant=True, workspace=qws, out=out)
+        ev[3].record()
+        if record:
+            torch.cuda.synchronize()
+            phase["hessian"].append(ev[0].elapsed_time(ev[1]))
+            phase["prepare"].append(ev[1].elapsed_time(ev[2]))
+            phase["quantize"].append(ev[2].elapsed_time(ev[3]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"# inputs generated in {t_gen:.1f}s; warmup done", file=sys.stderr, flush=True)
+    # timed region: exactly K steps, synchronized on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # per-phase HIP-event timings over K further steps (same stream as the kernels)
+    for _ in range(args.steps):
+        step(True)
+    assert int(info_t.item()) == 0, "damped Hessian not positive definite"
+    ph = {k: float(np.mean(v)) for k, v in phase.items()}
+
+    flops_syrk = float(n) * (n + 1) * T
+    achieved = flops_syrk / (ph["hessian"] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+    res = {
+        "metric": "ms per 4096x4096 4-bit g128 GPTQ layer (incl. H^-1) + % MFMA/HBM roofline",
+        "value": round(ms_step, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 MFMA (H) / fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: W {m}x{n} {job.weights[0].dtype}, X {T} tokens x {n} {job.x.dtype}, "
+                        f"{job.bits}-bit, group {job.group}, block {job.block}, damp {job.damp}",
+            "tokens": T, "m": m, "n": n, "bits": job.bits, "group": job.group, "block": job.block,
+            "parallelism": "single GPU",
+        },
+        "phases_ms": {k: round(v, 4) for k, v in ph.items()},
+        "ms_layer_incl_hinv": round(ph["prepare"] + ph["quantize"], 4),
+        "roofline": {
+            "kernel": "gptq_hessian_accumulate (MFMA fp16 SYRK, H += 2 X^T X)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TF16,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TF16, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(W_np, X_np, job, U.cpu().numpy())
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -82,4 +82,7 @@ def loss_rel(W: np.ndarray, H: np.ndarray, q_gpu, s_gpu, z_gpu, ref, group) -> f
     Wh_gpu = O.dequant_from(q_gpu, s_gpu, z_gpu, group)
     l_gpu = O.layer_loss(W, Wh_gpu, H)
     l_ora = O.layer_loss(W, ref["What"], H)
+    if l_ora == 0.0:  # exactly representable weights: both sides must be (numerically) lossless
+        scale = float(np.sum((np.asarray(W, np.float64) @ H) * W)) or 1.0
+        return abs(l_gpu) / scale
     return abs(l_gpu - l_ora) / l_ora
