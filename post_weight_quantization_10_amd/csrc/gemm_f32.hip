@@ -7,7 +7,8 @@
 // The sweep's compensation must stay fp32-accurate, so no 16-bit operands.
 //
 // Tile: 128x128 per workgroup of 256 threads (4 wave64s, each 64x64 = 2x2
-// MFMA 32x32 blocks), K staged through LDS 16 at a time, double-buffered.
+// MFMA 32x32 blocks), K staged through LDS 32 at a time, double-buffered,
+// 16-byte global loads where aligned; two workgroups per CU.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -15,14 +16,68 @@ namespace gptq {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16, PAD = 4;
+constexpr int BM = 128, BN = 128, BK = 32, PAD = 4;
 constexpr int LDT = BM + PAD;  // LDS row pitch (floats); BM == BN
 
-template <bool TRANS_A, bool TRANS_B>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d) {
+// Load a BK x 128 slab of op(X) into registers.  ALONG_K: X[i*ld + k] (k
+// contiguous, the tile is stored transposed into LDS); else X[k*ld + i].
+// Each thread moves 4 float4 groups; VEC uses 16-byte loads where the group
+// lies fully in bounds.
+template <bool ALONG_K, bool VEC>
+__device__ __forceinline__ void load_slab(const float* __restrict__ X, int64_t ld, int i0, int iEnd, int k0, int kEnd,
+                                          int tid, f32x4 (&r)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int i, k;
+    if (ALONG_K) { k = (tid & 7) * 4; i = (tid >> 3) + 32 * u; }
+    else { i = (tid & 31) * 4; k = (tid >> 5) + 8 * u; }
+    const int gi = i0 + i, gk = k0 + k;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (ALONG_K) {
+      const float* p = X + (int64_t)gi * ld + gk;
+      if (gi < iEnd) {
+        if (VEC && gk + 3 < kEnd) v = *(const f32x4*)p;
+        else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (gk + e < kEnd) ? p[e] : 0.f;
+        }
+      }
+    } else {
+      const float* p = X + (int64_t)gk * ld + gi;
+      if (gk < kEnd) {
+        if (VEC && gi + 3 < iEnd) v = *(const f32x4*)p;
+        else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (gi + e < iEnd) ? p[e] : 0.f;
+        }
+      }
+    }
+    r[u] = v;
+  }
+}
+
+template <bool ALONG_K>
+__device__ __forceinline__ void store_slab(float (*T)[LDT], int tid, const f32x4 (&r)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (ALONG_K) {
+      const int k = (tid & 7) * 4, i = (tid >> 3) + 32 * u;
+      T[k + 0][i] = r[u][0];
+      T[k + 1][i] = r[u][1];
+      T[k + 2][i] = r[u][2];
+      T[k + 3][i] = r[u][3];
+    } else {
+      const int i = (tid & 31) * 4, k = (tid >> 5) + 8 * u;
+      *(f32x4*)&T[k][i] = r[u];
+    }
+  }
+}
+
+template <bool TRANS_A, bool TRANS_B, bool VEC>
+__global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmDesc d) {
   if (d.info && *d.info != 0) return;
-  __shared__ float As[2][BK][LDT];
-  __shared__ float Bs[2][BK][LDT];
+  __shared__ __attribute__((aligned(16))) float As[2][BK][LDT];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BK][LDT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -60,50 +115,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
-  float ra[8], rb[8];
-
-  // global -> registers for the chunk starting at k0
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (TRANS_A) {  // A[k][i]: contiguous along i
-        const int i = tid & 127, kk = (tid >> 7) + 2 * u;
-        const int gi = r0 + i, gk = k0 + kk;
-        ra[u] = (gi < d.M && gk < kHi) ? A[(int64_t)gk * d.lda + gi] : 0.f;
-      } else {  // A[i][k]: contiguous along k
-        const int kk = tid & 15, i = (tid >> 4) + 16 * u;
-        const int gi = r0 + i, gk = k0 + kk;
-        ra[u] = (gi < d.M && gk < kHi) ? A[(int64_t)gi * d.lda + gk] : 0.f;
-      }
-      if (!TRANS_B) {  // B[k][j]: contiguous along j
-        const int j = tid & 127, kk = (tid >> 7) + 2 * u;
-        const int gj = c0 + j, gk = k0 + kk;
-        rb[u] = (gj < d.N && gk < kHi) ? B[(int64_t)gk * d.ldb + gj] : 0.f;
-      } else {  // B[j][k]: contiguous along k
-        const int kk = tid & 15, j = (tid >> 4) + 16 * u;
-        const int gj = c0 + j, gk = k0 + kk;
-        rb[u] = (gj < d.N && gk < kHi) ? B[(int64_t)gj * d.ldb + gk] : 0.f;
-      }
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (TRANS_A) As[buf][(tid >> 7) + 2 * u][tid & 127] = ra[u];
-      else As[buf][tid & 15][(tid >> 4) + 16 * u] = ra[u];
-      if (!TRANS_B) Bs[buf][(tid >> 7) + 2 * u][tid & 127] = rb[u];
-      else Bs[buf][tid & 15][(tid >> 4) + 16 * u] = rb[u];
-    }
-  };
-
+  f32x4 ra[4], rb[4];
   if (kLo < kHi) {
-    load(kLo);
-    store(0);
+    load_slab<!TRANS_A, VEC>(A, d.lda, r0, d.M, kLo, kHi, tid, ra);
+    load_slab<TRANS_B, VEC>(B, d.ldb, c0, d.N, kLo, kHi, tid, rb);
+    store_slab<!TRANS_A>(As[0], tid, ra);
+    store_slab<TRANS_B>(Bs[0], tid, rb);
     __syncthreads();
     int buf = 0;
     for (int k0 = kLo; k0 < kHi; k0 += BK) {
       const bool more = k0 + BK < kHi;
-      if (more) load(k0 + BK);
+      if (more) {
+        load_slab<!TRANS_A, VEC>(A, d.lda, r0, d.M, k0 + BK, kHi, tid, ra);
+        load_slab<TRANS_B, VEC>(B, d.ldb, c0, d.N, k0 + BK, kHi, tid, rb);
+      }
       const int kr = lane >> 5;
       const int cl = lane & 31;
 #pragma unroll
@@ -117,7 +142,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d) {
         acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
         acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
       }
-      if (more) store(buf ^ 1);
+      if (more) {
+        store_slab<!TRANS_A>(As[buf ^ 1], tid, ra);
+        store_slab<TRANS_B>(Bs[buf ^ 1], tid, rb);
+      }
       __syncthreads();
       buf ^= 1;
     }
@@ -140,6 +168,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d) {
       }
 }
 
+template <bool TA, bool TB>
+void launch(const GemmDesc& d, dim3 grid, hipStream_t s) {
+  const bool vec = d.lda % 4 == 0 && d.ldb % 4 == 0 && d.strideA % 4 == 0 && d.strideB % 4 == 0 &&
+                   ((uintptr_t)d.A & 15) == 0 && ((uintptr_t)d.B & 15) == 0;
+  if (vec) hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, true>), grid, dim3(256), 0, s, d);
+  else hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, false>), grid, dim3(256), 0, s, d);
+}
+
 }  // namespace
 
 hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s) {
@@ -148,10 +184,10 @@ hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s) 
   const int tM = (int)cdiv(d.M, BM), tN = (int)cdiv(d.N, BN);
   if (d.flags & GEMM_LOWER_TILES) grid = dim3((unsigned)(tM * (tM + 1) / 2), 1, (unsigned)d.batch);
   else grid = dim3((unsigned)tM, (unsigned)tN, (unsigned)d.batch);
-  if (!transA && !transB) hipLaunchKernelGGL((gemm_f32_kernel<false, false>), grid, dim3(256), 0, s, d);
-  else if (!transA && transB) hipLaunchKernelGGL((gemm_f32_kernel<false, true>), grid, dim3(256), 0, s, d);
-  else if (transA && !transB) hipLaunchKernelGGL((gemm_f32_kernel<true, false>), grid, dim3(256), 0, s, d);
-  else hipLaunchKernelGGL((gemm_f32_kernel<true, true>), grid, dim3(256), 0, s, d);
+  if (!transA && !transB) launch<false, false>(d, grid, s);
+  else if (!transA && transB) launch<false, true>(d, grid, s);
+  else if (transA && !transB) launch<true, false>(d, grid, s);
+  else launch<true, true>(d, grid, s);
   return hipGetLastError();
 }
 

@@ -13,8 +13,8 @@
 //
 //   1. reversed copy + damping  A = J H J + lambda I             (HBM-bound)
 //   2. blocked right-looking Cholesky of A, panels of NB = 64:
-//        leaf kernel: one workgroup factors the NB x NB diagonal block in
-//        LDS and also inverts it;
+//        leaf kernel: one workgroup factors the NB x NB diagonal block and
+//        inverts it in the same pass (registers + LDS broadcasts);
 //        panel solve  A21 <- A21 L11^{-T}  (MFMA GEMM with the leaf inverse)
 //        trailing     A22 <- A22 - A21 A21^T  (MFMA GEMM, lower tiles only)
 //   3. triangular inverse in place by recursive doubling: with the NB-block
@@ -66,54 +66,109 @@ __global__ __launch_bounds__(256) void reverse_damp_kernel(const float* H, float
 }
 
 // Factor the kb x kb diagonal block at (k0, k0) of A in place (lower) and
-// write its inverse to Dinv (NB x NB, zero above the diagonal).
+// write its inverse to Dinv (NB x NB, zero above the diagonal), in one pass.
+//
+// Thread (ty, tx) of a 16 x 16 grid keeps a 4 x 4 tile (rows 4ty.., columns
+// 4tx..) of the block being factored (Am) and of the running inverse (Tm) in
+// registers.  Step j, right-looking: d = A[j][j]; column j of L is
+// A[r][j]/sqrt(d); row j of L^{-1} is R[j][:]/sqrt(d); then
+//   A[r][c] -= L[r][j] L[c][j]        (r, c > j)
+//   R[r][c] -= L[r][j] Linv[j][c]     (r > j, c <= j)
+// with R = I initially (so that R[r][:] becomes row r of L^{-1} times L[r][r]).
+// The raw column j+1 of A and row j+1 of R are published to double-buffered
+// LDS by their owners, so each step needs one barrier.  Rows/columns past kb
+// are padded with the identity, which factors trivially.
 __global__ __launch_bounds__(256) void chol_leaf_kernel(float* A, int64_t lda, int64_t k0, int kb, float* Dinv,
                                                         int32_t* info, int64_t n) {
   if (*info != 0) return;
-  __shared__ float S[NB][NB + 1];
-  __shared__ float T[NB][NB + 1];
-  __shared__ float col[NB];
+  __shared__ __attribute__((aligned(16))) float colbuf[2][NB];
+  __shared__ __attribute__((aligned(16))) float rowbuf[2][NB];
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    const int r = idx / NB, c = idx % NB;
-    S[r][c] = (r < kb && c < kb && c <= r) ? A[(k0 + r) * lda + k0 + c] : 0.f;
-    T[r][c] = (r == c) ? 1.f : 0.f;
-  }
+  const int ty = tid >> 4, tx = tid & 15;
+  float Am[4][4], Tm[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r = 4 * ty + a, c = 4 * tx + b;
+      float v = 0.f;
+      if (r < kb && c < kb) { if (c <= r) v = A[(k0 + r) * lda + k0 + c]; }
+      else if (r == c) v = 1.f;
+      Am[a][b] = v;
+      Tm[a][b] = (r == c) ? 1.f : 0.f;
+    }
+  if (tx == 0)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) colbuf[0][4 * ty + a] = Am[a][0];
+  if (ty == 0)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) rowbuf[0][4 * tx + b] = Tm[0][b];
   __syncthreads();
-  const int tr = tid >> 4, tc = tid & 15;
-  for (int j = 0; j < kb; ++j) {
-    const float d = S[j][j];
-    if (!(d > 0.f) || !(d < INFINITY)) {  // uniform: every thread read the same d
-      if (tid == 0) atomicCAS(info, 0, (int32_t)(n - (k0 + j)));
-      return;
+
+  for (int jb = 0; jb < NB / 4; ++jb) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * jb + jj;
+      const float* cb = colbuf[j & 1];
+      const float* rb = rowbuf[j & 1];
+      const float d = cb[j];
+      if (!(d > 0.f) || !(d < INFINITY)) {  // uniform: every thread read the same d
+        if (tid == 0) atomicCAS(info, 0, (int32_t)(n - (k0 + j)));
+        return;
+      }
+      const float rs = __builtin_amdgcn_rsqf(d);
+      const float sd = d * rs;
+      const f32x4 cr = *(const f32x4*)&cb[4 * ty];
+      const f32x4 cc = *(const f32x4*)&cb[4 * tx];
+      const f32x4 rr = *(const f32x4*)&rb[4 * tx];
+      float lr[4], lc[4], tc[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) lr[a] = (4 * ty + a > j) ? cr[a] * rs : 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        lc[b] = (4 * tx + b > j) ? cc[b] * rs : 0.f;
+        tc[b] = (4 * tx + b <= j) ? rr[b] * rs : 0.f;
+      }
+      if (4 * ty + 3 > j) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            Am[a][b] = fmaf(-lr[a], lc[b], Am[a][b]);
+            Tm[a][b] = fmaf(-lr[a], tc[b], Tm[a][b]);
+          }
+      }
+      if (tx == jb) {  // column j of L
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int r = 4 * ty + a;
+          Am[a][jj] = (r > j) ? lr[a] : (r == j ? sd : Am[a][jj]);
+        }
+      }
+      if (ty == jb) {  // row j of L^{-1}
+#pragma unroll
+        for (int b = 0; b < 4; ++b) Tm[jj][b] = tc[b];
+      }
+      if (j + 1 < NB) {
+        const int jn = j + 1, jnb = jn >> 2, jnj = (jj + 1) & 3;
+        if (tx == jnb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) colbuf[jn & 1][4 * ty + a] = Am[a][jnj];
+        if (ty == jnb)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) rowbuf[jn & 1][4 * tx + b] = Tm[jnj][b];
+      }
+      __syncthreads();
     }
-    const float sd = sqrtf(d);
-    if (tid < kb) col[tid] = (tid > j) ? S[tid][j] / sd : 0.f;
-    __syncthreads();
-    if (tid < kb && tid > j) S[tid][j] = col[tid];
-    if (tid == j) S[j][j] = sd;
-    for (int r = j + 1 + tr; r < kb; r += 16) {
-      const float cr = col[r];
-      for (int c = j + 1 + tc; c <= r; c += 16) S[r][c] -= cr * col[c];
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r = 4 * ty + a, c = 4 * tx + b;
+      if (r < kb && c <= r) A[(k0 + r) * lda + k0 + c] = Am[a][b];
+      Dinv[r * NB + c] = (r < kb && c <= r) ? Tm[a][b] : 0.f;
     }
-    __syncthreads();
-  }
-  // inverse of the lower-triangular factor, row by row: T <- L^{-1}
-  for (int k = 0; k < kb; ++k) {
-    const float dk = S[k][k];
-    if (tid <= k) T[k][tid] = T[k][tid] / dk;
-    __syncthreads();
-    for (int r = k + 1 + tr; r < kb; r += 16) {
-      const float l = S[r][k];
-      for (int c = tc; c <= k; c += 16) T[r][c] -= l * T[k][c];
-    }
-    __syncthreads();
-  }
-  for (int idx = tid; idx < NB * NB; idx += 256) {
-    const int r = idx / NB, c = idx % NB;
-    if (r < kb && c <= r) A[(k0 + r) * lda + k0 + c] = S[r][c];
-    Dinv[idx] = (r < kb && c < kb && c <= r) ? T[r][c] : 0.f;
-  }
 }
 
 // Zero the strict upper triangle and put the NB-block inverses on the diagonal.

@@ -19,6 +19,7 @@
 // lane updates its own 8 columns.  Group minimum / maximum at a group start
 // are DPP reductions over the row.
 #include <algorithm>
+#include <utility>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -27,8 +28,7 @@ namespace gptq {
 
 namespace {
 
-constexpr int BMAX = 128;
-constexpr int UP_PITCH = BMAX + 4;
+constexpr int BMAX = 128;  // widest block; the E buffer has this leading dimension
 
 struct SweepArgs {
   const float* U;
@@ -38,21 +38,45 @@ struct SweepArgs {
   int w;      // block width (<= 128)
   int maxq;
   int64_t group;  // group size (<= 0: per row)
-  int inblock;    // 1: group starts are taken inside the block (0 < group <= B)
   int64_t G;
   float* S;
   int32_t* Z;
-  uint8_t* Q8;   // [m x n] codes
-  float* E;      // [m x 128] scaled errors of this block
-  float* err_sq; // [m] or null
+  uint8_t* Q8;    // [m x n] codes
+  float* E;       // [m x 128] scaled errors of this block
+  float* err_sq;  // [m] or null
 };
 
-template <int P>
-__device__ __forceinline__ float bcast_col(const float (&v)[8]) {
-  return row_bcast<(P >> 3)>(v[P & 7]);
-}
+// Lanes-per-row variants: 16 lanes (one DPP row) x 8 columns = 128 columns,
+// or 4 lanes (one DPP quad) x 8 columns = 32 columns.
+template <int LPR>
+struct RowOps;
+template <>
+struct RowOps<16> {
+  template <int SRC>
+  __device__ __forceinline__ static float bcast(float v) { return row_bcast<SRC>(v); }
+  __device__ __forceinline__ static float rmin(float v) { return row_min16(v); }
+  __device__ __forceinline__ static float rmax(float v) { return row_max16(v); }
+};
+template <>
+struct RowOps<4> {
+  template <int SRC>
+  __device__ __forceinline__ static float bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                              SRC | (SRC << 2) | (SRC << 4) | (SRC << 6), 0xF, 0xF, false));
+  }
+  __device__ __forceinline__ static float rmin(float v) {
+    v = fminf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    return fminf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  }
+  __device__ __forceinline__ static float rmax(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  }
+};
 
-// Quantizer parameters (s, z) from the range [lo, hi] of a group or row.
+// Quantizer parameters (s, z) from the range [lo, hi] of a group or row:
+// x_lo = min(0, lo), x_hi = max(0, hi) (an all-zero range becomes [0, 1]),
+// s = (x_hi - x_lo) / maxq, z = rint(-x_lo / s).
 __device__ __forceinline__ void qparams(float lo, float hi, int maxq, float& s, float& z) {
   lo = fminf(lo, 0.f);
   hi = fmaxf(hi, 0.f);
@@ -61,123 +85,194 @@ __device__ __forceinline__ void qparams(float lo, float hi, int maxq, float& s, 
   z = rintf(-lo / s);
 }
 
-template <int P>
-__device__ __forceinline__ void sweep_step(const SweepArgs& a, float (&v)[8], float (&ek)[8], float (&qk)[8],
-                                           float& s, float& inv_s, float& z, float& eacc, int& gcount, int l16,
-                                           bool active, int64_t r, const float (*Up)[UP_PITCH], const float* invd) {
-  if (a.inblock) {
-    if (gcount == 0) {  // first column of a group: (s, z) from the group's current values
-      float lo = INFINITY, hi = -INFINITY;
+struct GroupState {
+  float s, inv_s, nz, mz;  // scale, 1/scale, -z, maxq - z
+  float z;
+};
+
+// Range of columns [c0, c1) of this lane's 8 values (block-local column of
+// value k is 8*lane + k), reduced over the row's lanes, then (s, z).
+template <int LPR>
+__device__ __forceinline__ GroupState group_params(const float (&v)[8], int lr, int c0, int c1, int maxq) {
+  float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 8 * l16 + e;
-        if (c >= P && c < P + a.group && c < a.w) {
-          lo = fminf(lo, v[e]);
-          hi = fmaxf(hi, v[e]);
-        }
-      }
-      lo = row_min16(lo);
-      hi = row_max16(hi);
-      qparams(lo, hi, a.maxq, s, z);
-      inv_s = 1.f / s;
-      if (l16 == 0 && active) {
-        const int64_t gi = (a.i + P) / a.group;
-        a.S[r * a.G + gi] = s;
-        a.Z[r * a.G + gi] = (int32_t)z;
-      }
-      gcount = (int)a.group;
-    }
-    --gcount;
+  for (int k = 0; k < 8; ++k) {
+    const int c = 8 * lr + k;
+    const bool in = c >= c0 && c < c1;
+    lo = fminf(lo, in ? v[k] : INFINITY);
+    hi = fmaxf(hi, in ? v[k] : -INFINITY);
   }
-  const float vp = bcast_col<P>(v);
-  const float qz = __builtin_amdgcn_fmed3f(rintf(vp * inv_s), -z, (float)a.maxq - z);
-  const float err = fmaf(-s, qz, vp);
-  const float e = err * invd[P];
-  if (l16 == (P >> 3)) {
-    ek[P & 7] = e;
-    qk[P & 7] = qz + z;
-  }
-  eacc = fmaf(e, e, eacc);
-  const f32x4 u0 = *(const f32x4*)&Up[P][8 * l16];
-  const f32x4 u1 = *(const f32x4*)&Up[P][8 * l16 + 4];
-  v[0] = fmaf(-err, u0[0], v[0]);
-  v[1] = fmaf(-err, u0[1], v[1]);
-  v[2] = fmaf(-err, u0[2], v[2]);
-  v[3] = fmaf(-err, u0[3], v[3]);
-  v[4] = fmaf(-err, u1[0], v[4]);
-  v[5] = fmaf(-err, u1[1], v[5]);
-  v[6] = fmaf(-err, u1[2], v[6]);
-  v[7] = fmaf(-err, u1[3], v[7]);
+  lo = RowOps<LPR>::rmin(lo);
+  hi = RowOps<LPR>::rmax(hi);
+  GroupState g;
+  qparams(lo, hi, maxq, g.s, g.z);
+  g.inv_s = 1.f / g.s;
+  g.nz = -g.z;
+  g.mz = (float)maxq - g.z;
+  return g;
 }
 
-template <int P>
-struct Steps {
-  __device__ __forceinline__ static void run(const SweepArgs& a, float (&v)[8], float (&ek)[8], float (&qk)[8],
-                                             float& s, float& inv_s, float& z, float& eacc, int& gcount, int l16,
-                                             bool active, int64_t r, const float (*Up)[UP_PITCH], const float* invd) {
-    if (P >= a.w) return;
-    sweep_step<P>(a, v, ek, qk, s, inv_s, z, eacc, gcount, l16, active, r, Up, invd);
-    Steps<P + 1>::run(a, v, ek, qk, s, inv_s, z, eacc, gcount, l16, active, r, Up, invd);
-  }
-};
-template <>
-struct Steps<BMAX> {
-  __device__ __forceinline__ static void run(const SweepArgs&, float (&)[8], float (&)[8], float (&)[8], float&,
-                                             float&, float&, float&, int&, int, bool, int64_t,
-                                             const float (*)[UP_PITCH], const float*) {}
-};
+template <int LPR>
+__device__ __attribute__((noinline)) GroupState group_params_call(float v0, float v1, float v2, float v3, float v4,
+                                                                  float v5, float v6, float v7, int lr, int c0, int c1,
+                                                                  int maxq) {
+  const float v[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+  return group_params<LPR>(v, lr, c0, c1, maxq);
+}
 
+__device__ __forceinline__ void store_params(const SweepArgs& a, const GroupState& g, int64_t r, int64_t col,
+                                             bool writer) {
+  if (writer) {
+    const int64_t gi = col / a.group;
+    a.S[r * a.G + gi] = g.s;
+    a.Z[r * a.G + gi] = (int32_t)g.z;
+  }
+}
+
+// GMODE: 0 = (s, z) fixed for the whole block (per-row, or a group spanning
+// several blocks); 8..128 = group size known at compile time, groups start
+// inside the block; -1 = any other in-block group size (runtime).
+template <int LPR, int GMODE>
 __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
-  __shared__ __attribute__((aligned(16))) float Up[BMAX][UP_PITCH];
-  __shared__ float invd[BMAX];
+  constexpr int NSTEP = 8 * LPR;
+  constexpr int PITCH = NSTEP + 4;
+  constexpr int ROWS = 256 / LPR;
+  __shared__ __attribute__((aligned(16))) float Up[NSTEP * PITCH];
+  __shared__ float invd[NSTEP];
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int l16 = lane & 15;
-  const int64_t r = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  const int lr = tid & (LPR - 1);
+  const int64_t r = (int64_t)blockIdx.x * ROWS + tid / LPR;
   const bool active = r < a.m;
   const int w = a.w;
   const int64_t i = a.i;
+  const float* __restrict__ U = a.U;
 
-  if (tid < BMAX) invd[tid] = (tid < w) ? 1.f / a.U[(i + tid) * a.n + i + tid] : 0.f;
+  // factor rows of this block divided by their diagonal; zero on and below it
+  if (tid < NSTEP) invd[tid] = (tid < w) ? 1.f / U[(i + tid) * a.n + i + tid] : 0.f;
   __syncthreads();
-  for (int idx = tid; idx < BMAX * BMAX; idx += 256) {
-    const int p = idx >> 7, j = idx & (BMAX - 1);
+  for (int idx = tid; idx < NSTEP * NSTEP; idx += 256) {
+    const int p = idx / NSTEP, j = idx % NSTEP;
     float u = 0.f;
-    if (p < w && j < w && j > p) u = a.U[(i + p) * a.n + i + j] * invd[p];
-    Up[p][j] = u;
+    if (p < w && j < w && j > p) u = U[(i + p) * a.n + i + j] * invd[p];
+    Up[p * PITCH + j] = u;
   }
 
   float v[8], ek[8], qk[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = 8 * l16 + e;
-    v[e] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
-    ek[e] = 0.f;
-    qk[e] = 0.f;
+  for (int k = 0; k < 8; ++k) {
+    const int c = 8 * lr + k;
+    v[k] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
+    ek[k] = 0.f;
+    qk[k] = 0.f;
   }
-  float s = 1.f, z = 0.f;
-  if (!a.inblock && active) {
+  GroupState g;
+  g.s = 1.f;
+  g.z = 0.f;
+  if (GMODE == 0 && active) {
     const int64_t gi = a.group <= 0 ? 0 : i / a.group;
-    s = a.S[r * a.G + gi];
-    z = (float)a.Z[r * a.G + gi];
+    g.s = a.S[r * a.G + gi];
+    g.z = (float)a.Z[r * a.G + gi];
   }
-  float inv_s = 1.f / s;
-  float eacc = 0.f;
-  int gcount = 0;
+  g.inv_s = 1.f / g.s;
+  g.nz = -g.z;
+  g.mz = (float)a.maxq - g.z;
+  int next_group = 0;  // GMODE == -1: block-local column of the next group start
+  const bool writer = active && lr == 0;
   __syncthreads();
 
-  Steps<0>::run(a, v, ek, qk, s, inv_s, z, eacc, gcount, l16, active, r, Up, invd);
+  // factor row p of this lane's 8 columns, prefetched two columns ahead
+  f32x4 ua[3], ub[3];
+  ua[0] = *(const f32x4*)&Up[0 * PITCH + 8 * lr];
+  ub[0] = *(const f32x4*)&Up[0 * PITCH + 8 * lr + 4];
+  ua[1] = *(const f32x4*)&Up[1 * PITCH + 8 * lr];
+  ub[1] = *(const f32x4*)&Up[1 * PITCH + 8 * lr + 4];
+
+  // one column per step, fully unrolled so that register and DPP lane
+  // indices are compile-time constants
+  [&]<int... P>(std::integer_sequence<int, P...>) {
+    (
+        [&] {
+          if constexpr (P + 2 < NSTEP) {
+            ua[(P + 2) % 3] = *(const f32x4*)&Up[(P + 2) * PITCH + 8 * lr];
+            ub[(P + 2) % 3] = *(const f32x4*)&Up[(P + 2) * PITCH + 8 * lr + 4];
+          }
+          if constexpr (GMODE > 0) {
+            if constexpr (P % GMODE == 0) {
+              g = group_params<LPR>(v, lr, P, P + GMODE < w ? P + GMODE : w, a.maxq);
+              store_params(a, g, r, i + P, writer && P < w);
+            }
+          } else if constexpr (GMODE < 0) {
+            if (P == next_group && P < w) {
+              const int c1 = (int)((int64_t)P + a.group < (int64_t)w ? P + a.group : w);
+              g = group_params_call<LPR>(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], lr, P, c1, a.maxq);
+              store_params(a, g, r, i + P, writer);
+              next_group += (int)a.group;
+            }
+          }
+          const float vp = RowOps<LPR>::template bcast<(P >> 3)>(v[P & 7]);
+          const float qz = __builtin_amdgcn_fmed3f(rintf(vp * g.inv_s), g.nz, g.mz);
+          const float err = fmaf(-g.s, qz, vp);
+          if (lr == (P >> 3)) {  // the owner keeps the error and the code of its column
+            ek[P & 7] = err;
+            qk[P & 7] = qz + g.z;
+          }
+          const f32x4 u0 = ua[P % 3], u1 = ub[P % 3];
+          v[0] = fmaf(-err, u0[0], v[0]);
+          v[1] = fmaf(-err, u0[1], v[1]);
+          v[2] = fmaf(-err, u0[2], v[2]);
+          v[3] = fmaf(-err, u0[3], v[3]);
+          v[4] = fmaf(-err, u1[0], v[4]);
+          v[5] = fmaf(-err, u1[1], v[5]);
+          v[6] = fmaf(-err, u1[2], v[6]);
+          v[7] = fmaf(-err, u1[3], v[7]);
+        }(),
+        ...);
+  }(std::make_integer_sequence<int, NSTEP>{});
+
+  // scaled errors e = err / U_pp of this lane's columns, their squares summed over the row
+  float eacc = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    ek[k] *= invd[8 * lr + k];
+    eacc = fmaf(ek[k], ek[k], eacc);
+  }
+  if constexpr (LPR == 16) {
+    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0xB1, 0xF, 0xF, false));
+    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0x4E, 0xF, 0xF, false));
+    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0x124, 0xF, 0xF, false));
+    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0x128, 0xF, 0xF, false));
+  } else {
+    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0xB1, 0xF, 0xF, false));
+    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0x4E, 0xF, 0xF, false));
+  }
 
   if (active) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = 8 * l16 + e;
+    for (int k = 0; k < 8; ++k) {
+      const int c = 8 * lr + k;
       if (c < w) {
-        a.E[r * BMAX + c] = ek[e];
-        a.Q8[r * a.n + i + c] = (uint8_t)(int)qk[e];
+        a.E[r * BMAX + c] = ek[k];
+        a.Q8[r * a.n + i + c] = (uint8_t)(int)qk[k];
       }
     }
-    if (l16 == 0 && a.err_sq) a.err_sq[r] += eacc;
+    if (lr == 0 && a.err_sq) a.err_sq[r] += eacc;
+  }
+}
+
+template <int LPR>
+void launch_sweep(const SweepArgs& a, int gmode, hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(a.m, 256 / LPR)), block(256);
+  switch (gmode) {
+    case 0: hipLaunchKernelGGL((sweep_block_kernel<LPR, 0>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((sweep_block_kernel<LPR, 8>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((sweep_block_kernel<LPR, 16>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((sweep_block_kernel<LPR, 32>), grid, block, 0, st, a); break;
+    default:
+      if constexpr (LPR == 16) {
+        if (gmode == 64) { hipLaunchKernelGGL((sweep_block_kernel<LPR, 64>), grid, block, 0, st, a); break; }
+        if (gmode == 128) { hipLaunchKernelGGL((sweep_block_kernel<LPR, 128>), grid, block, 0, st, a); break; }
+      }
+      hipLaunchKernelGGL((sweep_block_kernel<LPR, -1>), grid, block, 0, st, a);
   }
 }
 
@@ -277,7 +372,9 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
 
   const int maxq = (1 << bits) - 1;
   const int64_t G = group <= 0 ? 1 : cdiv(n, group);
-  const int inblock = (group > 0 && group <= B) ? 1 : 0;
+  const bool inblock = group > 0 && group <= B;
+  const bool pow2 = group >= 8 && group <= 128 && (group & (group - 1)) == 0;
+  const int gmode = !inblock ? 0 : (pow2 && group <= (B <= 32 ? 32 : 128) ? (int)group : -1);
   const dim3 rg = rows_grid(n, m);
 
   if (dt == 0) hipLaunchKernelGGL((to_f32_kernel<0>), rg, dim3(256), 0, st, W, ldw, V, m, n);
@@ -298,8 +395,9 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
     if (group > B && i % group == 0)
       hipLaunchKernelGGL(row_params_kernel, dim3(prow), dim3(256), 0, st, (const float*)V, m, n, i, group, maxq, S,
                          Z, G, i / group);
-    SweepArgs a{U, V, n, m, i, w, maxq, group, inblock, G, S, Z, Q8, E, err_sq};
-    hipLaunchKernelGGL(sweep_block_kernel, dim3((unsigned)cdiv(m, 16)), dim3(256), 0, st, a);
+    SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, Q8, E, err_sq};
+    if (B <= 32) launch_sweep<4>(a, gmode, st);
+    else launch_sweep<16>(a, gmode, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (i + w < n) {
       GemmDesc g{};

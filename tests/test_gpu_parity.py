@@ -172,11 +172,13 @@ def test_sweep_parity(m, n, bits, group, block, wdt):
     got = Wt.float().cpu().numpy().astype(np.float64)
     tol = {"f32": 1e-6, "f16": 1e-3, "bf16": 8e-3}[wdt]
     assert np.allclose(got, Wh, rtol=tol, atol=tol * np.abs(Wh).max())
-    # per-row sum of squared scaled errors
-    err_rel = np.abs(res["err_sq"].cpu().numpy() - ref["err_sq"]) / np.maximum(ref["err_sq"], 1e-30)
+    # per-row sum of squared scaled errors; the absolute floor is 1e-4 of the
+    # energy uniform rounding errors would carry, sum_p s^2 / (12 U_pp^2)
+    gidx = np.zeros(n, dtype=np.int64) if group <= 0 else np.arange(n) // group
+    expect = np.sum(ref["s"][:, gidx] ** 2 / (12.0 * np.diag(U32).astype(np.float64)[None, :] ** 2), axis=1)
     rows_ok = ~(q != ref["q"]).any(axis=1)
-    if rows_ok.any():
-        assert err_rel[rows_ok].max() <= 1e-3
+    diff = np.abs(res["err_sq"].cpu().numpy() - ref["err_sq"])
+    assert np.all((diff <= 1e-3 * ref["err_sq"] + 1e-4 * expect)[rows_ok])
 
 
 def test_sweep_block_invariance_on_gpu():
