@@ -96,7 +96,7 @@ def main():
     U = torch.empty_like(H)
     hws = torch.empty(max(pw.hessian_workspace_bytes(n, T), 1), dtype=torch.uint8, device=dev)
     pws = torch.empty(pw.prepare_workspace_bytes(n), dtype=torch.uint8, device=dev)
-    qws = torch.empty(pw.quantize_workspace_bytes(m, n), dtype=torch.uint8, device=dev)
+    qws = torch.empty(pw.quantize_workspace_bytes(m, n, job.block), dtype=torch.uint8, device=dev)
     out = {
         "qcodes": torch.empty((m, pw.packed_words(n, job.bits)), dtype=torch.int32, device=dev),
         "scales": torch.empty((m, pw.n_groups(n, job.group)), dtype=torch.float32, device=dev),

@@ -143,12 +143,12 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp, float* U,
  *   scales     [m x G] float32 out, zeros [m x G] int32 out, G = 1 per-row,
  *              else ceil(n / group_size).
  *   err_sq     optional [m] float32 out (NULL to skip): sum_p e_p^2 per row.
- *   workspace, ws_bytes: at least gptq_quantize_workspace_bytes(m, n).
+ *   workspace, ws_bytes: at least gptq_quantize_workspace_bytes(m, n, block_size).
  * Errors: m < 1, n < 1, ldw < n, bits outside 2..8, block_size outside
  * 1..128, group/block not nesting, NULL required pointers, unknown dtype ->
  * GPTQ_ERR_INVALID_ARG; short workspace -> GPTQ_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */
-size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n);
+size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n, int64_t block_size);
 gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, int64_t ldw,
                                 const float* U, int32_t bits, int64_t group_size,
                                 int64_t block_size, uint32_t* qcodes, float* scales,

@@ -57,7 +57,7 @@ def _load() -> ctypes.CDLL:
     L.gptq_prepare_workspace_bytes.restype = sz
     L.gptq_prepare_hinv.argtypes = [vp, i64, f32, vp, vp, vp, vp, sz, vp]
     L.gptq_prepare_hinv.restype = i32
-    L.gptq_quantize_workspace_bytes.argtypes = [i64, i64]
+    L.gptq_quantize_workspace_bytes.argtypes = [i64, i64, i64]
     L.gptq_quantize_workspace_bytes.restype = sz
     L.gptq_quantize_layer.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp, vp, i32, vp, sz, vp]
     L.gptq_quantize_layer.restype = i32
@@ -109,8 +109,8 @@ def prepare_workspace_bytes(n: int) -> int:
     return int(_load().gptq_prepare_workspace_bytes(int(n)))
 
 
-def quantize_workspace_bytes(m: int, n: int) -> int:
-    return int(_load().gptq_quantize_workspace_bytes(int(m), int(n)))
+def quantize_workspace_bytes(m: int, n: int, block_size: int = 128) -> int:
+    return int(_load().gptq_quantize_workspace_bytes(int(m), int(n), int(block_size)))
 
 
 # ----------------------------------------------------------------------------- the three stages
@@ -184,7 +184,7 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, group_size: int,
         o["zeros"] = torch.empty((m, G), dtype=torch.int32, device=dev)
     if err_sq and "err_sq" not in o:
         o["err_sq"] = torch.empty((m,), dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else _workspace(quantize_workspace_bytes(m, n), dev)
+    ws = workspace if workspace is not None else _workspace(quantize_workspace_bytes(m, n, block_size), dev)
     st = _load().gptq_quantize_layer(W.data_ptr(), _DT[W.dtype], m, n, max(W.stride(0), n), U.data_ptr(), int(bits),
                                      int(group_size), int(block_size), o["qcodes"].data_ptr(), o["scales"].data_ptr(),
                                      o["zeros"].data_ptr(), _ptr(o.get("err_sq")) if err_sq else None,

@@ -13,7 +13,7 @@ hipError_t syrk_accumulate(float* H, int64_t n, const void* X, int dtype, int64_
 size_t prepare_workspace_bytes(int64_t n);
 hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t* info, float* lambda_out, void* ws,
                         hipStream_t s);
-size_t quantize_workspace_bytes(int64_t m, int64_t n);
+size_t quantize_workspace_bytes(int64_t m, int64_t n, int64_t B);
 hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, const float* U, int bits, int64_t group,
                           int64_t B, uint32_t* qcodes, float* S, int32_t* Z, float* err_sq, int write_dequant,
                           void* ws, hipStream_t st);
@@ -69,7 +69,9 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp, float* U, i
   return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
 }
 
-size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n) { return gptq::quantize_workspace_bytes(m, n); }
+size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n, int64_t block_size) {
+  return gptq::quantize_workspace_bytes(m, n, block_size);
+}
 
 gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, int64_t ldw, const float* U,
                                 int32_t bits, int64_t group_size, int64_t block_size, uint32_t* qcodes, float* scales,
@@ -81,7 +83,7 @@ gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, 
   if (group_size > 0 && !(group_size % block_size == 0 || block_size % group_size == 0)) return GPTQ_ERR_INVALID_ARG;
   if (W == nullptr || U == nullptr || qcodes == nullptr || scales == nullptr || zeros == nullptr)
     return GPTQ_ERR_INVALID_ARG;
-  if (workspace == nullptr || ws_bytes < gptq::quantize_workspace_bytes(m, n)) return GPTQ_ERR_WORKSPACE;
+  if (workspace == nullptr || ws_bytes < gptq::quantize_workspace_bytes(m, n, block_size)) return GPTQ_ERR_WORKSPACE;
   hipError_t e = gptq::quantize_layer(W, w_dtype, m, n, ldw, U, bits, group_size, block_size, qcodes, scales, zeros,
                                       err_sq, write_dequant, workspace, (hipStream_t)stream);
   return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;

@@ -115,6 +115,22 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmDesc d) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
+  // beta != 0: fetch this lane's C values now, so their latency overlaps the K loop
+  const float alpha = d.alpha, beta = d.beta;
+  f32x16 cpre[2][2];
+  if (beta != 0.f) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = r0 + wr * 64 + mb * 32 + mfma32_row(r, lane);
+          const int col = c0 + wc * 64 + nb * 32 + mfma32_col(lane);
+          cpre[mb][nb][r] = (row < d.M && col < d.N) ? C[(int64_t)row * d.ldc + col] : 0.f;
+        }
+  }
+
   f32x4 ra[4], rb[4];
   if (kLo < kHi) {
     load_slab<!TRANS_A, VEC>(A, d.lda, r0, d.M, kLo, kHi, tid, ra);
@@ -151,7 +167,6 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmDesc d) {
     }
   }
 
-  const float alpha = d.alpha, beta = d.beta;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -161,9 +176,8 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmDesc d) {
         const int row = r0 + wr * 64 + mb * 32 + mfma32_row(r, lane);
         const int col = c0 + wc * 64 + nb * 32 + mfma32_col(lane);
         if (row < d.M && col < d.N) {
-          float* p = C + (int64_t)row * d.ldc + col;
           const float v = alpha * acc[mb][nb][r];
-          *p = (beta == 0.f) ? v : fmaf(beta, *p, v);
+          C[(int64_t)row * d.ldc + col] = (beta == 0.f) ? v : fmaf(beta, cpre[mb][nb][r], v);
         }
       }
 }

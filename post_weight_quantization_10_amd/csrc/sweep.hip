@@ -44,6 +44,7 @@ struct SweepArgs {
   uint8_t* Q8;    // [m x n] codes
   float* E;       // [m x 128] scaled errors of this block
   float* err_sq;  // [m] or null
+  const float* Dblk;  // this block's factor rows divided by their diagonal ([NSTEP][NSTEP]), then 1/U_pp [NSTEP]
 };
 
 // Lanes-per-row variants: 16 lanes (one DPP row) x 8 columns = 128 columns,
@@ -147,21 +148,40 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
   const int64_t i = a.i;
   const float* __restrict__ U = a.U;
 
-  // factor rows of this block divided by their diagonal; zero on and below it
-  if (tid < NSTEP) invd[tid] = (tid < w) ? 1.f / U[(i + tid) * a.n + i + tid] : 0.f;
-  __syncthreads();
-  for (int idx = tid; idx < NSTEP * NSTEP; idx += 256) {
-    const int p = idx / NSTEP, j = idx % NSTEP;
-    float u = 0.f;
-    if (p < w && j < w && j > p) u = U[(i + p) * a.n + i + j] * invd[p];
-    Up[p * PITCH + j] = u;
+  // this block's factor rows divided by their diagonal (zero on and below it)
+  // and 1/U_pp, prepared once per layer by diag_blocks_kernel
+  {
+    constexpr int Q = NSTEP * NSTEP / 4;  // float4 groups
+    const f32x4* src = (const f32x4*)a.Dblk;
+    f32x4 t[Q / 256];
+#pragma unroll
+    for (int u = 0; u < Q / 256; ++u) t[u] = src[tid + 256 * u];
+#pragma unroll
+    for (int u = 0; u < Q / 256; ++u) {
+      const int q = tid + 256 * u;
+      const int p = q / (NSTEP / 4), j4 = q % (NSTEP / 4);
+      *(f32x4*)&Up[p * PITCH + 4 * j4] = t[u];
+    }
+    if (tid < NSTEP) invd[tid] = a.Dblk[NSTEP * NSTEP + tid];
   }
+  (void)U;
 
   float v[8], ek[8], qk[8];
+  const bool vec = ((a.n | i) & 3) == 0;  // 16-byte aligned rows of V
+  if (vec && active && 8 * lr + 8 <= w) {
+    const f32x4 x0 = *(const f32x4*)&a.V[r * a.n + i + 8 * lr];
+    const f32x4 x1 = *(const f32x4*)&a.V[r * a.n + i + 8 * lr + 4];
+    v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
+    v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = 8 * lr + k;
+      v[k] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int c = 8 * lr + k;
-    v[k] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
     ek[k] = 0.f;
     qk[k] = 0.f;
   }
@@ -247,16 +267,51 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
   }
 
   if (active) {
+    if (8 * lr + 8 <= w) {
+      *(f32x4*)&a.E[r * BMAX + 8 * lr] = f32x4{ek[0], ek[1], ek[2], ek[3]};
+      *(f32x4*)&a.E[r * BMAX + 8 * lr + 4] = f32x4{ek[4], ek[5], ek[6], ek[7]};
+      uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = 8 * lr + k;
-      if (c < w) {
-        a.E[r * BMAX + c] = ek[k];
-        a.Q8[r * a.n + i + c] = (uint8_t)(int)qk[k];
+      for (int k = 0; k < 4; ++k) {
+        lo |= (uint32_t)(int)qk[k] << (8 * k);
+        hi |= (uint32_t)(int)qk[k + 4] << (8 * k);
+      }
+      uint8_t* q = a.Q8 + r * a.n + i + 8 * lr;
+      if ((((uintptr_t)q) & 7) == 0) {
+        *(uint2*)q = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = (uint8_t)(int)qk[k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = 8 * lr + k;
+        if (c < w) {
+          a.E[r * BMAX + c] = ek[k];
+          a.Q8[r * a.n + i + c] = (uint8_t)(int)qk[k];
+        }
       }
     }
     if (lr == 0 && a.err_sq) a.err_sq[r] += eacc;
   }
+}
+
+// Per block of B columns starting at i = blk * B: rows p of U[i:i+w, i:i+w]
+// divided by U_pp, zero on and below the diagonal, padded to NSTEP x NSTEP,
+// followed by 1/U_pp (0 past w).
+template <int NSTEP>
+__global__ __launch_bounds__(256) void diag_blocks_kernel(const float* U, int64_t n, int64_t B, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * B;
+  const int w = (int)std::min<int64_t>(B, n - i);
+  float* dst = out + (int64_t)blockIdx.x * (NSTEP * NSTEP + NSTEP);
+  for (int idx = threadIdx.x; idx < NSTEP * NSTEP; idx += 256) {
+    const int p = idx / NSTEP, j = idx % NSTEP;
+    float u = 0.f;
+    if (p < w && j < w && j > p) u = U[(i + p) * n + i + j] / U[(i + p) * n + i + p];
+    dst[idx] = u;
+  }
+  for (int p = threadIdx.x; p < NSTEP; p += 256) dst[NSTEP * NSTEP + p] = (p < w) ? 1.f / U[(i + p) * n + i + p] : 0.f;
 }
 
 template <int LPR>
@@ -355,9 +410,17 @@ dim3 rows_grid(int64_t cols, int64_t rows) {
 
 }  // namespace
 
-size_t quantize_workspace_bytes(int64_t m, int64_t n) {
-  if (m < 1 || n < 1) return 0;
-  return align256((size_t)m * n * 4) + align256((size_t)m * n) + align256((size_t)m * BMAX * 4);
+// Workspace: fp32 working copy V [m x n], codes [m x n] bytes, E [m x 128],
+// then the prepared diagonal factor blocks.
+inline int nstep_for(int64_t B) { return B <= 32 ? 32 : BMAX; }
+inline size_t dblk_bytes(int64_t n, int64_t B) {
+  const int64_t ns = nstep_for(B);
+  return (size_t)cdiv(n, B) * (size_t)(ns * ns + ns) * 4;
+}
+
+size_t quantize_workspace_bytes(int64_t m, int64_t n, int64_t B) {
+  if (m < 1 || n < 1 || B < 1) return 0;
+  return align256((size_t)m * n * 4) + align256((size_t)m * n) + align256((size_t)m * BMAX * 4) + align256(dblk_bytes(n, B));
 }
 
 hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, const float* U, int bits,
@@ -369,6 +432,10 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   uint8_t* Q8 = (uint8_t*)p;
   p += align256((size_t)m * n);
   float* E = (float*)p;
+  p += align256((size_t)m * BMAX * 4);
+  float* Dblk = (float*)p;
+  const int nstep = nstep_for(B);
+  const int64_t dstride = (int64_t)nstep * nstep + nstep;
 
   const int maxq = (1 << bits) - 1;
   const int64_t G = group <= 0 ? 1 : cdiv(n, group);
@@ -387,6 +454,8 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   if (err_sq)
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(m, 256), 1024)), dim3(256), 0, st,
                        err_sq, m);
+  if (nstep == 32) hipLaunchKernelGGL((diag_blocks_kernel<32>), dim3((unsigned)cdiv(n, B)), dim3(256), 0, st, U, n, B, Dblk);
+  else hipLaunchKernelGGL((diag_blocks_kernel<BMAX>), dim3((unsigned)cdiv(n, B)), dim3(256), 0, st, U, n, B, Dblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -395,7 +464,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
     if (group > B && i % group == 0)
       hipLaunchKernelGGL(row_params_kernel, dim3(prow), dim3(256), 0, st, (const float*)V, m, n, i, group, maxq, S,
                          Z, G, i / group);
-    SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, Q8, E, err_sq};
+    SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, Q8, E, err_sq, Dblk + (i / B) * dstride};
     if (B <= 32) launch_sweep<4>(a, gmode, st);
     else launch_sweep<16>(a, gmode, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -13,6 +13,8 @@
 // fp32 accumulators of v_mfma_f32_32x32x16_{f16,bf16}.  Partial tiles go to
 // the workspace; a second kernel sums the splits in a fixed order, scales by
 // 2, adds to H and writes both triangles, so results are deterministic.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -21,10 +23,18 @@ namespace gptq {
 namespace {
 
 constexpr int TILE = 256;
-constexpr int KC16 = 32;   // tokens per LDS stage, 16-bit inputs
+constexpr int KC16 = 64;   // tokens per LDS stage, 16-bit inputs
 constexpr int KC32 = 16;   // tokens per LDS stage, fp32 inputs
-constexpr int PITCH16 = KC16 + 8;  // halfs per feature row in LDS (80 B)
+constexpr int PITCH16 = KC16;      // halfs per feature row in LDS (128 B, 8 slots of 16 B)
 constexpr int PITCH32 = TILE + 4;  // floats per token row in LDS
+constexpr int NXCD = 8;            // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int SB_H = 8, SB_W = 4;  // tile regions of 8 x 4 tiles (share 12 feature blocks)
+
+// LDS slot of 16-byte token group `slot` (0..7) in feature row `row`: XOR
+// swizzled by row bits 0-2 (eight consecutive rows read by the MFMA fragment
+// loads land on distinct banks) and bits 3-5 (the transposed stores of eight
+// feature octets land on distinct banks).
+__device__ __forceinline__ int swz(int row, int slot) { return slot ^ (row & 7) ^ ((row >> 3) & 7); }
 
 __device__ __forceinline__ void tile_of(int t, int& bi, int& bj) {
   int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
@@ -32,6 +42,29 @@ __device__ __forceinline__ void tile_of(int t, int& bi, int& bj) {
   while (r * (r + 1) / 2 > t) --r;
   bi = r;
   bj = t - r * (r + 1) / 2;
+}
+
+// The t-th lower tile when tiles are listed region by region (8 tile-rows by
+// 4 tile-columns, each region row-major), so that consecutive tiles share
+// feature blocks.
+__device__ __forceinline__ void region_tile(int t, int nt1, int& bi, int& bj) {
+  for (int si = 0; si * SB_H < nt1; ++si) {
+    const int r0 = si * SB_H, r1 = min(nt1, r0 + SB_H);
+    for (int sj = 0; sj * SB_W < r1; ++sj) {
+      const int c0 = sj * SB_W;
+      int cnt = 0;
+      for (int r = r0; r < r1; ++r) cnt += max(0, min(r + 1, c0 + SB_W) - c0);
+      if (t < cnt) {
+        for (int r = r0; r < r1; ++r) {
+          const int w = max(0, min(r + 1, c0 + SB_W) - c0);
+          if (t < w) { bi = r; bj = c0 + t; return; }
+          t -= w;
+        }
+      }
+      t -= cnt;
+    }
+  }
+  bi = bj = 0;
 }
 
 struct SyrkArgs {
@@ -42,8 +75,22 @@ struct SyrkArgs {
   int ntiles;
   int nsplit;
   int64_t nchunks;
-  float* partial;  // [nsplit][ntiles][256][256]
+  int64_t per_xcd;  // work items per XCD (items = nsplit * ntiles, padded to a multiple of NXCD)
+  float* partial;   // [nsplit][ntiles][256][256]
 };
+
+// Work item of this workgroup: XCD x (= blockIdx.x % 8) takes items
+// [x * per_xcd, (x + 1) * per_xcd) in order, item = split * ntiles + region
+// tile, so the workgroups resident on one XCD share token ranges and tiles.
+__device__ __forceinline__ bool syrk_item(const SyrkArgs& a, int& split, int& tlin, int& bi, int& bj) {
+  const int64_t item = (int64_t)(blockIdx.x % NXCD) * a.per_xcd + blockIdx.x / NXCD;
+  if (item >= (int64_t)a.nsplit * a.ntiles) return false;
+  split = (int)(item / a.ntiles);
+  const int nt1 = (int)cdiv(a.n, TILE);
+  region_tile((int)(item % a.ntiles), nt1, bi, bj);
+  tlin = bi * (bi + 1) / 2 + bj;
+  return true;
+}
 
 // ---------------------------------------------------------------------------- 16-bit inputs
 
@@ -54,10 +101,9 @@ void syrk16_kernel(SyrkArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  int bi, bj;
-  tile_of(blockIdx.x, bi, bj);
+  int split, tlin, bi, bj;
+  if (!syrk_item(a, split, tlin, bi, bj)) return;
   const bool diag = (bi == bj);
-  const int split = blockIdx.y;
   const int64_t cb = (int64_t)split * a.nchunks / a.nsplit;
   const int64_t ce = (int64_t)(split + 1) * a.nchunks / a.nsplit;
   const uint16_t* __restrict__ X = (const uint16_t*)a.X;
@@ -65,21 +111,35 @@ void syrk16_kernel(SyrkArgs a) {
   // loader role: operand (0: rows bi, 1: rows bj), feature octet, token octet
   const int op = tid >> 7;
   const int fo = tid & 31;
-  const int to = (tid >> 5) & 3;
-  const bool loader = !(diag && op == 1);
+  const int to = (tid >> 5) & 3;  // token octets to, to + 4 of the 64-token stage
   const int fbase = (op == 0 ? bi : bj) * TILE + fo * 8;
+  const bool loader = !(diag && op == 1) && fbase < a.n;
 
-  u32x4 rg[8];
+  u32x4 rg[16];
   auto gload = [&](int64_t chunk) {
-    const int64_t t0 = chunk * KC16 + to * 8;
+    const int64_t t0 = chunk * KC16;
+    const bool full = t0 + KC16 <= a.tokens;
+    if (VEC && full) {
+      if (loader) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t t = t0 + e;
+        for (int e = 0; e < 16; ++e) {
+          const int64_t t = t0 + (to + 4 * (e >> 3)) * 8 + (e & 7);
+          rg[e] = *(const u32x4*)(X + t * a.ldx + fbase);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) rg[e] = u32x4{0u, 0u, 0u, 0u};
+      }
+      return;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t t = t0 + (to + 4 * (e >> 3)) * 8 + (e & 7);
       u32x4 v = {0u, 0u, 0u, 0u};
       if (loader && t < a.tokens) {
         const uint16_t* p = X + t * a.ldx + fbase;
         if (VEC) {
-          if (fbase + 8 <= a.n) v = *(const u32x4*)p;
+          v = *(const u32x4*)p;
         } else {
           uint32_t h[8];
 #pragma unroll
@@ -90,21 +150,26 @@ void syrk16_kernel(SyrkArgs a) {
       rg[e] = v;
     }
   };
-  // 8x8 (token, feature) -> (feature, token) transpose, then 8 x 16-byte LDS stores
+  // 8x8 (token, feature) -> (feature, token) transposes, then 16-byte LDS stores
   auto lstore = [&](int buf) {
-    if (!loader) return;
-    uint16_t* base = &lds[buf][op][(fo * 8) * PITCH16 + to * 8];
+    if (diag && op == 1) return;
+    uint16_t* T = lds[buf][op];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint32_t lo[4], hi[4];
+    for (int h = 0; h < 2; ++h) {
+      const int slot = to + 4 * h;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t x0 = rg[2 * d][c], x1 = rg[2 * d + 1][c];
-        lo[d] = (x0 & 0xFFFFu) | (x1 << 16);          // feature 2c, tokens 2d, 2d+1
-        hi[d] = (x0 >> 16) | (x1 & 0xFFFF0000u);      // feature 2c+1
+      for (int c = 0; c < 4; ++c) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t x0 = rg[8 * h + 2 * d][c], x1 = rg[8 * h + 2 * d + 1][c];
+          lo[d] = (x0 & 0xFFFFu) | (x1 << 16);          // feature 2c, tokens 2d, 2d+1
+          hi[d] = (x0 >> 16) | (x1 & 0xFFFF0000u);      // feature 2c+1
+        }
+        const int r0 = fo * 8 + 2 * c, r1 = r0 + 1;
+        *(u32x4*)(T + r0 * PITCH16 + swz(r0, slot) * 8) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        *(u32x4*)(T + r1 * PITCH16 + swz(r1, slot) * 8) = u32x4{hi[0], hi[1], hi[2], hi[3]};
       }
-      *(u32x4*)(base + (2 * c) * PITCH16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-      *(u32x4*)(base + (2 * c + 1) * PITCH16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
     }
   };
 
@@ -125,15 +190,19 @@ void syrk16_kernel(SyrkArgs a) {
       const uint16_t* Ti = lds[buf][0];
       const uint16_t* Tj = diag ? lds[buf][0] : lds[buf][1];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int koff = ks * 16 + (lane >> 5) * 8;
+      for (int ks = 0; ks < KC16 / 16; ++ks) {
+        const int slot = ks * 2 + (lane >> 5);
         u32x4 av[4], bv[4];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          av[mb] = *(const u32x4*)(Ti + (wr * 128 + mb * 32 + (lane & 31)) * PITCH16 + koff);
+        for (int mb = 0; mb < 4; ++mb) {
+          const int row = wr * 128 + mb * 32 + (lane & 31);
+          av[mb] = *(const u32x4*)(Ti + row * PITCH16 + swz(row, slot) * 8);
+        }
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          bv[nb] = *(const u32x4*)(Tj + (wc * 128 + nb * 32 + (lane & 31)) * PITCH16 + koff);
+        for (int nb = 0; nb < 4; ++nb) {
+          const int row = wc * 128 + nb * 32 + (lane & 31);
+          bv[nb] = *(const u32x4*)(Tj + row * PITCH16 + swz(row, slot) * 8);
+        }
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -152,7 +221,7 @@ void syrk16_kernel(SyrkArgs a) {
     }
   }
 
-  float* out = a.partial + ((int64_t)split * a.ntiles + blockIdx.x) * (TILE * TILE);
+  float* out = a.partial + ((int64_t)split * a.ntiles + tlin) * (TILE * TILE);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -172,10 +241,9 @@ void syrk32_kernel(SyrkArgs a) {
   __shared__ float lds[2][2][KC32 * PITCH32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  int bi, bj;
-  tile_of(blockIdx.x, bi, bj);
+  int split, tlin, bi, bj;
+  if (!syrk_item(a, split, tlin, bi, bj)) return;
   const bool diag = (bi == bj);
-  const int split = blockIdx.y;
   const int64_t cb = (int64_t)split * a.nchunks / a.nsplit;
   const int64_t ce = (int64_t)(split + 1) * a.nchunks / a.nsplit;
   const float* __restrict__ X = (const float*)a.X;
@@ -235,7 +303,7 @@ void syrk32_kernel(SyrkArgs a) {
     }
   }
 
-  float* out = a.partial + ((int64_t)split * a.ntiles + blockIdx.x) * (TILE * TILE);
+  float* out = a.partial + ((int64_t)split * a.ntiles + tlin) * (TILE * TILE);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -294,6 +362,7 @@ int syrk_splits(int64_t n, int64_t tokens, int kc, int& ntiles, int64_t& nchunks
   const int64_t nt1 = cdiv(n, TILE);
   ntiles = (int)(nt1 * (nt1 + 1) / 2);
   nchunks = cdiv(tokens, kc);
+  // about 8 rounds of 256 workgroups, each split at least 4 stages long
   int64_t s = 2048 / ntiles;
   s = std::min<int64_t>(s, nchunks / 4);
   if (s < 1) s = 1;
@@ -317,8 +386,10 @@ hipError_t syrk_accumulate(float* H, int64_t n, const void* X, int dtype, int64_
   int64_t nchunks;
   const int kc = dtype == 2 ? KC32 : KC16;
   const int s = syrk_splits(n, tokens, kc, ntiles, nchunks);
-  SyrkArgs a{X, ldx, (int)n, tokens, ntiles, s, nchunks, (float*)ws};
-  dim3 grid((unsigned)ntiles, (unsigned)s);
+  const int64_t items = (int64_t)s * ntiles;
+  const int64_t per_xcd = cdiv(items, NXCD);
+  SyrkArgs a{X, ldx, (int)n, tokens, ntiles, s, nchunks, per_xcd, (float*)ws};
+  dim3 grid((unsigned)(per_xcd * NXCD));
   if (dtype == 2) {
     hipLaunchKernelGGL(syrk32_kernel, grid, dim3(256), 0, stream, a);
   } else {

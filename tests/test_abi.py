@@ -47,8 +47,9 @@ def test_workspace_sizes():
     assert pw.hessian_workspace_bytes(4096, 0) == 0
     assert pw.prepare_workspace_bytes(4096) >= 4096 * 4096 * 4
     assert pw.prepare_workspace_bytes(0) == 0
-    assert pw.quantize_workspace_bytes(4096, 4096) >= 4096 * 4096 * 5
-    assert pw.quantize_workspace_bytes(10, 0) == 0
+    assert pw.quantize_workspace_bytes(4096, 4096, 128) >= 4096 * 4096 * 5
+    assert pw.quantize_workspace_bytes(10, 0, 128) == 0
+    assert pw.quantize_workspace_bytes(10, 10, 0) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
