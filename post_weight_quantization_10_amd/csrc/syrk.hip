@@ -234,6 +234,226 @@ void syrk16_kernel(SyrkArgs a) {
       }
 }
 
+// ---------------------------------------------------------------------------- 16-bit inputs, DMA path
+//
+// Same tiles and work order as above, but X moves global -> LDS with
+// buffer_load_dwordx4 ... lds (no VGPR staging) through a ring of NSTAGE = 5
+// 32-token stages (all 160 KiB of LDS): three stages in flight while one is
+// consumed.  LDS keeps
+// X token-major (as in HBM): per stage and operand, 32 token rows of 512 B,
+// the 16-byte chunks of row t XOR-swizzled by h(t & 3) = {0, 6, 10, 12},
+// which keeps every fragment read bank-conflict-free whether the LDS serves
+// 16 lanes x 8 B or 32 lanes x 8 B per cycle.  MFMA operands are
+// read with ds_read_b64_tr_b16: within a 16-lane group, source lane j points
+// at [token t0 + j/4][features F + 4*(j%4)], and lane i receives feature F+i
+// for tokens t0..t0+3, i.e. the K-contiguous fragment the MFMA wants.
+// Tokens past the end of X read as zero (buffer bounds); features past n only
+// reach outputs that are never written.
+
+constexpr int DKC = 32;                        // tokens per stage
+constexpr int NSTAGE = 5;
+constexpr int OPB = DKC * TILE * 2;            // bytes per operand per stage (16 KiB)
+constexpr int STB = 2 * OPB;                   // bytes per stage
+
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __bf16 bf16x4_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
+#define LDS_AS __attribute__((address_space(3)))
+
+template <int DT>
+__device__ __forceinline__ uint2 tr_read(const char LDS_AS* p) {
+  if (DT == 0) {
+    fp16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((fp16x4_t LDS_AS*)p);
+    return __builtin_bit_cast(uint2, v);
+  } else {
+    bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4_t LDS_AS*)p);
+    return __builtin_bit_cast(uint2, v);
+  }
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane global -> LDS copy: lane l's 16 bytes at byte offset
+// voff of the buffer described by rs land at LDS address lds_addr + 16 l
+// (bounds-checked: past num_records they read as zero).  Written as inline
+// assembly so that the compiler does not treat the asynchronous LDS write as
+// aliasing every LDS read (it would then wait for all copies in flight before
+// each stage); ordering is explicit instead: wait_vmcnt before the stage's
+// barrier.  Nothing else in these kernels uses M0.  The instruction has no
+// register result.
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_addr, int voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voff),
+               "s"(rs));
+}
+
+__device__ __forceinline__ int dswz(int r) { return (0xCA60 >> (4 * (r & 3))) & 0xF; }  // {0, 6, 10, 12}
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t b = (uint64_t)base;
+  return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xFFFFu), (int)nbytes, 0x00020000};
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// the only cross-wave data here are the stage DMAs, which every wave has
+// already waited for with wait_vmcnt, and LDS reads of a stage are consumed
+// before the wave reaches the next barrier.  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// vmcnt-only wait (expcnt and lgkmcnt left at their "no wait" maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void syrk16_dma_kernel(SyrkArgs a) {
+  // one LDS object per stage, so the compiler can tell the stage being read
+  // from the stages the DMA is still writing
+  __shared__ __attribute__((aligned(1024))) char st0[STB];
+  __shared__ __attribute__((aligned(1024))) char st1[STB];
+  __shared__ __attribute__((aligned(1024))) char st2[STB];
+  __shared__ __attribute__((aligned(1024))) char st3[STB];
+  __shared__ __attribute__((aligned(1024))) char st4[STB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  int split, tlin, bi, bj;
+  if (!syrk_item(a, split, tlin, bi, bj)) return;
+  const bool diag = (bi == bj);
+  const int64_t cb = (int64_t)split * a.nchunks / a.nsplit;
+  const int64_t ce = (int64_t)(split + 1) * a.nchunks / a.nsplit;
+  const uint16_t* X = (const uint16_t*)a.X;
+  const int64_t row_bytes = a.ldx * 2;
+
+  // this lane's share of one stage: 4 x 1 KiB per operand (two token rows each)
+  auto issue = [&](int64_t chunk, char* stage) {
+    const int64_t t0 = chunk * DKC;
+    const int64_t rows = min<int64_t>(DKC, a.tokens - t0);
+    const i32x4 rs = make_rsrc(X + t0 * a.ldx, (uint32_t)(rows * row_bytes));
+    const uint32_t sbase = (uint32_t)(uintptr_t)((char LDS_AS*)stage);
+#pragma unroll
+    for (int op = 0; op < 2; ++op) {
+      if (op == 1 && diag) break;
+      const int fb = (op == 0 ? bi : bj) * TILE;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 2 * (4 * wave + q) + (lane >> 5);  // token row within the stage
+        const int c = (lane & 31) ^ dswz(r);             // logical 16-byte chunk held at this lane's slot
+        const int voff = (int)(r * row_bytes) + (fb + 8 * c) * 2;
+        dma16(rs, sbase + op * OPB + (2 * (4 * wave + q)) * 512, voff);
+      }
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = zero16();
+
+  // fragment addressing (see the comment above)
+  const int g = lane >> 4, j16 = lane & 15;
+  const int fa = wr * 128 + 16 * (g & 1) + 4 * (j16 & 3);   // + mb * 32
+  const int fbb = wc * 128 + 16 * (g & 1) + 4 * (j16 & 3);  // + nb * 32
+  const int trow = 8 * (g >> 1) + (j16 >> 2);               // + 16 * ks (+ 4 for the upper half)
+
+  // fragments of one K16 step: 4 A and 4 B operands of 8 halfs each
+  struct Frag {
+    uint4 a[4], b[4];
+  };
+  auto rd = [&](const char* st, int ks, Frag& F) {
+    const char* Ti = st;
+    const char* Tj = diag ? st : st + OPB;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 16 * ks + trow + 4 * h;
+      const int sw = dswz(r);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int f = fa + mb * 32;
+        const uint2 x = tr_read<DT>((const char LDS_AS*)(Ti + r * 512 + (((f >> 3) ^ sw) << 4) + ((f & 4) << 1)));
+        if (h == 0) { F.a[mb].x = x.x; F.a[mb].y = x.y; } else { F.a[mb].z = x.x; F.a[mb].w = x.y; }
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int f = fbb + nb * 32;
+        const uint2 x = tr_read<DT>((const char LDS_AS*)(Tj + r * 512 + (((f >> 3) ^ sw) << 4) + ((f & 4) << 1)));
+        if (h == 0) { F.b[nb].x = x.x; F.b[nb].y = x.y; } else { F.b[nb].z = x.x; F.b[nb].w = x.y; }
+      }
+    }
+  };
+  auto mma = [&](const Frag& F) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if (DT == 0)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, F.a[mb]),
+                                                              __builtin_bit_cast(half8, F.b[nb]), acc[mb][nb], 0, 0, 0);
+        else
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, F.a[mb]),
+                                                               __builtin_bit_cast(bf16x8, F.b[nb]), acc[mb][nb], 0, 0, 0);
+      }
+  };
+  // wait until this wave's copies of stage `stage` have landed, `ahead` later stages still in flight
+  auto wait_stage = [&](int64_t ahead) {
+    if (diag) {
+      if (ahead >= 3) wait_vmcnt<12>(); else if (ahead == 2) wait_vmcnt<8>(); else if (ahead == 1) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+    } else {
+      if (ahead >= 3) wait_vmcnt<24>(); else if (ahead == 2) wait_vmcnt<16>(); else if (ahead == 1) wait_vmcnt<8>();
+      else wait_vmcnt<0>();
+    }
+  };
+
+  // Software pipeline over stages (two K16 steps each).  The barrier that
+  // publishes stage c+1 sits between the two MFMA batches of stage c, so a
+  // wave waiting at it still has 16 MFMAs in flight; the first fragments of
+  // stage c+1 are read while the second batch of stage c executes.
+  Frag F0, F1;
+  auto step = [&](int64_t c, const char* cur, const char* nx, char* fill) {
+    mma(F0);                 // stage c, tokens 0..15
+    rd(cur, 1, F1);          // stage c, tokens 16..31
+    if (c + 1 < ce) {
+      wait_stage(min<int64_t>(2, ce - 2 - c));
+      stage_barrier();       // stage c+1 visible; stage c-1 no longer read by anyone
+      if (c + NSTAGE - 1 < ce) issue(c + NSTAGE - 1, fill);
+    }
+    mma(F1);
+    if (c + 1 < ce) rd(nx, 0, F0);  // stage c+1, tokens 0..15
+  };
+
+  if (cb < ce) {
+    issue(cb, st0);
+    if (cb + 1 < ce) issue(cb + 1, st1);
+    if (cb + 2 < ce) issue(cb + 2, st2);
+    if (cb + 3 < ce) issue(cb + 3, st3);
+    wait_stage(min<int64_t>(3, ce - 1 - cb));
+    stage_barrier();
+    rd(st0, 0, F0);
+  }
+  for (int64_t c = cb; c < ce; c += NSTAGE) {
+    step(c, st0, st1, st4);
+    if (c + 1 < ce) step(c + 1, st1, st2, st0);
+    if (c + 2 < ce) step(c + 2, st2, st3, st1);
+    if (c + 3 < ce) step(c + 3, st3, st4, st2);
+    if (c + 4 < ce) step(c + 4, st4, st0, st3);
+  }
+
+  float* out = a.partial + ((int64_t)split * a.ntiles + tlin) * (TILE * TILE);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wr * 128 + mb * 32 + mfma32_row(r, lane);
+        const int col = wc * 128 + nb * 32 + mfma32_col(lane);
+        out[row * TILE + col] = acc[mb][nb][r];
+      }
+}
+
 // ---------------------------------------------------------------------------- fp32 inputs
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -376,7 +596,8 @@ size_t syrk_workspace_bytes(int64_t n, int64_t tokens, int dtype) {
   if (n < 1 || tokens < 1) return 0;
   int ntiles;
   int64_t nchunks;
-  const int s = syrk_splits(n, tokens, dtype == 2 ? KC32 : KC16, ntiles, nchunks);
+  // the smallest stage size gives the most splits, so this bounds every path
+  const int s = syrk_splits(n, tokens, dtype == 2 ? KC32 : DKC, ntiles, nchunks);
   return (size_t)s * (size_t)ntiles * TILE * TILE * sizeof(float);
 }
 
@@ -384,24 +605,18 @@ hipError_t syrk_accumulate(float* H, int64_t n, const void* X, int dtype, int64_
                            hipStream_t stream) {
   int ntiles;
   int64_t nchunks;
-  const int kc = dtype == 2 ? KC32 : KC16;
+  const bool vec = dtype != 2 && (n % 8 == 0) && (ldx % 8 == 0) && (((uintptr_t)X & 15) == 0);
+  const int kc = dtype == 2 ? KC32 : (vec ? DKC : KC16);
   const int s = syrk_splits(n, tokens, kc, ntiles, nchunks);
   const int64_t items = (int64_t)s * ntiles;
   const int64_t per_xcd = cdiv(items, NXCD);
   SyrkArgs a{X, ldx, (int)n, tokens, ntiles, s, nchunks, per_xcd, (float*)ws};
   dim3 grid((unsigned)(per_xcd * NXCD));
-  if (dtype == 2) {
-    hipLaunchKernelGGL(syrk32_kernel, grid, dim3(256), 0, stream, a);
-  } else {
-    const bool vec = (n % 8 == 0) && (ldx % 8 == 0) && (((uintptr_t)X & 15) == 0);
-    if (dtype == 0) {
-      if (vec) hipLaunchKernelGGL((syrk16_kernel<0, true>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((syrk16_kernel<0, false>), grid, dim3(256), 0, stream, a);
-    } else {
-      if (vec) hipLaunchKernelGGL((syrk16_kernel<1, true>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((syrk16_kernel<1, false>), grid, dim3(256), 0, stream, a);
-    }
-  }
+  if (dtype == 2) hipLaunchKernelGGL(syrk32_kernel, grid, dim3(256), 0, stream, a);
+  else if (vec && dtype == 0) hipLaunchKernelGGL((syrk16_dma_kernel<0>), grid, dim3(256), 0, stream, a);
+  else if (vec) hipLaunchKernelGGL((syrk16_dma_kernel<1>), grid, dim3(256), 0, stream, a);
+  else if (dtype == 0) hipLaunchKernelGGL((syrk16_kernel<0, false>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((syrk16_kernel<1, false>), grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(syrk_reduce_kernel, dim3((unsigned)ntiles, 16), dim3(256), 0, stream, H, (int)n,
