@@ -306,44 +306,52 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void syrk16_dma_kernel(SyrkArgs a) {
-  // one LDS object per stage, so the compiler can tell the stage being read
-  // from the stages the DMA is still writing
-  __shared__ __attribute__((aligned(1024))) char st0[STB];
-  __shared__ __attribute__((aligned(1024))) char st1[STB];
-  __shared__ __attribute__((aligned(1024))) char st2[STB];
-  __shared__ __attribute__((aligned(1024))) char st3[STB];
-  __shared__ __attribute__((aligned(1024))) char st4[STB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Fragment read order within one K16 step, matched to the order in which the
+// MFMAs (mb-major over the 4 x 4 block grid) consume them: A0, B0..B3, A1..A3,
+// each as its two 4-token halves.
+__device__ __forceinline__ constexpr int rd_isb(int i) { return (i >= 2 && i < 10) ? 1 : 0; }
+__device__ __forceinline__ constexpr int rd_blk(int i) { return i < 2 ? 0 : (i < 10 ? (i - 2) >> 1 : 1 + ((i - 10) >> 1)); }
+__device__ __forceinline__ constexpr int rd_half(int i) { return i & 1; }
+
+template <int DT, bool DIAG>
+__device__ __forceinline__ void syrk16_dma_body(const SyrkArgs& a, int split, int tlin, int bi, int bj, char* st0,
+                                                char* st1, char* st2, char* st3, char* st4) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
-  int split, tlin, bi, bj;
-  if (!syrk_item(a, split, tlin, bi, bj)) return;
-  const bool diag = (bi == bj);
   const int64_t cb = (int64_t)split * a.nchunks / a.nsplit;
   const int64_t ce = (int64_t)(split + 1) * a.nchunks / a.nsplit;
   const uint16_t* X = (const uint16_t*)a.X;
   const int64_t row_bytes = a.ldx * 2;
 
-  // this lane's share of one stage: 4 x 1 KiB per operand (two token rows each)
-  auto issue = [&](int64_t chunk, char* stage) {
+  // This lane's share of one stage: for each operand, 4 copies of 1 KiB (two
+  // token rows each).  The byte offset within the stage's rows and the LDS
+  // destination are fixed per lane and copy; only the buffer base moves.
+  int voff[2][4];
+#pragma unroll
+  for (int op = 0; op < 2; ++op)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int fb = (op == 0 ? bi : bj) * TILE;
+      const int r = 2 * (4 * wave + q) + (lane >> 5);  // token row within the stage
+      const int c = (lane & 31) ^ dswz(r);             // logical 16-byte chunk held at this lane's slot
+      voff[op][q] = (int)(r * row_bytes) + (fb + 8 * c) * 2;
+    }
+  auto rsrc_of = [&](int64_t chunk) {
     const int64_t t0 = chunk * DKC;
     const int64_t rows = min<int64_t>(DKC, a.tokens - t0);
-    const i32x4 rs = make_rsrc(X + t0 * a.ldx, (uint32_t)(rows * row_bytes));
+    return make_rsrc(X + t0 * a.ldx, (uint32_t)(rows * row_bytes));
+  };
+  auto dma1 = [&](const i32x4& rs, char* stage, int k) {  // copy k of 8 (4 if DIAG)
+    const int op = k >> 2, q = k & 3;
     const uint32_t sbase = (uint32_t)(uintptr_t)((char LDS_AS*)stage);
+    dma16(rs, sbase + op * OPB + (2 * (4 * wave + q)) * 512, voff[op][q]);
+  };
+  constexpr int NCOPY = DIAG ? 4 : 8;
+  auto issue = [&](int64_t chunk, char* stage) {
+    const i32x4 rs = rsrc_of(chunk);
 #pragma unroll
-    for (int op = 0; op < 2; ++op) {
-      if (op == 1 && diag) break;
-      const int fb = (op == 0 ? bi : bj) * TILE;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = 2 * (4 * wave + q) + (lane >> 5);  // token row within the stage
-        const int c = (lane & 31) ^ dswz(r);             // logical 16-byte chunk held at this lane's slot
-        const int voff = (int)(r * row_bytes) + (fb + 8 * c) * 2;
-        dma16(rs, sbase + op * OPB + (2 * (4 * wave + q)) * 512, voff);
-      }
-    }
+    for (int k = 0; k < NCOPY; ++k) dma1(rs, stage, k);
   };
 
   f32x16 acc[4][4];
@@ -358,47 +366,40 @@ void syrk16_dma_kernel(SyrkArgs a) {
   const int fbb = wc * 128 + 16 * (g & 1) + 4 * (j16 & 3);  // + nb * 32
   const int trow = 8 * (g >> 1) + (j16 >> 2);               // + 16 * ks (+ 4 for the upper half)
 
-  // fragments of one K16 step: 4 A and 4 B operands of 8 halfs each
   struct Frag {
     uint4 a[4], b[4];
   };
+  // read i (0..15) of the K16 step ks of stage st into F
+  auto rd1 = [&](const char* st, int ks, Frag& F, int i) {
+    const int isb = rd_isb(i), blk = rd_blk(i), h = rd_half(i);
+    const char* T = (isb && !DIAG) ? st + OPB : st;
+    const int r = 16 * ks + trow + 4 * h;
+    const int f = (isb ? fbb : fa) + blk * 32;
+    const uint2 x = tr_read<DT>((const char LDS_AS*)(T + r * 512 + (((f >> 3) ^ dswz(r)) << 4) + ((f & 4) << 1)));
+    uint4& d = isb ? F.b[blk] : F.a[blk];
+    if (h == 0) { d.x = x.x; d.y = x.y; } else { d.z = x.x; d.w = x.y; }
+  };
   auto rd = [&](const char* st, int ks, Frag& F) {
-    const char* Ti = st;
-    const char* Tj = diag ? st : st + OPB;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = 16 * ks + trow + 4 * h;
-      const int sw = dswz(r);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int f = fa + mb * 32;
-        const uint2 x = tr_read<DT>((const char LDS_AS*)(Ti + r * 512 + (((f >> 3) ^ sw) << 4) + ((f & 4) << 1)));
-        if (h == 0) { F.a[mb].x = x.x; F.a[mb].y = x.y; } else { F.a[mb].z = x.x; F.a[mb].w = x.y; }
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int f = fbb + nb * 32;
-        const uint2 x = tr_read<DT>((const char LDS_AS*)(Tj + r * 512 + (((f >> 3) ^ sw) << 4) + ((f & 4) << 1)));
-        if (h == 0) { F.b[nb].x = x.x; F.b[nb].y = x.y; } else { F.b[nb].z = x.x; F.b[nb].w = x.y; }
-      }
-    }
+    for (int i = 0; i < 16; ++i) rd1(st, ks, F, i);
+  };
+  auto mfma1 = [&](const Frag& F, int i) {
+    const int mb = i >> 2, nb = i & 3;
+    if (DT == 0)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, F.a[mb]),
+                                                          __builtin_bit_cast(half8, F.b[nb]), acc[mb][nb], 0, 0, 0);
+    else
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, F.a[mb]),
+                                                           __builtin_bit_cast(bf16x8, F.b[nb]), acc[mb][nb], 0, 0, 0);
   };
   auto mma = [&](const Frag& F) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        if (DT == 0)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, F.a[mb]),
-                                                              __builtin_bit_cast(half8, F.b[nb]), acc[mb][nb], 0, 0, 0);
-        else
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, F.a[mb]),
-                                                               __builtin_bit_cast(bf16x8, F.b[nb]), acc[mb][nb], 0, 0, 0);
-      }
+    for (int i = 0; i < 16; ++i) mfma1(F, i);
   };
-  // wait until this wave's copies of stage `stage` have landed, `ahead` later stages still in flight
+  // wait until this wave's copies of the oldest stage in flight have landed,
+  // `ahead` later stages still in flight
   auto wait_stage = [&](int64_t ahead) {
-    if (diag) {
+    if (DIAG) {
       if (ahead >= 3) wait_vmcnt<12>(); else if (ahead == 2) wait_vmcnt<8>(); else if (ahead == 1) wait_vmcnt<4>();
       else wait_vmcnt<0>();
     } else {
@@ -408,20 +409,50 @@ void syrk16_dma_kernel(SyrkArgs a) {
   };
 
   // Software pipeline over stages (two K16 steps each).  The barrier that
-  // publishes stage c+1 sits between the two MFMA batches of stage c, so a
-  // wave waiting at it still has 16 MFMAs in flight; the first fragments of
-  // stage c+1 are read while the second batch of stage c executes.
+  // publishes stage c+1 sits between the two MFMA batches of stage c.  In the
+  // steady state every LDS fragment read is issued between two MFMAs (the
+  // second half of stage c is read under the first half's MFMAs, the first
+  // half of stage c+1 under the second half's), so with one wave per SIMD the
+  // read latency stays hidden behind the matrix pipe; the copies that refill
+  // the ring go out between the MFMAs of the second half.
   Frag F0, F1;
+  auto step_ss = [&](int64_t c, const char* cur, const char* nx, char* fill) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mfma1(F0, i);
+      rd1(cur, 1, F1, i);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    wait_stage(2);
+    stage_barrier();  // stage c+1 visible; stage c-1 no longer read by anyone
+    const i32x4 rs = rsrc_of(c + NSTAGE - 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mfma1(F1, i);
+      rd1(nx, 0, F0, i);
+      if ((i & 1) && (i >> 1) < NCOPY) dma1(rs, fill, i >> 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // general step (pipeline fill and drain)
   auto step = [&](int64_t c, const char* cur, const char* nx, char* fill) {
-    mma(F0);                 // stage c, tokens 0..15
-    rd(cur, 1, F1);          // stage c, tokens 16..31
+    mma(F0);
+    rd(cur, 1, F1);
     if (c + 1 < ce) {
       wait_stage(min<int64_t>(2, ce - 2 - c));
-      stage_barrier();       // stage c+1 visible; stage c-1 no longer read by anyone
+      stage_barrier();
       if (c + NSTAGE - 1 < ce) issue(c + NSTAGE - 1, fill);
     }
     mma(F1);
-    if (c + 1 < ce) rd(nx, 0, F0);  // stage c+1, tokens 0..15
+    if (c + 1 < ce) rd(nx, 0, F0);
   };
 
   if (cb < ce) {
@@ -433,7 +464,16 @@ void syrk16_dma_kernel(SyrkArgs a) {
     stage_barrier();
     rd(st0, 0, F0);
   }
-  for (int64_t c = cb; c < ce; c += NSTAGE) {
+  int64_t c = cb;
+  // steady state: all five steps of a ring turn refill (c + 8 < ce)
+  for (; c + 2 * NSTAGE - 2 < ce; c += NSTAGE) {
+    step_ss(c, st0, st1, st4);
+    step_ss(c + 1, st1, st2, st0);
+    step_ss(c + 2, st2, st3, st1);
+    step_ss(c + 3, st3, st4, st2);
+    step_ss(c + 4, st4, st0, st3);
+  }
+  for (; c < ce; c += NSTAGE) {
     step(c, st0, st1, st4);
     if (c + 1 < ce) step(c + 1, st1, st2, st0);
     if (c + 2 < ce) step(c + 2, st2, st3, st1);
@@ -452,6 +492,22 @@ void syrk16_dma_kernel(SyrkArgs a) {
         const int col = wc * 128 + nb * 32 + mfma32_col(lane);
         out[row * TILE + col] = acc[mb][nb][r];
       }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void syrk16_dma_kernel(SyrkArgs a) {
+  // one LDS object per stage, so the compiler can tell the stage being read
+  // from the stages the DMA is still writing
+  __shared__ __attribute__((aligned(1024))) char st0[STB];
+  __shared__ __attribute__((aligned(1024))) char st1[STB];
+  __shared__ __attribute__((aligned(1024))) char st2[STB];
+  __shared__ __attribute__((aligned(1024))) char st3[STB];
+  __shared__ __attribute__((aligned(1024))) char st4[STB];
+  int split, tlin, bi, bj;
+  if (!syrk_item(a, split, tlin, bi, bj)) return;
+  if (bi == bj) syrk16_dma_body<DT, true>(a, split, tlin, bi, bj, st0, st1, st2, st3, st4);
+  else syrk16_dma_body<DT, false>(a, split, tlin, bi, bj, st0, st1, st2, st3, st4);
 }
 
 // ---------------------------------------------------------------------------- fp32 inputs
