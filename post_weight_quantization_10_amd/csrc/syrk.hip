@@ -595,7 +595,9 @@ void syrk32_kernel(SyrkArgs a) {
 // ---------------------------------------------------------------------------- split reduction + mirror
 
 // One workgroup per 64x64 sub-block of a lower tile: H <- H + 2 * sum_s P_s,
-// written to both triangles (the upper one through an LDS transpose).
+// written to both triangles (the upper one through an LDS transpose).  Each
+// thread owns 4 rows x 4 columns and sums the splits in split order, with
+// 16-byte loads of four splits in flight per row (16 per thread).
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(float* H, int n, const float* partial, int ntiles,
                                                           int nsplit) {
   __shared__ float t[64][65];
@@ -605,26 +607,49 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(float* H, int n, const
   int bi, bj;
   tile_of(tile, bi, bj);
   const bool diag = (bi == bj);
+  if (diag && sc > sr) return;  // the diagonal tile's upper half mirrors its lower half
   const int tid = threadIdx.x;
-  const int c = tid & 63;
-#pragma unroll 4
-  for (int u = 0; u < 16; ++u) {
-    const int r = (tid >> 6) + 4 * u;
-    const int li = sr * 64 + r, lj = sc * 64 + c;
-    const int gi = bi * TILE + li, gj = bj * TILE + lj;
-    float sum = 0.f;
-    for (int s = 0; s < nsplit; ++s) sum += partial[((int64_t)s * ntiles + tile) * (TILE * TILE) + li * TILE + lj];
-    float h = 0.f;
-    if (gi < n && gj < n && (!diag || gi >= gj)) {
-      float* p = H + (int64_t)gi * n + gj;
-      h = *p + 2.f * sum;
-      *p = h;
-      if (diag && gi != gj) H[(int64_t)gj * n + gi] = h;
+  const int c4 = (tid & 15) * 4, r16 = tid >> 4;
+  const int64_t pstride = (int64_t)ntiles * (TILE * TILE);
+  const float* P = partial + (int64_t)tile * (TILE * TILE) + (sr * 64 + r16) * TILE + sc * 64 + c4;
+  f32x4 sum[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) sum[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= nsplit; s += 4) {
+    f32x4 p[4][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) p[v][u] = *(const f32x4*)(P + (s + v) * pstride + 16 * u * TILE);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sum[u] += p[v][u];
+  }
+  for (; s < nsplit; ++s)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sum[u] += *(const f32x4*)(P + s * pstride + 16 * u * TILE);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = r16 + 16 * u;
+    const int gi = bi * TILE + sr * 64 + r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int gj = bj * TILE + sc * 64 + c4 + e;
+      float h = 0.f;
+      if (gi < n && gj < n && (!diag || gi >= gj)) {
+        float* ph = H + (int64_t)gi * n + gj;
+        h = *ph + 2.f * sum[u][e];
+        *ph = h;
+        if (diag && gi != gj) H[(int64_t)gj * n + gi] = h;
+      }
+      t[r][c4 + e] = h;
     }
-    t[r][c] = h;
   }
   if (diag) return;  // uniform per block
   __syncthreads();
+  const int c = tid & 63;
 #pragma unroll 4
   for (int u = 0; u < 16; ++u) {
     const int r = (tid >> 6) + 4 * u;  // row of the mirrored block = column of the lower block
