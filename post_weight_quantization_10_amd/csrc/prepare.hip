@@ -12,11 +12,15 @@
 // inverse (2n^3/3 flops) instead of four factor-sized steps (4n^3/3).
 //
 //   1. reversed copy + damping  A = J H J + lambda I             (HBM-bound)
-//   2. blocked right-looking Cholesky of A, panels of NB = 64:
-//        leaf kernel: one workgroup factors the NB x NB diagonal block and
-//        inverts it in the same pass (registers + LDS broadcasts);
-//        panel solve  A21 <- A21 L11^{-T}  (MFMA GEMM with the leaf inverse)
-//        trailing     A22 <- A22 - A21 A21^T  (MFMA GEMM, lower tiles only)
+//   2. blocked right-looking Cholesky of A in NB = 64 column blocks, one
+//      kernel per block column k.  Workgroup 0 takes the next diagonal block:
+//      it applies the update from block column k to it, factors it and
+//      inverts the factor (Dinv_{k+1}).  Every other workgroup owns a 128 x 128
+//      lower tile of the trailing matrix: it solves the two panel slabs it
+//      needs on the fly, L21 = A21 Dinv_k^T (MFMA, fp32), applies
+//      A22 <- A22 - L21 L21^T (MFMA, fp32), and the tiles of the first tile
+//      column store their slab of L21.  So the next diagonal block is factored
+//      while the rest of the trailing update runs, one launch per block.
 //   3. triangular inverse in place by recursive doubling: with the NB-block
 //      inverses on the diagonal, for block sizes s = NB, 2NB, ...:
 //        L21^{-} = -L22^{-1} (L21 L11^{-1})   (two batched MFMA GEMMs)
@@ -65,110 +69,391 @@ __global__ __launch_bounds__(256) void reverse_damp_kernel(const float* H, float
   }
 }
 
-// Factor the kb x kb diagonal block at (k0, k0) of A in place (lower) and
-// write its inverse to Dinv (NB x NB, zero above the diagonal), in one pass.
+constexpr int TB = 128;          // trailing-update tile
+constexpr int LP = 65;           // LDS pitch of 64-column leaf matrices (floats)
+constexpr int LLP = 68;          // LDS pitch of the leaf factor: 16-byte aligned rows
+constexpr int SMEM = 20480;      // floats of LDS per workgroup (80 KiB)
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Diagonal block J = [j0, j0 + kb) (workgroup-wide, 256 threads).
 //
-// Thread (ty, tx) of a 16 x 16 grid keeps a 4 x 4 tile (rows 4ty.., columns
-// 4tx..) of the block being factored (Am) and of the running inverse (Tm) in
-// registers.  Step j, right-looking: d = A[j][j]; column j of L is
-// A[r][j]/sqrt(d); row j of L^{-1} is R[j][:]/sqrt(d); then
-//   A[r][c] -= L[r][j] L[c][j]        (r, c > j)
-//   R[r][c] -= L[r][j] Linv[j][c]     (r > j, c <= j)
-// with R = I initially (so that R[r][:] becomes row r of L^{-1} times L[r][r]).
-// The raw column j+1 of A and row j+1 of R are published to double-buffered
-// LDS by their owners, so each step needs one barrier.  Rows/columns past kb
-// are padded with the identity, which factors trivially.
-__global__ __launch_bounds__(256) void chol_leaf_kernel(float* A, int64_t lda, int64_t k0, int kb, float* Dinv,
-                                                        int32_t* info, int64_t n) {
-  if (*info != 0) return;
-  __shared__ __attribute__((aligned(16))) float colbuf[2][NB];
-  __shared__ __attribute__((aligned(16))) float rowbuf[2][NB];
-  const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
-  float Am[4][4], Tm[4][4];
+// If kp >= 0, first the update from block column K = [kp, kp + NB):
+//   Lrow = A[J, K] Dinv_K^T   (the rows J of that block column of the factor)
+//   D    = A[J, J] - Lrow Lrow^T
+// (two 64 x 64 x 64 MFMA products), else D = A[J, J].  Then D = L L^T and
+// Dinv_J = L^{-1}, written to dinv_out (NB x NB, zero outside the kb x kb
+// lower triangle).  Rows and columns past kb are padded with the identity.
+//
+// Wave 0 runs the right-looking Cholesky with lane i holding row i of D in
+// registers: at column j the pivot comes from lane j (readlane), l_i =
+// D[i][j] / sqrt(pivot), the next pivot's entry is updated first from a
+// readlane of l_{j+1}, the rest of the row from a broadcast of l through LDS.
+// Wave 1 forward-substitutes L X = I with lane c holding column c of X, one
+// chunk of 8 rows behind wave 0; the chunks are separated by workgroup
+// barriers, so no wave ever waits on a flag.
+__device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t n, int64_t j0, int64_t kp,
+                                        const float* __restrict__ dinv_prev, float* __restrict__ dinv_out,
+                                        int32_t* info, float* smem) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = (int)min<int64_t>(NB, n - j0);
+  float* sD = smem;              // 64 x LP
+  float* sP = sD + 64 * LP;      // 64 x LP
+  float* sQ = sP + 64 * LP;      // 64 x LP
+  float* sL = sQ + 64 * LP;      // 64 x LLP
+  float* bc = sL + 64 * LLP;     // 64
+  float* rinv = bc + 64;         // 64
+  int* failed = (int*)(rinv + 64);
+
+  // loads from clamped (in-range) addresses, then selects: no branches, all
+  // loads in flight together
+  // (the empty asm makes every load unconditional; otherwise the compiler
+  // moves each load under its select, one wait per load)
+  {
+    constexpr int NU = NB * NB / 256;
+    float v[NU], pv[NU], qv[NU];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int r = 4 * ty + a, c = 4 * tx + b;
-      float v = 0.f;
-      if (r < kb && c < kb) { if (c <= r) v = A[(k0 + r) * lda + k0 + c]; }
-      else if (r == c) v = 1.f;
-      Am[a][b] = v;
-      Tm[a][b] = (r == c) ? 1.f : 0.f;
+    for (int u = 0; u < NU; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e >> 6, c = e & 63;
+      const int rc = min(r, kb - 1), cc = min(c, kb - 1);
+      v[u] = A[(j0 + rc) * n + j0 + cc];
+      if (kp >= 0) {
+        pv[u] = A[(j0 + rc) * n + kp + c];
+        qv[u] = dinv_prev[r * NB + c];
+      }
     }
-  if (tx == 0)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) colbuf[0][4 * ty + a] = Am[a][0];
-  if (ty == 0)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) rowbuf[0][4 * tx + b] = Tm[0][b];
+    for (int u = 0; u < NU; ++u) {
+      asm volatile("" : "+v"(v[u]));
+      const int e = tid + 256 * u;
+      const int r = e >> 6, c = e & 63;
+      sD[r * LP + c] = (r < kb && c < kb) ? ((c <= r) ? v[u] : 0.f) : ((r == c) ? 1.f : 0.f);
+      if (kp >= 0) {
+        asm volatile("" : "+v"(pv[u]));
+        sP[r * LP + c] = (r < kb) ? pv[u] : 0.f;
+        sQ[r * LP + c] = qv[u];
+      }
+    }
+  }
+  if (tid == 0) *failed = 0;
   __syncthreads();
 
-  for (int jb = 0; jb < NB / 4; ++jb) {
+  if (kp >= 0) {
+    const int bm = wave >> 1, bn = wave & 1;  // this wave's 32 x 32 output block
+    const int kr = lane >> 5, cl = lane & 31;
+    f32x16 o = zero16();
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = 4 * jb + jj;
-      const float* cb = colbuf[j & 1];
-      const float* rb = rowbuf[j & 1];
-      const float d = cb[j];
-      if (!(d > 0.f) || !(d < INFINITY)) {  // uniform: every thread read the same d
-        if (tid == 0) atomicCAS(info, 0, (int32_t)(n - (k0 + j)));
-        return;
+    for (int kk = 0; kk < NB / 2; ++kk) {
+      const int k = 2 * kk + kr;
+      if (bn == 1 || kk < 16)  // Dinv_K is lower triangular
+        o = mfma_f32(sP[(32 * bm + cl) * LP + k], sQ[(32 * bn + cl) * LP + k], o);
+    }
+    __syncthreads();  // every wave is done reading A[J, K]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sP[(32 * bm + mfma32_row(r, lane)) * LP + 32 * bn + cl] = o[r];
+    __syncthreads();
+    if (!(bm == 0 && bn == 1)) {  // lower blocks of D
+      f32x16 u = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NB / 2; ++kk) {
+        const int k = 2 * kk + kr;
+        u = mfma_f32(sP[(32 * bm + cl) * LP + k], sP[(32 * bn + cl) * LP + k], u);
       }
-      const float rs = __builtin_amdgcn_rsqf(d);
-      const float sd = d * rs;
-      const f32x4 cr = *(const f32x4*)&cb[4 * ty];
-      const f32x4 cc = *(const f32x4*)&cb[4 * tx];
-      const f32x4 rr = *(const f32x4*)&rb[4 * tx];
-      float lr[4], lc[4], tc[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) lr[a] = (4 * ty + a > j) ? cr[a] * rs : 0.f;
+      for (int r = 0; r < 16; ++r) sD[(32 * bm + mfma32_row(r, lane)) * LP + 32 * bn + cl] -= u[r];
+    }
+    __syncthreads();
+  }
+
+  // Nine chunk barriers in every wave: wave 0 factors columns 8c..8c+7 in
+  // chunk c < 8, wave 1 inverts rows 8(c-1)..8c-1 in chunk c >= 1.
+  constexpr int NCH = NB / 8 + 1;
+  if (wave == 0) {
+    float a[NB];  // row `lane` of D
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        lc[b] = (4 * tx + b > j) ? cc[b] * rs : 0.f;
-        tc[b] = (4 * tx + b <= j) ? rr[b] * rs : 0.f;
-      }
-      if (4 * ty + 3 > j) {
+    for (int q = 0; q < NB; ++q) a[q] = sD[lane * LP + q];
+    bool bad = false;  // uniform
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+    for (int ch = 0; ch < NCH - 1; ++ch) {
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            Am[a][b] = fmaf(-lr[a], lc[b], Am[a][b]);
-            Tm[a][b] = fmaf(-lr[a], tc[b], Tm[a][b]);
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = 8 * ch + jj;
+        const float piv = readlane_f(a[j], j);
+        if (!bad && !(piv > 0.f && piv < INFINITY)) {
+          bad = true;
+          if (lane == 0) {
+            atomicCAS(info, 0, (int32_t)(n - (j0 + j)));
+            *failed = 1;
           }
-      }
-      if (tx == jb) {  // column j of L
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int r = 4 * ty + a;
-          Am[a][jj] = (r > j) ? lr[a] : (r == j ? sd : Am[a][jj]);
         }
-      }
-      if (ty == jb) {  // row j of L^{-1}
+        if (!bad) {
+          const float rs = __builtin_amdgcn_rsqf(piv);
+          const float l = lane > j ? a[j] * rs : (lane == j ? piv * rs : 0.f);
+          sL[lane * LLP + j] = l;
+          if (lane == 0) rinv[j] = rs;
+          if (j + 1 < NB) {
+            bc[lane] = l;
+            __builtin_amdgcn_wave_barrier();
+            // every broadcast read of this column in flight before the first use
+            f32x4 v[NB / 4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) Tm[jj][b] = tc[b];
-      }
-      if (j + 1 < NB) {
-        const int jn = j + 1, jnb = jn >> 2, jnj = (jj + 1) & 3;
-        if (tx == jnb)
+            for (int g = 0; g < NB / 4; ++g)  // constant trip count: the guards fold once j is known
+              if (4 * g + 3 >= j + 2) v[g] = *(const f32x4*)&bc[4 * g];
+            const float ln = readlane_f(l, j + 1);  // the next pivot's entry first, without LDS
+            a[j + 1] = fmaf(-l, ln, a[j + 1]);
 #pragma unroll
-          for (int a = 0; a < 4; ++a) colbuf[jn & 1][4 * ty + a] = Am[a][jnj];
-        if (ty == jnb)
+            for (int g = 0; g < NB / 4; ++g)
+              if (4 * g + 3 >= j + 2)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) rowbuf[jn & 1][4 * tx + b] = Tm[jnj][b];
+                for (int e = 0; e < 4; ++e)
+                  if (4 * g + e >= j + 2) a[4 * g + e] = fmaf(-l, v[g][e], a[4 * g + e]);
+            __builtin_amdgcn_wave_barrier();
+          }
+        }
+        asm volatile("" ::: "memory");
       }
       __syncthreads();
     }
-  }
+    __syncthreads();
+  } else if (wave == 1) {
+    float x[NB];  // column `lane` of L^{-1}
+    __syncthreads();
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+    for (int ch = 1; ch < NCH; ++ch) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int r = 4 * ty + a, c = 4 * tx + b;
-      if (r < kb && c <= r) A[(k0 + r) * lda + k0 + c] = Am[a][b];
-      Dinv[r * NB + c] = (r < kb && c <= r) ? Tm[a][b] : 0.f;
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = 8 * (ch - 1) + jj;
+        float s0 = (lane == j) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+        // every broadcast read of row j in flight before the first use
+        f32x4 v[NB / 4];
+#pragma unroll
+        for (int g = 0; g < NB / 4; ++g)  // constant trip count: the guards fold once j is known
+          if (4 * g < j) v[g] = *(const f32x4*)&sL[j * LLP + 4 * g];
+        const float rj = rinv[j];
+#pragma unroll
+        for (int g = 0; g < NB / 4; ++g) {
+          if (4 * g < j) {
+            if (4 * g + 0 < j) s0 = fmaf(-v[g][0], x[4 * g + 0], s0);
+            if (4 * g + 1 < j) s1 = fmaf(-v[g][1], x[4 * g + 1], s1);
+            if (4 * g + 2 < j) s2 = fmaf(-v[g][2], x[4 * g + 2], s2);
+            if (4 * g + 3 < j) s3 = fmaf(-v[g][3], x[4 * g + 3], s3);
+          }
+        }
+        x[j] = ((s0 + s1) + (s2 + s3)) * rj;
+        // materialize this row now and keep later rows' loads below it: otherwise
+        // the arithmetic is sunk to the final stores with every row's loads live
+        asm volatile("" : "+v"(x[j])::"memory");
+      }
+      __syncthreads();
     }
+    if (*failed == 0) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) dinv_out[j * NB + lane] = (j < kb && lane < kb) ? x[j] : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chol_first_kernel(const float* A, int64_t n, float* dinv, int32_t* info) {
+  if (*info != 0) return;
+  __shared__ __attribute__((aligned(16))) float smem[SMEM];
+  leaf_block(A, n, 0, -1, nullptr, dinv, info, smem);
+}
+
+// Panel layout in LDS: [rows][64] floats, 16-byte groups XOR-swizzled by row.
+__device__ __forceinline__ int pidx(int r, int k) { return r * 64 + (k ^ ((r & 15) << 2)); }
+
+template <bool VEC>
+__device__ __forceinline__ f32x4 ld4(const float* p) {
+  return VEC ? *(const f32x4*)p : f32x4{p[0], p[1], p[2], p[3]};
+}
+
+// Rows 32w..32w+31 of S (a 64-column panel in LDS) times Dinv^T, both 32-wide
+// output blocks, for this wave.
+__device__ __forceinline__ void panel_solve(const float* S, const float* sD, int w, int lane, f32x16 (&o)[2]) {
+  const int kr = lane >> 5, cl = lane & 31;
+  o[0] = zero16();
+  o[1] = zero16();
+#pragma unroll
+  for (int kk = 0; kk < NB / 2; ++kk) {
+    const int k = 2 * kk + kr;
+    const float av = S[pidx(32 * w + cl, k)];
+    if (kk < 16) o[0] = mfma_f32(av, sD[pidx(cl, k)], o[0]);  // Dinv is lower triangular
+    o[1] = mfma_f32(av, sD[pidx(32 + cl, k)], o[1]);
+  }
+}
+
+// One 128 x 128 lower tile t of the trailing matrix [R0, n)^2, R0 = k0 + NB.
+template <bool VEC>
+__device__ __forceinline__ void tile_update(float* __restrict__ A, float* __restrict__ L,
+                                            const float* __restrict__ dinv_k, int64_t n, int64_t k0, int t,
+                                            float* smem) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float* sD = smem;            // 64 x 64: Dinv_k
+  float* sR = sD + 64 * 64;    // 128 x 64: rows of the tile's row slab, A21 then L21
+  float* sC = sR + 128 * 64;   // 128 x 64: the same for the column slab
+  int tm = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+  while ((tm + 1) * (tm + 2) / 2 <= t) ++tm;
+  while (tm * (tm + 1) / 2 > t) --tm;
+  const int tn = t - tm * (tm + 1) / 2;
+  const int64_t R0 = k0 + NB;
+  const int64_t r0 = R0 + (int64_t)tm * TB, c0 = R0 + (int64_t)tn * TB;
+  const bool dg = tm == tn;
+  const int wr = wave >> 1, wc = wave & 1;
+  const bool active = !(dg && wr < wc);  // that quadrant of a diagonal tile lies above the diagonal
+
+  // Panel rows and Dinv_k: all loads in flight together, then to LDS.  Rows
+  // past n are clamped: they only reach outputs that are never stored.
+  {
+    f32x4 pr[8], pc[8], dv[4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e >> 4, g = 4 * (e & 15);
+      pr[u] = ld4<VEC>(A + min(r0 + r, n - 1) * n + k0 + g);
+      if (!dg) pc[u] = ld4<VEC>(A + min(c0 + r, n - 1) * n + k0 + g);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      dv[u] = *(const f32x4*)&dinv_k[(e >> 4) * NB + 4 * (e & 15)];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e >> 4, g = 4 * (e & 15);
+      *(f32x4*)&sR[pidx(r, g)] = pr[u];
+      if (!dg) *(f32x4*)&sC[pidx(r, g)] = pc[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      *(f32x4*)&sD[pidx(e >> 4, 4 * (e & 15))] = dv[u];
+    }
+  }
+  // C of this wave's 64 x 64 quadrant; its latency overlaps the panel solves
+  const bool interior = r0 + TB <= n && c0 + TB <= n;
+  const int64_t rbase = r0 + 64 * wr + 4 * (lane >> 5);
+  const int64_t cbase = c0 + 64 * wc + (lane & 31);
+  f32x16 cp[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) cp[mb][nb] = zero16();
+  // interior tiles: a uniform base and 32-bit lane offsets (the tile spans
+  // fewer than 2^31 bytes), so loads and stores need no 64-bit addresses
+  const float* tbase = A + (r0 * n + c0);
+  const uint32_t n32 = (uint32_t)n;
+  const uint32_t loff = (uint32_t)(64 * wr + 4 * (lane >> 5)) * n32 + (uint32_t)(64 * wc + (lane & 31));
+  if (active && interior) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cp[mb][nb][r] = tbase[loff + (uint32_t)(32 * mb + 8 * (r >> 2) + (r & 3)) * n32 + (uint32_t)(32 * nb)];
+  } else if (active) {  // entries past n are never stored: clamped loads
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float* colp = A + min(cbase + 32 * nb, n - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cp[mb][nb][r] = colp[min(rbase + 32 * mb + 8 * (r >> 2) + (r & 3), n - 1) * n];
+      }
+  }
+  __syncthreads();
+
+  // L21 slabs; each wave reads and then overwrites only its own 32 rows
+  const int cl = lane & 31;
+  f32x16 o[2];
+  panel_solve(sR, sD, wave, lane, o);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = 32 * wave + mfma32_row(r, lane);
+      sR[pidx(rr, 32 * nb + cl)] = o[nb][r];
+      if (tn == 0 && r0 + rr < n) L[(r0 + rr) * n + k0 + 32 * nb + cl] = o[nb][r];
+    }
+  if (!dg) {
+    panel_solve(sC, sD, wave, lane, o);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sC[pidx(32 * wave + mfma32_row(r, lane), 32 * nb + cl)] = o[nb][r];
+  }
+  __syncthreads();
+  if (!active) return;
+
+  const float* sB = dg ? sR : sC;
+  const int kr = lane >> 5;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
+#pragma unroll 8
+  for (int kk = 0; kk < NB / 2; ++kk) {
+    const int k = 2 * kk + kr;
+    const float a0 = sR[pidx(64 * wr + cl, k)], a1 = sR[pidx(64 * wr + 32 + cl, k)];
+    const float b0 = sB[pidx(64 * wc + cl, k)], b1 = sB[pidx(64 * wc + 32 + cl, k)];
+    acc[0][0] = mfma_f32(a0, b0, acc[0][0]);
+    acc[0][1] = mfma_f32(a0, b1, acc[0][1]);
+    acc[1][0] = mfma_f32(a1, b0, acc[1][0]);
+    acc[1][1] = mfma_f32(a1, b1, acc[1][1]);
+  }
+  // lower part only; the next diagonal block is left to workgroup 0, which
+  // reads it before the update
+  if (interior && !dg && tm != 0) {
+    float* tb = A + (r0 * n + c0);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          tb[loff + (uint32_t)(32 * mb + 8 * (r >> 2) + (r & 3)) * n32 + (uint32_t)(32 * nb)] =
+              cp[mb][nb][r] - acc[mb][nb][r];
+    return;
+  }
+  const int64_t skip_end = (tm == 0) ? R0 + NB : R0;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = rbase + 32 * mb + 8 * (r >> 2) + (r & 3);
+        const int64_t col = cbase + 32 * nb;
+        if (row < n && col <= row && !(row < skip_end && col < skip_end))
+          A[row * n + col] = cp[mb][nb][r] - acc[mb][nb][r];
+      }
+}
+
+// Block column k at k0 (n - k0 > NB): workgroup 0 factors diagonal block
+// k + 1, workgroups 1.. update the lower tiles of the trailing matrix.
+template <bool VEC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chol_step_kernel(float* A, float* L, float* dinv, int64_t n, int64_t k0,
+                                                           int32_t* info) {
+  if (*info != 0) return;
+  __shared__ __attribute__((aligned(16))) float smem[SMEM];
+  const int64_t kbk = k0 / NB;
+  if (blockIdx.x == 0)
+    leaf_block(A, n, k0 + NB, k0, dinv + kbk * NB * NB, dinv + (kbk + 1) * NB * NB, info, smem);
+  else
+    tile_update<VEC>(A, L, dinv + kbk * NB * NB, n, k0, (int)blockIdx.x - 1, smem);
 }
 
 // Zero the strict upper triangle and put the NB-block inverses on the diagonal.
@@ -194,9 +479,9 @@ __global__ __launch_bounds__(256) void write_u_kernel(const float* A, float* U, 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct PrepWs {
-  float* A;
-  float* tmp;
-  float* dinv;
+  float* A;     // damped, reversed H; its trailing part is updated in place
+  float* L;     // the factor, then its inverse
+  float* dinv;  // inverses of the NB x NB diagonal blocks of the factor
   float* lam;
 };
 
@@ -205,8 +490,8 @@ PrepWs carve(void* ws, int64_t n) {
   PrepWs w;
   w.A = (float*)p;
   p += align256((size_t)n * n * 4);
-  w.tmp = (float*)p;
-  p += align256((size_t)n * ((n + 1) / 2) * 4);
+  w.L = (float*)p;
+  p += align256((size_t)n * n * 4);
   w.dinv = (float*)p;
   p += align256((size_t)cdiv(n, NB) * NB * NB * 4);
   w.lam = (float*)p;
@@ -219,8 +504,7 @@ dim3 row_grid(int64_t n) { return dim3((unsigned)std::min<int64_t>(cdiv(n, 256),
 
 size_t prepare_workspace_bytes(int64_t n) {
   if (n < 1) return 0;
-  return align256((size_t)n * n * 4) + align256((size_t)n * ((n + 1) / 2) * 4) +
-         align256((size_t)cdiv(n, NB) * NB * NB * 4) + 256;
+  return 2 * align256((size_t)n * n * 4) + align256((size_t)cdiv(n, NB) * NB * NB * 4) + 256;
 }
 
 hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t* info, float* lambda_out, void* ws,
@@ -231,34 +515,20 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // blocked right-looking Cholesky of A (lower)
-  for (int64_t k0 = 0; k0 < n; k0 += NB) {
-    const int kb = (int)std::min<int64_t>(NB, n - k0);
-    float* dblk = w.dinv + (k0 / NB) * NB * NB;
-    hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(256), 0, s, w.A, n, k0, kb, dblk, info, n);
-    const int64_t rest = n - k0 - kb;
-    if (rest > 0) {
-      float* P = w.A + (k0 + kb) * n + k0;
-      GemmDesc g{};
-      g.A = P; g.lda = n;
-      g.B = dblk; g.ldb = NB;
-      g.C = P; g.ldc = n;
-      g.M = (int)rest; g.N = kb; g.K = kb; g.batch = 1;
-      g.alpha = 1.f; g.beta = 0.f; g.info = info;
-      if ((e = gemm_f32(g, false, true, s)) != hipSuccess) return e;
-      GemmDesc t{};
-      t.A = P; t.lda = n;
-      t.B = P; t.ldb = n;
-      t.C = w.A + (k0 + kb) * n + (k0 + kb); t.ldc = n;
-      t.M = (int)rest; t.N = (int)rest; t.K = kb; t.batch = 1;
-      t.alpha = -1.f; t.beta = 1.f; t.flags = GEMM_LOWER_TILES; t.info = info;
-      if ((e = gemm_f32(t, false, true, s)) != hipSuccess) return e;
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  // blocked right-looking Cholesky of A (lower): the factor's off-diagonal
+  // blocks go to L, the inverses of its diagonal blocks to dinv
+  hipLaunchKernelGGL(chol_first_kernel, dim3(1), dim3(256), 0, s, (const float*)w.A, n, w.dinv, info);
+  const bool vec = n % 4 == 0;
+  for (int64_t k0 = 0; k0 + NB < n; k0 += NB) {
+    const int64_t nt = cdiv(n - k0 - NB, TB);
+    const unsigned grid = (unsigned)(1 + nt * (nt + 1) / 2);
+    if (vec) hipLaunchKernelGGL((chol_step_kernel<true>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
+    else hipLaunchKernelGGL((chol_step_kernel<false>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
   }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // triangular inverse of the factor, in place, by recursive doubling
-  hipLaunchKernelGGL(trtri_init_kernel, row_grid(n), dim3(256), 0, s, w.A, n, (const float*)w.dinv, (const int32_t*)info);
+  hipLaunchKernelGGL(trtri_init_kernel, row_grid(n), dim3(256), 0, s, w.L, n, (const float*)w.dinv, (const int32_t*)info);
   for (int64_t bs = NB; bs < n; bs *= 2) {
     const int64_t full = n / (2 * bs);  // pairs of two complete bs-blocks
     const int64_t a_part = full * 2 * bs;
@@ -270,22 +540,22 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
       const int64_t s2 = pass == 0 ? bs : s2_part;
       const int64_t stride = 2 * bs * n + 2 * bs;
       GemmDesc g1{};  // tmp = L21 * Linv11
-      g1.A = w.A + (a + bs) * n + a; g1.lda = n; g1.strideA = stride;
-      g1.B = w.A + a * n + a; g1.ldb = n; g1.strideB = stride;
-      g1.C = w.tmp; g1.ldc = bs; g1.strideC = bs * bs;
+      g1.A = w.L + (a + bs) * n + a; g1.lda = n; g1.strideA = stride;
+      g1.B = w.L + a * n + a; g1.ldb = n; g1.strideB = stride;
+      g1.C = w.A; g1.ldc = bs; g1.strideC = bs * bs;
       g1.M = (int)s2; g1.N = (int)bs; g1.K = (int)bs; g1.batch = (int)count;
       g1.alpha = 1.f; g1.beta = 0.f; g1.flags = GEMM_B_LOWER; g1.info = info;
       if ((e = gemm_f32(g1, false, false, s)) != hipSuccess) return e;
       GemmDesc g2{};  // Linv21 = -Linv22 * tmp
-      g2.A = w.A + (a + bs) * n + (a + bs); g2.lda = n; g2.strideA = stride;
-      g2.B = w.tmp; g2.ldb = bs; g2.strideB = bs * bs;
-      g2.C = w.A + (a + bs) * n + a; g2.ldc = n; g2.strideC = stride;
+      g2.A = w.L + (a + bs) * n + (a + bs); g2.lda = n; g2.strideA = stride;
+      g2.B = w.A; g2.ldb = bs; g2.strideB = bs * bs;
+      g2.C = w.L + (a + bs) * n + a; g2.ldc = n; g2.strideC = stride;
       g2.M = (int)s2; g2.N = (int)bs; g2.K = (int)s2; g2.batch = (int)count;
       g2.alpha = -1.f; g2.beta = 0.f; g2.flags = GEMM_A_LOWER; g2.info = info;
       if ((e = gemm_f32(g2, false, false, s)) != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(write_u_kernel, row_grid(n), dim3(256), 0, s, (const float*)w.A, U, n, (const int32_t*)info);
+  hipLaunchKernelGGL(write_u_kernel, row_grid(n), dim3(256), 0, s, (const float*)w.L, U, n, (const int32_t*)info);
   return hipGetLastError();
 }
 
