@@ -68,6 +68,24 @@ def cpu_baseline(W16, X16, job, U_gpu):
                       f"{t1 - t0:.2f}/{t2 - t1:.2f}/{t3 - t2:.2f}"}
 
 
+def traffic_bytes(path):
+    """HBM bytes per Hessian launch from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        js = json.load(f)
+    src = os.path.join(ROOT, js.get("source", ""))
+    if not os.path.isfile(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != js.get("source_sha256"):
+            return None
+    return js.get("bytes_per_launch")
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -143,10 +161,7 @@ def main():
 
     flops_syrk = float(n) * (n + 1) * T
     achieved = flops_syrk / (ph["hessian"] * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = traffic_bytes(args.traffic)
     res = {
         "metric": "ms per 4096x4096 4-bit g128 GPTQ layer (incl. H^-1) + % MFMA/HBM roofline",
         "value": round(ms_step, 3),
@@ -169,7 +184,7 @@ def main():
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         "ms_layer_incl_hinv": round(ph["prepare"] + ph["quantize"], 4),
         "roofline": {
-            "kernel": "gptq_hessian_accumulate (MFMA fp16 SYRK, H += 2 X^T X)",
+            "kernel": "gptq_hessian_accumulate, H += 2 X^T X: syrk16_dma_kernel (MFMA fp16) + syrk_reduce_kernel",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_TF16,
