@@ -73,6 +73,9 @@ constexpr int TB = 128;          // trailing-update tile
 constexpr int LP = 65;           // LDS pitch of 64-column leaf matrices (floats)
 constexpr int LLP = 68;          // LDS pitch of the leaf factor: 16-byte aligned rows
 constexpr int SMEM = 20480;      // floats of LDS per workgroup (80 KiB)
+static_assert(3 * 64 * LP + 64 * LLP + 65 <= SMEM, "leaf LDS layout");
+static_assert(64 * LLP + 32 * 33 <= 2 * 64 * LP, "the inverse and the doubling products fit over the product buffers");
+static_assert(64 * 64 + 2 * 128 * 64 <= SMEM, "tile LDS layout");
 
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -90,13 +93,16 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 // Dinv_J = L^{-1}, written to dinv_out (NB x NB, zero outside the kb x kb
 // lower triangle).  Rows and columns past kb are padded with the identity.
 //
-// Wave 0 runs the right-looking Cholesky with lane i holding row i of D in
-// registers: at column j the pivot comes from lane j (readlane), l_i =
-// D[i][j] / sqrt(pivot), the next pivot's entry is updated first from a
-// readlane of l_{j+1}, the rest of the row from a broadcast of l through LDS.
-// Wave 1 forward-substitutes L X = I with lane c holding column c of X, one
-// chunk of 8 rows behind wave 0; the chunks are separated by workgroup
-// barriers, so no wave ever waits on a flag.
+// The factorization is blocked in four panels of PW = 16 columns: wave 0
+// factors a panel (lane i holds the panel's part of row i in registers; at
+// column j the pivot comes from lane j and each later panel column is updated
+// with a readlane of l: at most 15 FMAs per column, no LDS, no branch), then
+// all four waves apply the panel to the rest of the block with
+// v_mfma_f32_16x16x4f32.  The inverse: one wave inverts the four 16 x 16
+// diagonal blocks at once (lane = block, column; forward substitution), then
+// two levels of recursive doubling, X21 = -X22 (L21 X11), with MFMA products.
+// (A single wave issues an independent VALU op only every ~7 cycles, so the
+// work that is not on the column chain goes to the matrix cores.)
 __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t n, int64_t j0, int64_t kp,
                                         const float* __restrict__ dinv_prev, float* __restrict__ dinv_out,
                                         int32_t* info, float* smem) {
@@ -106,9 +112,10 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
   float* sD = smem;              // 64 x LP
   float* sP = sD + 64 * LP;      // 64 x LP
   float* sQ = sP + 64 * LP;      // 64 x LP
-  float* sL = sQ + 64 * LP;      // 64 x LLP
-  float* bc = sL + 64 * LLP;     // 64
-  float* rinv = bc + 64;         // 64
+  float* sL = sQ + 64 * LP;      // 64 x LLP: the factor, zero above the diagonal
+  float* sX = sP;                // 64 x LLP over sP and sQ once the update is applied: the inverse
+  float* sT = sP + 64 * LLP;     // 32 x 33: products of the doubling steps
+  float* rinv = sL + 64 * LLP;   // 64: 1 / L[j][j]
   int* failed = (int*)(rinv + 64);
 
   // loads from clamped (in-range) addresses, then selects: no branches, all
@@ -172,94 +179,132 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
     __syncthreads();
   }
 
-  // Nine chunk barriers in every wave: wave 0 factors columns 8c..8c+7 in
-  // chunk c < 8, wave 1 inverts rows 8(c-1)..8c-1 in chunk c >= 1.
-  constexpr int NCH = NB / 8 + 1;
+  // sX is free now (the update is applied): zero it, so that its upper
+  // blocks read as zero in the doubling products
+  for (int e = tid; e < 64 * LLP; e += 256) sX[e] = 0.f;
+
+  // ---- factor, PW-column panels
+  constexpr int PW = 16;
+  const int l16 = lane & 15, g16 = lane >> 4;
+  int badcol = -1;  // wave 0: first column whose pivot is not positive and finite (uniform)
+#pragma unroll 1
+  for (int c0 = 0; c0 < NB; c0 += PW) {
+    if (wave == 0) {
+      float a[PW];
+#pragma unroll
+      for (int k = 0; k < PW; ++k) a[k] = sD[lane * LP + c0 + k];
+#pragma unroll
+      for (int jj = 0; jj < PW; ++jj) {
+        const int j = c0 + jj;
+        const float piv = readlane_f(a[jj], j);
+        const bool ok = piv > 0.f && piv < INFINITY;
+        badcol = (badcol < 0 && !ok) ? j : badcol;
+        const float rs = __builtin_amdgcn_rsqf(piv);  // not finite after a failure: the rest is discarded
+        const float l = lane > j ? a[jj] * rs : (lane == j ? piv * rs : 0.f);
+        a[jj] = l;
+        if (lane == 0) rinv[j] = rs;
+#pragma unroll
+        for (int k = jj + 1; k < PW; ++k) a[k] = fmaf(-l, readlane_f(l, c0 + k), a[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < PW; ++k) sL[lane * LLP + c0 + k] = a[k];
+    }
+    __syncthreads();
+    // rows and columns [c0 + PW, NB) -= L[:, c0:c0+PW] L[:, c0:c0+PW]^T, 16 x 16
+    // blocks of the lower triangle, v_mfma_f32_16x16x4f32 (lane l: A[l%16][l/16],
+    // B[l/16][l%16]; result register r is row 4(l/16) + r, column l%16)
+    const int nb = (NB - c0 - PW) / 16;
+    for (int t = wave; t < nb * (nb + 1) / 2; t += 4) {
+      int bi = 0;
+      while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
+      const int bj = t - bi * (bi + 1) / 2;
+      const int r0 = c0 + PW + 16 * bi, s0 = c0 + PW + 16 * bj;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < PW; k += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sL[(r0 + l16) * LLP + c0 + k + g16],
+                                                    sL[(s0 + l16) * LLP + c0 + k + g16], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sD[(r0 + 4 * g16 + r) * LP + s0 + l16] -= acc[r];
+    }
+    __syncthreads();
+  }
+  if (wave == 0 && badcol >= 0 && lane == 0) {
+    atomicCAS(info, 0, (int32_t)(n - (j0 + badcol)));
+    *failed = 1;
+  }
+
+  // ---- inverse.  The four 16 x 16 diagonal blocks: lane = (block g16,
+  // column l16) forward-substitutes its column of the block's inverse.
   if (wave == 0) {
-    float a[NB];  // row `lane` of D
+    const int base = 16 * g16;
+    float x[16];
 #pragma unroll
-    for (int q = 0; q < NB; ++q) a[q] = sD[lane * LP + q];
-    bool bad = false;  // uniform
+    for (int j = 0; j < 16; ++j) {
+      f32x4 v[4];
 #pragma unroll
-    for (int ch = 0; ch < NCH - 1; ++ch) {
+      for (int g = 0; 4 * g < j; ++g) v[g] = *(const f32x4*)&sL[(base + j) * LLP + base + 4 * g];
+      float s0 = (l16 == j) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = 8 * ch + jj;
-        const float piv = readlane_f(a[j], j);
-        if (!bad && !(piv > 0.f && piv < INFINITY)) {
-          bad = true;
-          if (lane == 0) {
-            atomicCAS(info, 0, (int32_t)(n - (j0 + j)));
-            *failed = 1;
-          }
-        }
-        if (!bad) {
-          const float rs = __builtin_amdgcn_rsqf(piv);
-          const float l = lane > j ? a[j] * rs : (lane == j ? piv * rs : 0.f);
-          sL[lane * LLP + j] = l;
-          if (lane == 0) rinv[j] = rs;
-          if (j + 1 < NB) {
-            bc[lane] = l;
-            __builtin_amdgcn_wave_barrier();
-            // every broadcast read of this column in flight before the first use
-            f32x4 v[NB / 4];
-#pragma unroll
-            for (int g = 0; g < NB / 4; ++g)  // constant trip count: the guards fold once j is known
-              if (4 * g + 3 >= j + 2) v[g] = *(const f32x4*)&bc[4 * g];
-            const float ln = readlane_f(l, j + 1);  // the next pivot's entry first, without LDS
-            a[j + 1] = fmaf(-l, ln, a[j + 1]);
-#pragma unroll
-            for (int g = 0; g < NB / 4; ++g)
-              if (4 * g + 3 >= j + 2)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  if (4 * g + e >= j + 2) a[4 * g + e] = fmaf(-l, v[g][e], a[4 * g + e]);
-            __builtin_amdgcn_wave_barrier();
-          }
-        }
-        asm volatile("" ::: "memory");
+      for (int q = 0; q < j; ++q) {
+        if (q & 1) s1 = fmaf(-v[q >> 2][q & 3], x[q], s1);
+        else s0 = fmaf(-v[q >> 2][q & 3], x[q], s0);
       }
-      __syncthreads();
+      x[j] = (s0 + s1) * rinv[base + j];
     }
-    __syncthreads();
-  } else if (wave == 1) {
-    float x[NB];  // column `lane` of L^{-1}
-    __syncthreads();
 #pragma unroll
-    for (int ch = 1; ch < NCH; ++ch) {
+    for (int j = 0; j < 16; ++j) sX[(base + j) * LLP + base + l16] = x[j];
+  }
+  __syncthreads();
+
+  // 16 x 16 output block (row r0, column s0) of -X[r0.., kr..] T or of
+  // L[r0.., k..] X[k.., s0..]: C = sum over K of A[r][k] B[k][c]
+  auto prod16 = [&](const float* Am, int lda_, int ar, int ac, const float* Bm, int ldb_, int br, int bc_,
+                    int K) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; k += 4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Am[(ar + l16) * lda_ + ac + k + g16],
+                                                  Bm[(br + k + g16) * ldb_ + bc_ + l16], acc, 0, 0, 0);
+    return acc;
+  };
+  // doubling, 16 -> 32: pairs (0, 1) and (2, 3), wave 0 and wave 1
+  if (wave < 2) {
+    const int b0 = 32 * wave;  // X[b0+16.., b0..] = -X[b0+16.., b0+16..] (L[b0+16.., b0..] X[b0.., b0..])
+    const f32x4 t = prod16(sL, LLP, b0 + 16, b0, sX, LLP, b0, b0, 16);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = 8 * (ch - 1) + jj;
-        float s0 = (lane == j) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-        // every broadcast read of row j in flight before the first use
-        f32x4 v[NB / 4];
+    for (int r = 0; r < 4; ++r) sT[(16 * wave + 4 * g16 + r) * 33 + l16] = t[r];
+  }
+  __syncthreads();
+  if (wave < 2) {
+    const int b0 = 32 * wave;
+    const f32x4 t = prod16(sX, LLP, b0 + 16, b0 + 16, sT + 16 * wave * 33, 33, 0, 0, 16);
 #pragma unroll
-        for (int g = 0; g < NB / 4; ++g)  // constant trip count: the guards fold once j is known
-          if (4 * g < j) v[g] = *(const f32x4*)&sL[j * LLP + 4 * g];
-        const float rj = rinv[j];
+    for (int r = 0; r < 4; ++r) sX[(b0 + 16 + 4 * g16 + r) * LLP + b0 + l16] = -t[r];
+  }
+  __syncthreads();
+  // doubling, 32 -> 64: X[32.., ..32] = -X[32.., 32..] (L[32.., ..32] X[..32, ..32]);
+  // wave w computes the 16 x 16 block (w >> 1, w & 1) of each product
+  {
+    const int br = 16 * (wave >> 1), bcol = 16 * (wave & 1);
+    const f32x4 t = prod16(sL, LLP, 32 + br, 0, sX, LLP, 0, bcol, 32);
 #pragma unroll
-        for (int g = 0; g < NB / 4; ++g) {
-          if (4 * g < j) {
-            if (4 * g + 0 < j) s0 = fmaf(-v[g][0], x[4 * g + 0], s0);
-            if (4 * g + 1 < j) s1 = fmaf(-v[g][1], x[4 * g + 1], s1);
-            if (4 * g + 2 < j) s2 = fmaf(-v[g][2], x[4 * g + 2], s2);
-            if (4 * g + 3 < j) s3 = fmaf(-v[g][3], x[4 * g + 3], s3);
-          }
-        }
-        x[j] = ((s0 + s1) + (s2 + s3)) * rj;
-        // materialize this row now and keep later rows' loads below it: otherwise
-        // the arithmetic is sunk to the final stores with every row's loads live
-        asm volatile("" : "+v"(x[j])::"memory");
-      }
-      __syncthreads();
+    for (int r = 0; r < 4; ++r) sT[(br + 4 * g16 + r) * 33 + bcol + l16] = t[r];
+  }
+  __syncthreads();
+  {
+    const int br = 16 * (wave >> 1), bcol = 16 * (wave & 1);
+    const f32x4 t = prod16(sX, LLP, 32 + br, 32, sT, 33, 0, bcol, 32);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sX[(32 + br + 4 * g16 + r) * LLP + bcol + l16] = -t[r];
+  }
+  __syncthreads();
+  if (*failed == 0) {
+#pragma unroll
+    for (int u = 0; u < NB * NB / 256; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e >> 6, c = e & 63;
+      dinv_out[r * NB + c] = (r < kb && c < kb) ? sX[r * LLP + c] : 0.f;
     }
-    if (*failed == 0) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) dinv_out[j * NB + lane] = (j < kb && lane < kb) ? x[j] : 0.f;
-    }
-  } else {
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) __syncthreads();
   }
 }
 
