@@ -75,4 +75,43 @@ template <> struct Elem<2> {  // fp32
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+
+// ---------------------------------------------------------------------------- LDS-DMA staging
+
+#define LDS_AS __attribute__((address_space(3)))
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane global -> LDS copy: lane l's 16 bytes at byte offset
+// voff of the buffer described by rs land at LDS address lds_addr + 16 l
+// (bounds-checked: past num_records they read as zero).  Written as inline
+// assembly so that the compiler does not treat the asynchronous LDS write as
+// aliasing every LDS read (it would then wait for all copies in flight before
+// each stage); ordering is explicit instead: wait_vmcnt before the stage's
+// barrier.  Nothing else in these kernels uses M0.  The instruction has no
+// register result.
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_addr, int voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);  // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voff),
+               "s"(rs));
+}
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t b = (uint64_t)base;
+  return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xFFFFu), (int)nbytes, 0x00020000};
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// the only cross-wave data here are the stage DMAs, which every wave has
+// already waited for with wait_vmcnt, and LDS reads of a stage are consumed
+// before the wave reaches the next barrier.  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// vmcnt-only wait (expcnt and lgkmcnt left at their "no wait" maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 }  // namespace gptq

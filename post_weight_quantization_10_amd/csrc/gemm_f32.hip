@@ -182,6 +182,191 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmDesc d) {
       }
 }
 
+// ---------------------------------------------------------------------------- NN, LDS-DMA path
+//
+// C = alpha A B + beta C with A [M x K] and B [K x N] row-major, K-range
+// multiples of 32 (the sweep's block flushes and the doubling products of the
+// triangular inverse).  Both slabs of a 32-deep K step move HBM -> LDS with
+// buffer_load_dwordx4 ... lds (no VGPR staging, bounds-checked, so no edge
+// branches): A as 128 rows x 128 B, B as 32 rows x 512 B, their 16-byte chunks
+// XOR-swizzled so that the MFMA operand reads (one float per lane) spread over
+// the banks.  Two stages in a ring, two workgroups per CU; every operand read
+// sits between two MFMAs.
+
+constexpr int DBK = 32;                       // K per stage
+constexpr int DSTAGE_F = BM * DBK + DBK * BN;  // floats per stage (A then B): 32 KiB
+
+__device__ __forceinline__ int swzA(int row) { return (row >> 1) & 7; }  // chunk XOR for A rows
+__device__ __forceinline__ int swzB(int k) { return (k & 1) << 3; }      // chunk XOR for B rows
+
+__global__ __launch_bounds__(256, 2) void gemm_nn_dma_kernel(GemmDesc d) {
+  if (d.info && *d.info != 0) return;
+  __shared__ __attribute__((aligned(1024))) float stg0[DSTAGE_F];
+  __shared__ __attribute__((aligned(1024))) float stg1[DSTAGE_F];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int tm = blockIdx.x, tn = blockIdx.y;
+  const int r0 = tm * BM, c0 = tn * BN;
+  if (r0 >= d.M || c0 >= d.N) return;
+  const int64_t z = blockIdx.z;
+  const float* A = d.A + z * d.strideA;
+  const float* B = d.B + z * d.strideB;
+  float* C = d.C + z * d.strideC;
+  int kLo = 0, kHi = d.K;
+  if (d.flags & GEMM_A_LOWER) kHi = min(kHi, r0 + BM);
+  if (d.flags & GEMM_B_LOWER) kLo = c0;
+  const int nst = (kHi - kLo) / DBK;
+  const int mrows = min(BM, d.M - r0), ncols = min(BN, d.N - c0);
+
+  // this lane's copies of one stage: 4 for A (rows 32w + 8q + l/8), 4 for B
+  // (rows 8w + 2q + l/32); byte offsets relative to the stage's buffer bases
+  int voffA[4], voffB[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ra = 32 * wave + 8 * q + (lane >> 3);
+    voffA[q] = (int)((int64_t)ra * d.lda * 4) + ((((lane & 7) ^ swzA(ra))) << 4);
+    const int rb = 8 * wave + 2 * q + (lane >> 5);
+    voffB[q] = (int)((int64_t)rb * d.ldb * 4) + ((((lane & 31) ^ swzB(rb))) << 4);
+  }
+  const uint32_t aBytes = (uint32_t)(((int64_t)(mrows - 1) * d.lda + DBK) * 4);
+  const uint32_t bBytes = (uint32_t)(((int64_t)(DBK - 1) * d.ldb + ncols) * 4);
+  auto issue = [&](int st, float* stg) {
+    const int kc = kLo + st * DBK;
+    const i32x4 ra = make_rsrc(A + (int64_t)r0 * d.lda + kc, aBytes);
+    const i32x4 rb = make_rsrc(B + (int64_t)kc * d.ldb + c0, bBytes);
+    const uint32_t sb = (uint32_t)(uintptr_t)((float LDS_AS*)stg);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(ra, sb + (uint32_t)((32 * wave + 8 * q) * DBK * 4), voffA[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(rb, sb + (uint32_t)((BM * DBK + (8 * wave + 2 * q) * BN) * 4), voffB[q]);
+  };
+
+  // C of this wave's 64 x 64 quadrant, fetched first (interior tiles: one base
+  // plus constant offsets; edge tiles: clamped addresses, entries past M or N
+  // are never stored)
+  const float alpha = d.alpha, beta = d.beta;
+  const bool interior = mrows == BM && ncols == BN;
+  const int rl = wr * 64 + 4 * (lane >> 5), cl0 = wc * 64 + (lane & 31);
+  f32x16 cp[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) cp[mb][nb] = zero16();
+  if (beta != 0.f) {
+    if (interior) {
+      const float* base = C + (int64_t)(r0 + rl) * d.ldc + c0 + cl0;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            cp[mb][nb][r] = base[(int64_t)(32 * mb + 8 * (r >> 2) + (r & 3)) * d.ldc + 32 * nb];
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const float* colp = C + min(c0 + cl0 + 32 * nb, d.N - 1);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            cp[mb][nb][r] = colp[(int64_t)min(r0 + rl + 32 * mb + 8 * (r >> 2) + (r & 3), d.M - 1) * d.ldc];
+        }
+    }
+  }
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
+  const int kr = lane >> 5, cl = lane & 31;
+  // operand reads of one k pair (k = 2 kk + kr) from a stage
+  auto rdA = [&](const float* sA, int row, int k) { return sA[row * DBK + ((((k >> 2) ^ swzA(row))) << 2) + (k & 3)]; };
+  auto rdB = [&](const float* sB, int k, int col) { return sB[k * BN + ((((col >> 2) ^ swzB(k))) << 2) + (col & 3)]; };
+  auto compute = [&](const float* stg) {
+    const float* sA = stg;
+    const float* sB = stg + BM * DBK;
+    float a0 = rdA(sA, wr * 64 + cl, kr), a1 = rdA(sA, wr * 64 + 32 + cl, kr);
+    float b0 = rdB(sB, kr, wc * 64 + cl), b1 = rdB(sB, kr, wc * 64 + 32 + cl);
+#pragma unroll
+    for (int kk = 0; kk < DBK / 2; ++kk) {
+      const int kn = 2 * (kk + 1) + kr;
+      float na0 = 0.f, na1 = 0.f, nb0 = 0.f, nb1 = 0.f;
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+      if (kk + 1 < DBK / 2) na0 = rdA(sA, wr * 64 + cl, kn);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+      if (kk + 1 < DBK / 2) na1 = rdA(sA, wr * 64 + 32 + cl, kn);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+      if (kk + 1 < DBK / 2) nb0 = rdB(sB, kn, wc * 64 + cl);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+      if (kk + 1 < DBK / 2) nb1 = rdB(sB, kn, wc * 64 + 32 + cl);
+      a0 = na0; a1 = na1; b0 = nb0; b1 = nb1;
+    }
+    // keep each read one k pair (four MFMAs) ahead of its use
+#pragma unroll
+    for (int kk = 0; kk < DBK / 2 - 1; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+
+  // two-stage ring: the copy of step s+1 is in flight while step s computes
+  if (nst > 0) {
+    issue(0, stg0);
+    for (int st = 0; st < nst; st += 2) {
+      if (st + 1 < nst) { issue(st + 1, stg1); wait_vmcnt<8>(); } else wait_vmcnt<0>();
+      stage_barrier();  // step st visible to every wave
+      compute(stg0);
+      stage_barrier();  // everyone is done with stg0
+      if (st + 1 >= nst) break;
+      if (st + 2 < nst) { issue(st + 2, stg0); wait_vmcnt<8>(); } else wait_vmcnt<0>();
+      stage_barrier();
+      compute(stg1);
+      stage_barrier();
+    }
+  }
+
+  if (interior) {
+    float* base = C + (int64_t)(r0 + rl) * d.ldc + c0 + cl0;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = alpha * acc[mb][nb][r];
+          base[(int64_t)(32 * mb + 8 * (r >> 2) + (r & 3)) * d.ldc + 32 * nb] =
+              (beta == 0.f) ? v : fmaf(beta, cp[mb][nb][r], v);
+        }
+    return;
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + rl + 32 * mb + 8 * (r >> 2) + (r & 3);
+        const int col = c0 + cl0 + 32 * nb;
+        if (row < d.M && col < d.N) {
+          const float v = alpha * acc[mb][nb][r];
+          C[(int64_t)row * d.ldc + col] = (beta == 0.f) ? v : fmaf(beta, cp[mb][nb][r], v);
+        }
+      }
+}
+
+bool nn_dma_ok(const GemmDesc& d) {
+  const auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  return d.K % DBK == 0 && d.lda % 4 == 0 && d.ldb % 4 == 0 && d.N % 4 == 0 && d.strideA % 4 == 0 &&
+         d.strideB % 4 == 0 && al16(d.A) && al16(d.B) && !(d.flags & GEMM_LOWER_TILES) &&
+         (int64_t)(BM - 1) * d.lda * 4 + 4096 < ((int64_t)1 << 31) && (int64_t)(DBK - 1) * d.ldb * 4 + 4096 < ((int64_t)1 << 31);
+}
+
 template <bool TA, bool TB>
 void launch(const GemmDesc& d, dim3 grid, hipStream_t s) {
   const bool vec = d.lda % 4 == 0 && d.ldb % 4 == 0 && d.strideA % 4 == 0 && d.strideB % 4 == 0 &&
@@ -198,7 +383,8 @@ hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s) 
   const int tM = (int)cdiv(d.M, BM), tN = (int)cdiv(d.N, BN);
   if (d.flags & GEMM_LOWER_TILES) grid = dim3((unsigned)(tM * (tM + 1) / 2), 1, (unsigned)d.batch);
   else grid = dim3((unsigned)tM, (unsigned)tN, (unsigned)d.batch);
-  if (!transA && !transB) launch<false, false>(d, grid, s);
+  if (!transA && !transB && nn_dma_ok(d)) hipLaunchKernelGGL(gemm_nn_dma_kernel, grid, dim3(256), 0, s, d);
+  else if (!transA && !transB) launch<false, false>(d, grid, s);
   else if (!transA && transB) launch<false, true>(d, grid, s);
   else if (transA && !transB) launch<true, false>(d, grid, s);
   else launch<true, true>(d, grid, s);
