@@ -386,7 +386,29 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
       *(f32x4*)&sD[pidx(e >> 4, 4 * (e & 15))] = dv[u];
     }
   }
-  // C of this wave's 64 x 64 quadrant; its latency overlaps the panel solves
+  __syncthreads();
+
+  // L21 slabs; each wave reads and then overwrites only its own 32 rows
+  const int cl = lane & 31;
+  f32x16 o[2];
+  panel_solve(sR, sD, wave, lane, o);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = 32 * wave + mfma32_row(r, lane);
+      sR[pidx(rr, 32 * nb + cl)] = o[nb][r];
+      if (tn == 0 && r0 + rr < n) L[(r0 + rr) * n + k0 + 32 * nb + cl] = o[nb][r];
+    }
+  if (!dg) {
+    panel_solve(sC, sD, wave, lane, o);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sC[pidx(32 * wave + mfma32_row(r, lane), 32 * nb + cl)] = o[nb][r];
+  }
+  // C of this wave's 64 x 64 quadrant, fetched only now (so it is not live
+  // during the panel solves) and consumed after the rank update's MFMAs
   const bool interior = r0 + TB <= n && c0 + TB <= n;
   const int64_t rbase = r0 + 64 * wr + 4 * (lane >> 5);
   const int64_t cbase = c0 + 64 * wc + (lane & 31);
@@ -417,27 +439,6 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) cp[mb][nb][r] = colp[min(rbase + 32 * mb + 8 * (r >> 2) + (r & 3), n - 1) * n];
       }
-  }
-  __syncthreads();
-
-  // L21 slabs; each wave reads and then overwrites only its own 32 rows
-  const int cl = lane & 31;
-  f32x16 o[2];
-  panel_solve(sR, sD, wave, lane, o);
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = 32 * wave + mfma32_row(r, lane);
-      sR[pidx(rr, 32 * nb + cl)] = o[nb][r];
-      if (tn == 0 && r0 + rr < n) L[(r0 + rr) * n + k0 + 32 * nb + cl] = o[nb][r];
-    }
-  if (!dg) {
-    panel_solve(sC, sD, wave, lane, o);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sC[pidx(32 * wave + mfma32_row(r, lane), 32 * nb + cl)] = o[nb][r];
   }
   __syncthreads();
   if (!active) return;
@@ -490,7 +491,7 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
 // Block column k at k0 (n - k0 > NB): workgroup 0 factors diagonal block
 // k + 1, workgroups 1.. update the lower tiles of the trailing matrix.
 template <bool VEC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chol_step_kernel(float* A, float* L, float* dinv, int64_t n, int64_t k0,
+__global__ __launch_bounds__(256, 2) void chol_step_kernel(float* A, float* L, float* dinv, int64_t n, int64_t k0,
                                                            int32_t* info) {
   if (*info != 0) return;
   __shared__ __attribute__((aligned(16))) float smem[SMEM];
