@@ -9,6 +9,8 @@
 // Tile: 128x128 per workgroup of 256 threads (4 wave64s, each 64x64 = 2x2
 // MFMA 32x32 blocks), K staged through LDS 32 at a time, double-buffered,
 // 16-byte global loads where aligned; two workgroups per CU.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -199,7 +201,9 @@ constexpr int DSTAGE_F = BM * DBK + DBK * BN;  // floats per stage (A then B): 3
 __device__ __forceinline__ int swzA(int row) { return (row >> 1) & 7; }  // chunk XOR for A rows
 __device__ __forceinline__ int swzB(int k) { return (k & 1) << 3; }      // chunk XOR for B rows
 
-__global__ __launch_bounds__(256, 2) void gemm_nn_dma_kernel(GemmDesc d) {
+// Split-K (nsplit > 1): blockIdx.z = batch entry * nsplit + chunk; the chunk's
+// product (no alpha, no beta) goes to part[(z * tiles + tile)][128 x 128].
+__global__ __launch_bounds__(256, 2) void gemm_nn_dma_kernel(GemmDesc d, int nsplit, int chunk, float* part) {
   if (d.info && *d.info != 0) return;
   __shared__ __attribute__((aligned(1024))) float stg0[DSTAGE_F];
   __shared__ __attribute__((aligned(1024))) float stg1[DSTAGE_F];
@@ -209,13 +213,19 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_dma_kernel(GemmDesc d) {
   const int tm = blockIdx.x, tn = blockIdx.y;
   const int r0 = tm * BM, c0 = tn * BN;
   if (r0 >= d.M || c0 >= d.N) return;
-  const int64_t z = blockIdx.z;
+  const int64_t z = blockIdx.z / nsplit;
+  const int split = blockIdx.z % nsplit;
   const float* A = d.A + z * d.strideA;
   const float* B = d.B + z * d.strideB;
   float* C = d.C + z * d.strideC;
   int kLo = 0, kHi = d.K;
   if (d.flags & GEMM_A_LOWER) kHi = min(kHi, r0 + BM);
   if (d.flags & GEMM_B_LOWER) kLo = c0;
+  if (nsplit > 1) {
+    kLo += split * chunk;
+    kHi = min(kHi, kLo + chunk);
+    if (kLo >= kHi) return;  // the reduction skips chunks past the tile's K range
+  }
   const int nst = (kHi - kLo) / DBK;
   const int mrows = min(BM, d.M - r0), ncols = min(BN, d.N - c0);
 
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_dma_kernel(GemmDesc d) {
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) cp[mb][nb] = zero16();
-  if (beta != 0.f) {
+  if (beta != 0.f && nsplit == 1) {
     if (interior) {
       const float* base = C + (int64_t)(r0 + rl) * d.ldc + c0 + cl0;
 #pragma unroll
@@ -331,6 +341,16 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_dma_kernel(GemmDesc d) {
     }
   }
 
+  if (nsplit > 1) {
+    float* P = part + ((int64_t)blockIdx.z * gridDim.x * gridDim.y + (int64_t)tn * gridDim.x + tm) * (BM * BN);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) P[(rl + 32 * mb + 8 * (r >> 2) + (r & 3)) * BN + cl0 + 32 * nb] = acc[mb][nb][r];
+    return;
+  }
   if (interior) {
     float* base = C + (int64_t)(r0 + rl) * d.ldc + c0 + cl0;
 #pragma unroll
@@ -360,6 +380,39 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_dma_kernel(GemmDesc d) {
       }
 }
 
+// C tile = alpha * (sum of its chunks in chunk order) + beta * C; chunks past
+// the tile's K range were never computed and are skipped.
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmDesc d, int nsplit, int chunk, const float* part) {
+  if (d.info && *d.info != 0) return;
+  const int tm = blockIdx.x, tn = blockIdx.y;
+  const int r0 = tm * BM, c0 = tn * BN;
+  const int64_t z = blockIdx.z;
+  float* C = d.C + z * d.strideC;
+  int kLo = 0, kHi = d.K;
+  if (d.flags & GEMM_A_LOWER) kHi = min(kHi, r0 + BM);
+  if (d.flags & GEMM_B_LOWER) kLo = c0;
+  const int nvalid = kHi > kLo ? min(nsplit, (kHi - kLo + chunk - 1) / chunk) : 0;
+  const int64_t tstride = (int64_t)gridDim.x * gridDim.y * (BM * BN);
+  const float* P = part + ((z * nsplit) * gridDim.x * gridDim.y + (int64_t)tn * gridDim.x + tm) * (BM * BN);
+  const int tid = threadIdx.x;
+#pragma unroll 4
+  for (int u = 0; u < BM * BN / (4 * 256); ++u) {
+    const int e = 4 * (tid + 256 * u);
+    const int row = e / BN, col = e % BN;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nvalid; ++s) sum += *(const f32x4*)(P + s * tstride + e);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int gr = r0 + row, gc = c0 + col + q;
+      if (gr < d.M && gc < d.N) {
+        float* pc = C + (int64_t)gr * d.ldc + gc;
+        const float v = d.alpha * sum[q];
+        *pc = (d.beta == 0.f) ? v : fmaf(d.beta, *pc, v);
+      }
+    }
+  }
+}
+
 bool nn_dma_ok(const GemmDesc& d) {
   const auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   return d.K % DBK == 0 && d.lda % 4 == 0 && d.ldb % 4 == 0 && d.N % 4 == 0 && d.strideA % 4 == 0 &&
@@ -383,8 +436,29 @@ hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s) 
   const int tM = (int)cdiv(d.M, BM), tN = (int)cdiv(d.N, BN);
   if (d.flags & GEMM_LOWER_TILES) grid = dim3((unsigned)(tM * (tM + 1) / 2), 1, (unsigned)d.batch);
   else grid = dim3((unsigned)tM, (unsigned)tN, (unsigned)d.batch);
-  if (!transA && !transB && nn_dma_ok(d)) hipLaunchKernelGGL(gemm_nn_dma_kernel, grid, dim3(256), 0, s, d);
-  else if (!transA && !transB) launch<false, false>(d, grid, s);
+  if (!transA && !transB && nn_dma_ok(d)) {
+    // split K when the tiles alone would give fewer than about four work
+    // items per CU (the triangular products have K ranges from 128 to K, so
+    // balance needs more items than workgroup slots) and K is long: chunks of
+    // at least 256, multiples of 32, as many as the scratch holds
+    const int64_t tiles = (int64_t)tM * tN * d.batch;
+    int nsplit = 1, chunk = d.K;
+    if (d.ws && d.K >= 512 && tiles < 1024) {
+      int64_t want = std::min<int64_t>((1024 + tiles - 1) / tiles, d.K / 256);
+      want = std::min<int64_t>(want, d.ws_floats / (tiles * BM * BN));
+      if (want > 1) {
+        chunk = (int)cdiv(cdiv(d.K, want), DBK) * DBK;
+        nsplit = (int)cdiv(d.K, chunk);
+      }
+    }
+    if (nsplit > 1) {
+      const dim3 g2(grid.x, grid.y, grid.z * nsplit);
+      hipLaunchKernelGGL(gemm_nn_dma_kernel, g2, dim3(256), 0, s, d, nsplit, chunk, d.ws);
+      hipLaunchKernelGGL(gemm_split_reduce_kernel, grid, dim3(256), 0, s, d, nsplit, chunk, (const float*)d.ws);
+    } else {
+      hipLaunchKernelGGL(gemm_nn_dma_kernel, grid, dim3(256), 0, s, d, 1, d.K, (float*)nullptr);
+    }
+  } else if (!transA && !transB) launch<false, false>(d, grid, s);
   else if (!transA && transB) launch<false, true>(d, grid, s);
   else if (transA && !transB) launch<true, false>(d, grid, s);
   else launch<true, true>(d, grid, s);

@@ -22,6 +22,11 @@ struct GemmDesc {
   float alpha, beta;
   int flags;
   const int32_t* info;  // if non-null and *info != 0 the kernel does nothing
+  // Optional scratch for a split-K launch (K cut into chunks whose partial
+  // tiles are summed in chunk order by a second kernel: deterministic).  Used
+  // only when the tile grid alone would leave the GPU under-filled.
+  float* ws;
+  int64_t ws_floats;
 };
 
 // C = alpha * op(A) * op(B) + beta * C in fp32 on the MFMA pipe.

@@ -591,6 +591,9 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
       g1.C = w.A; g1.ldc = bs; g1.strideC = bs * bs;
       g1.M = (int)s2; g1.N = (int)bs; g1.K = (int)bs; g1.batch = (int)count;
       g1.alpha = 1.f; g1.beta = 0.f; g1.flags = GEMM_B_LOWER; g1.info = info;
+      // split-K scratch: the rest of A past the product buffer (at least n^2/2 floats)
+      const int64_t tmp_floats = (count * bs * bs + 63) / 64 * 64;
+      g1.ws = w.A + tmp_floats; g1.ws_floats = n * n - tmp_floats;
       if ((e = gemm_f32(g1, false, false, s)) != hipSuccess) return e;
       GemmDesc g2{};  // Linv21 = -Linv22 * tmp
       g2.A = w.L + (a + bs) * n + (a + bs); g2.lda = n; g2.strideA = stride;
@@ -598,6 +601,7 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
       g2.C = w.L + (a + bs) * n + a; g2.ldc = n; g2.strideC = stride;
       g2.M = (int)s2; g2.N = (int)bs; g2.K = (int)s2; g2.batch = (int)count;
       g2.alpha = -1.f; g2.beta = 0.f; g2.flags = GEMM_A_LOWER; g2.info = info;
+      g2.ws = g1.ws; g2.ws_floats = g1.ws_floats;
       if ((e = gemm_f32(g2, false, false, s)) != hipSuccess) return e;
     }
   }
