@@ -28,7 +28,8 @@ namespace gptq {
 
 namespace {
 
-constexpr int BMAX = 128;  // widest block; the E buffer has this leading dimension
+constexpr int BMAX = 128;  // widest block
+constexpr int ELD = 2 * BMAX;  // leading dimension of the E buffer: the errors of two consecutive blocks
 
 struct SweepArgs {
   const float* U;
@@ -268,8 +269,8 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
 
   if (active) {
     if (8 * lr + 8 <= w) {
-      *(f32x4*)&a.E[r * BMAX + 8 * lr] = f32x4{ek[0], ek[1], ek[2], ek[3]};
-      *(f32x4*)&a.E[r * BMAX + 8 * lr + 4] = f32x4{ek[4], ek[5], ek[6], ek[7]};
+      *(f32x4*)&a.E[r * ELD + 8 * lr] = f32x4{ek[0], ek[1], ek[2], ek[3]};
+      *(f32x4*)&a.E[r * ELD + 8 * lr + 4] = f32x4{ek[4], ek[5], ek[6], ek[7]};
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
       for (int k = 0; k < 8; ++k) {
         const int c = 8 * lr + k;
         if (c < w) {
-          a.E[r * BMAX + c] = ek[k];
+          a.E[r * ELD + c] = ek[k];
           a.Q8[r * a.n + i + c] = (uint8_t)(int)qk[k];
         }
       }
@@ -420,7 +421,7 @@ inline size_t dblk_bytes(int64_t n, int64_t B) {
 
 size_t quantize_workspace_bytes(int64_t m, int64_t n, int64_t B) {
   if (m < 1 || n < 1 || B < 1) return 0;
-  return align256((size_t)m * n * 4) + align256((size_t)m * n) + align256((size_t)m * BMAX * 4) + align256(dblk_bytes(n, B));
+  return align256((size_t)m * n * 4) + align256((size_t)m * n) + align256((size_t)m * ELD * 4) + align256(dblk_bytes(n, B));
 }
 
 hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, const float* U, int bits,
@@ -432,7 +433,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   uint8_t* Q8 = (uint8_t*)p;
   p += align256((size_t)m * n);
   float* E = (float*)p;
-  p += align256((size_t)m * BMAX * 4);
+  p += align256((size_t)m * ELD * 4);
   float* Dblk = (float*)p;
   const int nstep = nstep_for(B);
   const int64_t dstride = (int64_t)nstep * nstep + nstep;
@@ -459,23 +460,49 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  for (int64_t i = 0; i < n; i += B) {
-    const int w = (int)std::min<int64_t>(B, n - i);
+  // sweep one block [i, i + w) with its errors written at column eoff of E
+  auto sweep_block = [&](int64_t i, int w, int eoff) -> hipError_t {
     if (group > B && i % group == 0)
       hipLaunchKernelGGL(row_params_kernel, dim3(prow), dim3(256), 0, st, (const float*)V, m, n, i, group, maxq, S,
                          Z, G, i / group);
-    SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, Q8, E, err_sq, Dblk + (i / B) * dstride};
+    SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, Q8, E + eoff, err_sq, Dblk + (i / B) * dstride};
     if (B <= 32) launch_sweep<4>(a, gmode, st);
     else launch_sweep<16>(a, gmode, st);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (i + w < n) {
-      GemmDesc g{};
-      g.A = E; g.lda = BMAX;
-      g.B = U + i * n + i + w; g.ldb = n;
-      g.C = V + i + w; g.ldc = n;
-      g.M = (int)m; g.N = (int)(n - i - w); g.K = w; g.batch = 1;
-      g.alpha = -1.f; g.beta = 1.f;
-      if ((e = gemm_f32(g, false, false, st)) != hipSuccess) return e;
+    return hipGetLastError();
+  };
+  // V[:, c0:c0+N] -= E[:, 0:K] U[r0:r0+K, c0:c0+N]
+  auto flush = [&](int64_t r0, int K, int64_t c0, int64_t N) -> hipError_t {
+    if (N <= 0) return hipSuccess;
+    GemmDesc g{};
+    g.A = E; g.lda = ELD;
+    g.B = U + r0 * n + c0; g.ldb = n;
+    g.C = V + c0; g.ldc = n;
+    g.M = (int)m; g.N = (int)N; g.K = K; g.batch = 1;
+    g.alpha = -1.f; g.beta = 1.f;
+    return gemm_f32(g, false, false, st);
+  };
+  if (B % 32 == 0) {
+    // Blocks in pairs (lazy batch of 2B): after the first block only the
+    // second block's columns are brought up to date (K = B), and after the
+    // second one the rest of the row takes both blocks' errors at once
+    // (K = 2B): half the passes over V, twice the work per GEMM tile.
+    for (int64_t i = 0; i < n;) {
+      const int w1 = (int)std::min<int64_t>(B, n - i);
+      if ((e = sweep_block(i, w1, 0)) != hipSuccess) return e;
+      const int64_t j = i + w1;
+      if (j >= n) break;
+      const int w2 = (int)std::min<int64_t>(B, n - j);
+      if ((e = flush(i, w1, j, w2)) != hipSuccess) return e;
+      if ((e = sweep_block(j, w2, w1)) != hipSuccess) return e;
+      const int64_t k = j + w2;
+      if ((e = flush(i, w1 + w2, k, n - k)) != hipSuccess) return e;
+      i = k;
+    }
+  } else {
+    for (int64_t i = 0; i < n; i += B) {
+      const int w = (int)std::min<int64_t>(B, n - i);
+      if ((e = sweep_block(i, w, 0)) != hipSuccess) return e;
+      if ((e = flush(i, w, i + w, n - i - w)) != hipSuccess) return e;
     }
   }
   const int64_t words = cdiv(n * bits, 32);
