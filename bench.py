@@ -40,16 +40,16 @@ def parse():
 
 def cpu_baseline(W16, X16, job, U_gpu):
     """The fp64 oracle timed on a bounded sample of the same layer, scaled to
-    one full layer: H over 8 of the 128 token chunks (x16), the inverse factor
-    at full size (x1), the sweep over 256 of the 4096 rows (x16)."""
+    one full layer: H over 32 of the 128 token chunks (x4), the inverse factor
+    at full size (x1), the sweep over 1024 of the 4096 rows (x4)."""
     import numpy as np
 
     import oracle as O
     T = X16.shape[0]
     n = W16.shape[1]
     m = W16.shape[0]
-    tok = min(T, 8 * 2048)
-    rows = min(m, 256)
+    tok = min(T, 32 * 2048)
+    rows = min(m, 1024)
     t0 = time.perf_counter()
     H = O.hessian([X16[c:c + 2048] for c in range(0, tok, 2048)])
     t1 = time.perf_counter()
