@@ -29,7 +29,8 @@ namespace gptq {
 namespace {
 
 constexpr int BMAX = 128;  // widest block
-constexpr int ELD = 2 * BMAX;  // leading dimension of the E buffer: the errors of two consecutive blocks
+constexpr int LA = 2;          // blocks per lazy flush on the look-ahead path
+constexpr int ELD = LA * BMAX;  // leading dimension of the E buffer: the errors of LA consecutive blocks
 
 struct SweepArgs {
   const float* U;
@@ -46,6 +47,12 @@ struct SweepArgs {
   float* E;       // [m x 128] scaled errors of this block
   float* err_sq;  // [m] or null
   const float* Dblk;  // this block's factor rows divided by their diagonal ([NSTEP][NSTEP]), then 1/U_pp [NSTEP]
+  // look-ahead: errors of the kpend columns swept since the last flush
+  // (E buffer from column 0) and the factor rows of those columns restricted
+  // to this block's columns (U + r * n + i, leading dimension n)
+  const float* Ep;
+  int kpend;
+  const float* Upend;
 };
 
 // Lanes-per-row variants: 16 lanes (one DPP row) x 8 columns = 128 columns,
@@ -134,13 +141,72 @@ __device__ __forceinline__ void store_params(const SweepArgs& a, const GroupStat
 // GMODE: 0 = (s, z) fixed for the whole block (per-row, or a group spanning
 // several blocks); 8..128 = group size known at compile time, groups start
 // inside the block; -1 = any other in-block group size (runtime).
-template <int LPR, int GMODE>
+// The errors of the pending columns (swept since the last flush) applied to
+// this block's 128 columns for the workgroup's 16 rows, with
+// v_mfma_f32_16x16x4f32: wave w computes output column blocks 2w, 2w+1; the
+// factor rows stream through the Up buffer (64 at a time, pitch 144, which
+// keeps the operand reads bank-conflict-free).  The result lands in upd
+// (16 x 132) for the lanes' V loads.
+constexpr int KPMAX = (LA - 1) * BMAX;
+constexpr int EPITCH = KPMAX + 4;
+constexpr int CPITCH = 144;
+__device__ __forceinline__ void pending_update(const SweepArgs& a, int64_t r0, float* chunk, float* sE, float* upd) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g16 = lane >> 4;
+  const int kp = a.kpend;
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // 64 factor rows x 128 columns per chunk, 8 float4 per thread; the next
+  // chunk is loaded while the current one is multiplied
+  f32x4 xr[8];
+  auto load_chunk = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u;
+      const int kr = e >> 5, c4 = 4 * (e & 31);  // w is a multiple of 4 on this path
+      xr[u] = c4 < a.w ? *(const f32x4*)&a.Upend[(int64_t)(k0 + kr) * a.n + c4] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_chunk(0);
+  for (int e = tid; e < 16 * kp; e += 256) {
+    const int rr = e / kp, k = e % kp;
+    const int64_t row = min<int64_t>(r0 + rr, a.m - 1);  // rows past m: their results are never used
+    sE[rr * EPITCH + k] = a.Ep[row * ELD + k];
+  }
+  for (int k0 = 0; k0 < kp; k0 += 64) {
+    __syncthreads();  // the previous chunk is consumed (and sE is written)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u;
+      *(f32x4*)&chunk[(e >> 5) * CPITCH + 4 * (e & 31)] = xr[u];
+    }
+    if (k0 + 64 < kp) load_chunk(k0 + 64);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const float av = sE[l16 * EPITCH + k0 + 4 * kk + g16];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, chunk[(4 * kk + g16) * CPITCH + 16 * (2 * wave + q) + l16],
+                                                       acc[q], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) upd[(4 * g16 + rr) * (BMAX + 4) + 16 * (2 * wave + q) + l16] = acc[q][rr];
+  __syncthreads();  // upd complete; chunk (the Up buffer) free
+}
+
+template <int LPR, int GMODE, bool LOOK>
 __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
   constexpr int NSTEP = 8 * LPR;
   constexpr int PITCH = NSTEP + 4;
   constexpr int ROWS = 256 / LPR;
+  static_assert(!LOOK || (LPR == 16 && 64 * CPITCH <= NSTEP * PITCH), "look-ahead needs the 128-column layout");
   __shared__ __attribute__((aligned(16))) float Up[NSTEP * PITCH];
   __shared__ float invd[NSTEP];
+  __shared__ __attribute__((aligned(16))) float sE[LOOK ? 16 * EPITCH : 1];
+  __shared__ float upd[LOOK ? 16 * (BMAX + 4) : 1];
   const int tid = threadIdx.x;
   const int lr = tid & (LPR - 1);
   const int64_t r = (int64_t)blockIdx.x * ROWS + tid / LPR;
@@ -148,6 +214,9 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
   const int w = a.w;
   const int64_t i = a.i;
   const float* __restrict__ U = a.U;
+  if constexpr (LOOK) {
+    if (a.kpend > 0) pending_update(a, (int64_t)blockIdx.x * ROWS, Up, sE, upd);
+  }
 
   // this block's factor rows divided by their diagonal (zero on and below it)
   // and 1/U_pp, prepared once per layer by diag_blocks_kernel
@@ -179,6 +248,15 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
     for (int k = 0; k < 8; ++k) {
       const int c = 8 * lr + k;
       v[k] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
+    }
+  }
+  if constexpr (LOOK) {
+    if (a.kpend > 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = 8 * lr + k;
+        if (c < w) v[k] -= upd[(tid / LPR) * (BMAX + 4) + c];
+      }
     }
   }
 #pragma unroll
@@ -315,20 +393,20 @@ __global__ __launch_bounds__(256) void diag_blocks_kernel(const float* U, int64_
   for (int p = threadIdx.x; p < NSTEP; p += 256) dst[NSTEP * NSTEP + p] = (p < w) ? 1.f / U[(i + p) * n + i + p] : 0.f;
 }
 
-template <int LPR>
+template <int LPR, bool LOOK>
 void launch_sweep(const SweepArgs& a, int gmode, hipStream_t st) {
   const dim3 grid((unsigned)cdiv(a.m, 256 / LPR)), block(256);
   switch (gmode) {
-    case 0: hipLaunchKernelGGL((sweep_block_kernel<LPR, 0>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((sweep_block_kernel<LPR, 8>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((sweep_block_kernel<LPR, 16>), grid, block, 0, st, a); break;
-    case 32: hipLaunchKernelGGL((sweep_block_kernel<LPR, 32>), grid, block, 0, st, a); break;
+    case 0: hipLaunchKernelGGL((sweep_block_kernel<LPR, 0, LOOK>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((sweep_block_kernel<LPR, 8, LOOK>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((sweep_block_kernel<LPR, 16, LOOK>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((sweep_block_kernel<LPR, 32, LOOK>), grid, block, 0, st, a); break;
     default:
       if constexpr (LPR == 16) {
-        if (gmode == 64) { hipLaunchKernelGGL((sweep_block_kernel<LPR, 64>), grid, block, 0, st, a); break; }
-        if (gmode == 128) { hipLaunchKernelGGL((sweep_block_kernel<LPR, 128>), grid, block, 0, st, a); break; }
+        if (gmode == 64) { hipLaunchKernelGGL((sweep_block_kernel<LPR, 64, LOOK>), grid, block, 0, st, a); break; }
+        if (gmode == 128) { hipLaunchKernelGGL((sweep_block_kernel<LPR, 128, LOOK>), grid, block, 0, st, a); break; }
       }
-      hipLaunchKernelGGL((sweep_block_kernel<LPR, -1>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((sweep_block_kernel<LPR, -1, LOOK>), grid, block, 0, st, a);
   }
 }
 
@@ -460,14 +538,18 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // sweep one block [i, i + w) with its errors written at column eoff of E
-  auto sweep_block = [&](int64_t i, int w, int eoff) -> hipError_t {
+  // sweep one block [i, i + w) with its errors written at column eoff of E;
+  // on the look-ahead path the kpend columns before it (from column g0) are
+  // still to be applied to it
+  auto sweep_block = [&](int64_t i, int w, int eoff, bool look, int64_t g0) -> hipError_t {
     if (group > B && i % group == 0)
       hipLaunchKernelGGL(row_params_kernel, dim3(prow), dim3(256), 0, st, (const float*)V, m, n, i, group, maxq, S,
                          Z, G, i / group);
-    SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, Q8, E + eoff, err_sq, Dblk + (i / B) * dstride};
-    if (B <= 32) launch_sweep<4>(a, gmode, st);
-    else launch_sweep<16>(a, gmode, st);
+    SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, Q8, E + eoff, err_sq, Dblk + (i / B) * dstride,
+                E, (int)(i - g0), U + g0 * n + i};
+    if (B <= 32) launch_sweep<4, false>(a, gmode, st);
+    else if (look) launch_sweep<16, true>(a, gmode, st);
+    else launch_sweep<16, false>(a, gmode, st);
     return hipGetLastError();
   };
   // V[:, c0:c0+N] -= E[:, 0:K] U[r0:r0+K, c0:c0+N]
@@ -481,27 +563,29 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
     g.alpha = -1.f; g.beta = 1.f;
     return gemm_f32(g, false, false, st);
   };
-  if (B % 32 == 0) {
-    // Blocks in pairs (lazy batch of 2B): after the first block only the
-    // second block's columns are brought up to date (K = B), and after the
-    // second one the rest of the row takes both blocks' errors at once
-    // (K = 2B): half the passes over V, twice the work per GEMM tile.
-    for (int64_t i = 0; i < n;) {
-      const int w1 = (int)std::min<int64_t>(B, n - i);
-      if ((e = sweep_block(i, w1, 0)) != hipSuccess) return e;
-      const int64_t j = i + w1;
-      if (j >= n) break;
-      const int w2 = (int)std::min<int64_t>(B, n - j);
-      if ((e = flush(i, w1, j, w2)) != hipSuccess) return e;
-      if ((e = sweep_block(j, w2, w1)) != hipSuccess) return e;
-      const int64_t k = j + w2;
-      if ((e = flush(i, w1 + w2, k, n - k)) != hipSuccess) return e;
-      i = k;
+  // (pending K = t B is a multiple of the 64-row chunks; rows of V 16-byte aligned)
+  const bool look = B % 64 == 0 && (group <= 0 || group <= B) && n % 4 == 0;
+  if (look) {
+    // Look-ahead: LA blocks per flush.  Block t of a group first takes the
+    // errors of blocks 0..t-1 of its group (inside the sweep kernel, K = t B,
+    // on MFMA), then is swept; after the group, one GEMM with K = LA B brings
+    // the rest of the row up to date: a quarter of the passes over V and long
+    // K per GEMM tile.  (Groups wider than a block would need V updated past
+    // the block before their scales are taken, so they stay on the path below.)
+    for (int64_t g0 = 0; g0 < n;) {
+      int64_t i = g0;
+      for (int t = 0; t < LA && i < n; ++t) {
+        const int w = (int)std::min<int64_t>(B, n - i);
+        if ((e = sweep_block(i, w, (int)(i - g0), true, g0)) != hipSuccess) return e;
+        i += w;
+      }
+      if ((e = flush(g0, (int)(i - g0), i, n - i)) != hipSuccess) return e;
+      g0 = i;
     }
   } else {
     for (int64_t i = 0; i < n; i += B) {
       const int w = (int)std::min<int64_t>(B, n - i);
-      if ((e = sweep_block(i, w, 0)) != hipSuccess) return e;
+      if ((e = sweep_block(i, w, 0, false, i)) != hipSuccess) return e;
       if ((e = flush(i, w, i + w, n - i - w)) != hipSuccess) return e;
     }
   }

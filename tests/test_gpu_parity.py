@@ -142,6 +142,8 @@ SWEEP_CASES = [
     (48, 384, 4, 64, 128, "f16"),
     (31, 500, 3, 0, 128, "f16"),
     (16, 200, 4, 4, 8, "f32"),
+    (64, 1000, 4, 64, 64, "f16"),     # look-ahead path, B = 64, ragged last group and block
+    (130, 2048, 4, 128, 128, "bf16"),  # look-ahead path, four full groups of four blocks
 ]
 
 
