@@ -124,7 +124,10 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp, float* U,
  *     per-row mode takes them once from the original row;
  *   q = clamp(rint(v/s) + z, 0, maxq), what = s (q - z);
  *   e = (v - what)/U[p][p];  later columns of the block v_j -= e U[p][j];
- * and after each block [i, i2): V[:, i2:] -= E U[i:i2, i2:] (one GEMM).
+ * and the block's errors reach the later columns as V[:, i2:] -= E U[i:i2, i2:]
+ * before those columns are swept (the library may apply the errors of two
+ * consecutive blocks in one product; the result differs only in the order
+ * of floating-point sums).
  *
  *   W          [m x n] weights, leading dimension ldw >= n, type w_dtype.
  *              Read; if write_dequant != 0, overwritten by what = s(q - z)
