@@ -69,6 +69,23 @@ __global__ __launch_bounds__(256) void reverse_damp_kernel(const float* H, float
   }
 }
 
+// The same with 16-byte accesses (n % 4 == 0, 16-byte aligned rows): A[i][j..j+3]
+// is the reversed float4 H[n-1-i][n-4-j .. n-1-j].
+__global__ __launch_bounds__(256) void reverse_damp4_kernel(const float* H, float* A, int64_t n, const float* lam_ws) {
+  const float lam = *lam_ws;
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+    const float* src = H + (n - 1 - i) * n;
+    for (int64_t j = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); j < n; j += (int64_t)gridDim.x * 1024) {
+      const f32x4 x = *(const f32x4*)(src + n - 4 - j);
+      f32x4 y = {x[3], x[2], x[1], x[0]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e == i) y[e] += lam;
+      *(f32x4*)(A + i * n + j) = y;
+    }
+  }
+}
+
 constexpr int TB = 128;          // trailing-update tile
 constexpr int LP = 65;           // LDS pitch of 64-column leaf matrices (floats)
 constexpr int LLP = 68;          // LDS pitch of the leaf factor: 16-byte aligned rows
@@ -513,6 +530,44 @@ __global__ __launch_bounds__(256) void trtri_init_kernel(float* A, int64_t n, co
   }
 }
 
+// 16-byte variants (n % 4 == 0, 16-byte aligned rows; block boundaries never
+// split a float4 since NB % 4 == 0).
+__global__ __launch_bounds__(256) void trtri_init4_kernel(float* A, int64_t n, const float* Dinv, const int32_t* info) {
+  if (*info != 0) return;
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+    const int64_t bi = i / NB;
+    const float* drow = Dinv + bi * NB * NB + (i - bi * NB) * NB - bi * NB;  // + j
+    for (int64_t j = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); j < n; j += (int64_t)gridDim.x * 1024) {
+      float* dst = A + i * n + j;
+      if (j > i) {
+        *(f32x4*)dst = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else if (j / NB == bi) {
+        if (j + 3 <= i) *(f32x4*)dst = *(const f32x4*)(drow + j);
+        else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e] = (j + e > i) ? 0.f : drow[j + e];
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void write_u4_kernel(const float* A, float* U, int64_t n, const int32_t* info) {
+  if (*info != 0) return;
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+    const float* src = A + (n - 1 - i) * n;
+    for (int64_t j = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); j < n; j += (int64_t)gridDim.x * 1024) {
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      if (j + 3 >= i) {
+        const f32x4 x = *(const f32x4*)(src + n - 4 - j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (j + e >= i) ? x[3 - e] : 0.f;
+      }
+      *(f32x4*)(U + i * n + j) = y;
+    }
+  }
+}
+
 // U[i][j] = Linv[n-1-i][n-1-j] for i <= j, 0 below the diagonal.
 __global__ __launch_bounds__(256) void write_u_kernel(const float* A, float* U, int64_t n, const int32_t* info) {
   if (*info != 0) return;
@@ -545,6 +600,9 @@ PrepWs carve(void* ws, int64_t n) {
 }
 
 dim3 row_grid(int64_t n) { return dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)n); }
+dim3 row_grid4(int64_t n) {
+  return dim3((unsigned)std::min<int64_t>(cdiv(n, 1024), 64), (unsigned)std::min<int64_t>(n, 65535));
+}
 
 }  // namespace
 
@@ -557,7 +615,9 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
                         hipStream_t s) {
   PrepWs w = carve(ws, n);
   hipLaunchKernelGGL(damp_mean_kernel, dim3(1), dim3(1024), 0, s, H, n, damp, w.lam, lambda_out, info);
-  hipLaunchKernelGGL(reverse_damp_kernel, row_grid(n), dim3(256), 0, s, H, w.A, n, (const float*)w.lam);
+  const bool v4 = n % 4 == 0 && ((uintptr_t)H & 15) == 0 && ((uintptr_t)U & 15) == 0;
+  if (v4) hipLaunchKernelGGL(reverse_damp4_kernel, row_grid4(n), dim3(256), 0, s, H, w.A, n, (const float*)w.lam);
+  else hipLaunchKernelGGL(reverse_damp_kernel, row_grid(n), dim3(256), 0, s, H, w.A, n, (const float*)w.lam);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -574,7 +634,8 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // triangular inverse of the factor, in place, by recursive doubling
-  hipLaunchKernelGGL(trtri_init_kernel, row_grid(n), dim3(256), 0, s, w.L, n, (const float*)w.dinv, (const int32_t*)info);
+  if (v4) hipLaunchKernelGGL(trtri_init4_kernel, row_grid4(n), dim3(256), 0, s, w.L, n, (const float*)w.dinv, (const int32_t*)info);
+  else hipLaunchKernelGGL(trtri_init_kernel, row_grid(n), dim3(256), 0, s, w.L, n, (const float*)w.dinv, (const int32_t*)info);
   for (int64_t bs = NB; bs < n; bs *= 2) {
     const int64_t full = n / (2 * bs);  // pairs of two complete bs-blocks
     const int64_t a_part = full * 2 * bs;
@@ -605,7 +666,8 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
       if ((e = gemm_f32(g2, false, false, s)) != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(write_u_kernel, row_grid(n), dim3(256), 0, s, (const float*)w.L, U, n, (const int32_t*)info);
+  if (v4) hipLaunchKernelGGL(write_u4_kernel, row_grid4(n), dim3(256), 0, s, (const float*)w.L, U, n, (const int32_t*)info);
+  else hipLaunchKernelGGL(write_u_kernel, row_grid(n), dim3(256), 0, s, (const float*)w.L, U, n, (const int32_t*)info);
   return hipGetLastError();
 }
 

@@ -380,17 +380,32 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
 // divided by U_pp, zero on and below the diagonal, padded to NSTEP x NSTEP,
 // followed by 1/U_pp (0 past w).
 template <int NSTEP>
+// One workgroup per (block, 8 rows of it): every load of the workgroup in
+// flight at once.
 __global__ __launch_bounds__(256) void diag_blocks_kernel(const float* U, int64_t n, int64_t B, float* out) {
   const int64_t i = (int64_t)blockIdx.x * B;
   const int w = (int)std::min<int64_t>(B, n - i);
   float* dst = out + (int64_t)blockIdx.x * (NSTEP * NSTEP + NSTEP);
-  for (int idx = threadIdx.x; idx < NSTEP * NSTEP; idx += 256) {
-    const int p = idx / NSTEP, j = idx % NSTEP;
-    float u = 0.f;
-    if (p < w && j < w && j > p) u = U[(i + p) * n + i + j] / U[(i + p) * n + i + p];
-    dst[idx] = u;
+  const int p0 = 8 * blockIdx.y;
+  constexpr int PER = 8 * NSTEP / 256;  // elements per thread
+  float u[PER], d[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int p = p0 + idx / NSTEP, j = idx % NSTEP;
+    const bool in = p < w && j < w && j > p;
+    u[k] = in ? U[(i + p) * n + i + j] : 0.f;
+    d[k] = in ? U[(i + p) * n + i + p] : 1.f;
   }
-  for (int p = threadIdx.x; p < NSTEP; p += 256) dst[NSTEP * NSTEP + p] = (p < w) ? 1.f / U[(i + p) * n + i + p] : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    dst[(p0 + idx / NSTEP) * NSTEP + idx % NSTEP] = u[k] / d[k];
+  }
+  if (threadIdx.x < 8) {
+    const int p = p0 + threadIdx.x;
+    dst[NSTEP * NSTEP + p] = (p < w) ? 1.f / U[(i + p) * n + i + p] : 0.f;
+  }
 }
 
 template <int LPR, bool LOOK>
@@ -416,6 +431,36 @@ __global__ __launch_bounds__(256) void to_f32_kernel(const void* W, int64_t ldw,
   for (int64_t r = blockIdx.y; r < m; r += gridDim.y)
     for (int64_t c = blockIdx.x * 256 + threadIdx.x; c < n; c += (int64_t)gridDim.x * 256)
       V[r * n + c] = Elem<DT>::load(W, r * ldw + c);
+}
+
+// The same, 8 elements per thread with 16-byte accesses (n % 8 == 0,
+// ldw % 8 == 0, 16-byte aligned W).
+template <int DT>
+__global__ __launch_bounds__(256) void to_f32x8_kernel(const void* W, int64_t ldw, float* V, int64_t m, int64_t n) {
+  for (int64_t r = blockIdx.y; r < m; r += gridDim.y)
+    for (int64_t c = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x); c < n; c += (int64_t)gridDim.x * 2048) {
+      float x[8];
+      if (DT == 2) {
+        const f32x4 a = *(const f32x4*)((const float*)W + r * ldw + c), b = *(const f32x4*)((const float*)W + r * ldw + c + 4);
+        x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3]; x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+      } else {
+        const uint4 q = *(const uint4*)((const uint16_t*)W + r * ldw + c);
+        const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint16_t lo = (uint16_t)(wv[k] & 0xFFFFu), hi = (uint16_t)(wv[k] >> 16);
+          if (DT == 0) {
+            x[2 * k] = (float)__builtin_bit_cast(_Float16, lo);
+            x[2 * k + 1] = (float)__builtin_bit_cast(_Float16, hi);
+          } else {
+            x[2 * k] = bf16_to_f32(lo);
+            x[2 * k + 1] = bf16_to_f32(hi);
+          }
+        }
+      }
+      *(f32x4*)(V + r * n + c) = f32x4{x[0], x[1], x[2], x[3]};
+      *(f32x4*)(V + r * n + c + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
 }
 
 // (s, z) of columns [c0, c0 + width) of each row, one wave per row.
@@ -481,6 +526,43 @@ __global__ __launch_bounds__(256) void dequant_kernel(void* W, int64_t ldw, cons
   }
 }
 
+// The same, 8 elements per thread (n % 8 == 0, ldw % 8 == 0, 16-byte aligned W).
+template <int DT>
+__global__ __launch_bounds__(256) void dequant_x8_kernel(void* W, int64_t ldw, const uint8_t* Q8, const float* S,
+                                                         const int32_t* Z, int64_t m, int64_t n, int64_t group,
+                                                         int64_t G) {
+  for (int64_t r = blockIdx.y; r < m; r += gridDim.y)
+    for (int64_t c = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x); c < n; c += (int64_t)gridDim.x * 2048) {
+      const uint2 q = *(const uint2*)(Q8 + r * n + c);
+      float y[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t g = group <= 0 ? 0 : (c + k) / group;
+        const uint32_t qb = ((k < 4 ? q.x : q.y) >> (8 * (k & 3))) & 0xFFu;
+        y[k] = S[r * G + g] * ((float)qb - (float)Z[r * G + g]);
+      }
+      if (DT == 2) {
+        *(f32x4*)((float*)W + r * ldw + c) = f32x4{y[0], y[1], y[2], y[3]};
+        *(f32x4*)((float*)W + r * ldw + c + 4) = f32x4{y[4], y[5], y[6], y[7]};
+      } else {
+        uint32_t wv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint16_t lo, hi;
+          if (DT == 0) {
+            lo = __builtin_bit_cast(uint16_t, (_Float16)y[2 * k]);
+            hi = __builtin_bit_cast(uint16_t, (_Float16)y[2 * k + 1]);
+          } else {
+            lo = f32_to_bf16(y[2 * k]);
+            hi = f32_to_bf16(y[2 * k + 1]);
+          }
+          wv[k] = (uint32_t)lo | ((uint32_t)hi << 16);
+        }
+        *(uint4*)((uint16_t*)W + r * ldw + c) = uint4{wv[0], wv[1], wv[2], wv[3]};
+      }
+    }
+}
+
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 dim3 rows_grid(int64_t cols, int64_t rows) {
@@ -523,7 +605,12 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   const int gmode = !inblock ? 0 : (pow2 && group <= (B <= 32 ? 32 : 128) ? (int)group : -1);
   const dim3 rg = rows_grid(n, m);
 
-  if (dt == 0) hipLaunchKernelGGL((to_f32_kernel<0>), rg, dim3(256), 0, st, W, ldw, V, m, n);
+  const bool x8 = n % 8 == 0 && ldw % 8 == 0 && ((uintptr_t)W & 15) == 0;
+  const dim3 rg8 = rows_grid(cdiv(n, 8), m);
+  if (x8 && dt == 0) hipLaunchKernelGGL((to_f32x8_kernel<0>), rg8, dim3(256), 0, st, W, ldw, V, m, n);
+  else if (x8 && dt == 1) hipLaunchKernelGGL((to_f32x8_kernel<1>), rg8, dim3(256), 0, st, W, ldw, V, m, n);
+  else if (x8) hipLaunchKernelGGL((to_f32x8_kernel<2>), rg8, dim3(256), 0, st, W, ldw, V, m, n);
+  else if (dt == 0) hipLaunchKernelGGL((to_f32_kernel<0>), rg, dim3(256), 0, st, W, ldw, V, m, n);
   else if (dt == 1) hipLaunchKernelGGL((to_f32_kernel<1>), rg, dim3(256), 0, st, W, ldw, V, m, n);
   else hipLaunchKernelGGL((to_f32_kernel<2>), rg, dim3(256), 0, st, W, ldw, V, m, n);
   const unsigned prow = (unsigned)cdiv(m, 4);
@@ -533,8 +620,8 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   if (err_sq)
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(m, 256), 1024)), dim3(256), 0, st,
                        err_sq, m);
-  if (nstep == 32) hipLaunchKernelGGL((diag_blocks_kernel<32>), dim3((unsigned)cdiv(n, B)), dim3(256), 0, st, U, n, B, Dblk);
-  else hipLaunchKernelGGL((diag_blocks_kernel<BMAX>), dim3((unsigned)cdiv(n, B)), dim3(256), 0, st, U, n, B, Dblk);
+  if (nstep == 32) hipLaunchKernelGGL((diag_blocks_kernel<32>), dim3((unsigned)cdiv(n, B), 32 / 8), dim3(256), 0, st, U, n, B, Dblk);
+  else hipLaunchKernelGGL((diag_blocks_kernel<BMAX>), dim3((unsigned)cdiv(n, B), BMAX / 8), dim3(256), 0, st, U, n, B, Dblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -592,7 +679,10 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   const int64_t words = cdiv(n * bits, 32);
   hipLaunchKernelGGL(pack_kernel, rows_grid(words, m), dim3(256), 0, st, (const uint8_t*)Q8, m, n, bits, qcodes, words);
   if (write_dequant) {
-    if (dt == 0) hipLaunchKernelGGL((dequant_kernel<0>), rg, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
+    if (x8 && dt == 0) hipLaunchKernelGGL((dequant_x8_kernel<0>), rg8, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
+    else if (x8 && dt == 1) hipLaunchKernelGGL((dequant_x8_kernel<1>), rg8, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
+    else if (x8) hipLaunchKernelGGL((dequant_x8_kernel<2>), rg8, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
+    else if (dt == 0) hipLaunchKernelGGL((dequant_kernel<0>), rg, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
     else if (dt == 1) hipLaunchKernelGGL((dequant_kernel<1>), rg, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
     else hipLaunchKernelGGL((dequant_kernel<2>), rg, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
   }
