@@ -340,17 +340,30 @@ __device__ __forceinline__ f32x4 ld4(const float* p) {
 }
 
 // Rows 32w..32w+31 of S (a 64-column panel in LDS) times Dinv^T, both 32-wide
-// output blocks, for this wave.
+// output blocks, for this wave.  The operands of step kk + 1 are read while the
+// MFMAs of step kk run (two register sets).
 __device__ __forceinline__ void panel_solve(const float* S, const float* sD, int w, int lane, f32x16 (&o)[2]) {
   const int kr = lane >> 5, cl = lane & 31;
   o[0] = zero16();
   o[1] = zero16();
+  float av[2], d0[2], d1[2];
+  auto ld = [&](int kk, int b) {
+    const int k = 2 * kk + kr;
+    av[b] = S[pidx(32 * w + cl, k)];
+    if (kk < 16) d0[b] = sD[pidx(cl, k)];  // Dinv is lower triangular
+    d1[b] = sD[pidx(32 + cl, k)];
+  };
+  ld(0, 0);
 #pragma unroll
   for (int kk = 0; kk < NB / 2; ++kk) {
-    const int k = 2 * kk + kr;
-    const float av = S[pidx(32 * w + cl, k)];
-    if (kk < 16) o[0] = mfma_f32(av, sD[pidx(cl, k)], o[0]);  // Dinv is lower triangular
-    o[1] = mfma_f32(av, sD[pidx(32 + cl, k)], o[1]);
+    const int b = kk & 1;
+    if (kk + 1 < NB / 2) ld(kk + 1, b ^ 1);
+    if (kk < 16) o[0] = mfma_f32(av[b], d0[b], o[0]);
+    o[1] = mfma_f32(av[b], d1[b], o[1]);
+    // the reads of step kk + 1 ahead of the MFMAs of step kk
+    if (kk + 1 < NB / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (kk < 16) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    else __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
 }
 
@@ -372,7 +385,11 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
   const int64_t r0 = R0 + (int64_t)tm * TB, c0 = R0 + (int64_t)tn * TB;
   const bool dg = tm == tn;
   const int wr = wave >> 1, wc = wave & 1;
-  const bool active = !(dg && wr < wc);  // that quadrant of a diagonal tile lies above the diagonal
+  // A quadrant of a diagonal tile above the diagonal has nothing to do, and
+  // neither has the first quadrant of tile 0: that is the next diagonal block,
+  // which workgroup 0 updates itself.
+  const bool active = !(dg && wr < wc) && !(tm == 0 && wr == 0 && wc == 0);
+  const uint32_t n32 = (uint32_t)n;
 
   // Panel rows and Dinv_k: all loads in flight together, then to LDS.  Rows
   // past n are clamped: they only reach outputs that are never stored.
@@ -406,6 +423,10 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
   __syncthreads();
 
   // L21 slabs; each wave reads and then overwrites only its own 32 rows
+  // the first tile column stores its slab of L21: rows past n fall outside
+  // this buffer and are dropped
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+      L + (r0 * n + k0), 0, (int)((uint32_t)min<int64_t>(TB, n - r0) * n32 * 4u), 0x00020000);
   const int cl = lane & 31;
   f32x16 o[2];
   panel_solve(sR, sD, wave, lane, o);
@@ -415,7 +436,10 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
     for (int r = 0; r < 16; ++r) {
       const int rr = 32 * wave + mfma32_row(r, lane);
       sR[pidx(rr, 32 * nb + cl)] = o[nb][r];
-      if (tn == 0 && r0 + rr < n) L[(r0 + rr) * n + k0 + 32 * nb + cl] = o[nb][r];
+      const float v = o[nb][r];  // (a bit cast of the vector element itself reads element 0)
+      if (tn == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), lrs,
+                                              ((uint32_t)rr * n32 + (uint32_t)(32 * nb + cl)) * 4u, 0, 0);
     }
   if (!dg) {
     panel_solve(sC, sD, wave, lane, o);
@@ -427,35 +451,32 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
   // C of this wave's 64 x 64 quadrant, fetched only now (so it is not live
   // during the panel solves) and consumed after the rank update's MFMAs
   const bool interior = r0 + TB <= n && c0 + TB <= n;
-  const int64_t rbase = r0 + 64 * wr + 4 * (lane >> 5);
-  const int64_t cbase = c0 + 64 * wc + (lane & 31);
   f32x16 cp[2][2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) cp[mb][nb] = zero16();
-  // interior tiles: a uniform base and 32-bit lane offsets (the tile spans
-  // fewer than 2^31 bytes), so loads and stores need no 64-bit addresses
-  const float* tbase = A + (r0 * n + c0);
-  const uint32_t n32 = (uint32_t)n;
-  const uint32_t loff = (uint32_t)(64 * wr + 4 * (lane >> 5)) * n32 + (uint32_t)(64 * wc + (lane & 31));
-  if (active && interior) {
+  // A buffer resource over the tile's rows inside the matrix and 32-bit lane
+  // offsets (the tile spans fewer than 128 n elements, n < 2^22).  Loads past
+  // the last row read as zero and entries past n are never stored, so edge
+  // tiles need no clamping; a store that must not happen gets an offset past
+  // the buffer and is dropped, so no store is behind a branch.
+  const uint32_t lr0 = (uint32_t)(64 * wr + 4 * (lane >> 5)), lc0 = (uint32_t)(64 * wc + (lane & 31));
+  const uint32_t rlim = (uint32_t)(min<int64_t>(TB, n - r0) - 1), clim = (uint32_t)(min<int64_t>(TB, n - c0) - 1);
+  const __amdgpu_buffer_rsrc_t trs =
+      __builtin_amdgcn_make_buffer_rsrc(A + (r0 * n + c0), 0, (int)((rlim + 1) * n32 * 4u), 0x00020000);
+  const uint32_t loff = (lr0 * n32 + lc0) * 4u;
+  auto coff = [&](int mb, int nb, int r) {
+    return loff + ((uint32_t)(32 * mb + 8 * (r >> 2) + (r & 3)) * n32 + (uint32_t)(32 * nb)) * 4u;
+  };
+  if (active) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          cp[mb][nb][r] = tbase[loff + (uint32_t)(32 * mb + 8 * (r >> 2) + (r & 3)) * n32 + (uint32_t)(32 * nb)];
-  } else if (active) {  // entries past n are never stored: clamped loads
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const float* colp = A + min(cbase + 32 * nb, n - 1);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cp[mb][nb][r] = colp[min(rbase + 32 * mb + 8 * (r >> 2) + (r & 3), n - 1) * n];
-      }
+          cp[mb][nb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(trs, coff(mb, nb, r), 0, 0));
   }
   __syncthreads();
   if (!active) return;
@@ -467,41 +488,53 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
-#pragma unroll 8
-  for (int kk = 0; kk < NB / 2; ++kk) {
+  // operands of step kk + 1 read while the MFMAs of step kk run
+  float a0[2], a1[2], b0[2], b1[2];
+  auto ld = [&](int kk, int b) {
     const int k = 2 * kk + kr;
-    const float a0 = sR[pidx(64 * wr + cl, k)], a1 = sR[pidx(64 * wr + 32 + cl, k)];
-    const float b0 = sB[pidx(64 * wc + cl, k)], b1 = sB[pidx(64 * wc + 32 + cl, k)];
-    acc[0][0] = mfma_f32(a0, b0, acc[0][0]);
-    acc[0][1] = mfma_f32(a0, b1, acc[0][1]);
-    acc[1][0] = mfma_f32(a1, b0, acc[1][0]);
-    acc[1][1] = mfma_f32(a1, b1, acc[1][1]);
+    a0[b] = sR[pidx(64 * wr + cl, k)];
+    a1[b] = sR[pidx(64 * wr + 32 + cl, k)];
+    b0[b] = sB[pidx(64 * wc + cl, k)];
+    b1[b] = sB[pidx(64 * wc + 32 + cl, k)];
+  };
+  ld(0, 0);
+#pragma unroll
+  for (int kk = 0; kk < NB / 2; ++kk) {
+    const int b = kk & 1;
+    if (kk + 1 < NB / 2) ld(kk + 1, b ^ 1);
+    acc[0][0] = mfma_f32(a0[b], b0[b], acc[0][0]);
+    acc[0][1] = mfma_f32(a0[b], b1[b], acc[0][1]);
+    acc[1][0] = mfma_f32(a1[b], b0[b], acc[1][0]);
+    acc[1][1] = mfma_f32(a1[b], b1[b], acc[1][1]);
+    // the reads of step kk + 1 (two paired reads) ahead of the MFMAs of step kk
+    if (kk + 1 < NB / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   }
   // lower part only; the next diagonal block is left to workgroup 0, which
   // reads it before the update
-  if (interior && !dg && tm != 0) {
-    float* tb = A + (r0 * n + c0);
+  if (interior && !dg) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          tb[loff + (uint32_t)(32 * mb + 8 * (r >> 2) + (r & 3)) * n32 + (uint32_t)(32 * nb)] =
-              cp[mb][nb][r] - acc[mb][nb][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, cp[mb][nb][r] - acc[mb][nb][r]), trs,
+                                                coff(mb, nb, r), 0, 0);
     return;
   }
-  const int64_t skip_end = (tm == 0) ? R0 + NB : R0;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = rbase + 32 * mb + 8 * (r >> 2) + (r & 3);
-        const int64_t col = cbase + 32 * nb;
-        if (row < n && col <= row && !(row < skip_end && col < skip_end))
-          A[row * n + col] = cp[mb][nb][r] - acc[mb][nb][r];
+        const uint32_t lr = lr0 + (uint32_t)(32 * mb + 8 * (r >> 2) + (r & 3)), lc = lc0 + (uint32_t)(32 * nb);
+        // inside the matrix, and on or below the diagonal of a diagonal tile
+        // (there r0 = c0, and tile 0's first quadrant is inactive)
+        const bool st = lr <= rlim && lc <= clim && (!dg || lc <= lr);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, cp[mb][nb][r] - acc[mb][nb][r]), trs,
+                                              st ? coff(mb, nb, r) : 0x80000000u, 0, 0);
       }
 }
 
