@@ -339,31 +339,39 @@ __device__ __forceinline__ f32x4 ld4(const float* p) {
   return VEC ? *(const f32x4*)p : f32x4{p[0], p[1], p[2], p[3]};
 }
 
+// K order of the 32 steps of a K = 64 product with v_mfma_f32_32x32x2f32:
+// step s gives lane half kr (lanes 32 kr ..) the index
+// k = 32 (s / 16) + 16 kr + s % 16, so each lane walks contiguous runs of k
+// (16-byte LDS reads, four steps per read) and steps 0..15 see only k < 32.
+// Any order is the same sum; the first operand and the second use the same one.
+__device__ __forceinline__ int kgroup(int g, int kr) { return 32 * (g >> 2) + 16 * kr + 4 * (g & 3); }  // g = s / 4
+
 // Rows 32w..32w+31 of S (a 64-column panel in LDS) times Dinv^T, both 32-wide
-// output blocks, for this wave.  The operands of step kk + 1 are read while the
-// MFMAs of step kk run (two register sets).
+// output blocks, for this wave.  The operands of steps 4g+4.. are read while
+// the MFMAs of steps 4g.. run.
 __device__ __forceinline__ void panel_solve(const float* S, const float* sD, int w, int lane, f32x16 (&o)[2]) {
   const int kr = lane >> 5, cl = lane & 31;
   o[0] = zero16();
   o[1] = zero16();
-  float av[2], d0[2], d1[2];
-  auto ld = [&](int kk, int b) {
-    const int k = 2 * kk + kr;
-    av[b] = S[pidx(32 * w + cl, k)];
-    if (kk < 16) d0[b] = sD[pidx(cl, k)];  // Dinv is lower triangular
-    d1[b] = sD[pidx(32 + cl, k)];
+  f32x4 av[2], d0[2], d1[2];
+  auto ld = [&](int g, int b) {
+    const int k = kgroup(g, kr);
+    av[b] = *(const f32x4*)&S[pidx(32 * w + cl, k)];
+    if (g < 4) d0[b] = *(const f32x4*)&sD[pidx(cl, k)];  // Dinv is lower triangular: columns 0..31 need k < 32
+    d1[b] = *(const f32x4*)&sD[pidx(32 + cl, k)];
   };
   ld(0, 0);
 #pragma unroll
-  for (int kk = 0; kk < NB / 2; ++kk) {
-    const int b = kk & 1;
-    if (kk + 1 < NB / 2) ld(kk + 1, b ^ 1);
-    if (kk < 16) o[0] = mfma_f32(av[b], d0[b], o[0]);
-    o[1] = mfma_f32(av[b], d1[b], o[1]);
-    // the reads of step kk + 1 ahead of the MFMAs of step kk
-    if (kk + 1 < NB / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    if (kk < 16) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    else __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  for (int g = 0; g < 8; ++g) {
+    const int b = g & 1;
+    if (g + 1 < 8) ld(g + 1, b ^ 1);
+    __builtin_amdgcn_sched_barrier(0);  // keeps the reads ahead of this group's MFMAs
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (g < 4) o[0] = mfma_f32(av[b][q], d0[b][q], o[0]);
+      o[1] = mfma_f32(av[b][q], d1[b][q], o[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -488,27 +496,29 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
-  // operands of step kk + 1 read while the MFMAs of step kk run
-  float a0[2], a1[2], b0[2], b1[2];
-  auto ld = [&](int kk, int b) {
-    const int k = 2 * kk + kr;
-    a0[b] = sR[pidx(64 * wr + cl, k)];
-    a1[b] = sR[pidx(64 * wr + 32 + cl, k)];
-    b0[b] = sB[pidx(64 * wc + cl, k)];
-    b1[b] = sB[pidx(64 * wc + 32 + cl, k)];
+  // the operands of steps 4g+4.. read while the MFMAs of steps 4g.. run
+  f32x4 a0[2], a1[2], b0[2], b1[2];
+  auto ld = [&](int g, int b) {
+    const int k = kgroup(g, kr);
+    a0[b] = *(const f32x4*)&sR[pidx(64 * wr + cl, k)];
+    a1[b] = *(const f32x4*)&sR[pidx(64 * wr + 32 + cl, k)];
+    b0[b] = *(const f32x4*)&sB[pidx(64 * wc + cl, k)];
+    b1[b] = *(const f32x4*)&sB[pidx(64 * wc + 32 + cl, k)];
   };
   ld(0, 0);
 #pragma unroll
-  for (int kk = 0; kk < NB / 2; ++kk) {
-    const int b = kk & 1;
-    if (kk + 1 < NB / 2) ld(kk + 1, b ^ 1);
-    acc[0][0] = mfma_f32(a0[b], b0[b], acc[0][0]);
-    acc[0][1] = mfma_f32(a0[b], b1[b], acc[0][1]);
-    acc[1][0] = mfma_f32(a1[b], b0[b], acc[1][0]);
-    acc[1][1] = mfma_f32(a1[b], b1[b], acc[1][1]);
-    // the reads of step kk + 1 (two paired reads) ahead of the MFMAs of step kk
-    if (kk + 1 < NB / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  for (int g = 0; g < 8; ++g) {
+    const int b = g & 1;
+    if (g + 1 < 8) ld(g + 1, b ^ 1);
+    __builtin_amdgcn_sched_barrier(0);  // keeps the reads ahead of this group's MFMAs
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[0][0] = mfma_f32(a0[b][q], b0[b][q], acc[0][0]);
+      acc[0][1] = mfma_f32(a0[b][q], b1[b][q], acc[0][1]);
+      acc[1][0] = mfma_f32(a1[b][q], b0[b][q], acc[1][0]);
+      acc[1][1] = mfma_f32(a1[b][q], b1[b][q], acc[1][1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   // lower part only; the next diagonal block is left to workgroup 0, which
   // reads it before the update
