@@ -210,19 +210,25 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
       float a[PW];
 #pragma unroll
       for (int k = 0; k < PW; ++k) a[k] = sD[lane * LP + c0 + k];
+      float myrs = 0.f, mypiv = 1.f;  // lane c0 + jj keeps column jj's pivot and its 1/sqrt
 #pragma unroll
       for (int jj = 0; jj < PW; ++jj) {
         const int j = c0 + jj;
         const float piv = readlane_f(a[jj], j);
-        const bool ok = piv > 0.f && piv < INFINITY;
-        badcol = (badcol < 0 && !ok) ? j : badcol;
         const float rs = __builtin_amdgcn_rsqf(piv);  // not finite after a failure: the rest is discarded
-        const float l = lane > j ? a[jj] * rs : (lane == j ? piv * rs : 0.f);
+        // lane j holds the pivot itself (piv rs = sqrt(piv)); rows above it get 0
+        const float l = lane >= j ? a[jj] * rs : 0.f;
+        myrs = lane == j ? rs : myrs;
+        mypiv = lane == j ? piv : mypiv;
         a[jj] = l;
-        if (lane == 0) rinv[j] = rs;
 #pragma unroll
         for (int k = jj + 1; k < PW; ++k) a[k] = fmaf(-l, readlane_f(l, c0 + k), a[k]);
       }
+      // the panel's first column whose pivot is not positive and finite
+      const bool inpan = lane >= c0 && lane < c0 + PW;
+      const uint64_t badm = __ballot(inpan && !(mypiv > 0.f && mypiv < INFINITY));
+      if (badcol < 0 && badm != 0) badcol = (int)__builtin_ctzll(badm);
+      if (inpan) rinv[lane] = myrs;
 #pragma unroll
       for (int k = 0; k < PW; ++k) sL[lane * LLP + c0 + k] = a[k];
     }
