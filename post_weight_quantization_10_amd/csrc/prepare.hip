@@ -89,9 +89,10 @@ __global__ __launch_bounds__(256) void reverse_damp4_kernel(const float* H, floa
 constexpr int TB = 128;          // trailing-update tile
 constexpr int LP = 65;           // LDS pitch of 64-column leaf matrices (floats)
 constexpr int LLP = 68;          // LDS pitch of the leaf factor: 16-byte aligned rows
+constexpr int PP = 68;           // LDS pitch of the leaf's product operands: 16-byte aligned rows
 constexpr int SMEM = 20480;      // floats of LDS per workgroup (80 KiB)
-static_assert(3 * 64 * LP + 64 * LLP + 65 <= SMEM, "leaf LDS layout");
-static_assert(64 * LLP + 32 * 33 <= 2 * 64 * LP, "the inverse and the doubling products fit over the product buffers");
+static_assert(64 * LP + 2 * 64 * PP + 64 * LLP + 65 <= SMEM, "leaf LDS layout");
+static_assert(64 * LLP + 32 * 33 <= 2 * 64 * PP, "the inverse and the doubling products fit over the product buffers");
 static_assert(64 * 64 + 2 * 128 * 64 <= SMEM, "tile LDS layout");
 
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
@@ -127,19 +128,43 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = (int)min<int64_t>(NB, n - j0);
   float* sD = smem;              // 64 x LP
-  float* sP = sD + 64 * LP;      // 64 x LP
-  float* sQ = sP + 64 * LP;      // 64 x LP
-  float* sL = sQ + 64 * LP;      // 64 x LLP: the factor, zero above the diagonal
+  float* sP = sD + 64 * LP;      // 64 x PP
+  float* sQ = sP + 64 * PP;      // 64 x PP
+  float* sL = sQ + 64 * PP;      // 64 x LLP: the factor, zero above the diagonal
   float* sX = sP;                // 64 x LLP over sP and sQ once the update is applied: the inverse
   float* sT = sP + 64 * LLP;     // 32 x 33: products of the doubling steps
   float* rinv = sL + 64 * LLP;   // 64: 1 / L[j][j]
   int* failed = (int*)(rinv + 64);
 
-  // loads from clamped (in-range) addresses, then selects: no branches, all
-  // loads in flight together
-  // (the empty asm makes every load unconditional; otherwise the compiler
-  // moves each load under its select, one wait per load)
-  {
+  // All loads in flight together, then to LDS.  (The empty asm makes every
+  // load unconditional; otherwise the compiler moves each load under its
+  // select, one wait per load.)
+  if (kb == NB && (n & 3) == 0) {  // full block: 16-byte loads
+    f32x4 v[4], pv[4], qv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e >> 4, c = 4 * (e & 15);
+      v[u] = *(const f32x4*)&A[(j0 + r) * n + j0 + c];
+      if (kp >= 0) {
+        pv[u] = *(const f32x4*)&A[(j0 + r) * n + kp + c];
+        qv[u] = *(const f32x4*)&dinv_prev[r * NB + c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      asm volatile("" : "+v"(v[u]));
+      const int e = tid + 256 * u;
+      const int r = e >> 4, c = 4 * (e & 15);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sD[r * LP + c + q] = (c + q <= r) ? v[u][q] : 0.f;
+      if (kp >= 0) {
+        asm volatile("" : "+v"(pv[u]));
+        *(f32x4*)&sP[r * PP + c] = pv[u];
+        *(f32x4*)&sQ[r * PP + c] = qv[u];
+      }
+    }
+  } else {  // the last, partial block (or n not a multiple of 4): clamped addresses, then selects
     constexpr int NU = NB * NB / 256;
     float v[NU], pv[NU], qv[NU];
 #pragma unroll
@@ -161,52 +186,99 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
       sD[r * LP + c] = (r < kb && c < kb) ? ((c <= r) ? v[u] : 0.f) : ((r == c) ? 1.f : 0.f);
       if (kp >= 0) {
         asm volatile("" : "+v"(pv[u]));
-        sP[r * LP + c] = (r < kb) ? pv[u] : 0.f;
-        sQ[r * LP + c] = qv[u];
+        sP[r * PP + c] = (r < kb) ? pv[u] : 0.f;
+        sQ[r * PP + c] = qv[u];
       }
     }
   }
   if (tid == 0) *failed = 0;
   __syncthreads();
 
+  // The two products with v_mfma_f32_16x16x4f32 (lane l: A[l%16][l/16],
+  // B[l/16][l%16]; result register r is row 4(l/16) + r, column l%16) on
+  // 16 x 16 output blocks.  MFMA step 4t + q of a K = 64 sum gives lane
+  // quarter kq = l/16 the index k = 16t + 4kq + q: one 16-byte read per
+  // operand and group t, and a block that needs only k < 16(t+1) stops there.
   if (kp >= 0) {
-    const int bm = wave >> 1, bn = wave & 1;  // this wave's 32 x 32 output block
-    const int kr = lane >> 5, cl = lane & 31;
-    f32x16 o = zero16();
+    const int i16 = lane & 15, kq = lane >> 4;
+    {  // Lrow rows 16w.. = P[16w.., :] Dinv_K^T; column block bj needs k < 16(bj+1) (Dinv_K is lower)
+      f32x4 acc[4];
 #pragma unroll
-    for (int kk = 0; kk < NB / 2; ++kk) {
-      const int k = 2 * kk + kr;
-      if (bn == 1 || kk < 16)  // Dinv_K is lower triangular
-        o = mfma_f32(sP[(32 * bm + cl) * LP + k], sQ[(32 * bn + cl) * LP + k], o);
-    }
-    __syncthreads();  // every wave is done reading A[J, K]
+      for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sP[(32 * bm + mfma32_row(r, lane)) * LP + 32 * bn + cl] = o[r];
-    __syncthreads();
-    if (!(bm == 0 && bn == 1)) {  // lower blocks of D
-      f32x16 u = zero16();
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 av = *(const f32x4*)&sP[(16 * wave + i16) * PP + 16 * t + 4 * kq];
 #pragma unroll
-      for (int kk = 0; kk < NB / 2; ++kk) {
-        const int k = 2 * kk + kr;
-        u = mfma_f32(sP[(32 * bm + cl) * LP + k], sP[(32 * bn + cl) * LP + k], u);
+        for (int bj = t; bj < 4; ++bj) {
+          const f32x4 bv = *(const f32x4*)&sQ[(16 * bj + i16) * PP + 16 * t + 4 * kq];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc[bj], 0, 0, 0);
+        }
       }
+      __syncthreads();  // every wave is done reading A[J, K]
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sD[(32 * bm + mfma32_row(r, lane)) * LP + 32 * bn + cl] -= u[r];
+      for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sP[(16 * wave + 4 * kq + r) * PP + 16 * bj + i16] = acc[bj][r];
+    }
+    __syncthreads();
+    {  // D -= Lrow Lrow^T on the ten lower 16 x 16 blocks: 3, 3, 2, 2 of them per wave
+      // blocks (bi, bj): wave 0 (0,0) (1,0) (1,1); wave 1 (2,0) (2,1) (2,2); wave 2 (3,0) (3,1); wave 3 (3,2) (3,3)
+      const int nblk = wave < 2 ? 3 : 2;
+      const int bi0 = wave == 0 ? 0 : (wave == 1 ? 2 : 3);
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        if (b < nblk) {
+          const int bi = wave == 0 ? (b == 0 ? 0 : 1) : bi0;
+          const int bj = wave == 0 ? (b == 0 ? 0 : b - 1) : (wave == 3 ? 2 + b : b);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const f32x4 av = *(const f32x4*)&sP[(16 * bi + i16) * PP + 16 * t + 4 * kq];
+            const f32x4 bv = *(const f32x4*)&sP[(16 * bj + i16) * PP + 16 * t + 4 * kq];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sD[(16 * bi + 4 * kq + r) * LP + 16 * bj + i16] -= acc[r];
+        }
+      }
     }
     __syncthreads();
   }
 
-  // sX is free now (the update is applied): zero it, so that its upper
-  // blocks read as zero in the doubling products
-  for (int e = tid; e < 64 * LLP; e += 256) sX[e] = 0.f;
+  // sX is free now (the update is applied): waves 1..3 zero it while wave 0
+  // factors the first panel, so that its upper blocks read as zero in the
+  // doubling products
+  if (wave > 0)
+    for (int e = tid - 64; e < 64 * LLP; e += 192) sX[e] = 0.f;
 
-  // ---- factor, PW-column panels
+  // ---- factor, PW-column panels.  Panel p: wave 0 applies panel p-1 to the
+  // panel's own 16 columns and factors them (lane i holds row i of the panel
+  // in registers; at column j the pivot comes from lane j and each later
+  // panel column is updated with a readlane of l: no LDS, no branch), while
+  // waves 1..3 apply panel p-1 to the column blocks after it.  One barrier
+  // per panel.
   constexpr int PW = 16;
   const int l16 = lane & 15, g16 = lane >> 4;
+  // D[16bi.., 16bj..] -= L[16bi.., q0:q0+16] L[16bj.., q0:q0+16]^T: a 16 x 16
+  // block, v_mfma_f32_16x16x4f32 (lane l: A[l%16][l/16], B[l/16][l%16];
+  // result register r is row 4(l/16) + r, column l%16)
+  auto upd = [&](int bi, int bj, int q0) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < PW; k += 4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sL[(16 * bi + l16) * LLP + q0 + k + g16],
+                                                  sL[(16 * bj + l16) * LLP + q0 + k + g16], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sD[(16 * bi + 4 * g16 + r) * LP + 16 * bj + l16] -= acc[r];
+  };
   int badcol = -1;  // wave 0: first column whose pivot is not positive and finite (uniform)
 #pragma unroll 1
-  for (int c0 = 0; c0 < NB; c0 += PW) {
+  for (int p = 0; p < NB / PW; ++p) {
+    const int c0 = PW * p;
     if (wave == 0) {
+      for (int bi = p; p > 0 && bi < NB / 16; ++bi) upd(bi, p, c0 - PW);
       float a[PW];
 #pragma unroll
       for (int k = 0; k < PW; ++k) a[k] = sD[lane * LP + c0 + k];
@@ -231,24 +303,15 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
       if (inpan) rinv[lane] = myrs;
 #pragma unroll
       for (int k = 0; k < PW; ++k) sL[lane * LLP + c0 + k] = a[k];
-    }
-    __syncthreads();
-    // rows and columns [c0 + PW, NB) -= L[:, c0:c0+PW] L[:, c0:c0+PW]^T, 16 x 16
-    // blocks of the lower triangle, v_mfma_f32_16x16x4f32 (lane l: A[l%16][l/16],
-    // B[l/16][l%16]; result register r is row 4(l/16) + r, column l%16)
-    const int nb = (NB - c0 - PW) / 16;
-    for (int t = wave; t < nb * (nb + 1) / 2; t += 4) {
-      int bi = 0;
-      while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
-      const int bj = t - bi * (bi + 1) / 2;
-      const int r0 = c0 + PW + 16 * bi, s0 = c0 + PW + 16 * bj;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < PW; k += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sL[(r0 + l16) * LLP + c0 + k + g16],
-                                                    sL[(s0 + l16) * LLP + c0 + k + g16], acc, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sD[(r0 + 4 * g16 + r) * LP + s0 + l16] -= acc[r];
+    } else if (p > 0) {
+      // lower blocks (bi, bj) with p < bj <= bi, one per wave in turn
+      const int nb = NB / 16 - 1 - p;
+      for (int t = wave - 1; t < nb * (nb + 1) / 2; t += 3) {
+        int bi = 0;
+        while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
+        const int bj = t - bi * (bi + 1) / 2;
+        upd(p + 1 + bi, p + 1 + bj, c0 - PW);
+      }
     }
     __syncthreads();
   }
@@ -441,26 +504,39 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
   // this buffer and are dropped
   const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
       L + (r0 * n + k0), 0, (int)((uint32_t)min<int64_t>(TB, n - r0) * n32 * 4u), 0x00020000);
-  const int cl = lane & 31;
+  const int cl = lane & 31, kr = lane >> 5;
+  // The solved rows go back in place.  Output register r of a 32 x 32 block
+  // is row 32w + 4kr + 8(r/4) + r%4 (column cl), so its swizzled LDS index is
+  // a lane term plus a constant: (row & 15) = 4kr | (8(r/4 % 2) + r%4).
+  auto put = [&](float* S, const f32x16 (&v)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int lc = (32 * nb + cl) ^ (kr << 4);
+      float* base = S + (32 * wave + 4 * kr) * 64;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rc = 8 * (r >> 2) + (r & 3);
+        base[rc * 64 + (lc ^ ((rc & 15) << 2))] = v[nb][r];
+      }
+    }
+  };
   f32x16 o[2];
   panel_solve(sR, sD, wave, lane, o);
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = 32 * wave + mfma32_row(r, lane);
-      sR[pidx(rr, 32 * nb + cl)] = o[nb][r];
-      const float v = o[nb][r];  // (a bit cast of the vector element itself reads element 0)
-      if (tn == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), lrs,
-                                              ((uint32_t)rr * n32 + (uint32_t)(32 * nb + cl)) * 4u, 0, 0);
-    }
-  if (!dg) {
-    panel_solve(sC, sD, wave, lane, o);
+  put(sR, o);
+  if (tn == 0) {  // row 32w + 4kr + rc of the slab: a lane term plus a uniform multiple of n
+    const uint32_t lb = (uint32_t)(32 * wave + 4 * kr) * n32 + (uint32_t)cl;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sC[pidx(32 * wave + mfma32_row(r, lane), 32 * nb + cl)] = o[nb][r];
+      for (int r = 0; r < 16; ++r) {
+        const float v = o[nb][r];  // (a bit cast of the vector element itself reads element 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), lrs,
+                                              (lb + (uint32_t)(8 * (r >> 2) + (r & 3)) * n32 + 32u * nb) * 4u, 0, 0);
+      }
+  }
+  if (!dg) {
+    panel_solve(sC, sD, wave, lane, o);
+    put(sC, o);
   }
   // C of this wave's 64 x 64 quadrant, fetched only now (so it is not live
   // during the panel solves) and consumed after the rank update's MFMAs
@@ -496,7 +572,6 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
   if (!active) return;
 
   const float* sB = dg ? sR : sC;
-  const int kr = lane >> 5;
   f32x16 acc[2][2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
