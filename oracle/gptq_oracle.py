@@ -15,6 +15,9 @@ describe the method.  Short names used in the citations below:
             (hungho77.github.io, /hung/blog/gptq-second-order-quantization/)
   [SOQ-vi]  the Vietnamese edition of that post (/hung/vi/blog/...)
 
+Beyond the per-layer path, dequant_matmul is the runtime consumer of the
+packed layer (weights unpacked and dequantized next to 16-bit activations).
+
 Readings taken where the pages are silent or disagree (each is also listed in
 the design notes):
 
@@ -355,6 +358,25 @@ def unpack_codes(words: np.ndarray, bits: int, n: int) -> np.ndarray:
         both = ext[:, w] | (ext[:, w + 1] << np.uint64(32))
         out[:, j] = ((both >> np.uint64(off)) & mask).astype(np.int64)
     return out
+
+
+# ----------------------------------------------------------------------------- runtime use of the packed layer
+
+def dequant_matmul(X: np.ndarray, words: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, group: int,
+                   n: int) -> np.ndarray:
+    """Y = X What^T, [tokens x m], for a packed layer.
+
+    The weight-only path keeps activations in 16-bit floats; at run time the
+    packed b-bit weights are unpacked and dequantized, What = s (q - z) (R5),
+    and multiplied with the activations ([SOQ] "What the original results
+    established": speed comes from moving fewer weight bytes and unpacking
+    them efficiently; [SOQ-vi] closing paragraph: the artifact still needs a
+    packed INT4 kernel for the target device).  X [tokens x n] is taken
+    exactly as given; words, s, z are the layer outputs of quantize_layer.
+    fp64 throughout."""
+    q = unpack_codes(words, bits, n)
+    What = dequant_from(q, s, z, group)
+    return np.asarray(X, dtype=np.float64) @ What.T
 
 
 # ----------------------------------------------------------------------------- whole layer

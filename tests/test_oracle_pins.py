@@ -336,3 +336,50 @@ def test_pack_roundtrip_all_widths():
             w = O.pack_codes(q, bits)
             assert w.shape == (3, O.packed_words(n, bits))
             assert np.array_equal(O.unpack_codes(w, bits, n), q)
+
+
+# ----------------------------------------------------------------------------- the packed layer at run time
+
+def test_dequant_matmul_zero_point_codes_give_zero():
+    """Codes equal to their group's zero point dequantize to 0: Y = 0."""
+    rng = np.random.default_rng(21)
+    m, n, group, bits = 5, 256, 64, 4
+    z = rng.integers(0, 16, (m, n // group))
+    q = np.repeat(z, group, axis=1)
+    s = rng.uniform(0.01, 0.1, (m, n // group))
+    X = rng.normal(size=(3, n))
+    assert np.array_equal(O.dequant_matmul(X, O.pack_codes(q, bits), s, z, bits, group, n), np.zeros((3, m)))
+
+
+def test_dequant_matmul_single_code_selects_its_column():
+    """One code one step above its zero point, all others at it: Y[:, r] is
+    s[r, g(c)] X[:, c] for that column c only (bit order, column index, group
+    index and the X W^T orientation all matter)."""
+    rng = np.random.default_rng(22)
+    m, n, bits = 4, 96, 3
+    for group in (0, 32):
+        G = O.n_groups(n, group)
+        z = rng.integers(0, 4, (m, G))
+        s = rng.uniform(0.5, 2.0, (m, G))
+        X = rng.normal(size=(2, n))
+        for r, c in ((0, 0), (1, 31), (2, 32), (3, 95), (1, 50)):
+            g = 0 if group <= 0 else c // group
+            q = np.repeat(z, n if group <= 0 else group, axis=1)[:, :n].copy()
+            q[r, c] += 1
+            Y = O.dequant_matmul(X, O.pack_codes(q, bits), s, z, bits, group, n)
+            want = np.zeros((2, m))
+            want[:, r] = s[r, g] * X[:, c]
+            assert np.allclose(Y, want, rtol=0, atol=1e-15), (group, r, c)
+
+
+def test_dequant_matmul_matches_rtn_layer():
+    """Round-to-nearest quantization of W, packed, then run: equals X What^T
+    with What as the quantizer itself produced it."""
+    rng = np.random.default_rng(23)
+    m, n = 6, 384
+    X = rng.normal(size=(4, n))
+    W = rng.normal(0, 0.02, (m, n))
+    for bits, group in ((4, 128), (4, 0), (3, 64), (8, 128)):
+        r = O.rtn(W, bits, group)
+        Y = O.dequant_matmul(X, O.pack_codes(r["q"], bits), r["s"], r["z"], bits, group, n)
+        assert np.allclose(Y, X @ r["What"].T, rtol=1e-13, atol=1e-15)
