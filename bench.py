@@ -9,6 +9,11 @@ restore W, zero H, gptq_hessian_accumulate, gptq_prepare_hinv,
 gptq_quantize_layer (with the dequantized weights written back).
 
 Prints one JSON line (rank 0).  Multi-GPU runs are not supported.
+
+--kernel w4a16 instead times the runtime use of a packed layer,
+gptq_dequant_matmul (Y = X What^T with 4-bit g128 codes unpacked next to fp16
+activations), on an MLP-shaped layer (28672 x 8192) for one decode token; its
+line carries the same keys, with GB/s of the packed layer as the metric.
 """
 from __future__ import annotations
 
@@ -32,6 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="attn", choices=["attn", "tiny"])
+    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16"],
+                    help="layer: the quantization path (default); w4a16: the packed layer at run time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_attn_4096x262144_traffic.json"),
                     help="JSON with rocprofv3 FETCH/WRITE bytes per SYRK launch (optional)")
@@ -68,6 +75,75 @@ def cpu_baseline(W16, X16, job, U_gpu):
                       f"{t1 - t0:.2f}/{t2 - t1:.2f}/{t3 - t2:.2f}"}
 
 
+def bench_w4a16(args):
+    """gptq_dequant_matmul on a 28672 x 8192 4-bit g128 layer (MLP up/gate
+    projection shape), one fp16 decode token; synthetic packed layer (codes,
+    scales, zero points) and activations from synth/.  A step is one call.
+    Bytes counted: codes m n / 2, scales and zeros 8 m G, X and Y."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_10_amd as pw
+    import synth
+    m, n, T, group = 28672, 8192, 1, 128
+    dev = torch.device("cuda:0")
+    q, s, z = synth.packed_layer(m, n, 4, group, seed=7)
+    # pack on the host (4-bit: code j at bits 4 (j % 8) of word j / 8)
+    qq = q.reshape(m, n // 8, 8).astype(np.uint32)
+    words = np.zeros((m, n // 8), dtype=np.uint32)
+    for k in range(8):
+        words |= qq[:, :, k] << np.uint32(4 * k)
+    qw = torch.from_numpy(words.view(np.int32)).to(dev)
+    sd, zd = torch.from_numpy(s).to(dev), torch.from_numpy(z).to(dev)
+    X = torch.from_numpy(synth.activations(T, n, "f16", seed=8)).to(dev)
+    Y = torch.empty((T, m), dtype=torch.float16, device=dev)
+    ws = torch.empty(max(pw.dequant_matmul_workspace_bytes(T, m, n), 1), dtype=torch.uint8, device=dev)
+    for _ in range(max(args.warmup, 1) * 10):
+        pw.dequant_matmul(X, qw, sd, zd, 4, group, Y=Y, workspace=ws)
+    reps = 20 * args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        pw.dequant_matmul(X, qw, sd, zd, 4, group, Y=Y, workspace=ws)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / reps
+    # the same calls timed with HIP events on the stream the kernels run on
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        pw.dequant_matmul(X, qw, sd, zd, 4, group, Y=Y, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    us_ev = a.elapsed_time(b) * 1e3 / reps
+    G = n // group
+    nbytes = m * n / 2 + 8.0 * m * G + 2.0 * T * n + 2.0 * T * m
+    gbs = nbytes / (us * 1e-6) / 1e9
+    gbs_ev = nbytes / (us_ev * 1e-6) / 1e9
+    res = {
+        "metric": "GB/s of the packed 4-bit layer, W4A16 dequant-matmul (28672x8192 g128, 1 fp16 token)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 x u4 -> fp32 sums", "data": "synthetic",
+        "config": {"workload": f"w4a16 decode: W {m}x{n} 4-bit g{group} packed, X {T}x{n} fp16, Y {T}x{m} fp16",
+                   "tokens": T, "m": m, "n": n, "bits": 4, "group": group, "parallelism": "single GPU"},
+        "roofline": {"kernel": "gptq_dequant_matmul: dqmm4_stream_kernel + dqmm_reduce_kernel", "bound": "hbm",
+                     "achieved": round(gbs_ev, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                     "frac": round(gbs_ev / PEAK_HBM, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        rows = 1024
+        t1 = time.perf_counter()
+        O.dequant_matmul(synth.as_float64(X.cpu().numpy(), "f16"), words[:rows], s[:rows], z[:rows], 4, group, n)
+        dt = time.perf_counter() - t1
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        res["cpu_baseline"] = {"value": round(nbytes / (dt * m / rows) / 1e9, 3),
+                               "unit": "GB/s (estimated from the sample)", "cores": threads, "kind": "oracle",
+                               "sample": f"fp64 oracle unpack + dequantize + matmul of {rows} of {m} rows "
+                                         f"({dt:.2f} s), scaled x{m // rows}"}
+    print(json.dumps(res), flush=True)
+
+
 def traffic_bytes(path):
     """HBM bytes per Hessian launch from the committed rocprofv3 counter
     summary, or None when there is none or the kernel source has changed
@@ -92,6 +168,9 @@ def main():
         print("bench.py runs on one GPU only: the quantizer's data-parallel path here is a single-GPU build "
               "(multi-GPU sharding is a design note, not implemented)", file=sys.stderr)
         sys.exit(2)
+    if args.kernel == "w4a16":
+        bench_w4a16(args)
+        return
     import numpy as np
     import torch
 

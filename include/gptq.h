@@ -11,6 +11,11 @@
  *                            column, compensating later columns from the rows
  *                            of U, and emitting packed codes, scales and zeros
  *
+ * and one call that uses the packed result at run time:
+ *
+ *   gptq_dequant_matmul      Y = X What^T with the packed codes unpacked and
+ *                            dequantized next to 16-bit activations
+ *
  * Sources (web pages describing the method):
  *   [OBQ]    "Part 2: Adaptive Rounding: Optimal Brain Quantizer (OBQ)"
  *   [GPTQ]   "Part 3: Adaptive Rounding: GPTQ"
@@ -157,6 +162,44 @@ gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, 
                                 int64_t block_size, uint32_t* qcodes, float* scales,
                                 int32_t* zeros, float* err_sq, int32_t write_dequant,
                                 void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gptq_dequant_matmul: Y = X What^T with What = s (q - z) taken from a packed
+ * layer (the codes, scales and zeros gptq_quantize_layer wrote).
+ *
+ * The weight-only runtime path: activations stay 16-bit and the packed
+ * weights are unpacked and dequantized on the fly, so far fewer weight bytes
+ * cross HBM ([SOQ] "What the original results established"; [SOQ-vi], closing
+ * paragraph: the artifact needs a packed INT4 kernel for the target device).
+ * Sums are taken in fp32 with the zero points folded out of the products:
+ * per group, s (sum_c (q_c + b) x_c - (z + b) sum_c x_c) for a constant b,
+ * every product exact in fp32; Y is rounded once to x_dtype.
+ *
+ *   X          [tokens x n] activations, leading dimension ldx >= n
+ *              (ldx % 8 == 0, X 16-byte aligned), x_dtype GPTQ_F16 or GPTQ_BF16.
+ *   qcodes     [m x ceil(n*bits/32)] uint32, the packed layout of
+ *              gptq_quantize_layer (16-byte aligned).
+ *   scales     [m x G] float32, zeros [m x G] int32 (G as for
+ *              gptq_quantize_layer).
+ *   bits, group_size: as passed to gptq_quantize_layer.  This version runs
+ *              bits == 4 with n % 32 == 0 and group_size <= 0 (per row) or a
+ *              multiple of 128; other valid combinations return
+ *              GPTQ_ERR_UNSUPPORTED.
+ *   Y          [tokens x m] out, leading dimension ldy >= m, type x_dtype.
+ *   workspace, ws_bytes: at least gptq_dequant_matmul_workspace_bytes(tokens,
+ *              m, n) bytes (0 for shapes that need no partial sums; then
+ *              workspace may be NULL).
+ * tokens == 0 is a no-op.  The result does not depend on the launch shape
+ * chosen for (tokens, m, n) except through the order of fp32 sums.
+ * Errors: m < 1, n < 1, tokens < 0, ldx < n, ldy < m, bits outside 2..8,
+ * x_dtype not 16-bit, NULL required pointers -> GPTQ_ERR_INVALID_ARG; the
+ * cases above -> GPTQ_ERR_UNSUPPORTED; short workspace -> GPTQ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t gptq_dequant_matmul_workspace_bytes(int64_t tokens, int64_t m, int64_t n);
+gptq_status gptq_dequant_matmul(const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx,
+                                const uint32_t* qcodes, const float* scales, const int32_t* zeros,
+                                int64_t m, int64_t n, int32_t bits, int64_t group_size, void* Y,
+                                int64_t ldy, void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,8 @@ Stages (same names as the C ABI):
     hessian_accumulate(H, X)                    H += 2 X^T X   (X token-major)
     prepare_hinv(H, damp)                       -> U, lambda, info
     quantize_layer(W, U, bits, group, block)    -> packed codes, scales, zeros
+and the runtime use of the packed layer:
+    dequant_matmul(X, qcodes, scales, zeros, bits, group, n)  -> Y = X What^T
 """
 from __future__ import annotations
 
@@ -61,6 +63,10 @@ def _load() -> ctypes.CDLL:
     L.gptq_quantize_workspace_bytes.restype = sz
     L.gptq_quantize_layer.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp, vp, i32, vp, sz, vp]
     L.gptq_quantize_layer.restype = i32
+    L.gptq_dequant_matmul_workspace_bytes.argtypes = [i64, i64, i64]
+    L.gptq_dequant_matmul_workspace_bytes.restype = sz
+    L.gptq_dequant_matmul.argtypes = [vp, i32, i64, i64, vp, vp, vp, i64, i64, i32, i64, vp, i64, vp, sz, vp]
+    L.gptq_dequant_matmul.restype = i32
     _lib = L
     return L
 
@@ -111,6 +117,10 @@ def prepare_workspace_bytes(n: int) -> int:
 
 def quantize_workspace_bytes(m: int, n: int, block_size: int = 128) -> int:
     return int(_load().gptq_quantize_workspace_bytes(int(m), int(n), int(block_size)))
+
+
+def dequant_matmul_workspace_bytes(tokens: int, m: int, n: int) -> int:
+    return int(_load().gptq_dequant_matmul_workspace_bytes(int(tokens), int(m), int(n)))
 
 
 # ----------------------------------------------------------------------------- the three stages
@@ -206,3 +216,37 @@ def gptq_layer(W: torch.Tensor, X: torch.Tensor, bits: int, group_size: int, blo
         raise GPTQError("gptq_prepare_hinv (damped Hessian not positive definite)", GPTQ_ERR_INVALID_ARG)
     res.update({"H": H, "U": U, "lambda": lam, "info": info})
     return res
+
+
+# ----------------------------------------------------------------------------- runtime use of the packed layer
+
+def dequant_matmul(X: torch.Tensor, qcodes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, bits: int,
+                   group_size: int, Y: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X What^T [tokens x m] in X's dtype (fp16 or bf16), with What = s (q - z)
+    unpacked from the packed layer (qcodes [m x words], scales / zeros [m x G]).
+    X is [tokens x n], unit column stride."""
+    _require(X.is_cuda and X.dim() == 2 and X.stride(1) == 1 and X.dtype in (torch.float16, torch.bfloat16),
+             "X must be a [tokens, n] fp16/bf16 CUDA tensor with unit column stride")
+    m = qcodes.shape[0]
+    T, n = X.shape
+    dev = X.device
+    _require(qcodes.device == dev and qcodes.dtype == torch.int32 and qcodes.is_contiguous()
+             and qcodes.shape == (m, packed_words(n, bits)), "qcodes must be contiguous int32 [m, words]")
+    G = n_groups(n, group_size)
+    _require(scales.shape == (m, G) and scales.dtype == torch.float32 and scales.is_contiguous()
+             and scales.device == dev, "scales must be contiguous float32 [m, G]")
+    _require(zeros.shape == (m, G) and zeros.dtype == torch.int32 and zeros.is_contiguous() and zeros.device == dev,
+             "zeros must be contiguous int32 [m, G]")
+    if Y is None:
+        Y = torch.empty((T, m), dtype=X.dtype, device=dev)
+    _require(Y.dtype == X.dtype and Y.dim() == 2 and Y.shape == (T, m) and Y.stride(1) == 1 and Y.device == dev,
+             "Y must be [tokens, m] in X's dtype with unit column stride")
+    need = dequant_matmul_workspace_bytes(T, m, n)
+    ws = workspace if workspace is not None else (_workspace(need, dev) if need > 0 else None)
+    st = _load().gptq_dequant_matmul(X.data_ptr(), _DT[X.dtype], T, max(X.stride(0), n), qcodes.data_ptr(),
+                                     scales.data_ptr(), zeros.data_ptr(), m, n, int(bits), int(group_size),
+                                     Y.data_ptr(), max(Y.stride(0), m), _ptr(ws), 0 if ws is None else ws.numel(),
+                                     _stream(dev))
+    _check("gptq_dequant_matmul", st)
+    return Y

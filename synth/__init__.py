@@ -43,7 +43,7 @@ import numpy as np
 
 CHUNK = 2048  # tokens per calibration sequence / generation chunk
 
-_TAGS = {"W": 1, "Xscale": 2, "Xz": 3, "Wout": 4, "L": 5}
+_TAGS = {"W": 1, "Xscale": 2, "Xz": 3, "Wout": 4, "L": 5, "P": 6, "A": 7}
 
 
 def _rng(seed: int, workload_id: int, tensor: str, chunk: int = 0, sub: int = 0) -> np.random.Generator:
@@ -273,3 +273,28 @@ def as_float64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f32(a).astype(np.float64)
     return a.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- packed layers at run time
+
+def packed_layer(m: int, n: int, bits: int, group: int, seed: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Codes q [m x n] uniform on 0..2^bits-1, zero points z [m x G] uniform on
+    the same range, scales s [m x G] log-normal around 0.01 (the size of
+    4-bit scales of weights with std 0.02): the structure of a quantized
+    layer's outputs, without running the quantizer."""
+    G = 1 if group <= 0 else (n + group - 1) // group
+    rng = _rng(seed, 0, f"P:{m}x{n}:{bits}:{group}")
+    q = rng.integers(0, 1 << bits, (m, n), dtype=np.int64)
+    z = rng.integers(0, 1 << bits, (m, G), dtype=np.int64).astype(np.int32)
+    s = (0.01 * rng.lognormal(0.0, 0.5, (m, G))).astype(np.float32)
+    return q, s, z
+
+
+def activations(tokens: int, n: int, dtype: str = "f16", seed: int = 0) -> np.ndarray:
+    """Token-major activations [tokens x n]: normal with log-normal per-channel
+    scales (a few channels much larger, as in transformer layers); fp16, or
+    bf16 as raw uint16."""
+    rng = _rng(seed, 0, f"A:{tokens}x{n}")
+    ch = rng.lognormal(0.0, 0.75, n)
+    X = (rng.standard_normal((tokens, n)) * ch).astype(np.float32)
+    return _cast(X, dtype)

@@ -101,3 +101,37 @@ def test_prepare_rejects():
     assert f(None, 16, 0.01, FAKE, FAKE, FAKE, FAKE, BIG, None) == pw.GPTQ_ERR_INVALID_ARG
     assert f(FAKE, 16, 0.01, FAKE, None, FAKE, FAKE, BIG, None) == pw.GPTQ_ERR_INVALID_ARG
     assert f(FAKE, 16, 0.01, FAKE, FAKE, FAKE, FAKE, 8, None) == pw.GPTQ_ERR_WORKSPACE
+
+
+def _dqmm(**kw):
+    a = dict(X=FAKE, dt=0, T=4, ldx=256, q=FAKE, s=FAKE, z=FAKE, m=64, n=256, bits=4, g=128, Y=FAKE, ldy=64, ws=FAKE,
+             wsb=BIG)
+    a.update(kw)
+    return _lib().gptq_dequant_matmul(a["X"], a["dt"], a["T"], a["ldx"], a["q"], a["s"], a["z"], a["m"], a["n"],
+                                      a["bits"], a["g"], a["Y"], a["ldy"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(m=0), dict(n=0), dict(T=-1), dict(ldx=128), dict(ldy=32), dict(dt=2), dict(dt=7), dict(bits=1),
+    dict(bits=9), dict(X=None), dict(q=None), dict(s=None), dict(z=None), dict(Y=None),
+])
+def test_dequant_matmul_rejects(kw):
+    assert _dqmm(**kw) == pw.GPTQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(bits=3), dict(bits=8), dict(g=64), dict(g=32), dict(n=240, ldx=240), dict(ldx=260),
+    dict(X=ctypes.c_void_p(0x1008)), dict(q=ctypes.c_void_p(0x1004)),
+])
+def test_dequant_matmul_unsupported(kw):
+    assert _dqmm(**kw) == pw.GPTQ_ERR_UNSUPPORTED
+
+
+def test_dequant_matmul_workspace():
+    assert pw.dequant_matmul_workspace_bytes(0, 64, 256) == 0
+    small = pw.dequant_matmul_workspace_bytes(1, 4096, 4096)      # decode shape: K is split
+    assert small >= 4096 * 4
+    assert pw.dequant_matmul_workspace_bytes(65536, 4096, 4096) == 0  # enough tiles: no partials
+    assert _dqmm(T=1, m=4096, n=4096, ldx=4096, ldy=4096, ws=None, wsb=0) == pw.GPTQ_ERR_WORKSPACE
+    assert _dqmm(T=1, m=4096, n=4096, ldx=4096, ldy=4096, wsb=small - 4) == pw.GPTQ_ERR_WORKSPACE
+    assert _dqmm(T=0, ws=None, wsb=0) == pw.GPTQ_OK  # no tokens: no-op
