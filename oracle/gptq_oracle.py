@@ -149,7 +149,8 @@ def check_schedule(n: int, group: int, block: int) -> None:
 
 # ----------------------------------------------------------------------------- the sweep
 
-def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group: int, block: Optional[int]) -> Dict[str, np.ndarray]:
+def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group: int, block: Optional[int],
+                  follow: Optional[Tuple[np.ndarray, np.ndarray]] = None, tie: float = 0.0) -> Dict[str, np.ndarray]:
     """GPTQ's column sweep over one layer ([GPTQ] "Algorithm GPTQ"; [SOQ-vi]
     "Lazy batch update").
 
@@ -168,9 +169,19 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group: int, block: Op
                                                  delta_rem = delta_p (H^-1)_{p,rem}/(H^-1)_pp,
                                                  read from row p of U)
 
+    follow = (q_other, z_other), tie = d compares against a sweep that rounds
+    in another precision: wherever this sweep's own pre-rounding value (V_p/s,
+    or -x_lo/s for a zero point) lies within d steps of a rounding boundary
+    and the other side's code or zero point is one of the two roundings next
+    to that boundary, this sweep takes the other side's choice (both are
+    correct roundings of a value the two precisions place on different sides
+    of the boundary; every later column of the row depends on which one was
+    taken).  Nothing else changes; "followed" counts the decisions taken over
+    that differ from this sweep's own.
+
     Returns q [m x n] int64, s and z [m x G], E [m x n], What [m x n],
     t [m x n] = V_p / s (pre-rounding value in steps) and tz [m x G] = -x_lo/s
-    (pre-rounding zero point), err_sq [m] = sum_p e_p^2."""
+    (pre-rounding zero point), err_sq [m] = sum_p e_p^2, followed (int)."""
     V = np.array(W, dtype=np.float64, copy=True)
     m, n = V.shape
     if U.shape != (n, n):
@@ -186,12 +197,31 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group: int, block: Op
     Z = np.zeros((m, G))
     TZ = np.zeros((m, G))
     maxq = maxq_of(bits)
+    if follow is not None:
+        fq = np.asarray(follow[0]).astype(np.int64)
+        fz = np.asarray(follow[1]).astype(np.int64)
+        if fq.shape != (m, n) or fz.shape != (m, G):
+            raise ValueError("follow codes must be m x n and zero points m x G")
+    followed = 0
+
+    def take_over(own: np.ndarray, pre: np.ndarray, below: np.ndarray, above: np.ndarray,
+                  other: np.ndarray) -> np.ndarray:
+        """own decision, or the other side's where pre is a near-tie and the
+        other side chose one of the two roundings next to it (below, above)."""
+        nonlocal followed
+        near = boundary_distance(pre) < tie
+        ok = near & ((other == below) | (other == above)) & (other != own)
+        followed += int(ok.sum())
+        return np.where(ok, other, own)
 
     def take_params(p: int, g_idx: int, vals: np.ndarray):
         s, z = quant_params(vals, bits)
-        S[:, g_idx], Z[:, g_idx] = s, z
         lo = np.minimum(vals.min(axis=1), 0.0)
         TZ[:, g_idx] = -lo / s
+        if follow is not None:
+            fl = np.floor(TZ[:, g_idx]).astype(np.int64)
+            z = take_over(z.astype(np.int64), TZ[:, g_idx], fl, fl + 1, fz[:, g_idx]).astype(np.float64)
+        S[:, g_idx], Z[:, g_idx] = s, z
 
     if group <= 0:
         take_params(0, 0, V)
@@ -204,6 +234,10 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group: int, block: Op
             s, z = S[:, gi], Z[:, gi]
             T[:, p] = V[:, p] / s
             q[:, p] = np.clip(np.rint(T[:, p]) + z, 0, maxq).astype(np.int64)
+            if follow is not None:
+                below = np.clip(np.floor(T[:, p]) + z, 0, maxq).astype(np.int64)
+                above = np.clip(np.floor(T[:, p]) + 1 + z, 0, maxq).astype(np.int64)
+                q[:, p] = take_over(q[:, p], T[:, p], below, above, fq[:, p])
             what = s * (q[:, p] - z)
             e = (V[:, p] - what) / U[p, p]
             E[:, p] = e
@@ -214,7 +248,7 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, bits: int, group: int, block: Op
     gidx = np.zeros(n, dtype=np.int64) if group <= 0 else np.arange(n) // group
     What = S[:, gidx] * (q - Z[:, gidx])
     return {"q": q, "s": S, "z": Z, "E": E, "What": What, "t": T, "tz": TZ,
-            "err_sq": np.sum(E * E, axis=1)}
+            "err_sq": np.sum(E * E, axis=1), "followed": followed}
 
 
 def obs_step(v_row: np.ndarray, U: np.ndarray, p: int, what_p: float) -> np.ndarray:

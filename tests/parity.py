@@ -2,13 +2,15 @@
 
 Tolerances:
   * H: ||H_gpu - H_oracle||_F / ||H_oracle||_F <= 1e-5.
-  * Codes: bit-exact, except that a row's first mismatch must sit where the
-    oracle's pre-rounding value (v/s, or the zero point -x_lo/s of that
-    column's group) lies within 1e-4 of a rounding boundary; after such a
-    near-tie a row may legitimately diverge (every later value in the row
-    depends on it), and overall >= 99.9 % of codes must be identical.
-  * Scales: relative 1e-5 on every group that starts at or before the row's
-    first code mismatch.
+  * Codes and zero points: bit-exact along one history.  Where the oracle's
+    pre-rounding value (v/s, or the zero point -x_lo/s of a group) lies
+    within 1e-4 steps of a rounding boundary, the fp32 kernel and the fp64
+    oracle may round to the two sides of it; both are correct roundings, and
+    every later value of that row depends on which one was taken.  So the
+    oracle's sweep is run again on the same inputs taking the GPU's choice at
+    such near-ties (and nowhere else); every code and zero point must then be
+    identical.  The first run's identical fraction is reported, not gated.
+  * Scales: relative 1e-5 on every group of the followed run.
   * Layer loss ||(W - What) X||^2 (one fp64 evaluator for both sides): within
     1e-3 relative.
 """
@@ -23,7 +25,6 @@ import oracle as O
 
 H_RTOL = 1e-5
 TIE = 1e-4
-SAME_FRAC = 0.999
 SCALE_RTOL = 1e-5
 LOSS_RTOL = 1e-3
 
@@ -72,9 +73,9 @@ def compare_codes(q_gpu: np.ndarray, s_gpu: np.ndarray, z_gpu: np.ndarray, ref: 
     }
 
 
-def assert_codes(rep: Dict[str, float], label: str = "") -> None:
+def assert_codes(rep: Dict[str, float], label: str = "", min_same: float = 0.0) -> None:
     assert not rep["unexcused"], f"{label}: first mismatch not at a near-tie: {rep['unexcused'][:5]}"
-    assert rep["same_frac"] >= SAME_FRAC, f"{label}: only {rep['same_frac']:.5f} of codes identical"
+    assert rep["same_frac"] >= min_same, f"{label}: only {rep['same_frac']:.5f} of codes identical"
     assert rep["scale_rel_max"] <= SCALE_RTOL, f"{label}: scale rel err {rep['scale_rel_max']:.3e}"
 
 
@@ -86,3 +87,23 @@ def loss_rel(W: np.ndarray, H: np.ndarray, q_gpu, s_gpu, z_gpu, ref, group) -> f
         scale = float(np.sum((np.asarray(W, np.float64) @ H) * W)) or 1.0
         return abs(l_gpu) / scale
     return abs(l_gpu - l_ora) / l_ora
+
+
+def follow_check(q_gpu: np.ndarray, s_gpu: np.ndarray, z_gpu: np.ndarray, W: np.ndarray, U: np.ndarray,
+                 bits: int, group: int, block, label: str = "") -> Dict[str, np.ndarray]:
+    """The oracle's sweep on the same W and U, taking the GPU's rounding at
+    near-ties only (within TIE steps of a boundary); every code and zero point
+    must then match and every scale agree to SCALE_RTOL.  Returns that run."""
+    ref = O.gptq_quantize(W, U, bits, group, block, follow=(q_gpu, z_gpu), tie=TIE)
+    bad = np.argwhere(q_gpu != ref["q"])
+    zbad = np.argwhere(z_gpu.astype(np.int64) != ref["z"].astype(np.int64))
+    srel = float(np.max(np.abs(s_gpu.astype(np.float64) - ref["s"]) / np.abs(ref["s"]))) if ref["s"].size else 0.0
+    say(f"  {label} followed {ref['followed']} near-tie decisions; codes differing after that {len(bad)}, "
+        f"zero points {len(zbad)}, scale rel {srel:.2e}")
+    if len(bad):
+        r, c = bad[0]
+        raise AssertionError(f"{label}: {len(bad)} codes differ away from near-ties; first at row {r} col {c}: "
+                             f"gpu {q_gpu[r, c]} oracle {ref['q'][r, c]} (t = {ref['t'][r, c]:.6f})")
+    assert not len(zbad), f"{label}: {len(zbad)} zero points differ away from near-ties, first {zbad[0]}"
+    assert srel <= SCALE_RTOL, f"{label}: scale rel err {srel:.3e}"
+    return ref

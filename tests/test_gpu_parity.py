@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 import synth
-from parity import (H_RTOL, LOSS_RTOL, assert_codes, compare_codes, h_rel_err, loss_rel, say)
+from parity import (H_RTOL, LOSS_RTOL, assert_codes, compare_codes, follow_check, h_rel_err, loss_rel, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,6 +167,7 @@ def test_sweep_parity(m, n, bits, group, block, wdt):
     rep = compare_codes(q, s, z, ref, group)
     say(f"  same {rep['same_frac']:.6f} diverged rows {rep['rows_diverged']} scale rel {rep['scale_rel_max']:.2e}")
     assert_codes(rep, "sweep")
+    fr = follow_check(q, s, z, Wd, U32.astype(np.float64), bits, group, block, "sweep")
     lr = loss_rel(Wd, H, q, s, z, ref, group)
     assert lr <= LOSS_RTOL, f"loss rel {lr:.3e}"
     # the dequantized weights written back equal s (q - z) rounded to W's dtype
@@ -178,9 +179,8 @@ def test_sweep_parity(m, n, bits, group, block, wdt):
     # energy uniform rounding errors would carry, sum_p s^2 / (12 U_pp^2)
     gidx = np.zeros(n, dtype=np.int64) if group <= 0 else np.arange(n) // group
     expect = np.sum(ref["s"][:, gidx] ** 2 / (12.0 * np.diag(U32).astype(np.float64)[None, :] ** 2), axis=1)
-    rows_ok = ~(q != ref["q"]).any(axis=1)
-    diff = np.abs(res["err_sq"].cpu().numpy() - ref["err_sq"])
-    assert np.all((diff <= 1e-3 * ref["err_sq"] + 1e-4 * expect)[rows_ok])
+    diff = np.abs(res["err_sq"].cpu().numpy() - fr["err_sq"])
+    assert np.all(diff <= 1e-3 * fr["err_sq"] + 1e-4 * expect)
 
 
 def test_sweep_block_invariance_on_gpu():
@@ -194,8 +194,10 @@ def test_sweep_block_invariance_on_gpu():
     for B in (1, 32, 128):
         res = pw.quantize_layer(to_dev(W, "f16"), U, bits, group, B, write_dequant=False)
         torch.cuda.synchronize()
-        rep = compare_codes(unpack(res, n, bits), res["scales"].cpu().numpy(), res["zeros"].cpu().numpy(), ref, group)
-        assert_codes(rep, f"B={B}")
+        q, s, z = unpack(res, n, bits), res["scales"].cpu().numpy(), res["zeros"].cpu().numpy()
+        assert_codes(compare_codes(q, s, z, ref, group), f"B={B}")
+        follow_check(q, s, z, W.astype(np.float64), U_ref.astype(np.float32).astype(np.float64), bits, group, None,
+                     f"B={B}")
 
 
 def test_sweep_diagonal_hessian_is_rtn():
@@ -234,6 +236,7 @@ def test_tiny_workload_end_to_end():
     rep = compare_codes(q, s, z, ref, job.group)
     say(f"[tiny] same {rep['same_frac']:.6f} diverged rows {rep['rows_diverged']}")
     assert_codes(rep, "tiny")
+    follow_check(q, s, z, W.astype(np.float64), ref["U"], job.bits, job.group, job.block, "tiny")
     assert loss_rel(W.astype(np.float64), ref["H"], q, s, z, ref, job.group) <= LOSS_RTOL
     # GPTQ beats round-to-nearest on this layer
     r = O.rtn(W.astype(np.float64), job.bits, job.group)
@@ -259,4 +262,5 @@ def test_reduced_workload_end_to_end(recipe):
     rep = compare_codes(q, s, z, ref, group)
     say(f"[{recipe}] same {rep['same_frac']:.6f} diverged rows {rep['rows_diverged']}")
     assert_codes(rep, recipe)
+    follow_check(q, s, z, W.astype(np.float64), ref["U"], bits, group, 128, recipe)
     assert loss_rel(W.astype(np.float64), ref["H"], q, s, z, ref, group) <= LOSS_RTOL

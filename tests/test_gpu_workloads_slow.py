@@ -41,7 +41,7 @@ def test_attention_projection_end_to_end_oracle():
     import oracle as O
     import post_weight_quantization_10_amd as pw
     import synth
-    from parity import LOSS_RTOL, assert_codes, compare_codes, say
+    from parity import LOSS_RTOL, assert_codes, compare_codes, follow_check, say
     wl = synth.workloads()["attn"]
     job = wl.jobs[0]
     W = synth.stacked_weight(job, wl.seed, wl.wid)
@@ -62,6 +62,7 @@ def test_attention_projection_end_to_end_oracle():
     rep = compare_codes(q, s, z, ref, job.group)
     say(f"[attn end-to-end] identical {rep['same_frac']:.6f} diverged rows {rep['rows_diverged']}")
     assert_codes(rep, "attn end-to-end")
+    follow_check(q, s, z, W[rows].astype(np.float64), U, job.bits, job.group, job.block, "attn end-to-end")
     Wr = W[rows].astype(np.float64)
     l_gpu = O.layer_loss(Wr, O.dequant_from(q, s, z, job.group), H)
     l_ref = O.layer_loss(Wr, ref["What"], H)

@@ -383,3 +383,67 @@ def test_dequant_matmul_matches_rtn_layer():
         r = O.rtn(W, bits, group)
         Y = O.dequant_matmul(X, O.pack_codes(r["q"], bits), r["s"], r["z"], bits, group, n)
         assert np.allclose(Y, X @ r["What"].T, rtol=1e-13, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- following another sweep at near-ties
+
+def test_follow_own_result_changes_nothing():
+    """Following the sweep's own codes and zero points is the plain sweep."""
+    W, X = _rand_layer(10, 96, 500, 31)
+    _, _, _, U = _prep(X)
+    a = O.gptq_quantize(W, U, 3, 32, block=32)
+    b = O.gptq_quantize(W, U, 3, 32, block=32, follow=(a["q"], a["z"]), tie=0.5)
+    assert b["followed"] == 0
+    for k in ("q", "s", "z", "E", "What"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_follow_takes_only_adjacent_roundings_at_near_ties():
+    """Round-to-nearest layer (diagonal U), one value 1e-6 steps past the
+    boundary 2.5: the other side's 'below' rounding is taken within the tie
+    band, not outside it, and never a non-adjacent code or a code away from
+    a tie.  Row [-1, 2, x], 4 bits: s = 3/15, z = rint(1/s) = 5
+    ([SOQ-vi] asymmetric min/max grid)."""
+    s = 3.0 / 15.0
+    W = np.array([[-1.0, 2.0, s * (2.5 + 1e-6)]])
+    U = np.eye(3)
+    own = O.gptq_quantize(W, U, 4, 0, None)
+    assert own["z"][0, 0] == 5 and list(own["q"][0]) == [0, 15, 8]
+    z = own["z"].astype(np.int64)
+    below = np.array([[0, 15, 7]])
+    r = O.gptq_quantize(W, U, 4, 0, None, follow=(below, z), tie=1e-4)
+    assert r["followed"] == 1 and r["q"][0, 2] == 7
+    assert r["What"][0, 2] == pytest.approx(s * 2)
+    assert O.gptq_quantize(W, U, 4, 0, None, follow=(below, z), tie=1e-7)["followed"] == 0
+    for other in ([[0, 15, 9]], [[1, 15, 8]], [[0, 14, 8]]):   # not adjacent / not at a tie
+        r = O.gptq_quantize(W, U, 4, 0, None, follow=(np.array(other), z), tie=1e-4)
+        assert r["followed"] == 0 and list(r["q"][0]) == [0, 15, 8]
+    # zero point at a near-tie: -lo/s = 5 + 0.5 + 1e-6 -> own 6, the other side's 5 is taken
+    lo = -(5.5 + 1e-6) * s
+    W2 = np.array([[lo, lo + 15 * s, 0.0]])
+    own2 = O.gptq_quantize(W2, U, 4, 0, None)
+    assert own2["z"][0, 0] == 6
+    r2 = O.gptq_quantize(W2, U, 4, 0, None, follow=(own2["q"], np.array([[5]])), tie=1e-4)
+    assert r2["z"][0, 0] == 5 and r2["followed"] >= 1
+    assert O.gptq_quantize(W2, U, 4, 0, None, follow=(own2["q"], np.array([[4]])), tie=1e-4)["z"][0, 0] == 6
+
+
+def test_follow_flip_is_compensated():
+    """A decision taken over at column p changes that code only, and the
+    later columns are compensated for it: W - What = E U still holds
+    (the identity of [GPTQ] 'Observation 3' with H_d^-1 = U^T U), codes
+    before p are unchanged, and the sweep stays a valid quantizer run."""
+    W, X = _rand_layer(6, 64, 400, 32)
+    _, _, _, U = _prep(X)
+    a = O.gptq_quantize(W, U, 4, 0, None)
+    r, p = 2, 17
+    t = a["t"][r, p]
+    other = a["q"].copy()
+    # the rounding on the other side of the nearest boundary
+    other[r, p] = int(np.clip(np.floor(t) + a["z"][r, 0] + (1 if np.rint(t) == np.floor(t) else 0), 0, 15))
+    b = O.gptq_quantize(W, U, 4, 0, None, follow=(other, a["z"]), tie=1.0)   # every boundary counts as near
+    assert b["q"][r, p] == other[r, p] != a["q"][r, p]
+    np.testing.assert_array_equal(b["q"][r, :p], a["q"][r, :p])
+    np.testing.assert_array_equal(np.delete(b["q"], r, axis=0), np.delete(a["q"], r, axis=0))
+    np.testing.assert_allclose(W - b["What"], b["E"] @ U, atol=1e-13)
+    assert not np.allclose(b["E"][r, p + 1:], a["E"][r, p + 1:])

@@ -20,7 +20,7 @@ import torch
 
 import oracle as O
 import synth
-from parity import H_RTOL, LOSS_RTOL, assert_codes, compare_codes, say
+from parity import H_RTOL, LOSS_RTOL, assert_codes, compare_codes, follow_check, say
 
 DEV = "cuda:0"
 
@@ -111,6 +111,7 @@ def run_job(workload: str, job_index: int, sample_rows: int = 128, sample_cols: 
     say(f"  codes identical {rep['same_frac']:.6f}, rows diverged {rep['rows_diverged']}/{len(rows)}, "
         f"scale rel {rep['scale_rel_max']:.2e}")
     assert_codes(rep, workload)
+    follow_check(q, s, z, Wr, Ug, job.bits, job.group, job.block, workload)
     Hs = Hd.copy()
     Hs[np.diag_indices(n)] -= lam_ref
     Wh = O.dequant_from(q, s, z, job.group)
