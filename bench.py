@@ -126,7 +126,7 @@ def bench_w4a16(args):
         "dtype": "fp16 x u4 -> fp32 sums", "data": "synthetic",
         "config": {"workload": f"w4a16 decode: W {m}x{n} 4-bit g{group} packed, X {T}x{n} fp16, Y {T}x{m} fp16",
                    "tokens": T, "m": m, "n": n, "bits": 4, "group": group, "parallelism": "single GPU"},
-        "roofline": {"kernel": "gptq_dequant_matmul: dqmm4_stream_kernel + dqmm_reduce_kernel", "bound": "hbm",
+        "roofline": {"kernel": "gptq_dequant_matmul: dqmm4_task_kernel + dqmm_reduce_kernel", "bound": "hbm",
                      "achieved": round(gbs_ev, 1), "peak": PEAK_HBM, "unit": "GB/s",
                      "frac": round(gbs_ev / PEAK_HBM, 4), "traffic": None},
     }

@@ -7,10 +7,13 @@
 // target device).
 //
 // How (4-bit codes, fp16 or bf16 activations):
-//   * A workgroup owns 64 rows of W (16 per wave) and up to 64 tokens, and
-//     walks 512-column slices of K.  A wave's codes for a slice (16 rows x
-//     256 bytes) are requested first, 16 bytes per lane; the slice of X goes
-//     to LDS meanwhile.
+//   * Up to 16 tokens (decode): a workgroup takes 64 rows of W over one K
+//     range of 512 or 1024 columns; each wave requests all of its codes at
+//     once while the workgroup stages X and the group parameters in LDS.
+//     More tokens: a workgroup owns 64 rows and up to 64 tokens and walks
+//     512-column slices of K; a wave's codes for a slice (16 rows x 256
+//     bytes) are requested first, 16 bytes per lane; the slice of X goes to
+//     LDS meanwhile.
 //   * Zero points are folded out of the products.  For a 32-bit word of eight
 //     codes, ((w >> 4i) & 0x000F000F) | 0x64006400 is the fp16 pair
 //     (1024 + q_i, 1024 + q_{i+4}), and one packed fp16 subtraction of 1024
@@ -24,9 +27,10 @@
 //     the piece's 16 (one 16-byte load), one word per MFMA step; X is staged
 //     in LDS with the same pair order inside each eight-column word, so the
 //     two operands agree.
-//   * When rows x token groups alone would leave the GPU under-filled, K is
-//     cut into strided sets of slices whose fp32 partial outputs a second
-//     kernel sums in a fixed order (deterministic) and converts to X's dtype.
+//   * When K is cut (always for decode; for more tokens when rows x token
+//     groups alone would leave the GPU under-filled), the fp32 partial
+//     outputs of the K sets are summed by a second kernel in a fixed order
+//     (deterministic) and converted to X's dtype.
 #include <algorithm>
 
 #include "common.hpp"
@@ -203,15 +207,6 @@ __global__ __launch_bounds__(256, 2) void dqmm4_kernel(DqArgs a) {
   }
 }
 
-// Decode-sized batches (tokens <= 16): every wave streams its own task, 16
-// rows over a range of K, with the codes of four 256-column chunks in flight
-// and X read straight from L2 (it is small and shared by every wave) two
-// chunks ahead; no LDS, no barrier.  X's eight columns of a word are put in
-// the pair order of the unpacked codes with four byte permutes.  fp16: the
-// zero point leaves with the bias, (1024 + q) - (1024 + z) = q - z exactly,
-// so the sums carry (q - z) x and Y += s acc per group.  bf16 (no packed
-// bf16 subtract): 128 + q stays, a second MFMA with all-ones weights gives
-// sum(x) for the same columns, and Y += s (acc - (128 + z) sum(x)).
 // fp16 pairs a - b (exact here: both are 1024 + a small integer); bf16: a
 template <int DT>
 __device__ __forceinline__ uint32_t hsub(uint32_t a, uint32_t b) {
@@ -220,174 +215,153 @@ __device__ __forceinline__ uint32_t hsub(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, d);
 }
 
-constexpr int DS_CH = 256;      // columns per chunk (two 128-column pieces)
-constexpr int DS_AHEAD = 4;     // chunks of codes in flight per wave
-constexpr int DS_XAHEAD = 2;    // chunks of X in flight per wave
-constexpr int DS_WAVES = 3072;  // waves that keep HBM busy (12 per CU)
-
-// G128: groups of exactly one 128-column piece (the usual g128), so every
-// piece opens and closes its group and no bookkeeping is needed.  FULL: n is
-// a multiple of 256, so no chunk runs past the end of a row and X needs no
-// masking.
-template <int DT, bool G128, bool FULL>
-__global__ __launch_bounds__(256) void dqmm4_stream_kernel(DqArgs a, int64_t KR) {
+// Decode-sized batches (tokens <= 16), one task per workgroup: 64 rows of W
+// (16 per wave) over a range of KR columns.  Each wave asks for all of its
+// codes at once (KR / 128 loads of 16 bytes per lane: 8 KiB per wave at
+// KR = 1024), so a CU keeps tens of KiB of codes in flight with no loop and
+// no wait inside a wave; meanwhile the workgroup stages the range's slice of
+// X (in the pair order of the unpacked codes) and the scale and zero point
+// of each (row, piece) in LDS.  Lane
+// (g4, l16) holds words 4 g4 .. 4 g4 + 3 of row l16 in every 128-column
+// piece, one word per MFMA step, and reads the same columns of token l16 of
+// the staged X.  fp16: the zero point leaves with the bias,
+// (1024 + q) - (1024 + z) = q - z exactly, so the sums carry (q - z) x and
+// Y += s acc per group.  bf16 (no packed bf16 subtract): 128 + q stays, a
+// second MFMA with all-ones weights gives sum(x) for the same columns, and
+// Y += s (acc - (128 + z) sum(x)).  Tokens past T read whatever the staged
+// rows hold: they only reach output columns that are never written.  Columns
+// past n are staged as zeros, so the codes there (another row's, or zeros
+// past the buffer) add nothing.
+template <int DT, bool G128, int KR, int TT>
+__global__ __launch_bounds__(256) void dqmm4_task_kernel(DqArgs a) {
+  constexpr int NP = KR / 128;     // pieces per range
+  constexpr int XP = KR * 2 + 16;  // LDS bytes per staged token row (rows 4 banks apart)
+  constexpr int NXW = TT * KR / 8 / 256;  // staged 8-column words per thread (upper bound)
+  static_assert(NP % 4 == 0 && NXW >= 1, "range of whole groups of four pieces");
+  __shared__ __attribute__((aligned(16))) char xs[TT * XP];
+  __shared__ float ps[64][NP + 1];
+  __shared__ int pz[64][NP + 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
-  const int64_t task = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t RB = cdiv(a.m, 16);
-  if (task >= RB * a.KS) return;  // the whole wave: there is no barrier in this kernel
-  const int64_t rb = task / a.KS, ks = task % a.KS;
-  const int64_t kb = ks * KR, ke = min<int64_t>(a.n, kb + KR);
-  const int nch = (int)cdiv(ke - kb, DS_CH);
+  // consecutive workgroups take consecutive row blocks of one K range
+  const int64_t nrb = cdiv(a.m, 64);
+  const int64_t rb = blockIdx.x % nrb, ks = blockIdx.x / nrb;
+  const int64_t kb = ks * KR;
+  const int64_t r0 = rb * 64;
+  const int64_t rw = r0 + 16 * wave;
   constexpr uint32_t MAGIC = DT == 0 ? 0x64006400u : 0x43004300u;
 
-  const int64_t rows_here = min<int64_t>(16, a.m - 16 * rb);
-  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.Q + 16 * rb * a.W), 0, (int)(rows_here * a.W * 4), 0x00020000);
-  // this lane's words of chunk j: kb/8 + 32 j + 16 p + 4 g4 .. +3 of row l16
-  const uint32_t qoff = ((uint32_t)l16 * (uint32_t)a.W + (uint32_t)(kb / 8) + 4u * g4) * 4u;
-  // X through a buffer over its T rows: lanes of tokens past T read zeros
-  const __amdgpu_buffer_rsrc_t xrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.X, 0, (int)(a.T * a.ldx * 2), 0x00020000);
-  const uint32_t xoff = (uint32_t)(l16 * a.ldx + kb + 32 * g4) * 2u;
-  const int64_t rA = min<int64_t>(16 * rb + l16, a.m - 1);  // row of this lane's codes
-  const int64_t rO = 16 * rb + 4 * g4;                      // first of this lane's four output rows
-  // scales and zero points through buffers with 32-bit offsets (m G < 2^29)
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)a.S, 0, (int)(a.m * a.G * 4), 0x00020000);
-  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.Z, 0, (int)(a.m * a.G * 4), 0x00020000);
-  const uint32_t zoffA = (uint32_t)(rA * a.G) * 4u;
-  uint32_t poff[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) poff[v] = (uint32_t)(min<int64_t>(rO + v, a.m - 1) * a.G) * 4u;
-  // 128-column pieces, counted from the wave's first one (kb is a multiple
-  // of 256); a group is gp whole pieces (gp = 0: the whole row).  32-bit
-  // bookkeeping only: piece P of the range is global piece pb + P.
+  // group of piece P of the range (clamped: pieces past n add nothing)
   const uint32_t pb = (uint32_t)(kb >> 7);
-  const int npc = (int)cdiv(ke - kb, 128);
   const uint32_t gp = a.group > 0 ? (uint32_t)(a.group >> 7) : 0u;
   const uint32_t gmax = (uint32_t)(a.G - 1);
   auto group_of = [&](int P) -> uint32_t {
-    if (G128) return pb + (uint32_t)P;
-    if (gp == 0) return 0u;
-    const uint32_t g = gp == 1 ? pb + (uint32_t)P : (pb + (uint32_t)P) / gp;
+    uint32_t g;
+    if (G128) g = pb + (uint32_t)P;
+    else if (gp == 0) g = 0u;
+    else g = gp == 1 ? pb + (uint32_t)P : (pb + (uint32_t)P) / gp;
     return g < gmax ? g : gmax;
   };
-  auto starts_group = [&](int P) { return P == 0 || (gp != 0 && (gp == 1 || (pb + (uint32_t)P) % gp == 0)); };
-  auto ends_group = [&](int P) {
-    return P == npc - 1 || (gp != 0 && (gp == 1 || (pb + (uint32_t)P + 1) % gp == 0));
-  };
 
-  u32x4 qb[DS_AHEAD][2];
-  u32x4 xb[DS_XAHEAD][8];
-  // Every load below is issued unconditionally: past the range they read
-  // other rows' values, or zeros past the buffer, and are never used.
-  auto load_q = [&](int slot, int j) {
+  // 1. parameters: thread e = tid + 256 u takes (row e / NP, piece e % NP)
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)a.S, 0, (int)(a.m * a.G * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.Z, 0, (int)(a.m * a.G * 4), 0x00020000);
+  uint32_t sv[NP / 4], zv[NP / 4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      qb[slot][p] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 128u * j + 64u * p, 0, 0);
-  };
-  // Columns past the range (the range's last chunk only): zero, so that
-  // whatever the codes there are, they add nothing.
-  const int xlim = (int)(ke - kb) - 32 * g4;
-  const int nfull = (int)((ke - kb) / DS_CH);  // chunks entirely inside the range
-  auto load_x = [&](int slot, int j) {
+  for (int u = 0; u < NP / 4; ++u) {
+    const int e = tid + 256 * u;
+    const int64_t r = min<int64_t>(r0 + e / NP, a.m - 1);
+    const uint32_t off = (uint32_t)(r * a.G + group_of(e % NP)) * 4u;
+    sv[u] = __builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0);
+    zv[u] = __builtin_amdgcn_raw_buffer_load_b32(zrs, off, 0, 0);
+  }
+  // 2. X: the range's columns of tokens < min(T, TT), one 8-column word per
+  // load, zero past n
+  const int tst = (int)min<int64_t>(a.T, TT);
+  const int nw = (int)((min<int64_t>(a.n, kb + KR) - kb) >> 3);  // words of the range inside the row
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.X, 0, (int)(a.T * a.ldx * 2), 0x00020000);
+  u32x4 xv[NXW];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {  // piece e / 4, word e % 4
-      const int c = DS_CH * j + 128 * (e >> 2) + 8 * (e & 3);
-      xb[slot][e] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + 2u * (uint32_t)c, 0, 0);
-    }
-    if (!FULL && j >= nfull) {  // uniform
+  for (int u = 0; u < NXW; ++u) {
+    const int e = tid + 256 * u;
+    const int t = e / (KR / 8), w = e % (KR / 8);
+    const bool ok = t < tst && w < nw;
+    xv[u] = __builtin_amdgcn_raw_buffer_load_b128(xrs, ok ? (uint32_t)(t * a.ldx + kb + 8 * w) * 2u : 0x80000000u, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the codes go out after X and the parameters
+  // 3. this wave's codes: piece P, words 4 g4 .. 4 g4 + 3 of row rw + l16
+  const int64_t rows_here = max<int64_t>(0, min<int64_t>(16, a.m - rw));
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.Q + min<int64_t>(rw, a.m - 1) * a.W), 0, (int)(rows_here * a.W * 4), 0x00020000);
+  const uint32_t qoff = ((uint32_t)l16 * (uint32_t)a.W + (uint32_t)(kb / 8) + 4u * g4) * 4u;
+  u32x4 qv[NP];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = DS_CH * j + 128 * (e >> 2) + 8 * (e & 3);
-        if (c >= xlim) xb[slot][e] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  // group parameters of the two pieces of a chunk, two chunks ahead: the zero
-  // point of this lane's code row; scales (and bf16 zero points) of its four
-  // output rows
-  int zA[2][2];
-  float sO[2][2][4];
-  int zO[2][2][4];
-  auto load_par = [&](int slot, int j) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint32_t gi4 = 4u * group_of(2 * j + p);
-      if (DT == 0) zA[slot][p] = __builtin_amdgcn_raw_buffer_load_b32(zrs, zoffA + gi4, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        sO[slot][p][v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, poff[v] + gi4, 0, 0));
-        if (DT != 0) zO[slot][p][v] = __builtin_amdgcn_raw_buffer_load_b32(zrs, poff[v] + gi4, 0, 0);
-      }
-    }
-  };
-#pragma unroll
-  for (int d = 0; d < DS_AHEAD; ++d) load_q(d, d);
-#pragma unroll
-  for (int d = 0; d < DS_XAHEAD; ++d) load_x(d, d);
-  load_par(0, 0);
-  load_par(1, 1);
+  for (int P = 0; P < NP; ++P) qv[P] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 64u * P, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
 
+  // 4. stage parameters and X (X's eight columns in pair order)
+#pragma unroll
+  for (int u = 0; u < NP / 4; ++u) {
+    const int e = tid + 256 * u;
+    ps[e / NP][e % NP] = __builtin_bit_cast(float, sv[u]);
+    pz[e / NP][e % NP] = (int)zv[u];
+  }
+#pragma unroll
+  for (int u = 0; u < NXW; ++u) {
+    const int e = tid + 256 * u;
+    const int t = e / (KR / 8), w = e % (KR / 8);
+    if (t < tst) {
+      const u32x4 x = xv[u];
+      const u32x4 pr = {__builtin_amdgcn_perm(x.z, x.x, 0x05040100u), __builtin_amdgcn_perm(x.z, x.x, 0x07060302u),
+                        __builtin_amdgcn_perm(x.w, x.y, 0x05040100u), __builtin_amdgcn_perm(x.w, x.y, 0x07060302u)};
+      *(u32x4*)(xs + t * XP + 16 * w) = pr;
+    }
+  }
+  __syncthreads();
+
+  // 5. products
+  const char* xrow = xs + min(l16, TT - 1) * XP + 64 * g4;
+  const int prA = 16 * wave + l16;     // LDS row of this lane's codes
+  const int prO = 16 * wave + 4 * g4;  // LDS rows of this lane's four outputs
   f32x4 tot = {0.f, 0.f, 0.f, 0.f}, acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
-  for (int j0 = 0; j0 < nch; j0 += DS_AHEAD) {
 #pragma unroll
-    for (int d = 0; d < DS_AHEAD; ++d) {
-      const int j = j0 + d;
-      if (j >= nch) break;
-      const int xs = d % DS_XAHEAD;  // DS_AHEAD is a multiple of DS_XAHEAD
+  for (int P = 0; P < NP; ++P) {
+    uint32_t zb = 0;  // fp16 (1024 + z, 1024 + z) of this lane's row
+    if (DT == 0) {
+      const uint32_t z = (uint32_t)pz[prA][P];
+      zb = MAGIC | z | (z << 16);
+    }
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int P = 2 * j + p;
-        if (!FULL && P >= npc) break;
-        const bool first = G128 || starts_group(P);
-        const bool last = G128 || ends_group(P);
-        if (first) {
-          acc = f32x4{0.f, 0.f, 0.f, 0.f};
-          acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        const int ps = d & 1;  // parameter slot of chunk j
-        uint32_t zb = 0;       // fp16 (1024 + z, 1024 + z) of this lane's row
-        if (DT == 0) {
-          const uint32_t z = (uint32_t)zA[ps][p];
-          zb = MAGIC | z | (z << 16);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = qb[d][p][i];
-          // (no bit cast of a vector element below: it would read element 0)
-          const uint32_t h0 = hsub<DT>((w & 0x000F000Fu) | MAGIC, zb);
-          const uint32_t h1 = hsub<DT>(((w >> 4) & 0x000F000Fu) | MAGIC, zb);
-          const uint32_t h2 = hsub<DT>(((w >> 8) & 0x000F000Fu) | MAGIC, zb);
-          const uint32_t h3 = hsub<DT>(((w >> 12) & 0x000F000Fu) | MAGIC, zb);
-          const u32x4 ai = {h0, h1, h2, h3};
-          const u32x4 xv = xb[xs][4 * p + i];
-          const u32x4 bi = {__builtin_amdgcn_perm(xv.z, xv.x, 0x05040100u), __builtin_amdgcn_perm(xv.z, xv.x, 0x07060302u),
-                            __builtin_amdgcn_perm(xv.w, xv.y, 0x05040100u), __builtin_amdgcn_perm(xv.w, xv.y, 0x07060302u)};
-          if (DT == 0) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ai), __builtin_bit_cast(half8_t, bi),
-                                                         acc, 0, 0, 0);
-          } else {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, ai),
-                                                          __builtin_bit_cast(bf168_t, bi), acc, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, ones),
-                                                           __builtin_bit_cast(bf168_t, bi), acc1, 0, 0, 0);
-          }
-        }
-        if (last) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float sc = sO[ps][p][v];
-            if (DT == 0) tot[v] = fmaf(sc, acc[v], tot[v]);
-            else tot[v] = fmaf(sc, fmaf(-(128.f + (float)zO[ps][p][v]), acc1[v], acc[v]), tot[v]);
-          }
-        }
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = qv[P][i];
+      const uint32_t h0 = hsub<DT>((w & 0x000F000Fu) | MAGIC, zb);
+      const uint32_t h1 = hsub<DT>(((w >> 4) & 0x000F000Fu) | MAGIC, zb);
+      const uint32_t h2 = hsub<DT>(((w >> 8) & 0x000F000Fu) | MAGIC, zb);
+      const uint32_t h3 = hsub<DT>(((w >> 12) & 0x000F000Fu) | MAGIC, zb);
+      const u32x4 ai = {h0, h1, h2, h3};
+      const u32x4 bi = *(const u32x4*)(xrow + 256 * P + 16 * i);
+      if (DT == 0) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ai), __builtin_bit_cast(half8_t, bi),
+                                                     acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, ai), __builtin_bit_cast(bf168_t, bi),
+                                                      acc, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, ones),
+                                                       __builtin_bit_cast(bf168_t, bi), acc1, 0, 0, 0);
       }
-      load_q(d, j + DS_AHEAD);
-      load_x(xs, j + DS_XAHEAD);
-      load_par(d & 1, j + 2);
+    }
+    if (G128 || P == NP - 1 || group_of(P + 1) != group_of(P)) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float sc = ps[prO + v][P];
+        if (DT == 0) tot[v] = fmaf(sc, acc[v], tot[v]);
+        else tot[v] = fmaf(sc, fmaf(-(128.f + (float)pz[prO + v][P]), acc1[v], acc[v]), tot[v]);
+      }
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 
@@ -395,7 +369,7 @@ __global__ __launch_bounds__(256) void dqmm4_stream_kernel(DqArgs a, int64_t KR)
   if (t < a.T) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t r = rO + v;
+      const int64_t r = rw + 4 * g4 + v;
       if (r >= a.m) continue;
       if (a.P) a.P[(ks * a.T + t) * a.m + r] = tot[v];
       else Elem<DT>::store(a.Y, t * a.ldy + r, tot[v]);
@@ -404,21 +378,40 @@ __global__ __launch_bounds__(256) void dqmm4_stream_kernel(DqArgs a, int64_t KR)
 }
 
 // Y[t][r] = sum over the K sets of the partials, in set order, in X's dtype.
+// A thread takes four consecutive rows of one token (16-byte loads when m is
+// a multiple of 4), all KS loads in flight at once.
 template <int DT>
 __global__ __launch_bounds__(256) void dqmm_reduce_kernel(const float* P, int KS, int64_t T, int64_t m, void* Y,
                                                           int64_t ldy) {
-  for (int64_t t = blockIdx.y; t < T; t += gridDim.y)
-    for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < m; r += (int64_t)gridDim.x * 256) {
-      float s = 0.f;
-      for (int k = 0; k < KS; ++k) s += P[((int64_t)k * T + t) * m + r];
-      Elem<DT>::store(Y, t * ldy + r, s);
+  const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (r >= m) return;
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if ((m & 3) == 0) {
+      constexpr int U = 8;  // loads in flight per pass
+      for (int k0 = 0; k0 < KS; k0 += U) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (k0 + u < KS) v[u] = *(const f32x4*)(P + ((int64_t)(k0 + u) * T + t) * m + r);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (k0 + u < KS) s += v[u];
+      }
+    } else {
+      for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (r + e < m) s[e] += P[((int64_t)k * T + t) * m + r + e];
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (r + e < m) Elem<DT>::store(Y, t * ldy + r + e, s[e]);
+  }
 }
 
 // K sets and the columns of each: the staged kernel for more than 16 tokens
-// (slices of 512), the streaming kernel for up to 16 (ranges of whole
-// 256-column chunks, enough waves to keep HBM busy, at least 512 columns
-// each)
+// (slices of 512), the task kernel for up to 16 (ranges of 512 or 1024)
 struct DqSplit {
   int ks;
   int64_t kr;
@@ -429,10 +422,26 @@ DqSplit dq_split(int64_t T, int64_t m, int64_t n) {
     if (base >= DQ_SLOTS) return {1, cdiv(n, DQ_KR) * DQ_KR};
     return {(int)std::min<int64_t>(cdiv(n, DQ_KR), cdiv(DQ_SLOTS, base)), DQ_KR};
   }
-  const int64_t rb = cdiv(m, 16);
-  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(cdiv(DS_WAVES, rb), cdiv(n, 512)));
-  const int64_t kr = cdiv(cdiv(n, want), DS_CH) * DS_CH;
+  // ranges of 1024 columns while that still gives about four workgroups per
+  // CU, else 512
+  const int64_t kr = cdiv(m, 64) * cdiv(n, 1024) >= 1024 ? 1024 : 512;
   return {(int)cdiv(n, kr), kr};
+}
+
+template <int DT, bool G128>
+void launch_task_g(const DqArgs& a, int64_t kr, int64_t T, dim3 grid, hipStream_t st) {
+  if (kr == 1024) {
+    if (T <= 4) hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 1024, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 1024, 16>), grid, dim3(256), 0, st, a);
+  } else {
+    if (T <= 4) hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 512, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 512, 16>), grid, dim3(256), 0, st, a);
+  }
+}
+template <int DT>
+void launch_task(const DqArgs& a, bool g128, int64_t kr, int64_t T, dim3 grid, hipStream_t st) {
+  if (g128) launch_task_g<DT, true>(a, kr, T, grid, st);
+  else launch_task_g<DT, false>(a, kr, T, grid, st);
 }
 
 }  // namespace
@@ -460,24 +469,16 @@ hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const u
   a.KS = sp.ks;
   a.P = a.KS > 1 ? (float*)ws : nullptr;
   if (T <= 16) {
-    const dim3 grid((unsigned)cdiv(cdiv(m, 16) * a.KS, 4));
-    const bool g128 = group == 128, full = n % DS_CH == 0;
-#define DQ_STREAM(D, G, F) hipLaunchKernelGGL((dqmm4_stream_kernel<D, G, F>), grid, dim3(256), 0, st, a, sp.kr)
-    if (dt == 0) {
-      if (g128) { if (full) DQ_STREAM(0, true, true); else DQ_STREAM(0, true, false); }
-      else { if (full) DQ_STREAM(0, false, true); else DQ_STREAM(0, false, false); }
-    } else {
-      if (g128) { if (full) DQ_STREAM(1, true, true); else DQ_STREAM(1, true, false); }
-      else { if (full) DQ_STREAM(1, false, true); else DQ_STREAM(1, false, false); }
-    }
-#undef DQ_STREAM
+    const dim3 grid((unsigned)(cdiv(m, 64) * a.KS));
+    if (dt == 0) launch_task<0>(a, group == 128, sp.kr, T, grid, st);
+    else launch_task<1>(a, group == 128, sp.kr, T, grid, st);
   } else {
     const dim3 grid((unsigned)cdiv(m, DQ_ROWS), (unsigned)a.KS, (unsigned)cdiv(T, DQ_TOK));
     if (dt == 0) hipLaunchKernelGGL(dqmm4_kernel<0>, grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(dqmm4_kernel<1>, grid, dim3(256), 0, st, a);
   }
   if (a.KS > 1) {
-    const dim3 rg((unsigned)std::min<int64_t>(cdiv(m, 256), 64), (unsigned)std::min<int64_t>(T, 65535));
+    const dim3 rg((unsigned)cdiv(m, 1024), (unsigned)std::min<int64_t>(T, 65535));
     if (dt == 0) hipLaunchKernelGGL(dqmm_reduce_kernel<0>, rg, dim3(256), 0, st, (const float*)a.P, a.KS, T, m, Y, ldy);
     else hipLaunchKernelGGL(dqmm_reduce_kernel<1>, rg, dim3(256), 0, st, (const float*)a.P, a.KS, T, m, Y, ldy);
   }

@@ -7,13 +7,13 @@ bytes.
 
 Tolerance per output element, from the kernel's arithmetic (every product
 (b + q) x is exact in fp32, b = 0 for fp16 and 128 for bf16 activations):
-  * fp32 sums: at most L + 8 roundings of 2^-24 each, L <= 512 columns per
-    accumulator (a group's pieces inside one 512-column slice), each bounded
-    by B = sum_c s_g (2b + q_c + z_g) |x_c|, plus the per-group and per-slice
-    combinations (G + slices more);
+  * fp32 sums: at most L + 8 roundings of 2^-24 each, L <= 1024 columns per
+    accumulator (a group's pieces inside one K range of 512 or 1024 columns),
+    each bounded by B = sum_c s_g (2b + q_c + z_g) |x_c|, plus the per-group
+    and per-range combinations (G + ranges more, ranges <= n / 512);
   * one rounding to the output dtype: u |Y|, u = 2^-11 (fp16), 2^-8 (bf16),
     and half of fp16's smallest subnormal.
-So |Y_gpu - Y| <= u |Y| + 2^-24 (520 + G + slices) B + 2^-25.  That bound
+So |Y_gpu - Y| <= u |Y| + 2^-24 (1032 + G + ranges) B + 2^-25.  That bound
 is loose (it assumes every rounding is worst-case and aligned), so the RMS
 error is also checked against the output rounding alone: rms <= 2u rms(Y).
 """
@@ -54,7 +54,7 @@ def _check(Yg: torch.Tensor, X64, q, s, z, group, n, dt, what):
     G = s.shape[1]
     slices = (n + 511) // 512
     u = U_OUT[dt]
-    tol = u * np.abs(Y) + 2.0 ** -24 * (520 + G + slices) * Bmat + 2.0 ** -25
+    tol = u * np.abs(Y) + 2.0 ** -24 * (1032 + G + slices) * Bmat + 2.0 ** -25
     err = np.abs(Yk - Y)
     worst = float(np.max(err / tol))
     rms = float(np.sqrt(np.mean(err ** 2)) / max(np.sqrt(np.mean(Y ** 2)), 1e-30))
@@ -75,6 +75,9 @@ DQ_CASES = [
     (256, 320, 2048, 128, "f16"),
     (1000, 512, 512, 128, "f16"),    # many tokens: no K split
     (3, 11008, 4096, 128, "f16"),    # an MLP up-projection shape
+    (5, 16384, 4096, 128, "f16"),    # 1024-column K ranges, up to 16 staged tokens
+    (2, 8192, 8192, 0, "bf16"),      # 1024-column ranges, one group per row across ranges
+    (9, 16320, 4160, 128, "bf16"),   # 1024-column ranges, ragged rows, a 64-column last range and group
 ]
 
 
