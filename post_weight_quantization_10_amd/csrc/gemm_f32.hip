@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmDesc d) {
 // branches): A as 128 rows x 128 B, B as 32 rows x 512 B, their 16-byte chunks
 // XOR-swizzled so that the MFMA operand reads (one float per lane) spread over
 // the banks.  Two stages in a ring, two workgroups per CU; every operand read
-// sits between two MFMAs.
+// sits between two MFMAs, two k pairs ahead of its use.
 
 constexpr int DBK = 32;                       // K per stage
 constexpr int DSTAGE_F = BM * DBK + DBK * BN;  // floats per stage (A then B): 32 KiB
@@ -298,31 +298,36 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_dma_kernel(GemmDesc d, int nsp
   auto compute = [&](const float* stg) {
     const float* sA = stg;
     const float* sB = stg + BM * DBK;
-    float a0 = rdA(sA, wr * 64 + cl, kr), a1 = rdA(sA, wr * 64 + 32 + cl, kr);
-    float b0 = rdB(sB, kr, wc * 64 + cl), b1 = rdB(sB, kr, wc * 64 + 32 + cl);
+    // operands of k pair kk in slot kk % 3, read two pairs (eight MFMAs) ahead
+    float fa0[3], fa1[3], fb0[3], fb1[3];
+    auto rdk = [&](int kk, int sl) {
+      const int k = 2 * kk + kr;
+      fa0[sl] = rdA(sA, wr * 64 + cl, k); fa1[sl] = rdA(sA, wr * 64 + 32 + cl, k);
+      fb0[sl] = rdB(sB, k, wc * 64 + cl); fb1[sl] = rdB(sB, k, wc * 64 + 32 + cl);
+    };
+    rdk(0, 0);
+    rdk(1, 1);
 #pragma unroll
     for (int kk = 0; kk < DBK / 2; ++kk) {
-      const int kn = 2 * (kk + 1) + kr;
-      float na0 = 0.f, na1 = 0.f, nb0 = 0.f, nb1 = 0.f;
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-      if (kk + 1 < DBK / 2) na0 = rdA(sA, wr * 64 + cl, kn);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-      if (kk + 1 < DBK / 2) na1 = rdA(sA, wr * 64 + 32 + cl, kn);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-      if (kk + 1 < DBK / 2) nb0 = rdB(sB, kn, wc * 64 + cl);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
-      if (kk + 1 < DBK / 2) nb1 = rdB(sB, kn, wc * 64 + 32 + cl);
-      a0 = na0; a1 = na1; b0 = nb0; b1 = nb1;
+      const int s = kk % 3, sn = (kk + 2) % 3, kn = 2 * (kk + 2) + kr;
+      const bool more = kk + 2 < DBK / 2;
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa0[s], fb0[s], acc[0][0], 0, 0, 0);
+      if (more) fa0[sn] = rdA(sA, wr * 64 + cl, kn);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa0[s], fb1[s], acc[0][1], 0, 0, 0);
+      if (more) fa1[sn] = rdA(sA, wr * 64 + 32 + cl, kn);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa1[s], fb0[s], acc[1][0], 0, 0, 0);
+      if (more) fb0[sn] = rdB(sB, kn, wc * 64 + cl);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa1[s], fb1[s], acc[1][1], 0, 0, 0);
+      if (more) fb1[sn] = rdB(sB, kn, wc * 64 + 32 + cl);
     }
-    // keep each read one k pair (four MFMAs) ahead of its use
 #pragma unroll
-    for (int kk = 0; kk < DBK / 2 - 1; ++kk)
+    for (int kk = 0; kk < DBK / 2 - 2; ++kk)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   // two-stage ring: the copy of step s+1 is in flight while step s computes
