@@ -14,6 +14,10 @@ Prints one JSON line (rank 0).  Multi-GPU runs are not supported.
 gptq_dequant_matmul (Y = X What^T with 4-bit g128 codes unpacked next to fp16
 activations), on an MLP-shaped layer (28672 x 8192) for one decode token; its
 line carries the same keys, with GB/s of the packed layer as the metric.
+
+--kernel peaks measures the chip's attainable peaks with kernels that do
+nothing else (libgptq_peaks.so): dense fp16 and fp32 MFMA streams, an HBM
+read stream and an HBM copy; the line gives each beside the published peak.
 """
 from __future__ import annotations
 
@@ -29,6 +33,10 @@ sys.path.insert(0, ROOT)
 PEAK_TF16 = 2500.0     # MI355X dense fp16 MFMA, TFLOP/s
 PEAK_TF32 = 157.3      # MI355X fp32 MFMA, TFLOP/s
 PEAK_HBM = 8000.0      # GB/s
+# measured on one MI355X by `bench.py --kernel peaks` (profiles/attainable_peaks.md):
+# fp16 MFMA stream with random operands, HBM read stream
+ATTAIN_TF16 = 1726.4
+ATTAIN_HBM_READ = 6390.2
 
 
 def parse():
@@ -37,8 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="attn", choices=["attn", "tiny"])
-    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16"],
-                    help="layer: the quantization path (default); w4a16: the packed layer at run time")
+    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "peaks"],
+                    help="layer: the quantization path (default); w4a16: the packed layer at run time; "
+                         "peaks: measured attainable MFMA and HBM rates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_attn_4096x262144_traffic.json"),
                     help="JSON with rocprofv3 FETCH/WRITE bytes per SYRK launch (optional)")
@@ -128,7 +137,9 @@ def bench_w4a16(args):
                    "tokens": T, "m": m, "n": n, "bits": 4, "group": group, "parallelism": "single GPU"},
         "roofline": {"kernel": "gptq_dequant_matmul: dqmm4_task_kernel + dqmm_reduce_kernel", "bound": "hbm",
                      "achieved": round(gbs_ev, 1), "peak": PEAK_HBM, "unit": "GB/s",
-                     "frac": round(gbs_ev / PEAK_HBM, 4), "traffic": None},
+                     "frac": round(gbs_ev / PEAK_HBM, 4), "traffic": None,
+                     "attainable": {"peak": ATTAIN_HBM_READ, "frac": round(gbs_ev / ATTAIN_HBM_READ, 4),
+                                    "source": "bench.py --kernel peaks (HBM read stream)"}},
     }
     if not args.no_cpu_baseline:
         import oracle as O
@@ -162,6 +173,70 @@ def traffic_bytes(path):
     return js.get("bytes_per_launch")
 
 
+def bench_peaks(args):
+    """Attainable peaks, each the best of a few timed launches on the current
+    stream (HIP events): MFMA streams of 1024 workgroups x 4 waves, eight
+    independent accumulators per wave; HBM read of 4 GiB and copy of 2 GiB,
+    grid 4096 x 256 threads."""
+    import ctypes
+
+    import torch
+
+    from post_weight_quantization_10_amd import build as B
+    if not os.path.exists(B.PROBE_PATH):
+        raise RuntimeError(f"{B.PROBE_PATH} is missing: build it with python -m post_weight_quantization_10_amd.build")
+    L = ctypes.CDLL(B.PROBE_PATH)
+    L.gptq_peaks_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p]
+    L.gptq_peaks_launch.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    reps = max(3, args.steps)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+
+    out = {}
+    g_mfma, iters = 1024, 2048
+    bits = torch.randint(-2 ** 31, 2 ** 31 - 1, (g_mfma * 256 * 4,), dtype=torch.int32, device=dev)
+    sink = torch.empty(g_mfma * 256, dtype=torch.float32, device=dev)
+    for which, key, flop in ((0, "mfma_fp16", 2 * 32 * 32 * 16), (1, "mfma_fp32", 2 * 32 * 32 * 2)):
+        def run(which=which):
+            assert L.gptq_peaks_launch(which, bits.data_ptr(), sink.data_ptr(), 0, iters, g_mfma, st) == 0
+        t = best(run)
+        out[key] = g_mfma * 4 * iters * 16 * flop / t / 1e12
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_()
+    words = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    t = best(lambda: L.gptq_peaks_launch(2, src.data_ptr(), words.data_ptr(), nbytes, 0, 4096, st))
+    out["hbm_read"] = nbytes / t / 1e9
+    half = nbytes // 2
+    dst = torch.empty(half // 4, dtype=torch.int32, device=dev)
+    t = best(lambda: L.gptq_peaks_launch(3, src.data_ptr(), dst.data_ptr(), half, 0, 4096, st))
+    out["hbm_copy"] = 2 * half / t / 1e9
+    assert torch.equal(dst, src[: half // 4])
+    spec = {"mfma_fp16": PEAK_TF16, "mfma_fp32": PEAK_TF32, "hbm_read": PEAK_HBM, "hbm_copy": PEAK_HBM}
+    units = {"mfma_fp16": "TFLOP/s", "mfma_fp32": "TFLOP/s", "hbm_read": "GB/s", "hbm_copy": "GB/s (read + write)"}
+    res = {"metric": "measured attainable peaks (MFMA streams, HBM streams)", "value": round(out["mfma_fp16"], 1),
+           "unit": "TFLOP/s (fp16 MFMA)", "n_gpus": 1, "steps": reps, "warmup": 1, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "fp16/fp32 MFMA, u32 loads", "data": "synthetic",
+           "config": {"workload": "peak probes: MFMA 1024 workgroups x 4 waves x 2048 x 16 instructions; "
+                                  "HBM read 4 GiB, copy 2 GiB"},
+           "peaks": {k: {"measured": round(v, 1), "published": spec[k], "unit": units[k],
+                         "frac": round(v / spec[k], 4)} for k, v in out.items()}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -170,6 +245,9 @@ def main():
         sys.exit(2)
     if args.kernel == "w4a16":
         bench_w4a16(args)
+        return
+    if args.kernel == "peaks":
+        bench_peaks(args)
         return
     import numpy as np
     import torch
@@ -270,6 +348,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TF16, 4),
             "traffic": traffic,
+            "attainable": {"peak": ATTAIN_TF16, "frac": round(achieved / ATTAIN_TF16, 4),
+                           "source": "bench.py --kernel peaks (fp16 MFMA stream, random operands)"},
         },
     }
     if not args.no_cpu_baseline:

@@ -1,4 +1,5 @@
-"""Build the gfx950 shared library (libgptq_mi355x.so) in-tree with hipcc.
+"""Build the gfx950 shared library (libgptq_mi355x.so) in-tree with hipcc, and
+the measurement probe (libgptq_peaks.so, csrc/probe/) beside it.
 
 Usage:  python -m post_weight_quantization_10_amd.build   (or build() from Python)
 """
@@ -16,6 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libgptq_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+PROBE_SRC = os.path.join(CSRC, "probe", "peaks.hip")
+PROBE_PATH = os.path.join(HERE, "libgptq_peaks.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -34,6 +37,8 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    if src == PROBE_SRC:
+        obj = os.path.join(BUILD_DIR, "probe_" + os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
@@ -47,16 +52,17 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max(1, min(len(srcs), os.cpu_count() or 1))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}")
-    os.replace(tmp, LIB_PATH)
-    if verbose:
-        print(f"built {LIB_PATH}")
+    with cf.ThreadPoolExecutor(max(1, min(len(srcs) + 1, os.cpu_count() or 1))) as ex:
+        objs = list(ex.map(_compile, srcs + [PROBE_SRC]))
+    for out, parts in ((LIB_PATH, objs[:-1]), (PROBE_PATH, objs[-1:])):
+        tmp = out + ".tmp"
+        cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *parts, "-o", tmp]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}")
+        os.replace(tmp, out)
+        if verbose:
+            print(f"built {out}")
     return LIB_PATH
 
 

@@ -135,3 +135,21 @@ def test_dequant_matmul_workspace():
     assert _dqmm(T=1, m=4096, n=4096, ldx=4096, ldy=4096, ws=None, wsb=0) == pw.GPTQ_ERR_WORKSPACE
     assert _dqmm(T=1, m=4096, n=4096, ldx=4096, ldy=4096, wsb=small - 4) == pw.GPTQ_ERR_WORKSPACE
     assert _dqmm(T=0, ws=None, wsb=0) == pw.GPTQ_OK  # no tokens: no-op
+
+
+def test_peaks_probe_library():
+    """The measurement probe (bench.py --kernel peaks) is its own library:
+    it loads, exports its one entry point, and rejects bad requests before
+    any launch."""
+    from post_weight_quantization_10_amd import build as B
+    if not os.path.exists(B.PROBE_PATH):
+        pytest.skip("probe library not built")
+    L = ctypes.CDLL(B.PROBE_PATH)
+    f = L.gptq_peaks_launch
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(7, None, None, 16, 1, 1, None) == -1   # unknown probe
+    assert f(2, None, None, 24, 0, 1, None) == -1   # bytes not a multiple of 16
+    assert f(0, None, None, 0, 1, 0, None) == -1    # empty grid
+    assert "gptq_peaks_launch" not in open(os.path.join(ROOT, "include", "gptq.h")).read()
