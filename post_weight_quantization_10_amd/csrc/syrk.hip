@@ -278,7 +278,10 @@ __device__ __forceinline__ constexpr int rd_isb(int i) { return (i >= 2 && i < 1
 __device__ __forceinline__ constexpr int rd_blk(int i) { return i < 2 ? 0 : (i < 10 ? (i - 2) >> 1 : 1 + ((i - 10) >> 1)); }
 __device__ __forceinline__ constexpr int rd_half(int i) { return i & 1; }
 
-template <int DT, bool DIAG>
+// IDLE: the wave of a diagonal tile whose 128 x 128 block lies strictly above
+// the diagonal (never read by the reduction): it takes its share of the ring
+// refills and every barrier, and reads and multiplies nothing.
+template <int DT, bool DIAG, bool IDLE>
 __device__ __forceinline__ void syrk16_dma_body(const SyrkArgs& a, int split, int tlin, int bi, int bj, char* st0,
                                                 char* st1, char* st2, char* st3, char* st4) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -336,6 +339,7 @@ __device__ __forceinline__ void syrk16_dma_body(const SyrkArgs& a, int split, in
   };
   // read i (0..15) of the K16 step ks of stage st into F
   auto rd1 = [&](const char* st, int ks, Frag& F, int i) {
+    if constexpr (IDLE) return;
     const int isb = rd_isb(i), blk = rd_blk(i), h = rd_half(i);
     const char* T = (isb && !DIAG) ? st + OPB : st;
     const int r = 16 * ks + trow + 4 * h;
@@ -349,6 +353,7 @@ __device__ __forceinline__ void syrk16_dma_body(const SyrkArgs& a, int split, in
     for (int i = 0; i < 16; ++i) rd1(st, ks, F, i);
   };
   auto mfma1 = [&](const Frag& F, int i) {
+    if constexpr (IDLE) return;
     const int mb = i >> 2, nb = i & 3;
     if (DT == 0)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, F.a[mb]),
@@ -387,10 +392,12 @@ __device__ __forceinline__ void syrk16_dma_body(const SyrkArgs& a, int split, in
       mfma1(F0, i);
       rd1(cur, 1, F1, i);
     }
+    if constexpr (!IDLE) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
     }
     wait_stage(2);
     stage_barrier();  // stage c+1 visible; stage c-1 no longer read by anyone
@@ -401,10 +408,12 @@ __device__ __forceinline__ void syrk16_dma_body(const SyrkArgs& a, int split, in
       rd1(nx, 0, F0, i);
       if ((i & 1) && (i >> 1) < NCOPY) dma1(rs, fill, i >> 1);
     }
+    if constexpr (!IDLE) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
   };
   // general step (pipeline fill and drain)
@@ -446,6 +455,7 @@ __device__ __forceinline__ void syrk16_dma_body(const SyrkArgs& a, int split, in
     if (c + 4 < ce) step(c + 4, st4, st0, st3);
   }
 
+  if constexpr (IDLE) return;
   float* out = a.partial + ((int64_t)split * a.ntiles + tlin) * (TILE * TILE);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -471,8 +481,10 @@ void syrk16_dma_kernel(SyrkArgs a) {
   __shared__ __attribute__((aligned(1024))) char st4[STB];
   int split, tlin, bi, bj;
   if (!syrk_item(a, split, tlin, bi, bj)) return;
-  if (bi == bj) syrk16_dma_body<DT, true>(a, split, tlin, bi, bj, st0, st1, st2, st3, st4);
-  else syrk16_dma_body<DT, false>(a, split, tlin, bi, bj, st0, st1, st2, st3, st4);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (bi != bj) syrk16_dma_body<DT, false, false>(a, split, tlin, bi, bj, st0, st1, st2, st3, st4);
+  else if (wave == 1) syrk16_dma_body<DT, true, true>(a, split, tlin, bi, bj, st0, st1, st2, st3, st4);
+  else syrk16_dma_body<DT, true, false>(a, split, tlin, bi, bj, st0, st1, st2, st3, st4);
 }
 
 // ---------------------------------------------------------------------------- fp32 inputs
