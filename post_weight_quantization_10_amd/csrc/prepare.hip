@@ -87,6 +87,7 @@ __global__ __launch_bounds__(256) void reverse_damp4_kernel(const float* H, floa
 }
 
 constexpr int TB = 128;          // trailing-update tile
+constexpr int PRE_TILES = 256;   // above this many tiles a step solves its panel slabs in a kernel of their own
 constexpr int LP = 65;           // LDS pitch of 64-column leaf matrices (floats)
 constexpr int LLP = 68;          // LDS pitch of the leaf factor: 16-byte aligned rows
 constexpr int PP = 68;           // LDS pitch of the leaf's product operands: 16-byte aligned rows
@@ -445,7 +446,10 @@ __device__ __forceinline__ void panel_solve(const float* S, const float* sD, int
 }
 
 // One 128 x 128 lower tile t of the trailing matrix [R0, n)^2, R0 = k0 + NB.
-template <bool VEC>
+// PRE: the panel slabs were solved beforehand (panel_solve_kernel wrote every
+// slab of L21 for this block column), so the tile loads its two slabs of L
+// instead of A21 and Dinv_k and goes straight to the rank update.
+template <bool VEC, bool PRE>
 __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __restrict__ L,
                                             const float* __restrict__ dinv_k, int64_t n, int64_t k0, int t,
                                             float* smem) {
@@ -468,21 +472,25 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
   const bool active = !(dg && wr < wc) && !(tm == 0 && wr == 0 && wc == 0);
   const uint32_t n32 = (uint32_t)n;
 
-  // Panel rows and Dinv_k: all loads in flight together, then to LDS.  Rows
-  // past n are clamped: they only reach outputs that are never stored.
+  // Panel rows and Dinv_k (PRE: the solved rows of L): all loads in flight
+  // together, then to LDS.  Rows past n are clamped: they only reach outputs
+  // that are never stored.
   {
+    const float* P = PRE ? L : A;
     f32x4 pr[8], pc[8], dv[4];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = tid + 256 * u;
       const int r = e >> 4, g = 4 * (e & 15);
-      pr[u] = ld4<VEC>(A + min(r0 + r, n - 1) * n + k0 + g);
-      if (!dg) pc[u] = ld4<VEC>(A + min(c0 + r, n - 1) * n + k0 + g);
+      pr[u] = ld4<VEC>(P + min(r0 + r, n - 1) * n + k0 + g);
+      if (!dg) pc[u] = ld4<VEC>(P + min(c0 + r, n - 1) * n + k0 + g);
     }
+    if (!PRE) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 256 * u;
-      dv[u] = *(const f32x4*)&dinv_k[(e >> 4) * NB + 4 * (e & 15)];
+      for (int u = 0; u < 4; ++u) {
+        const int e = tid + 256 * u;
+        dv[u] = *(const f32x4*)&dinv_k[(e >> 4) * NB + 4 * (e & 15)];
+      }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -491,10 +499,12 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
       *(f32x4*)&sR[pidx(r, g)] = pr[u];
       if (!dg) *(f32x4*)&sC[pidx(r, g)] = pc[u];
     }
+    if (!PRE) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + 256 * u;
-      *(f32x4*)&sD[pidx(e >> 4, 4 * (e & 15))] = dv[u];
+      for (int u = 0; u < 4; ++u) {
+        const int e = tid + 256 * u;
+        *(f32x4*)&sD[pidx(e >> 4, 4 * (e & 15))] = dv[u];
+      }
     }
   }
   __syncthreads();
@@ -521,22 +531,24 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
     }
   };
   f32x16 o[2];
-  panel_solve(sR, sD, wave, lane, o);
-  put(sR, o);
-  if (tn == 0) {  // row 32w + 4kr + rc of the slab: a lane term plus a uniform multiple of n
-    const uint32_t lb = (uint32_t)(32 * wave + 4 * kr) * n32 + (uint32_t)cl;
+  if (!PRE) {
+    panel_solve(sR, sD, wave, lane, o);
+    put(sR, o);
+    if (tn == 0) {  // row 32w + 4kr + rc of the slab: a lane term plus a uniform multiple of n
+      const uint32_t lb = (uint32_t)(32 * wave + 4 * kr) * n32 + (uint32_t)cl;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float v = o[nb][r];  // (a bit cast of the vector element itself reads element 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), lrs,
-                                              (lb + (uint32_t)(8 * (r >> 2) + (r & 3)) * n32 + 32u * nb) * 4u, 0, 0);
-      }
-  }
-  if (!dg) {
-    panel_solve(sC, sD, wave, lane, o);
-    put(sC, o);
+        for (int r = 0; r < 16; ++r) {
+          const float v = o[nb][r];  // (a bit cast of the vector element itself reads element 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), lrs,
+                                                (lb + (uint32_t)(8 * (r >> 2) + (r & 3)) * n32 + 32u * nb) * 4u, 0, 0);
+        }
+    }
+    if (!dg) {
+      panel_solve(sC, sD, wave, lane, o);
+      put(sC, o);
+    }
   }
   // C of this wave's 64 x 64 quadrant, fetched only now (so it is not live
   // during the panel solves) and consumed after the rank update's MFMAs
@@ -631,7 +643,7 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
 
 // Block column k at k0 (n - k0 > NB): workgroup 0 factors diagonal block
 // k + 1, workgroups 1.. update the lower tiles of the trailing matrix.
-template <bool VEC>
+template <bool VEC, bool PRE>
 __global__ __launch_bounds__(256, 2) void chol_step_kernel(float* A, float* L, float* dinv, int64_t n, int64_t k0,
                                                            int32_t* info) {
   if (*info != 0) return;
@@ -640,7 +652,63 @@ __global__ __launch_bounds__(256, 2) void chol_step_kernel(float* A, float* L, f
   if (blockIdx.x == 0)
     leaf_block(A, n, k0 + NB, k0, dinv + kbk * NB * NB, dinv + (kbk + 1) * NB * NB, info, smem);
   else
-    tile_update<VEC>(A, L, dinv + kbk * NB * NB, n, k0, (int)blockIdx.x - 1, smem);
+    tile_update<VEC, PRE>(A, L, dinv + kbk * NB * NB, n, k0, (int)blockIdx.x - 1, smem);
+}
+
+// Every 128-row slab of block column k of the factor, L21 = A21 Dinv_k^T
+// (the solve each tile would otherwise repeat for its two slabs), written to
+// L; one workgroup per slab.  Used when the trailing matrix has more tiles
+// than the GPU runs at once, so the tiles of the step only load their slabs.
+template <bool VEC>
+__global__ __launch_bounds__(256) void panel_solve_kernel(const float* A, float* L, const float* dinv, int64_t n,
+                                                          int64_t k0, const int32_t* info) {
+  if (*info != 0) return;
+  __shared__ __attribute__((aligned(16))) float sD[64 * 64];
+  __shared__ __attribute__((aligned(16))) float sR[128 * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t r0 = k0 + NB + (int64_t)blockIdx.x * TB;
+  const float* dinv_k = dinv + (k0 / NB) * NB * NB;
+  {
+    f32x4 pr[8], dv[4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u;
+      pr[u] = ld4<VEC>(A + min(r0 + (e >> 4), n - 1) * n + k0 + 4 * (e & 15));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      dv[u] = *(const f32x4*)&dinv_k[(e >> 4) * NB + 4 * (e & 15)];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u;
+      *(f32x4*)&sR[pidx(e >> 4, 4 * (e & 15))] = pr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      *(f32x4*)&sD[pidx(e >> 4, 4 * (e & 15))] = dv[u];
+    }
+  }
+  __syncthreads();
+  f32x16 o[2];
+  panel_solve(sR, sD, wave, lane, o);
+  // rows past n fall outside this buffer and are dropped
+  const uint32_t n32 = (uint32_t)n;
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+      L + (r0 * n + k0), 0, (int)((uint32_t)min<int64_t>(TB, n - r0) * n32 * 4u), 0x00020000);
+  const int cl = lane & 31, kr = lane >> 5;
+  const uint32_t lb = (uint32_t)(32 * wave + 4 * kr) * n32 + (uint32_t)cl;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = o[nb][r];  // (a bit cast of the vector element itself reads element 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), lrs,
+                                            (lb + (uint32_t)(8 * (r >> 2) + (r & 3)) * n32 + 32u * nb) * 4u, 0, 0);
+    }
 }
 
 // Zero the strict upper triangle and put the NB-block inverses on the diagonal.
@@ -752,8 +820,23 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
   for (int64_t k0 = 0; k0 + NB < n; k0 += NB) {
     const int64_t nt = cdiv(n - k0 - NB, TB);
     const unsigned grid = (unsigned)(1 + nt * (nt + 1) / 2);
-    if (vec) hipLaunchKernelGGL((chol_step_kernel<true>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
-    else hipLaunchKernelGGL((chol_step_kernel<false>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
+    // more tiles than CUs: solve the slabs once (PRE), else in the tiles
+    if (grid - 1 > PRE_TILES) {
+      if (vec) {
+        hipLaunchKernelGGL((panel_solve_kernel<true>), dim3((unsigned)nt), dim3(256), 0, s, (const float*)w.A, w.L,
+                           (const float*)w.dinv, n, k0, (const int32_t*)info);
+        hipLaunchKernelGGL((chol_step_kernel<true, true>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
+      } else {
+        hipLaunchKernelGGL((panel_solve_kernel<false>), dim3((unsigned)nt), dim3(256), 0, s, (const float*)w.A, w.L,
+                           (const float*)w.dinv, n, k0, (const int32_t*)info);
+        hipLaunchKernelGGL((chol_step_kernel<false, true>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0,
+                           info);
+      }
+    } else if (vec) {
+      hipLaunchKernelGGL((chol_step_kernel<true, false>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
+    } else {
+      hipLaunchKernelGGL((chol_step_kernel<false, false>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
+    }
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
