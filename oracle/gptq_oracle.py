@@ -14,9 +14,13 @@ describe the method.  Short names used in the citations below:
   [SOQ]     the English blog post on GPTQ second-order quantization
             (hungho77.github.io, /hung/blog/gptq-second-order-quantization/)
   [SOQ-vi]  the Vietnamese edition of that post (/hung/vi/blog/...)
+  [OptRot]  "OptRot: Mitigating Weight Outliers via Data-Free Rotations for
+            Post-Training Quantization" (abstract and Figure 1)
 
 Beyond the per-layer path, dequant_matmul is the runtime consumer of the
-packed layer (weights unpacked and dequantized next to 16-bit activations).
+packed layer (weights unpacked and dequantized next to 16-bit activations),
+and hadamard_rotate is the fixed rotation applied before GPTQ that [OptRot]
+uses as its baseline.
 
 Readings taken where the pages are silent or disagree (each is also listed in
 the design notes):
@@ -46,6 +50,14 @@ the design notes):
   R8  Columns are swept left to right ([GPTQ] "Observation 1").
   R9  Block size and group size must nest (group % block == 0 or
       block % group == 0); the last block and group may be short.
+  R10 The fixed rotation is R = blockdiag(H_b, ..., H_b) / sqrt(b), H_b the
+      Sylvester-ordered Hadamard matrix of order b (a power of two dividing
+      the row length); rows are rotated as M <- M R.  With W' = W R and
+      X' = X R the layer output is unchanged (X' W'^T = X W^T, R orthogonal),
+      so R folds into the previous layer and costs nothing at run time
+      ([OptRot] Figure 1, "fusible" rotations); H' = 2 X'^T X' = R^T H R.
+      Weight incoherence (the quantity [OptRot] Theorem 3.1 bounds the error
+      with) is read as mu_W = sqrt(m n) max |W_ij| / ||W||_F.
 """
 from __future__ import annotations
 
@@ -433,3 +445,44 @@ def boundary_distance(t: np.ndarray) -> np.ndarray:
     """Distance (in quantization steps) of a pre-rounding value to the nearest
     rounding boundary k + 1/2."""
     return np.abs(t - (np.floor(t) + 0.5))
+
+
+# ----------------------------------------------------------------------------- fixed rotation before GPTQ
+
+def hadamard_matrix(b: int) -> np.ndarray:
+    """Sylvester-ordered Hadamard matrix of order b (a power of two):
+    H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]] (reading R10)."""
+    if b < 1 or b & (b - 1):
+        raise ValueError("order must be a power of two")
+    Hm = np.ones((1, 1))
+    while Hm.shape[0] < b:
+        Hm = np.block([[Hm, Hm], [Hm, -Hm]])
+    return Hm
+
+
+def default_rotation_block(n: int) -> int:
+    """The largest power of two dividing n, at most 4096."""
+    b = 1
+    while n % (2 * b) == 0 and 2 * b <= 4096:
+        b *= 2
+    return b
+
+
+def hadamard_rotate(M: np.ndarray, block: int = 0) -> np.ndarray:
+    """M R with R = blockdiag(H_b, ..., H_b) / sqrt(b) over the columns of M
+    (reading R10; [OptRot] abstract and Figure 1: a fixed, fusible rotation
+    applied before GPTQ to spread weight outliers).  block <= 0 takes the
+    largest power of two dividing the row length (at most 4096)."""
+    M = np.asarray(M, dtype=np.float64)
+    rows, n = M.shape
+    b = default_rotation_block(n) if block <= 0 else int(block)
+    if b & (b - 1) or n % b:
+        raise ValueError("block must be a power of two dividing the row length")
+    R = hadamard_matrix(b) / math.sqrt(b)
+    return (M.reshape(rows, n // b, b) @ R).reshape(rows, n)
+
+
+def weight_incoherence(W: np.ndarray) -> float:
+    """mu_W = sqrt(m n) max |W_ij| / ||W||_F (reading R10)."""
+    W = np.asarray(W, dtype=np.float64)
+    return float(math.sqrt(W.size) * np.max(np.abs(W)) / np.linalg.norm(W))
