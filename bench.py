@@ -15,6 +15,10 @@ gptq_dequant_matmul (Y = X What^T with 4-bit g128 codes unpacked next to fp16
 activations), on an MLP-shaped layer (28672 x 8192) for one decode token; its
 line carries the same keys, with GB/s of the packed layer as the metric.
 
+--kernel rotate times gptq_rotate_hadamard on the attention-projection
+calibration activations (262144 x 4096 fp16, one 4096-wide Hadamard block per
+row, in place): the fixed rotation applied before GPTQ; GB/s of HBM traffic.
+
 --kernel peaks measures the chip's attainable peaks with kernels that do
 nothing else (libgptq_peaks.so): dense fp16 and fp32 MFMA streams, an HBM
 read stream and an HBM copy; the line gives each beside the published peak.
@@ -45,9 +49,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="attn", choices=["attn", "tiny"])
-    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "peaks"],
+    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "rotate", "peaks"],
                     help="layer: the quantization path (default); w4a16: the packed layer at run time; "
-                         "peaks: measured attainable MFMA and HBM rates")
+                         "rotate: the Hadamard rotation before GPTQ; peaks: measured attainable MFMA and HBM rates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_attn_4096x262144_traffic.json"),
                     help="JSON with rocprofv3 FETCH/WRITE bytes per SYRK launch (optional)")
@@ -173,6 +177,65 @@ def traffic_bytes(path):
     return js.get("bytes_per_launch")
 
 
+def bench_rotate(args):
+    """gptq_rotate_hadamard on 262144 x 4096 fp16 activations (block 4096), in
+    place; a step is one call.  Bytes counted: every element read and written
+    once (2 x 2 bytes)."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_10_amd as pw
+    import synth
+    T, n = 262144, 4096
+    dev = torch.device("cuda:0")
+    wl = synth.workloads()["attn"]
+    job = wl.jobs[0]
+    X = torch.from_numpy(synth.x_full(job.x, wl.seed, wl.wid)).to(dev)
+    for _ in range(max(args.warmup, 1)):
+        pw.rotate_hadamard(X)
+    torch.cuda.synchronize()
+    reps = 2 * max(args.steps, 1)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        pw.rotate_hadamard(X)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        pw.rotate_hadamard(X)
+    b.record()
+    torch.cuda.synchronize()
+    ms_ev = a.elapsed_time(b) / reps
+    nbytes = 2.0 * 2.0 * T * n
+    gbs, gbs_ev = nbytes / (ms * 1e-3) / 1e9, nbytes / (ms_ev * 1e-3) / 1e9
+    res = {
+        "metric": "GB/s of the Hadamard rotation before GPTQ (262144 x 4096 fp16 activations, block 4096)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 in/out, fp32 butterflies", "data": "synthetic",
+        "config": {"workload": f"rotate X {T}x{n} fp16 in place, Hadamard block {n}", "tokens": T, "n": n,
+                   "block": n, "parallelism": "single GPU"},
+        "roofline": {"kernel": "gptq_rotate_hadamard: hadamard_rows_kernel", "bound": "hbm",
+                     "achieved": round(gbs_ev, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                     "frac": round(gbs_ev / PEAK_HBM, 4), "traffic": None,
+                     "attainable": {"peak": 4943.7, "frac": round(gbs_ev / 4943.7, 4),
+                                    "source": "bench.py --kernel peaks (HBM copy stream)"}},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        rows = 256
+        sample = X[:rows].float().cpu().numpy().astype(np.float64)
+        t1 = time.perf_counter()
+        O.hadamard_rotate(sample)
+        dt = time.perf_counter() - t1
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        res["cpu_baseline"] = {"value": round(nbytes / (dt * T / rows) / 1e9, 3),
+                               "unit": "GB/s (estimated from the sample)", "cores": threads, "kind": "oracle",
+                               "sample": f"fp64 oracle hadamard_rotate of {rows} of {T} rows ({dt:.2f} s), scaled"}
+    print(json.dumps(res), flush=True)
+
+
 def bench_peaks(args):
     """Attainable peaks, each the best of a few timed launches on the current
     stream (HIP events): MFMA streams of 1024 workgroups x 4 waves, eight
@@ -248,6 +311,9 @@ def main():
         return
     if args.kernel == "peaks":
         bench_peaks(args)
+        return
+    if args.kernel == "rotate":
+        bench_rotate(args)
         return
     import numpy as np
     import torch

@@ -11,10 +11,15 @@
  *                            column, compensating later columns from the rows
  *                            of U, and emitting packed codes, scales and zeros
  *
- * and one call that uses the packed result at run time:
+ * one call that uses the packed result at run time:
  *
  *   gptq_dequant_matmul      Y = X What^T with the packed codes unpacked and
  *                            dequantized next to 16-bit activations
+ *
+ * and one that prepares a layer for it with a fixed rotation:
+ *
+ *   gptq_rotate_hadamard     M <- M R (block-diagonal Hadamard), applied to
+ *                            the weights and the activations alike
  *
  * Sources (web pages describing the method):
  *   [OBQ]    "Part 2: Adaptive Rounding: Optimal Brain Quantizer (OBQ)"
@@ -200,6 +205,33 @@ gptq_status gptq_dequant_matmul(const void* X, int32_t x_dtype, int64_t tokens, 
                                 const uint32_t* qcodes, const float* scales, const int32_t* zeros,
                                 int64_t m, int64_t n, int32_t bits, int64_t group_size, void* Y,
                                 int64_t ldy, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fixed rotation before GPTQ ("OptRot: Mitigating Weight Outliers via
+ * Data-Free Rotations for Post-Training Quantization", abstract and Figure 1:
+ * a rotation that folds into the previous layer, applied to spread weight
+ * outliers; the Hadamard rotation is its baseline).
+ *
+ * gptq_rotate_hadamard: M <- M R in place, R = blockdiag(H_b, ..., H_b) /
+ * sqrt(b), H_b the Sylvester-ordered Hadamard matrix of order b
+ * (H_2k = [[H_k, H_k], [H_k, -H_k]]).  Rotate both the weights (W' = W R)
+ * and the calibration activations (X' = X R): X' W'^T = X W^T and
+ * H' = 2 X'^T X' = R^T H R, so gptq_hessian_accumulate on X' and
+ * gptq_quantize_layer on W' quantize the rotated layer, whose run-time input
+ * is X R.  Computed in fp32, rounded once to M's dtype.
+ *   M       [rows x ld] device, row-major, 16-byte aligned; dtype
+ *           GPTQ_F16/BF16/F32; columns [0, n) are rotated, the rest untouched.
+ *   rows    >= 0 (0 is a no-op).
+ *   n       row length, a multiple of b.
+ *   ld      >= n; a multiple of 8 (16-bit) or 4 (fp32) elements.
+ *   block   b: a power of two, 16 <= b <= 4096, dividing n; 0 takes the
+ *           largest power of two dividing n (at most 4096).
+ * Errors: rows < 0, n < 1, ld < n, unknown dtype, block < 0, block not a
+ * power of two or not dividing n, NULL M (rows > 0) -> GPTQ_ERR_INVALID_ARG;
+ * b < 16 or > 4096, misaligned M or ld -> GPTQ_ERR_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_rotate_hadamard(void* M, int32_t dtype, int64_t rows, int64_t n, int64_t ld,
+                                 int64_t block, void* stream);
 
 #ifdef __cplusplus
 }

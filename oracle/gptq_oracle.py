@@ -50,7 +50,7 @@ the design notes):
   R8  Columns are swept left to right ([GPTQ] "Observation 1").
   R9  Block size and group size must nest (group % block == 0 or
       block % group == 0); the last block and group may be short.
-  R10 The fixed rotation is R = blockdiag(H_b, ..., H_b) / sqrt(b), H_b the
+  R12 The fixed rotation is R = blockdiag(H_b, ..., H_b) / sqrt(b), H_b the
       Sylvester-ordered Hadamard matrix of order b (a power of two dividing
       the row length); rows are rotated as M <- M R.  With W' = W R and
       X' = X R the layer output is unchanged (X' W'^T = X W^T, R orthogonal),
@@ -451,7 +451,7 @@ def boundary_distance(t: np.ndarray) -> np.ndarray:
 
 def hadamard_matrix(b: int) -> np.ndarray:
     """Sylvester-ordered Hadamard matrix of order b (a power of two):
-    H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]] (reading R10)."""
+    H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]] (reading R12)."""
     if b < 1 or b & (b - 1):
         raise ValueError("order must be a power of two")
     Hm = np.ones((1, 1))
@@ -470,7 +470,7 @@ def default_rotation_block(n: int) -> int:
 
 def hadamard_rotate(M: np.ndarray, block: int = 0) -> np.ndarray:
     """M R with R = blockdiag(H_b, ..., H_b) / sqrt(b) over the columns of M
-    (reading R10; [OptRot] abstract and Figure 1: a fixed, fusible rotation
+    (reading R12; [OptRot] abstract and Figure 1: a fixed, fusible rotation
     applied before GPTQ to spread weight outliers).  block <= 0 takes the
     largest power of two dividing the row length (at most 4096)."""
     M = np.asarray(M, dtype=np.float64)
@@ -483,6 +483,6 @@ def hadamard_rotate(M: np.ndarray, block: int = 0) -> np.ndarray:
 
 
 def weight_incoherence(W: np.ndarray) -> float:
-    """mu_W = sqrt(m n) max |W_ij| / ||W||_F (reading R10)."""
+    """mu_W = sqrt(m n) max |W_ij| / ||W||_F (reading R12)."""
     W = np.asarray(W, dtype=np.float64)
     return float(math.sqrt(W.size) * np.max(np.abs(W)) / np.linalg.norm(W))

@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
     L.gptq_dequant_matmul_workspace_bytes.restype = sz
     L.gptq_dequant_matmul.argtypes = [vp, i32, i64, i64, vp, vp, vp, i64, i64, i32, i64, vp, i64, vp, sz, vp]
     L.gptq_dequant_matmul.restype = i32
+    L.gptq_rotate_hadamard.argtypes = [vp, i32, i64, i64, i64, i64, vp]
+    L.gptq_rotate_hadamard.restype = i32
     _lib = L
     return L
 
@@ -250,3 +252,17 @@ def dequant_matmul(X: torch.Tensor, qcodes: torch.Tensor, scales: torch.Tensor, 
                                      _stream(dev))
     _check("gptq_dequant_matmul", st)
     return Y
+
+
+def rotate_hadamard(M: torch.Tensor, block: int = 0) -> torch.Tensor:
+    """M <- M R in place (R block-diagonal Hadamard of order `block`, scaled
+    to be orthogonal; 0 = the largest power of two dividing the row length,
+    at most 4096).  M is [rows, n] fp16/bf16/fp32 with unit column stride.
+    Returns M."""
+    _require(M.is_cuda and M.dim() == 2 and M.stride(1) == 1 and M.dtype in _DT,
+             "M must be a [rows, n] fp16/bf16/fp32 CUDA tensor with unit column stride")
+    rows, n = M.shape
+    st = _load().gptq_rotate_hadamard(M.data_ptr() if rows else None, _DT[M.dtype], rows, n, max(M.stride(0), n),
+                                      int(block), _stream(M.device))
+    _check("gptq_rotate_hadamard", st)
+    return M

@@ -22,6 +22,9 @@ bool dequant_matmul_supported(int bits, int64_t n, int64_t group);
 hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const uint32_t* Q, const float* S,
                           const int32_t* Z, int64_t m, int64_t n, int64_t group, void* Y, int64_t ldy, void* ws,
                           hipStream_t st);
+int rotation_block(int64_t n, int64_t block);
+bool rotation_supported(int64_t n, int64_t block);
+hipError_t rotate_hadamard(void* M, int dt, int64_t rows, int64_t n, int64_t ld, int64_t block, hipStream_t st);
 }  // namespace gptq
 
 namespace {
@@ -118,6 +121,20 @@ gptq_status gptq_dequant_matmul(const void* X, int32_t x_dtype, int64_t tokens, 
   if (need > 0 && (workspace == nullptr || ws_bytes < need)) return GPTQ_ERR_WORKSPACE;
   hipError_t e = gptq::dequant_matmul(X, x_dtype, tokens, ldx, qcodes, scales, zeros, m, n, group_size, Y, ldy,
                                       workspace, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+}
+
+gptq_status gptq_rotate_hadamard(void* M, int32_t dtype, int64_t rows, int64_t n, int64_t ld, int64_t block,
+                                 void* stream) {
+  if (rows < 0 || n < 1 || ld < n || !dtype_ok(dtype) || block < 0) return GPTQ_ERR_INVALID_ARG;
+  if (block > 0 && ((block & (block - 1)) != 0 || n % block != 0)) return GPTQ_ERR_INVALID_ARG;
+  if (rows == 0) return GPTQ_OK;
+  if (M == nullptr) return GPTQ_ERR_INVALID_ARG;
+  const int64_t per16 = dtype == GPTQ_F32 ? 4 : 8;  // elements per 16 bytes
+  if (!gptq::rotation_supported(n, block) || ld % per16 != 0 || ((uintptr_t)M & 15) != 0 ||
+      rows * (n / gptq::rotation_block(n, block)) / (4096 / gptq::rotation_block(n, block)) >= ((int64_t)1 << 31) - 1)
+    return GPTQ_ERR_UNSUPPORTED;
+  hipError_t e = gptq::rotate_hadamard(M, dtype, rows, n, ld, block, (hipStream_t)stream);
   return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
 }
 

@@ -153,3 +153,20 @@ def test_peaks_probe_library():
     assert f(2, None, None, 24, 0, 1, None) == -1   # bytes not a multiple of 16
     assert f(0, None, None, 0, 1, 0, None) == -1    # empty grid
     assert "gptq_peaks_launch" not in open(os.path.join(ROOT, "include", "gptq.h")).read()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(rows=-1), "INVALID"), (dict(n=0), "INVALID"), (dict(ld=100), "INVALID"), (dict(dtype=7), "INVALID"),
+    (dict(block=-1), "INVALID"), (dict(block=48), "INVALID"), (dict(block=2048, n=1024, ld=1024), "INVALID"),
+    (dict(M=None), "INVALID"),
+    (dict(block=8), "UNSUPPORTED"), (dict(n=24, ld=24), "UNSUPPORTED"), (dict(ld=260), "UNSUPPORTED"),
+    (dict(block=8192, n=8192, ld=8192), "UNSUPPORTED"), (dict(M=0x1008), "UNSUPPORTED"),
+    (dict(rows=0, M=None), "OK"),
+])
+def test_rotate_rejects(kw, expect):
+    """Checks made on the host before any launch (no GPU needed)."""
+    a = dict(M=0x1000, dtype=pw.F16, rows=4, n=256, ld=256, block=0)
+    a.update(kw)
+    st = _lib().gptq_rotate_hadamard(a["M"], a["dtype"], a["rows"], a["n"], a["ld"], a["block"], None)
+    want = {"INVALID": pw.GPTQ_ERR_INVALID_ARG, "UNSUPPORTED": pw.GPTQ_ERR_UNSUPPORTED, "OK": pw.GPTQ_OK}[expect]
+    assert st == want, (kw, st)

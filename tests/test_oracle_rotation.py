@@ -1,4 +1,4 @@
-"""Pins of the oracle's fixed rotation (hadamard_rotate, reading R10: the
+"""Pins of the oracle's fixed rotation (hadamard_rotate, reading R12: the
 Sylvester-ordered Hadamard matrix, block-diagonal, scaled to be orthogonal;
 [OptRot] abstract and Figure 1: a fusible rotation applied before GPTQ)."""
 import math
