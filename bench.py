@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "rotate", "peaks"],
                     help="layer: the quantization path (default); w4a16: the packed layer at run time; "
                          "rotate: the Hadamard rotation before GPTQ; peaks: measured attainable MFMA and HBM rates")
+    ap.add_argument("--bits", type=int, default=4, choices=[3, 4], help="code width for --kernel w4a16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_attn_4096x262144_traffic.json"),
                     help="JSON with rocprofv3 FETCH/WRITE bytes per SYRK launch (optional)")
@@ -88,6 +89,23 @@ def cpu_baseline(W16, X16, job, U_gpu):
                       f"{t1 - t0:.2f}/{t2 - t1:.2f}/{t3 - t2:.2f}"}
 
 
+def pack_rows(q, bits: int):
+    """Codes [m x n] (0 <= q < 2^bits) as per-row little-endian bit-streams of
+    uint32 words (code j at bits [bits j, bits j + bits) of the row's stream),
+    the layout gptq_quantize_layer writes; built on the host before timing."""
+    import numpy as np
+    m, n = q.shape
+    W = (n * bits + 31) // 32
+    out = np.zeros((m, W), dtype=np.uint32)
+    for r0 in range(0, m, 2048):
+        qb = q[r0:r0 + 2048].astype(np.uint8)
+        bitsarr = ((qb[:, :, None] >> np.arange(bits, dtype=np.uint8)) & 1).reshape(qb.shape[0], n * bits)
+        pad = np.zeros((qb.shape[0], W * 32 - n * bits), dtype=np.uint8)
+        packed = np.packbits(np.concatenate([bitsarr, pad], axis=1), axis=1, bitorder="little")
+        out[r0:r0 + 2048] = packed.view("<u4")
+    return out
+
+
 def bench_w4a16(args):
     """gptq_dequant_matmul on a 28672 x 8192 4-bit g128 layer (MLP up/gate
     projection shape), one fp16 decode token; synthetic packed layer (codes,
@@ -100,45 +118,43 @@ def bench_w4a16(args):
     import synth
     m, n, T, group = 28672, 8192, 1, 128
     dev = torch.device("cuda:0")
-    q, s, z = synth.packed_layer(m, n, 4, group, seed=7)
-    # pack on the host (4-bit: code j at bits 4 (j % 8) of word j / 8)
-    qq = q.reshape(m, n // 8, 8).astype(np.uint32)
-    words = np.zeros((m, n // 8), dtype=np.uint32)
-    for k in range(8):
-        words |= qq[:, :, k] << np.uint32(4 * k)
+    bits = args.bits
+    q, s, z = synth.packed_layer(m, n, bits, group, seed=7)
+    words = pack_rows(q, bits)
     qw = torch.from_numpy(words.view(np.int32)).to(dev)
     sd, zd = torch.from_numpy(s).to(dev), torch.from_numpy(z).to(dev)
     X = torch.from_numpy(synth.activations(T, n, "f16", seed=8)).to(dev)
     Y = torch.empty((T, m), dtype=torch.float16, device=dev)
     ws = torch.empty(max(pw.dequant_matmul_workspace_bytes(T, m, n), 1), dtype=torch.uint8, device=dev)
     for _ in range(max(args.warmup, 1) * 10):
-        pw.dequant_matmul(X, qw, sd, zd, 4, group, Y=Y, workspace=ws)
+        pw.dequant_matmul(X, qw, sd, zd, bits, group, Y=Y, workspace=ws)
     reps = 20 * args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(reps):
-        pw.dequant_matmul(X, qw, sd, zd, 4, group, Y=Y, workspace=ws)
+        pw.dequant_matmul(X, qw, sd, zd, bits, group, Y=Y, workspace=ws)
     torch.cuda.synchronize()
     us = (time.perf_counter() - t0) * 1e6 / reps
     # the same calls timed with HIP events on the stream the kernels run on
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        pw.dequant_matmul(X, qw, sd, zd, 4, group, Y=Y, workspace=ws)
+        pw.dequant_matmul(X, qw, sd, zd, bits, group, Y=Y, workspace=ws)
     b.record()
     torch.cuda.synchronize()
     us_ev = a.elapsed_time(b) * 1e3 / reps
     G = n // group
-    nbytes = m * n / 2 + 8.0 * m * G + 2.0 * T * n + 2.0 * T * m
+    nbytes = m * n * bits / 8 + 8.0 * m * G + 2.0 * T * n + 2.0 * T * m
     gbs = nbytes / (us * 1e-6) / 1e9
     gbs_ev = nbytes / (us_ev * 1e-6) / 1e9
     res = {
-        "metric": "GB/s of the packed 4-bit layer, W4A16 dequant-matmul (28672x8192 g128, 1 fp16 token)",
+        "metric": f"GB/s of the packed {bits}-bit layer, W{bits}A16 dequant-matmul (28672x8192 g128, 1 fp16 token)",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
         "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp16 x u4 -> fp32 sums", "data": "synthetic",
-        "config": {"workload": f"w4a16 decode: W {m}x{n} 4-bit g{group} packed, X {T}x{n} fp16, Y {T}x{m} fp16",
-                   "tokens": T, "m": m, "n": n, "bits": 4, "group": group, "parallelism": "single GPU"},
+        "dtype": f"fp16 x u{bits} -> fp32 sums", "data": "synthetic",
+        "config": {"workload": f"w{bits}a16 decode: W {m}x{n} {bits}-bit g{group} packed, X {T}x{n} fp16, "
+                               f"Y {T}x{m} fp16",
+                   "tokens": T, "m": m, "n": n, "bits": bits, "group": group, "parallelism": "single GPU"},
         "roofline": {"kernel": "gptq_dequant_matmul: dqmm4_task_kernel + dqmm_reduce_kernel", "bound": "hbm",
                      "achieved": round(gbs_ev, 1), "peak": PEAK_HBM, "unit": "GB/s",
                      "frac": round(gbs_ev / PEAK_HBM, 4), "traffic": None,
@@ -149,7 +165,7 @@ def bench_w4a16(args):
         import oracle as O
         rows = 1024
         t1 = time.perf_counter()
-        O.dequant_matmul(synth.as_float64(X.cpu().numpy(), "f16"), words[:rows], s[:rows], z[:rows], 4, group, n)
+        O.dequant_matmul(synth.as_float64(X.cpu().numpy(), "f16"), words[:rows], s[:rows], z[:rows], bits, group, n)
         dt = time.perf_counter() - t1
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         res["cpu_baseline"] = {"value": round(nbytes / (dt * m / rows) / 1e9, 3),

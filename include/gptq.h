@@ -187,9 +187,9 @@ gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, 
  *   scales     [m x G] float32, zeros [m x G] int32 (G as for
  *              gptq_quantize_layer).
  *   bits, group_size: as passed to gptq_quantize_layer.  This version runs
- *              bits == 4 with n % 32 == 0 and group_size <= 0 (per row) or a
- *              multiple of 128; other valid combinations return
- *              GPTQ_ERR_UNSUPPORTED.
+ *              bits == 4 (any tokens) and bits == 3 (tokens <= 16), with
+ *              n % 32 == 0 and group_size <= 0 (per row) or a multiple of
+ *              128; other valid combinations return GPTQ_ERR_UNSUPPORTED.
  *   Y          [tokens x m] out, leading dimension ldy >= m, type x_dtype.
  *   workspace, ws_bytes: at least gptq_dequant_matmul_workspace_bytes(tokens,
  *              m, n) bytes (0 for shapes that need no partial sums; then

@@ -18,8 +18,8 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
                           int64_t B, uint32_t* qcodes, float* S, int32_t* Z, float* err_sq, int write_dequant,
                           void* ws, hipStream_t st);
 size_t dequant_matmul_workspace_bytes(int64_t tokens, int64_t m, int64_t n);
-bool dequant_matmul_supported(int bits, int64_t n, int64_t group);
-hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const uint32_t* Q, const float* S,
+bool dequant_matmul_supported(int bits, int64_t n, int64_t group, int64_t tokens);
+hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const uint32_t* Q, int bits, const float* S,
                           const int32_t* Z, int64_t m, int64_t n, int64_t group, void* Y, int64_t ldy, void* ws,
                           hipStream_t st);
 int rotation_block(int64_t n, int64_t block);
@@ -114,12 +114,12 @@ gptq_status gptq_dequant_matmul(const void* X, int32_t x_dtype, int64_t tokens, 
   const auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   const int64_t G = group_size > 0 ? (n + group_size - 1) / group_size : 1;
   const int64_t lim = (int64_t)1 << 31;  // byte ranges addressed with 32-bit buffer offsets
-  if (!gptq::dequant_matmul_supported(bits, n, group_size) || ldx % 8 != 0 || !al16(X) || !al16(qcodes) ||
+  if (!gptq::dequant_matmul_supported(bits, n, group_size, tokens) || ldx % 8 != 0 || !al16(X) || !al16(qcodes) ||
       (int64_t)64 * n * 4 >= lim || m * G * 4 >= lim || (int64_t)16 * ldx * 2 >= lim)
     return GPTQ_ERR_UNSUPPORTED;
   const size_t need = gptq::dequant_matmul_workspace_bytes(tokens, m, n);
   if (need > 0 && (workspace == nullptr || ws_bytes < need)) return GPTQ_ERR_WORKSPACE;
-  hipError_t e = gptq::dequant_matmul(X, x_dtype, tokens, ldx, qcodes, scales, zeros, m, n, group_size, Y, ldy,
+  hipError_t e = gptq::dequant_matmul(X, x_dtype, tokens, ldx, qcodes, bits, scales, zeros, m, n, group_size, Y, ldy,
                                       workspace, (hipStream_t)stream);
   return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
 }

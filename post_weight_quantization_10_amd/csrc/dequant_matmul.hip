@@ -6,7 +6,8 @@
 // ends on the same point: the artifact needs a packed INT4 kernel for the
 // target device).
 //
-// How (4-bit codes, fp16 or bf16 activations):
+// How (4-bit codes, and 3-bit codes for up to 16 tokens; fp16 or bf16
+// activations):
 //   * Up to 16 tokens (decode): a workgroup takes 64 rows of W over one K
 //     range of 512 or 1024 columns; each wave requests all of its codes at
 //     once while the workgroup stages X and the group parameters in LDS.
@@ -49,6 +50,7 @@ constexpr int DQ_SLOTS = 512;         // workgroups that fill the GPU (2 per CU)
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 struct DqArgs {
   const void* X;
@@ -232,7 +234,27 @@ __device__ __forceinline__ uint32_t hsub(uint32_t a, uint32_t b) {
 // rows hold: they only reach output columns that are never written.  Columns
 // past n are staged as zeros, so the codes there (another row's, or zeros
 // past the buffer) add nothing.
-template <int DT, bool G128, int KR, int TT>
+// 32 3-bit codes (a little-endian 96-bit stream w0 w1 w2, code c at bit 3c)
+// as four words of eight 4-bit codes (code 8i + k at bits 4k of word i): the
+// layout the 4-bit path unpacks.  Per word, the 24-bit window of its eight
+// codes is spread 3 -> 4 bits in three mask-and-shift steps.
+__device__ __forceinline__ u32x4 spread3(uint32_t w0, uint32_t w1, uint32_t w2) {
+  const uint32_t win[4] = {w0 & 0xFFFFFFu, __builtin_amdgcn_alignbit(w1, w0, 24) & 0xFFFFFFu,
+                           __builtin_amdgcn_alignbit(w2, w1, 16) & 0xFFFFFFu, w2 >> 8};
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = win[i];
+    const uint32_t x = (t & 0xFFFu) | ((t & 0xFFF000u) << 4);         // codes 0-3 | 4-7 at bits 0 | 16, 3 apart
+    const uint32_t y = (x & 0x003F003Fu) | ((x & 0x0FC00FC0u) << 2);  // pairs at bits 0 | 8 | 16 | 24, 3 apart
+    out[i] = (y & 0x07070707u) | ((y & 0x38383838u) << 1);           // 4 apart
+  }
+  return out;
+}
+
+// BITS = 3: each lane's 32 codes of a piece are three words (a 12-byte load)
+// turned into the 4-bit layout by spread3; everything else as for 4 bits.
+template <int DT, bool G128, int KR, int TT, int BITS>
 __global__ __launch_bounds__(256) void dqmm4_task_kernel(DqArgs a) {
   constexpr int NP = KR / 128;     // pieces per range
   constexpr int XP = KR * 2 + 16;  // LDS bytes per staged token row (rows 4 banks apart)
@@ -295,10 +317,16 @@ __global__ __launch_bounds__(256) void dqmm4_task_kernel(DqArgs a) {
   const int64_t rows_here = max<int64_t>(0, min<int64_t>(16, a.m - rw));
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.Q + min<int64_t>(rw, a.m - 1) * a.W), 0, (int)(rows_here * a.W * 4), 0x00020000);
-  const uint32_t qoff = ((uint32_t)l16 * (uint32_t)a.W + (uint32_t)(kb / 8) + 4u * g4) * 4u;
-  u32x4 qv[NP];
+  // a piece is 128 columns: 16 words at 4 bits, 12 at 3; lane quarter g4
+  // takes its 32 columns
+  const uint32_t qoff = ((uint32_t)l16 * (uint32_t)a.W + (uint32_t)(kb * BITS / 32) + (uint32_t)BITS * g4) * 4u;
+  u32x4 qv[BITS == 4 ? NP : 1];
+  u32x3 q3[BITS == 3 ? NP : 1];
 #pragma unroll
-  for (int P = 0; P < NP; ++P) qv[P] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 64u * P, 0, 0);
+  for (int P = 0; P < NP; ++P) {
+    if constexpr (BITS == 4) qv[P] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 64u * P, 0, 0);
+    else q3[P] = __builtin_amdgcn_raw_buffer_load_b96(qrs, qoff + 48u * P, 0, 0);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // 4. stage parameters and X (X's eight columns in pair order)
@@ -334,9 +362,17 @@ __global__ __launch_bounds__(256) void dqmm4_task_kernel(DqArgs a) {
       const uint32_t z = (uint32_t)pz[prA][P];
       zb = MAGIC | z | (z << 16);
     }
+    u32x4 words;
+    if constexpr (BITS == 4) {
+      words = qv[P];
+    } else {
+      const u32x3 c = q3[P];
+      const uint32_t c0 = c.x, c1 = c.y, c2 = c.z;
+      words = spread3(c0, c1, c2);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t w = qv[P][i];
+      const uint32_t w = words[i];
       const uint32_t h0 = hsub<DT>((w & 0x000F000Fu) | MAGIC, zb);
       const uint32_t h1 = hsub<DT>(((w >> 4) & 0x000F000Fu) | MAGIC, zb);
       const uint32_t h2 = hsub<DT>(((w >> 8) & 0x000F000Fu) | MAGIC, zb);
@@ -428,20 +464,25 @@ DqSplit dq_split(int64_t T, int64_t m, int64_t n) {
   return {(int)cdiv(n, kr), kr};
 }
 
-template <int DT, bool G128>
+template <int DT, bool G128, int BITS>
 void launch_task_g(const DqArgs& a, int64_t kr, int64_t T, dim3 grid, hipStream_t st) {
   if (kr == 1024) {
-    if (T <= 4) hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 1024, 4>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 1024, 16>), grid, dim3(256), 0, st, a);
+    if (T <= 4) hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 1024, 4, BITS>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 1024, 16, BITS>), grid, dim3(256), 0, st, a);
   } else {
-    if (T <= 4) hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 512, 4>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 512, 16>), grid, dim3(256), 0, st, a);
+    if (T <= 4) hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 512, 4, BITS>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dqmm4_task_kernel<DT, G128, 512, 16, BITS>), grid, dim3(256), 0, st, a);
   }
 }
 template <int DT>
-void launch_task(const DqArgs& a, bool g128, int64_t kr, int64_t T, dim3 grid, hipStream_t st) {
-  if (g128) launch_task_g<DT, true>(a, kr, T, grid, st);
-  else launch_task_g<DT, false>(a, kr, T, grid, st);
+void launch_task(const DqArgs& a, bool g128, int bits, int64_t kr, int64_t T, dim3 grid, hipStream_t st) {
+  if (bits == 3) {
+    if (g128) launch_task_g<DT, true, 3>(a, kr, T, grid, st);
+    else launch_task_g<DT, false, 3>(a, kr, T, grid, st);
+  } else {
+    if (g128) launch_task_g<DT, true, 4>(a, kr, T, grid, st);
+    else launch_task_g<DT, false, 4>(a, kr, T, grid, st);
+  }
 }
 
 }  // namespace
@@ -452,17 +493,17 @@ size_t dequant_matmul_workspace_bytes(int64_t tokens, int64_t m, int64_t n) {
   return ks > 1 ? (size_t)ks * (size_t)tokens * (size_t)m * 4 : 0;
 }
 
-bool dequant_matmul_supported(int bits, int64_t n, int64_t group) {
-  return bits == 4 && n % 32 == 0 && (group <= 0 || group % 128 == 0);
+bool dequant_matmul_supported(int bits, int64_t n, int64_t group, int64_t tokens) {
+  return (bits == 4 || (bits == 3 && tokens <= 16)) && n % 32 == 0 && (group <= 0 || group % 128 == 0);
 }
 
-hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const uint32_t* Q, const float* S,
+hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const uint32_t* Q, int bits, const float* S,
                           const int32_t* Z, int64_t m, int64_t n, int64_t group, void* Y, int64_t ldy, void* ws,
                           hipStream_t st) {
   if (T == 0) return hipSuccess;
   DqArgs a{};
   a.X = X; a.ldx = ldx; a.T = T;
-  a.Q = Q; a.W = cdiv(n * 4, 32);
+  a.Q = Q; a.W = cdiv(n * bits, 32);
   a.S = S; a.Z = Z; a.group = group; a.G = group > 0 ? cdiv(n, group) : 1;
   a.m = m; a.n = n; a.Y = Y; a.ldy = ldy;
   const DqSplit sp = dq_split(T, m, n);
@@ -470,8 +511,8 @@ hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const u
   a.P = a.KS > 1 ? (float*)ws : nullptr;
   if (T <= 16) {
     const dim3 grid((unsigned)(cdiv(m, 64) * a.KS));
-    if (dt == 0) launch_task<0>(a, group == 128, sp.kr, T, grid, st);
-    else launch_task<1>(a, group == 128, sp.kr, T, grid, st);
+    if (dt == 0) launch_task<0>(a, group == 128, bits, sp.kr, T, grid, st);
+    else launch_task<1>(a, group == 128, bits, sp.kr, T, grid, st);
   } else {
     const dim3 grid((unsigned)cdiv(m, DQ_ROWS), (unsigned)a.KS, (unsigned)cdiv(T, DQ_TOK));
     if (dt == 0) hipLaunchKernelGGL(dqmm4_kernel<0>, grid, dim3(256), 0, st, a);

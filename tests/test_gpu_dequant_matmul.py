@@ -44,9 +44,9 @@ def _layer_dev(q, s, z, bits):
             torch.from_numpy(z).to(DEV), words)
 
 
-def _check(Yg: torch.Tensor, X64, q, s, z, group, n, dt, what):
-    words = O.pack_codes(q, 4)
-    Y = O.dequant_matmul(X64, words, s, z, 4, group, n)
+def _check(Yg: torch.Tensor, X64, q, s, z, group, n, dt, what, bits=4):
+    words = O.pack_codes(q, bits)
+    Y = O.dequant_matmul(X64, words, s, z, bits, group, n)
     Yk = Yg.float().cpu().numpy().astype(np.float64)
     gidx = np.zeros(n, dtype=np.int64) if group <= 0 else np.arange(n) // group
     b = 0.0 if dt == "f16" else 128.0
@@ -79,6 +79,15 @@ DQ_CASES = [
     (2, 8192, 8192, 0, "bf16"),      # 1024-column ranges, one group per row across ranges
     (9, 16320, 4160, 128, "bf16"),   # 1024-column ranges, ragged rows, a 64-column last range and group
 ]
+# 3-bit codes (a per-row bit-stream: codes straddle words), decode sizes only
+DQ3_CASES = [
+    (1, 64, 256, 0, "f16"),
+    (1, 4096, 4096, 0, "f16"),       # the MLP recipe's per-row 3-bit layer shape, one token
+    (4, 11008, 4096, 128, "bf16"),
+    (16, 4096, 11008, 0, "f16"),     # 11008 columns: 344 words per row, a 768-column last range
+    (7, 16320, 4160, 128, "f16"),    # 1024-column ranges, ragged rows, a 64-column last range
+    (2, 8192, 8192, 256, "bf16"),
+]
 
 
 @pytest.mark.parametrize("T,m,n,group,dt", DQ_CASES)
@@ -92,6 +101,18 @@ def test_dequant_matmul_parity(T, m, n, group, dt):
     torch.cuda.synchronize()
     assert Yg.shape == (T, m) and Yg.dtype == (torch.float16 if dt == "f16" else torch.bfloat16)
     _check(Yg, X64, q, s, z, group, n, dt, f"T={T} m={m} n={n} g={group}")
+
+
+@pytest.mark.parametrize("T,m,n,group,dt", DQ3_CASES)
+def test_dequant_matmul_3bit_parity(T, m, n, group, dt):
+    say(f"[dequant_matmul 3-bit] T={T} m={m} n={n} group={group} {dt}")
+    q, s, z = synth.packed_layer(m, n, 3, group, seed=3 * T + m + n)
+    X = synth.activations(T, n, dt, seed=m + 1)
+    X64 = synth.as_float64(X, dt)
+    qw, sd, zd, _ = _layer_dev(q, s, z, 3)
+    Yg = pw.dequant_matmul(_x_dev(X, dt), qw, sd, zd, 3, group)
+    torch.cuda.synchronize()
+    _check(Yg, X64, q, s, z, group, n, dt, f"3-bit T={T} m={m} n={n} g={group}", bits=3)
 
 
 def test_dequant_matmul_strides_and_determinism():
@@ -143,8 +164,12 @@ def test_dequant_matmul_unsupported_on_device():
     z = torch.zeros((8, 1), dtype=torch.int32, device=DEV)
     with pytest.raises(pw.GPTQError):
         pw.dequant_matmul(X[:, :90], torch.zeros((8, 12), dtype=torch.int32, device=DEV), s, z, 4, 0)
-    with pytest.raises(pw.GPTQError):
-        pw.dequant_matmul(X, torch.zeros((8, 9), dtype=torch.int32, device=DEV), s, z, 3, 0)
+    with pytest.raises(pw.GPTQError):  # 3-bit codes: decode batches (up to 16 tokens) only
+        pw.dequant_matmul(torch.zeros((17, 96), dtype=torch.float16, device=DEV),
+                          torch.zeros((8, 9), dtype=torch.int32, device=DEV), s, z, 3, 0)
+    Y3 = pw.dequant_matmul(X, torch.zeros((8, 9), dtype=torch.int32, device=DEV), s, z, 3, 0)
+    torch.cuda.synchronize()
+    assert torch.all(Y3 == 0)
     Y = pw.dequant_matmul(X, qw, s, z, 4, 0)
     torch.cuda.synchronize()
     assert torch.all(Y == 0)
