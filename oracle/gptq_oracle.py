@@ -19,8 +19,12 @@ describe the method.  Short names used in the citations below:
 
 Beyond the per-layer path, dequant_matmul is the runtime consumer of the
 packed layer (weights unpacked and dequantized next to 16-bit activations),
-and hadamard_rotate is the fixed rotation applied before GPTQ that [OptRot]
-uses as its baseline.
+hadamard_rotate is the fixed rotation applied before GPTQ that [OptRot]
+uses as its baseline, and quantize_mlp_stack is the network-level loop
+([GPTQ] "Algorithm GPTQ": one layer at a time, each layer's calibration
+inputs taken from the network as quantized so far; [SOQ] "Calibration for a
+multimodal or VLA backbone": later blocks see activations already changed by
+the earlier quantized blocks).
 
 Readings taken where the pages are silent or disagree (each is also listed in
 the design notes):
@@ -58,6 +62,11 @@ the design notes):
       ([OptRot] Figure 1, "fusible" rotations); H' = 2 X'^T X' = R^T H R.
       Weight incoherence (the quantity [OptRot] Theorem 3.1 bounds the error
       with) is read as mu_W = sqrt(m n) max |W_ij| / ||W||_F.
+  R13 The network the loop runs through is a stack of MLP blocks shaped like
+      a 7B transformer's: x <- x + W_down (silu(W_gate x) * (W_up x)),
+      silu(v) = v / (1 + e^-v); gate and up share one Hessian (same input),
+      down gets its own from the block's hidden activations.  The pages fix
+      neither the block nor normalisation; attention and norms are left out.
 """
 from __future__ import annotations
 
@@ -486,3 +495,45 @@ def weight_incoherence(W: np.ndarray) -> float:
     """mu_W = sqrt(m n) max |W_ij| / ||W||_F (reading R12)."""
     W = np.asarray(W, dtype=np.float64)
     return float(math.sqrt(W.size) * np.max(np.abs(W)) / np.linalg.norm(W))
+
+
+# ----------------------------------------------------------------------------- the network-level loop
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """v / (1 + e^-v) (reading R13)."""
+    v = np.asarray(v, dtype=np.float64)
+    return v / (1.0 + np.exp(-v))
+
+
+def swiglu(G: np.ndarray, Uo: np.ndarray) -> np.ndarray:
+    """silu(G) * Uo, the hidden activations of an MLP block (reading R13)."""
+    return silu(G) * np.asarray(Uo, dtype=np.float64)
+
+
+def quantize_mlp_stack(blocks, X0: np.ndarray, bits: int, group: int, block: int, damp_rel: float):
+    """Quantize a stack of MLP blocks one layer at a time, each layer's
+    calibration inputs computed by the network as quantized so far ([GPTQ]
+    "Algorithm GPTQ"; [SOQ] "Calibration for a multimodal or VLA backbone";
+    the block of reading R13).  blocks: list of (W_gate [f x d], W_up [f x d],
+    W_down [d x f]).  Per block: H from X, gate and up quantized with its
+    factor; A = swiglu(X What_gate^T, X What_up^T); H from A, down quantized;
+    X <- X + A What_down^T.  Returns a list of dicts (the three sweeps' outputs
+    plus the block's inputs X and A) and the final X."""
+    X = np.asarray(X0, dtype=np.float64)
+    out = []
+    for Wg, Wu, Wd in blocks:
+        H = hessian([X])
+        U, info = inverse_cholesky_upper(damp(H, damp_rel)[0])
+        if info:
+            raise ValueError("block input Hessian not positive definite")
+        rg = gptq_quantize(np.asarray(Wg, np.float64), U, bits, group, block)
+        ru = gptq_quantize(np.asarray(Wu, np.float64), U, bits, group, block)
+        A = swiglu(X @ rg["What"].T, X @ ru["What"].T)
+        H2 = hessian([A])
+        U2, info = inverse_cholesky_upper(damp(H2, damp_rel)[0])
+        if info:
+            raise ValueError("hidden-activation Hessian not positive definite")
+        rd = gptq_quantize(np.asarray(Wd, np.float64), U2, bits, group, block)
+        out.append({"gate": rg, "up": ru, "down": rd, "X": X, "A": A, "U": U, "U2": U2})
+        X = X + A @ rd["What"].T
+    return out, X
