@@ -19,6 +19,11 @@ line carries the same keys, with GB/s of the packed layer as the metric.
 calibration activations (262144 x 4096 fp16, one 4096-wide Hadamard block per
 row, in place): the fixed rotation applied before GPTQ; GB/s of HBM traffic.
 
+--kernel stack times the network-level loop (quantize_mlp_stack) over two
+7B-shaped MLP blocks (d 4096, f 11008, 4-bit g128) with 8192 calibration
+tokens: per block, H, factor and sweep for gate/up (shared H) and down, the
+quantized forward through gptq_dequant_matmul, SwiGLU and the residual.
+
 --kernel peaks measures the chip's attainable peaks with kernels that do
 nothing else (libgptq_peaks.so): dense fp16 and fp32 MFMA streams, an HBM
 read stream and an HBM copy; the line gives each beside the published peak.
@@ -49,7 +54,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="attn", choices=["attn", "tiny"])
-    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "rotate", "peaks"],
+    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "rotate", "stack", "peaks"],
                     help="layer: the quantization path (default); w4a16: the packed layer at run time; "
                          "rotate: the Hadamard rotation before GPTQ; peaks: measured attainable MFMA and HBM rates")
     ap.add_argument("--bits", type=int, default=4, choices=[3, 4], help="code width for --kernel w4a16")
@@ -252,6 +257,84 @@ def bench_rotate(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_stack(args):
+    """quantize_mlp_stack over 2 MLP blocks of a 7B shape (d 4096, f 11008,
+    weights N(0, 0.02^2) with 0.1 % x10 outliers, fp16), 8192 calibration
+    tokens of the attention-projection recipe; a step is the whole loop.
+    Phase times from HIP events on the stream, one block traced by hand:
+    hessian (both), prepare (both), sweeps (three), forward (three products,
+    SwiGLU, residual)."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_10_amd as pw
+    import synth
+    d, f, T, L, bits, group, B = 4096, 11008, 8192, 2, 4, 128, 128
+    dev = torch.device("cuda:0")
+    blocks = []
+    for l in range(L):
+        ws = [synth.small_layer(r, c, 16, seed=300 + 3 * l + k, w_dtype="f16", outlier_frac=0.001)[0]
+              for k, (r, c) in enumerate([(f, d), (f, d), (d, f)])]
+        blocks.append(tuple(torch.from_numpy(w).to(dev) for w in ws))
+    X0 = torch.from_numpy(synth.activations(T, d, "f16", seed=301)).to(dev)
+    for _ in range(max(args.warmup, 1)):
+        pw.quantize_mlp_stack(blocks, X0, bits, group, B, 0.01)
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pw.quantize_mlp_stack(blocks, X0, bits, group, B, 0.01)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # phases of one block, HIP events between the same calls quantize_mlp_stack makes
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(9)]
+    Wg, Wu, Wd = blocks[0]
+    X = X0.clone()
+    ev[0].record()
+    H = torch.zeros((d, d), dtype=torch.float32, device=dev)
+    pw.hessian_accumulate(H, X)
+    ev[1].record()
+    U, _, _ = pw.prepare_hinv(H, 0.01)
+    ev[2].record()
+    rg = pw.quantize_layer(Wg.clone(), U, bits, group, B, write_dequant=False)
+    ru = pw.quantize_layer(Wu.clone(), U, bits, group, B, write_dequant=False)
+    ev[3].record()
+    G = pw.dequant_matmul(X, rg["qcodes"], rg["scales"], rg["zeros"], bits, group)
+    Uo = pw.dequant_matmul(X, ru["qcodes"], ru["scales"], ru["zeros"], bits, group)
+    A = pw.swiglu(G, Uo)
+    ev[4].record()
+    H2 = torch.zeros((f, f), dtype=torch.float32, device=dev)
+    pw.hessian_accumulate(H2, A)
+    ev[5].record()
+    U2, _, _ = pw.prepare_hinv(H2, 0.01)
+    ev[6].record()
+    rd = pw.quantize_layer(Wd.clone(), U2, bits, group, B, write_dequant=False)
+    ev[7].record()
+    Y = pw.dequant_matmul(A, rd["qcodes"], rd["scales"], rd["zeros"], bits, group)
+    pw.residual_add(X, Y)
+    ev[8].record()
+    torch.cuda.synchronize()
+    t = [ev[i].elapsed_time(ev[i + 1]) for i in range(8)]
+    phases = {"hessian": round(t[0] + t[4], 3), "prepare": round(t[1] + t[5], 3), "sweeps": round(t[2] + t[6], 3),
+              "forward": round(t[3] + t[7], 3)}
+    fwd_flops = 2.0 * T * d * f * 3
+    fwd_ms = t[3] + t[7]
+    res = {
+        "metric": "ms per 7B-shaped MLP block of the network-level loop (d 4096, f 11008, 8192 tokens, 4-bit g128)",
+        "value": round(ms / L, 3), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 MFMA (H, forward) / fp32", "data": "synthetic",
+        "config": {"workload": f"{L} MLP blocks d {d} f {f}, X0 {T}x{d} fp16, {bits}-bit g{group} B{B}",
+                   "tokens": T, "d": d, "f": f, "blocks": L, "parallelism": "single GPU"},
+        "phases_ms_one_block": phases,
+        "roofline": {"kernel": "gptq_dequant_matmul (many tokens: the LDS-staged kernel), the block's forward products",
+                     "bound": "mfma", "achieved": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2), "peak": PEAK_TF16,
+                     "unit": "TFLOP/s", "frac": round(fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_TF16, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_peaks(args):
     """Attainable peaks, each the best of a few timed launches on the current
     stream (HIP events): MFMA streams of 1024 workgroups x 4 waves, eight
@@ -330,6 +413,9 @@ def main():
         return
     if args.kernel == "rotate":
         bench_rotate(args)
+        return
+    if args.kernel == "stack":
+        bench_stack(args)
         return
     import numpy as np
     import torch

@@ -21,6 +21,10 @@
  *   gptq_rotate_hadamard     M <- M R (block-diagonal Hadamard), applied to
  *                            the weights and the activations alike
  *
+ * and the elementwise steps of the network-level loop over MLP blocks:
+ *
+ *   gptq_swiglu, gptq_residual_add
+ *
  * Sources (web pages describing the method):
  *   [OBQ]    "Part 2: Adaptive Rounding: Optimal Brain Quantizer (OBQ)"
  *   [GPTQ]   "Part 3: Adaptive Rounding: GPTQ"
@@ -232,6 +236,28 @@ gptq_status gptq_dequant_matmul(const void* X, int32_t x_dtype, int64_t tokens, 
  * ---------------------------------------------------------------------- */
 gptq_status gptq_rotate_hadamard(void* M, int32_t dtype, int64_t rows, int64_t n, int64_t ld,
                                  int64_t block, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The network-level loop ("Part 3: Adaptive Rounding: GPTQ", 'Algorithm
+ * GPTQ': one layer at a time, each layer's calibration inputs collected from
+ * the network as quantized so far; [SOQ] 'Calibration for a multimodal or VLA
+ * backbone': later blocks see activations already changed by the earlier
+ * quantized blocks).  Over MLP blocks x <- x + W_down (silu(W_gate x) *
+ * (W_up x)) the products run in gptq_dequant_matmul; these two calls do the
+ * elementwise rest, in fp32 with one rounding to the activations' dtype.
+ *
+ * gptq_swiglu:       A = silu(G) * Uo, silu(v) = v / (1 + e^-v).
+ * gptq_residual_add: X <- X + Y.
+ *   G, Uo, A / X, Y  [tokens x f] (resp. [tokens x d]) device, row-major with
+ *                    the common leading dimension ld >= f (d); dtype
+ *                    GPTQ_F16 or GPTQ_BF16.  A may alias G or Uo.
+ * tokens == 0 is a no-op.  Errors: tokens < 0, f (d) < 1, ld too small,
+ * dtype not 16-bit, NULL pointers (tokens > 0) -> GPTQ_ERR_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_swiglu(const void* G, const void* Uo, void* A, int32_t dtype, int64_t tokens,
+                        int64_t f, int64_t ld, void* stream);
+gptq_status gptq_residual_add(void* X, const void* Y, int32_t dtype, int64_t tokens, int64_t d,
+                              int64_t ld, void* stream);
 
 #ifdef __cplusplus
 }

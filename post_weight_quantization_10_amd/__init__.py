@@ -69,6 +69,10 @@ def _load() -> ctypes.CDLL:
     L.gptq_dequant_matmul.restype = i32
     L.gptq_rotate_hadamard.argtypes = [vp, i32, i64, i64, i64, i64, vp]
     L.gptq_rotate_hadamard.restype = i32
+    L.gptq_swiglu.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp]
+    L.gptq_swiglu.restype = i32
+    L.gptq_residual_add.argtypes = [vp, vp, i32, i64, i64, i64, vp]
+    L.gptq_residual_add.restype = i32
     _lib = L
     return L
 
@@ -266,3 +270,75 @@ def rotate_hadamard(M: torch.Tensor, block: int = 0) -> torch.Tensor:
                                       int(block), _stream(M.device))
     _check("gptq_rotate_hadamard", st)
     return M
+
+
+def _rows16(t: torch.Tensor, name: str):
+    _require(t.is_cuda and t.dim() == 2 and t.stride(1) == 1 and t.dtype in (torch.float16, torch.bfloat16),
+             f"{name} must be a [tokens, width] fp16/bf16 CUDA tensor with unit column stride")
+
+
+def swiglu(G: torch.Tensor, Uo: torch.Tensor, A: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A = silu(G) * Uo (the hidden activations of an MLP block)."""
+    _rows16(G, "G")
+    _require(Uo.shape == G.shape and Uo.dtype == G.dtype and Uo.stride() == G.stride() and Uo.device == G.device,
+             "Uo must match G")
+    if A is None:
+        A = torch.empty_strided(G.shape, G.stride(), dtype=G.dtype, device=G.device)
+    _require(A.shape == G.shape and A.dtype == G.dtype and A.stride() == G.stride(), "A must match G")
+    T, f = G.shape
+    st = _load().gptq_swiglu(G.data_ptr(), Uo.data_ptr(), A.data_ptr(), _DT[G.dtype], T, f, max(G.stride(0), f),
+                             _stream(G.device))
+    _check("gptq_swiglu", st)
+    return A
+
+
+def residual_add(X: torch.Tensor, Y: torch.Tensor) -> torch.Tensor:
+    """X <- X + Y in place; returns X."""
+    _rows16(X, "X")
+    _require(Y.shape == X.shape and Y.dtype == X.dtype and Y.stride() == X.stride() and Y.device == X.device,
+             "Y must match X")
+    T, d = X.shape
+    st = _load().gptq_residual_add(X.data_ptr(), Y.data_ptr(), _DT[X.dtype], T, d, max(X.stride(0), d),
+                                   _stream(X.device))
+    _check("gptq_residual_add", st)
+    return X
+
+
+def quantize_mlp_stack(blocks, X0: torch.Tensor, bits: int = 4, group_size: int = 128, block_size: int = 128,
+                       damp: float = 0.01, keep_inputs: bool = False):
+    """The network-level loop over MLP blocks x <- x + W_down (silu(W_gate x) *
+    (W_up x)): one layer at a time, each layer's calibration inputs computed by
+    the network as quantized so far.  blocks: list of (W_gate [f, d], W_up
+    [f, d], W_down [d, f]) CUDA tensors (fp16/bf16; not modified).  X0:
+    [tokens, d] calibration activations in the same dtype.  Per block: H from
+    X (shared by gate and up), both swept with its factor; G and Uo through
+    gptq_dequant_matmul from the packed codes; A = swiglu(G, Uo); H from A,
+    down swept; X <- X + A What_down^T.  Returns (list of per-block dicts with
+    the three quantize_layer results, plus X, A, G, Uo and Y when keep_inputs),
+    final X)."""
+    X = X0.clone()
+    out = []
+    for Wg, Wu, Wd in blocks:
+        d = X.shape[1]
+        H = torch.zeros((d, d), dtype=torch.float32, device=X.device)
+        hessian_accumulate(H, X)
+        U, _, info = prepare_hinv(H, damp)
+        rg = quantize_layer(Wg.clone(), U, bits, group_size, block_size, write_dequant=False)
+        ru = quantize_layer(Wu.clone(), U, bits, group_size, block_size, write_dequant=False)
+        G = dequant_matmul(X, rg["qcodes"], rg["scales"], rg["zeros"], bits, group_size)
+        Uo = dequant_matmul(X, ru["qcodes"], ru["scales"], ru["zeros"], bits, group_size)
+        A = swiglu(G, Uo)
+        f = A.shape[1]
+        H2 = torch.zeros((f, f), dtype=torch.float32, device=X.device)
+        hessian_accumulate(H2, A)
+        U2, _, info2 = prepare_hinv(H2, damp)
+        rd = quantize_layer(Wd.clone(), U2, bits, group_size, block_size, write_dequant=False)
+        Y = dequant_matmul(A, rd["qcodes"], rd["scales"], rd["zeros"], bits, group_size)
+        if int(info.item()) != 0 or int(info2.item()) != 0:
+            raise GPTQError("gptq_prepare_hinv (a block's Hessian is not positive definite)", GPTQ_ERR_INVALID_ARG)
+        rec = {"gate": rg, "up": ru, "down": rd, "U": U, "U2": U2}
+        if keep_inputs:
+            rec.update({"X": X.clone(), "G": G, "Uo": Uo, "A": A, "Y": Y})
+        X = residual_add(X, Y)
+        out.append(rec)
+    return out, X

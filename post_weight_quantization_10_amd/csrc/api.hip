@@ -25,6 +25,9 @@ hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const u
 int rotation_block(int64_t n, int64_t block);
 bool rotation_supported(int64_t n, int64_t block);
 hipError_t rotate_hadamard(void* M, int dt, int64_t rows, int64_t n, int64_t ld, int64_t block, hipStream_t st);
+hipError_t swiglu(const void* G, const void* U, void* A, int dt, int64_t rows, int64_t cols, int64_t ld,
+                  hipStream_t st);
+hipError_t residual_add(void* X, const void* Y, int dt, int64_t rows, int64_t cols, int64_t ld, hipStream_t st);
 }  // namespace gptq
 
 namespace {
@@ -135,6 +138,25 @@ gptq_status gptq_rotate_hadamard(void* M, int32_t dtype, int64_t rows, int64_t n
       rows * (n / gptq::rotation_block(n, block)) / (4096 / gptq::rotation_block(n, block)) >= ((int64_t)1 << 31) - 1)
     return GPTQ_ERR_UNSUPPORTED;
   hipError_t e = gptq::rotate_hadamard(M, dtype, rows, n, ld, block, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+}
+
+gptq_status gptq_swiglu(const void* G, const void* Uo, void* A, int32_t dtype, int64_t tokens, int64_t f,
+                        int64_t ld, void* stream) {
+  if (tokens < 0 || f < 1 || ld < f || !(dtype == GPTQ_F16 || dtype == GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
+  if (tokens == 0) return GPTQ_OK;
+  if (G == nullptr || Uo == nullptr || A == nullptr || tokens * (ld / f + 1) * f >= ((int64_t)1 << 40))
+    return GPTQ_ERR_INVALID_ARG;
+  hipError_t e = gptq::swiglu(G, Uo, A, dtype, tokens, f, ld, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+}
+
+gptq_status gptq_residual_add(void* X, const void* Y, int32_t dtype, int64_t tokens, int64_t d, int64_t ld,
+                              void* stream) {
+  if (tokens < 0 || d < 1 || ld < d || !(dtype == GPTQ_F16 || dtype == GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
+  if (tokens == 0) return GPTQ_OK;
+  if (X == nullptr || Y == nullptr || tokens * (ld / d + 1) * d >= ((int64_t)1 << 40)) return GPTQ_ERR_INVALID_ARG;
+  hipError_t e = gptq::residual_add(X, Y, dtype, tokens, d, ld, (hipStream_t)stream);
   return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
 }
 

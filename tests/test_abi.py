@@ -170,3 +170,18 @@ def test_rotate_rejects(kw, expect):
     st = _lib().gptq_rotate_hadamard(a["M"], a["dtype"], a["rows"], a["n"], a["ld"], a["block"], None)
     want = {"INVALID": pw.GPTQ_ERR_INVALID_ARG, "UNSUPPORTED": pw.GPTQ_ERR_UNSUPPORTED, "OK": pw.GPTQ_OK}[expect]
     assert st == want, (kw, st)
+
+
+def test_swiglu_and_residual_reject():
+    """Host-side checks of the network loop's elementwise calls (no launch)."""
+    L = _lib()
+    P = 0x1000
+    assert L.gptq_swiglu(P, P, P, pw.F16, -1, 8, 8, None) == pw.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_swiglu(P, P, P, pw.F16, 4, 0, 8, None) == pw.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_swiglu(P, P, P, pw.F16, 4, 16, 8, None) == pw.GPTQ_ERR_INVALID_ARG   # ld < f
+    assert L.gptq_swiglu(P, P, P, pw.F32, 4, 8, 8, None) == pw.GPTQ_ERR_INVALID_ARG   # 16-bit only
+    assert L.gptq_swiglu(None, P, P, pw.F16, 4, 8, 8, None) == pw.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_swiglu(None, None, None, pw.F16, 0, 8, 8, None) == pw.GPTQ_OK         # no tokens
+    assert L.gptq_residual_add(P, P, pw.BF16, 4, 8, 4, None) == pw.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_residual_add(P, None, pw.BF16, 4, 8, 8, None) == pw.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_residual_add(None, None, pw.F16, 0, 8, 8, None) == pw.GPTQ_OK
