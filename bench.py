@@ -327,7 +327,7 @@ def bench_stack(args):
         "config": {"workload": f"{L} MLP blocks d {d} f {f}, X0 {T}x{d} fp16, {bits}-bit g{group} B{B}",
                    "tokens": T, "d": d, "f": f, "blocks": L, "parallelism": "single GPU"},
         "phases_ms_one_block": phases,
-        "roofline": {"kernel": "gptq_dequant_matmul (many tokens: the LDS-staged kernel), the block's forward products",
+        "roofline": {"kernel": "gptq_dequant_matmul (many tokens: dqmm4_gemm_kernel), the block's forward products",
                      "bound": "mfma", "achieved": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2), "peak": PEAK_TF16,
                      "unit": "TFLOP/s", "frac": round(fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_TF16, 4),
                      "traffic": None},

@@ -11,7 +11,10 @@
 //   * Up to 16 tokens (decode): a workgroup takes 64 rows of W over one K
 //     range of 512 or 1024 columns; each wave requests all of its codes at
 //     once while the workgroup stages X and the group parameters in LDS.
-//     More tokens: a workgroup owns 64 rows and up to 64 tokens and walks
+//     More tokens, fp16, at least 128 tiles of 128 tokens x 128 rows: a
+//     GEMM-shaped kernel (X staged in LDS, codes unpacked in registers as the
+//     MFMA's other operand).  Otherwise a workgroup owns 64 rows and up to 64
+//     tokens and walks
 //     512-column slices of K; a wave's codes for a slice (16 rows x 256
 //     bytes) are requested first, 16 bytes per lane; the slice of X goes to
 //     LDS meanwhile.
@@ -413,6 +416,159 @@ __global__ __launch_bounds__(256) void dqmm4_task_kernel(DqArgs a) {
   }
 }
 
+// Many tokens, fp16 activations (prefill and calibration forward passes): a
+// GEMM-shaped workgroup of 128 tokens x 128 rows of W, four waves of 64 x 64
+// (2 x 2 blocks of v_mfma_f32_32x32x16_f16), K in steps of 64 columns.  The
+// A operand is X, staged once per step in LDS (double-buffered, one barrier
+// per step) in the pair order of the unpacked codes; the B operand is the
+// codes themselves, one 8-code word per lane and MFMA step, unpacked in
+// registers to exact fp16 (q - z) with the magic-number subtraction, so every
+// product is exact in fp32.  Lane half g of a wave takes words 4g .. 4g+3 of
+// a row's step (one 16-byte load); MFMA step s sums over words s and 4 + s.
+// Per group, Y += s acc for each output row.  Each code is unpacked once per
+// 128-token tile (the 64-token staged kernel above: once per 64 tokens, and
+// with 16 x 16 MFMA blocks re-reading X from LDS four times as often).
+constexpr int GM = 128, GN = 128, GK = 64;
+constexpr int GXP = GK + 8;  // LDS pitch of a staged X row (halves): 144 bytes
+
+__global__ __launch_bounds__(256, 2) void dqmm4_gemm_kernel(DqArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][GM * GXP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int64_t t0 = (int64_t)blockIdx.x * GM;  // first token of the tile
+  const int64_t r0 = (int64_t)blockIdx.y * GN;  // first row of W
+  constexpr uint32_t MAGIC = 0x64006400u;
+
+  // this lane's two code rows (one per 32-row block of the wave)
+  const int64_t rw = r0 + 64 * wn;
+  const int64_t rows_here = max<int64_t>(0, min<int64_t>(64, a.m - rw));
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.Q + min<int64_t>(rw, a.m - 1) * a.W), 0, (int)(rows_here * a.W * 4), 0x00020000);
+  uint32_t qoff[2];
+  int64_t zrow[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    qoff[nb] = ((uint32_t)(32 * nb + l32) * (uint32_t)a.W + 4u * g) * 4u;
+    zrow[nb] = min<int64_t>(rw + 32 * nb + l32, a.m - 1);
+  }
+  // X staging: thread -> (token tid / 2, 32-column half tid % 2), four words
+  const int xt = tid >> 1, xh = tid & 1;
+  const bool xok = t0 + xt < a.T;
+  const uint16_t* xrow = (const uint16_t*)a.X + (t0 + (xok ? xt : 0)) * a.ldx;
+  auto load_x = [&](int64_t k0, u32x4 (&r)[4]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int64_t c = k0 + 32 * xh + 8 * w;
+      r[w] = (xok && c < a.n) ? *(const u32x4*)(xrow + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_x = [&](int buf, const u32x4 (&r)[4]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32x4 d = r[w];
+      const u32x4 e = {__builtin_amdgcn_perm(d.z, d.x, 0x05040100u), __builtin_amdgcn_perm(d.z, d.x, 0x07060302u),
+                       __builtin_amdgcn_perm(d.w, d.y, 0x05040100u), __builtin_amdgcn_perm(d.w, d.y, 0x07060302u)};
+      *(u32x4*)&xs[buf][xt * GXP + 32 * xh + 8 * w] = e;
+    }
+  };
+  auto load_q = [&](int64_t k0, u32x4 (&q)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      q[nb] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff[nb] + (uint32_t)(k0 / 8) * 4u, 0, 0);
+  };
+
+  f32x16 acc[2][2], tot[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      acc[mb][nb] = zero16();
+      tot[mb][nb] = zero16();
+    }
+  const int64_t nsteps = cdiv(a.n, GK);
+  const int64_t gsteps = a.group > 0 ? a.group / GK : nsteps;  // steps per group (groups are multiples of 128)
+  uint32_t zb[2];
+  float sc[2];
+  auto params = [&](int64_t gi) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t z = (uint32_t)a.Z[zrow[nb] * a.G + gi];
+      zb[nb] = MAGIC | z | (z << 16);
+      sc[nb] = a.S[zrow[nb] * a.G + gi];
+    }
+  };
+
+  u32x4 xr[4], qc[2], qn[2];
+  load_x(0, xr);
+  load_q(0, qc);
+  params(0);
+  store_x(0, xr);
+  __syncthreads();
+  for (int64_t ks = 0; ks < nsteps; ++ks) {
+    const int buf = (int)(ks & 1);
+    const bool more = ks + 1 < nsteps;
+    if (more) {
+      load_x((ks + 1) * GK, xr);
+      load_q((ks + 1) * GK, qn);
+    }
+    const uint16_t* xa = xs[buf] + (64 * wm + l32) * GXP + 32 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 bq[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t w = qc[nb][s];
+        bq[nb] = u32x4{hsub<0>((w & 0x000F000Fu) | MAGIC, zb[nb]), hsub<0>(((w >> 4) & 0x000F000Fu) | MAGIC, zb[nb]),
+                       hsub<0>(((w >> 8) & 0x000F000Fu) | MAGIC, zb[nb]),
+                       hsub<0>(((w >> 12) & 0x000F000Fu) | MAGIC, zb[nb])};
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4 ax = *(const u32x4*)(xa + mb * 32 * GXP + 8 * s);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, ax),
+                                                              __builtin_bit_cast(half8_t, bq[nb]), acc[mb][nb], 0, 0, 0);
+      }
+    }
+    // a group ends after this step: fold its sums in with the scale of each output row
+    if (!more || (ks + 1) % gsteps == 0) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tot[mb][nb][r] = fmaf(sc[nb], acc[mb][nb][r], tot[mb][nb][r]);
+          acc[mb][nb] = zero16();
+        }
+      if (more) params(a.group > 0 ? (ks + 1) / gsteps : 0);
+    }
+    if (more) {
+      store_x(buf ^ 1, xr);
+      qc[0] = qn[0];
+      qc[1] = qn[1];
+    }
+    __syncthreads();
+  }
+
+  // Y[t][r]: MFMA output element r of lane l is token 8(r/4) + 4(l/32) + r%4 of
+  // the block and row l%32; 32 lanes store 32 consecutive rows of one token
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int64_t row = rw + 32 * nb + l32;
+      if (row >= a.m) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t t = t0 + 64 * wm + 32 * mb + mfma32_row(r, lane);
+        if (t < a.T) Elem<0>::store(a.Y, t * a.ldy + row, tot[mb][nb][r]);
+      }
+    }
+}
+
 // Y[t][r] = sum over the K sets of the partials, in set order, in X's dtype.
 // A thread takes four consecutive rows of one token (16-byte loads when m is
 // a multiple of 4), all KS loads in flight at once.
@@ -447,7 +603,8 @@ __global__ __launch_bounds__(256) void dqmm_reduce_kernel(const float* P, int KS
 }
 
 // K sets and the columns of each: the staged kernel for more than 16 tokens
-// (slices of 512), the task kernel for up to 16 (ranges of 512 or 1024)
+// (slices of 512), the task kernel for up to 16 (ranges of 512 or 1024); the
+// GEMM-shaped kernel never cuts K (its partial-sum workspace is unused)
 struct DqSplit {
   int ks;
   int64_t kr;
@@ -513,6 +670,12 @@ hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const u
     const dim3 grid((unsigned)(cdiv(m, 64) * a.KS));
     if (dt == 0) launch_task<0>(a, group == 128, bits, sp.kr, T, grid, st);
     else launch_task<1>(a, group == 128, bits, sp.kr, T, grid, st);
+  } else if (dt == 0 && bits == 4 && cdiv(T, GM) * cdiv(m, GN) >= 128) {
+    // enough 128 x 128 tiles to fill the GPU without cutting K
+    a.KS = 1;
+    a.P = nullptr;
+    const dim3 grid((unsigned)cdiv(T, GM), (unsigned)cdiv(m, GN));
+    hipLaunchKernelGGL(dqmm4_gemm_kernel, grid, dim3(256), 0, st, a);
   } else {
     const dim3 grid((unsigned)cdiv(m, DQ_ROWS), (unsigned)a.KS, (unsigned)cdiv(T, DQ_TOK));
     if (dt == 0) hipLaunchKernelGGL(dqmm4_kernel<0>, grid, dim3(256), 0, st, a);

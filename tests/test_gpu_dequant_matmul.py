@@ -75,6 +75,9 @@ DQ_CASES = [
     (256, 320, 2048, 128, "f16"),
     (1000, 512, 512, 128, "f16"),    # many tokens: no K split
     (3, 11008, 4096, 128, "f16"),    # an MLP up-projection shape
+    (1100, 2100, 1024, 128, "f16"),  # 128 x 128 tiles (GEMM-shaped kernel), ragged tokens and rows
+    (1024, 2048, 1536, 384, "f16"),  # GEMM-shaped: groups of three 128-column pieces
+    (2048, 1024, 992, 0, "f16"),     # GEMM-shaped, one group per row, a 32-column last K step
     (5, 16384, 4096, 128, "f16"),    # 1024-column K ranges, up to 16 staged tokens
     (2, 8192, 8192, 0, "bf16"),      # 1024-column ranges, one group per row across ranges
     (9, 16320, 4160, 128, "bf16"),   # 1024-column ranges, ragged rows, a 64-column last range and group
