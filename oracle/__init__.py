@@ -6,4 +6,4 @@ from .gptq_oracle import (hessian, damp, inverse_cholesky_upper, quant_params, q
                           layer_loss_direct, pack_codes, unpack_codes, packed_words, n_groups,
                           quantize_layer_from_x, boundary_distance, dequant_from, maxq_of, check_schedule, dequant_matmul,
                           hadamard_matrix, hadamard_rotate, default_rotation_block, weight_incoherence,
-                          silu, swiglu, quantize_mlp_stack)
+                          silu, swiglu, quantize_mlp_stack, obq_greedy)

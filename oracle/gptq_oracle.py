@@ -67,6 +67,15 @@ the design notes):
       silu(v) = v / (1 + e^-v); gate and up share one Hessian (same input),
       down gets its own from the block's hidden activations.  The pages fix
       neither the block nor normalisation; attention and norms are left out.
+  R14 OBQ's greedy order ([OBQ] "Greedy Search"; the loss-increase formula
+      there is lost from the text): the score of an unquantized weight p is
+      dL_p = (what_p - w_p)^2 / [H^-1]_pp with what_p its rounding on the grid
+      (OBS's factor 1/2 dropped: it moves no argmin), H^-1 = U^T U from the
+      same upper factor the fixed-order sweep reads, and equal scores go to
+      the smaller column index.  Because the order jumps across groups, every
+      group's (or the row's) grid is fixed once from the ORIGINAL weights,
+      before any compensation (R7 cannot apply: a group has no "first column
+      reached").
 """
 from __future__ import annotations
 
@@ -334,6 +343,111 @@ def gptq_quantize_naive(W: np.ndarray, Hd: np.ndarray, bits: int, group: int) ->
         V[:, p + 1:] += np.outer(delta, Ginv[0, 1:] / Ginv[0, 0])
         V[:, p] += delta
     return {"q": q, "s": S, "z": Z, "V": V}
+
+
+def obq_greedy(W: np.ndarray, U: np.ndarray, bits: int, group: int,
+               follow: Optional[Tuple[Optional[np.ndarray], Optional[np.ndarray], Optional[np.ndarray]]] = None,
+               tie: float = 0.0, order_tie: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """OBQ's greedy-order quantization of each row ([OBQ] "Greedy Search",
+    "The OBS / GPTQ Trick", "Generalized Weight Update"; reading R14).
+
+    Each row runs on its own copy of H^-1 = U^T U.  At every step, among the
+    row's unquantized weights, the one whose rounding adds the least to the
+    proxy loss, dL_p = (what_p - w_p)^2 / [H^-1]_pp, is quantized; the rest
+    move by (what_p - w_p) [H^-1]_{p,rem} / [H^-1]_pp, and the row's H^-1
+    loses weight p by the rank-one downdate H^-1 - H^-1_{:,p} H^-1_{p,:} /
+    [H^-1]_pp.  The grid of every group is fixed from the original row.
+
+    follow = (q_other, z_other, order_other) (each may be None) and tie,
+    order_tie compare against a run in another precision: a rounding or zero
+    point within `tie` steps of a boundary takes the other side's adjacent
+    choice (as in gptq_quantize); at a step where the other side quantized
+    column g and g is still unquantized here, g is taken instead of this run's
+    own pick k when sqrt(dL_g) <= sqrt(dL_k) + order_tie (s_g / sqrt([H^-1]_gg)
+    + s_k / sqrt([H^-1]_kk)), i.e. when the two scores agree to order_tie grid
+    steps in sqrt-loss units.  order_tie defaults to tie.
+
+    Returns q [m x n] int64 codes, s, z [m x G], order [m x n] (column
+    quantized at each step), loss [m] = sum of the chosen dL, What [m x n],
+    followed (decisions taken over that differ from this run's own),
+    order_margin (largest followed sqrt-loss gap in the units above)."""
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    U = np.asarray(U, dtype=np.float64)
+    if U.shape != (n, n):
+        raise ValueError("U must be n x n")
+    Hinv0 = U.T @ U
+    G = n_groups(n, group)
+    gcol = np.zeros(n, dtype=np.int64) if group <= 0 else np.arange(n) // group
+    maxq = maxq_of(bits)
+    S = np.zeros((m, G))
+    Z = np.zeros((m, G))
+    otie = tie if order_tie is None else order_tie
+    fq = fz = fo = None
+    if follow is not None:
+        fq, fz, fo = follow
+    followed = 0
+    margin = 0.0
+    for g in range(G):
+        cols = np.arange(n) if group <= 0 else np.arange(g * group, min((g + 1) * group, n))
+        s, z = quant_params(W[:, cols], bits)
+        if fz is not None:
+            tz = -np.minimum(W[:, cols].min(axis=1), 0.0) / s
+            near = boundary_distance(tz) < tie
+            other = np.asarray(fz)[:, g].astype(np.int64)
+            fl = np.floor(tz).astype(np.int64)
+            ok = near & ((other == fl) | (other == fl + 1)) & (other != z)
+            followed += int(ok.sum())
+            z = np.where(ok, other, z)
+        S[:, g], Z[:, g] = s, z
+    q = np.zeros((m, n), dtype=np.int64)
+    order = np.zeros((m, n), dtype=np.int64)
+    loss = np.zeros(m)
+    for r in range(m):
+        w = W[r].copy()
+        Hi = Hinv0.copy()
+        active = np.ones(n, dtype=bool)
+        sr, zr = S[r, gcol], Z[r, gcol]
+        for step in range(n):
+            idx = np.flatnonzero(active)
+            d = np.diag(Hi)[idx]
+            qc = np.clip(np.rint(w[idx] / sr[idx]) + zr[idx], 0, maxq)
+            err = sr[idx] * (qc - zr[idx]) - w[idx]
+            score = err * err / d
+            k = int(np.argmin(score))           # first minimum: smallest column
+            if fo is not None and active[fo[r, step]]:
+                kg = int(np.searchsorted(idx, fo[r, step]))
+                rho = np.sqrt(score)
+                unit = sr[idx] / np.sqrt(d)
+                gap = (rho[kg] - rho[k]) / (unit[kg] + unit[k])
+                if kg != k and gap <= otie:
+                    followed += 1
+                    margin = max(margin, gap)
+                    k = kg
+            p = int(idx[k])
+            code = int(qc[k])
+            if fq is not None:
+                t = w[p] / sr[p]
+                other = int(fq[r, p])
+                lo_c = int(np.clip(np.floor(t) + zr[p], 0, maxq))
+                hi_c = int(np.clip(np.floor(t) + 1 + zr[p], 0, maxq))
+                if boundary_distance(np.array([t]))[0] < tie and other in (lo_c, hi_c) and other != code:
+                    followed += 1
+                    code = other
+            what = sr[p] * (code - zr[p])
+            delta = what - w[p]
+            loss[r] += delta * delta / Hi[p, p]
+            q[r, p] = code
+            order[r, step] = p
+            rem = active.copy()
+            rem[p] = False
+            w[rem] += delta * Hi[p, rem] / Hi[p, p]
+            w[p] = what
+            Hi = Hi - np.outer(Hi[:, p], Hi[p, :]) / Hi[p, p]
+            active[p] = False
+    What = S[:, gcol] * (q - Z[:, gcol])
+    return {"q": q, "s": S, "z": Z, "order": order, "loss": loss, "What": What, "followed": followed,
+            "order_margin": margin}
 
 
 # ----------------------------------------------------------------------------- comparators and measures
