@@ -24,6 +24,10 @@ row, in place): the fixed rotation applied before GPTQ; GB/s of HBM traffic.
 tokens: per block, H, factor and sweep for gate/up (shared H) and down, the
 quantized forward through gptq_dequant_matmul, SwiGLU and the residual.
 
+--kernel obq times OBQ's greedy-order quantization (gptq_quantize_greedy)
+of a 4096 x n fp16 layer (n = 256 by default, --obq-n), 4-bit: every row
+picks its weights in order of least added loss on its own copy of H^-1.
+
 --kernel peaks measures the chip's attainable peaks with kernels that do
 nothing else (libgptq_peaks.so): dense fp16 and fp32 MFMA streams, an HBM
 read stream and an HBM copy; the line gives each beside the published peak.
@@ -54,10 +58,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="attn", choices=["attn", "tiny"])
-    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "rotate", "stack", "peaks"],
+    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "rotate", "stack", "peaks", "obq"],
                     help="layer: the quantization path (default); w4a16: the packed layer at run time; "
                          "rotate: the Hadamard rotation before GPTQ; peaks: measured attainable MFMA and HBM rates")
     ap.add_argument("--bits", type=int, default=4, choices=[3, 4], help="code width for --kernel w4a16")
+    ap.add_argument("--obq-n", type=int, default=256, help="row length for --kernel obq (m = 4096 rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_attn_4096x262144_traffic.json"),
                     help="JSON with rocprofv3 FETCH/WRITE bytes per SYRK launch (optional)")
@@ -257,6 +262,87 @@ def bench_rotate(args):
     print(json.dumps(res), flush=True)
 
 
+# LDS bandwidth of the chip: 128 bytes per clock per CU, 256 CUs, 2.4 GHz.
+PEAK_LDS = 128 * 256 * 2.4e9 / 1e9  # GB/s
+
+
+def bench_obq(args):
+    """gptq_quantize_greedy (OBQ's greedy order) on a 4096 x n fp16 layer,
+    4-bit g128 (per-row grid when n < 128), against the factor U of a
+    lognormal-input Hessian prepared on the GPU beforehand; a step is one
+    call (H^-1 = U^T U packed, then every row's greedy sweep).  Flops
+    counted per row: the rank-one downdates, sum over R of R (R - 1) (one
+    multiply-add per entry of the (R-1)-triangle) ~ n^3 / 3."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_10_amd as pw
+    import synth
+    m, n, bits = 4096, args.obq_n, 4
+    group = 128 if n >= 128 else 0
+    dev = torch.device("cuda:0")
+    W, X = synth.small_layer(m, n, 4 * 2048, seed=41, law="lognormal", w_dtype="f16", x_dtype="f16",
+                             outlier_channels=2)
+    Wd = torch.from_numpy(W).to(dev)
+    H = torch.zeros((n, n), dtype=torch.float32, device=dev)
+    pw.hessian_accumulate(H, torch.from_numpy(X).to(dev))
+    U, lam, info = pw.prepare_hinv(H, 0.01)
+    torch.cuda.synchronize()
+    if int(info.item()) != 0:
+        raise SystemExit("damped Hessian not positive definite")
+    ws = torch.empty(max(pw.greedy_workspace_bytes(m, n), 1), dtype=torch.uint8, device=dev)
+    out = pw.quantize_greedy(Wd, U, bits, group, workspace=ws)
+    for _ in range(max(args.warmup, 1)):
+        pw.quantize_greedy(Wd, U, bits, group, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    reps = max(args.steps, 1)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        pw.quantize_greedy(Wd, U, bits, group, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        pw.quantize_greedy(Wd, U, bits, group, workspace=ws, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    ms_ev = a.elapsed_time(b) / reps
+    flops = 2.0 * m * sum(R * (R - 1) / 2 for R in range(1, n + 1))
+    tf_ev = flops / (ms_ev * 1e-3) / 1e12
+    lds_bytes = 12.0 / 2.0 * flops  # per downdate entry: read and write it, read c_j (12 B per 2 flops)
+    path = "LDS-resident H^-1" if n <= 280 else "workspace-resident H^-1"
+    res = {
+        "metric": f"ms per layer, OBQ greedy-order quantization ({m}x{n} fp16, 4-bit g{group or n})",
+        "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"OBQ greedy: W {m}x{n} fp16, H from 8192 lognormal-input tokens, "
+                               f"4-bit g{group or n}, {path}",
+                   "m": m, "n": n, "bits": bits, "group": group, "parallelism": "single GPU"},
+        "roofline": {"kernel": "gptq_quantize_greedy: greedy_kernel (+ hinv_pack_kernel)", "bound": "alu",
+                     "achieved": round(tf_ev, 3), "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(tf_ev / 157.3, 4), "traffic": None,
+                     "attainable": {"peak": round(PEAK_LDS * 2 / 12 / 1e3, 2), "unit": "TFLOP/s",
+                                    "frac": round(tf_ev / (PEAK_LDS * 2 / 12 / 1e3), 4),
+                                    "lds_GBps": round(lds_bytes / (ms_ev * 1e-3) / 1e9, 1),
+                                    "source": "LDS bandwidth 128 B/clk/CU x 256 CU x 2.4 GHz, 12 B per 2 flops"}},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        rows = 96
+        Ucpu = U.cpu().numpy().astype(np.float64)
+        t1 = time.perf_counter()
+        O.obq_greedy(W[:rows].astype(np.float64), Ucpu, bits, group)
+        dt = time.perf_counter() - t1
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        res["cpu_baseline"] = {"value": round(dt * m / rows * 1e3, 1), "unit": "ms per layer (estimated from the sample)",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"fp64 oracle obq_greedy of {rows} of {m} rows ({dt:.2f} s), "
+                                         f"scaled x{m / rows:.1f}"}
+    print(json.dumps(res), flush=True)
+
+
 def bench_stack(args):
     """quantize_mlp_stack over 2 MLP blocks of a 7B shape (d 4096, f 11008,
     weights N(0, 0.02^2) with 0.1 % x10 outliers, fp16), 8192 calibration
@@ -416,6 +502,9 @@ def main():
         return
     if args.kernel == "stack":
         bench_stack(args)
+        return
+    if args.kernel == "obq":
+        bench_obq(args)
         return
     import numpy as np
     import torch

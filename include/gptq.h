@@ -11,6 +11,12 @@
  *                            column, compensating later columns from the rows
  *                            of U, and emitting packed codes, scales and zeros
  *
+ * OBQ's greedy-order alternative to the sweep, for small layers:
+ *
+ *   gptq_quantize_greedy     per row, quantize the weight whose rounding adds
+ *                            the least loss, compensate, and downdate that
+ *                            row's own copy of the inverse Hessian
+ *
  * one call that uses the packed result at run time:
  *
  *   gptq_dequant_matmul      Y = X What^T with the packed codes unpacked and
@@ -171,6 +177,46 @@ gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, 
                                 int64_t block_size, uint32_t* qcodes, float* scales,
                                 int32_t* zeros, float* err_sq, int32_t write_dequant,
                                 void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gptq_quantize_greedy: OBQ's greedy-order quantization of W against the
+ * same factor U ([OBQ] "Greedy Search"; "The OBS / GPTQ Trick" for the
+ * rank-one downdate of H^-1; "Generalized Weight Update" for the
+ * compensation).
+ *
+ * Each row runs on its own copy of H^-1 = U^T U.  At every step the row's
+ * unquantized weight with the smallest dL_p = (what_p - w_p)^2 / [H^-1]_pp
+ * (equal scores: the smaller column) is rounded on its group's grid, the other
+ * unquantized weights move by (what_p - w_p) [H^-1]_{p,k} / [H^-1]_pp, and
+ * weight p leaves H^-1 by H^-1 - H^-1_{:,p} H^-1_{p,:} / [H^-1]_pp.  Since
+ * the order jumps across groups, every group's grid (s, z, the quantizer of
+ * gptq_quantize_layer) is taken once from the ORIGINAL row.  Work per row is
+ * about n^3/3 flops against n^2 for the sweep ([OBQ] "Limitations of OBQ"),
+ * so this is for small layers.
+ *
+ *   W          [m x n] weights (read only), leading dimension ldw >= n,
+ *              w_dtype GPTQ_F16 / GPTQ_BF16 / GPTQ_F32.
+ *   U          [n x n] float32 upper factor from gptq_prepare_hinv.
+ *   bits       2..8.  group_size <= 0: one grid per row; else groups of
+ *              group_size columns (the last may be short).
+ *   qcodes, scales, zeros: outputs in the layout of gptq_quantize_layer.
+ *   order      [m x n] int32 out, optional (NULL): the column quantized at
+ *              each step.
+ *   loss       [m] float32 out, optional (NULL): the sum of the chosen dL_p,
+ *              which equals (w - what)^T H_d (w - what) for the row.
+ *   workspace, ws_bytes: at least gptq_quantize_greedy_workspace_bytes(m, n)
+ *              bytes (the packed H^-1, and for n > 280 one packed copy per
+ *              resident workgroup, at most 512).
+ * This version runs n <= 4096 and group_size <= 0 or >= 16; other valid
+ * requests return GPTQ_ERR_UNSUPPORTED.  Bad sizes, bits, dtype or NULL
+ * required pointers -> GPTQ_ERR_INVALID_ARG; short workspace ->
+ * GPTQ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t gptq_quantize_greedy_workspace_bytes(int64_t m, int64_t n);
+gptq_status gptq_quantize_greedy(const void* W, int32_t w_dtype, int64_t m, int64_t n, int64_t ldw,
+                                 const float* U, int32_t bits, int64_t group_size, uint32_t* qcodes,
+                                 float* scales, int32_t* zeros, int32_t* order, float* loss,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * gptq_dequant_matmul: Y = X What^T with What = s (q - z) taken from a packed

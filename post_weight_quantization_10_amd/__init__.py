@@ -73,6 +73,10 @@ def _load() -> ctypes.CDLL:
     L.gptq_swiglu.restype = i32
     L.gptq_residual_add.argtypes = [vp, vp, i32, i64, i64, i64, vp]
     L.gptq_residual_add.restype = i32
+    L.gptq_quantize_greedy_workspace_bytes.argtypes = [i64, i64]
+    L.gptq_quantize_greedy_workspace_bytes.restype = sz
+    L.gptq_quantize_greedy.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gptq_quantize_greedy.restype = i32
     _lib = L
     return L
 
@@ -206,6 +210,43 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, group_size: int,
                                      o["zeros"].data_ptr(), _ptr(o.get("err_sq")) if err_sq else None,
                                      1 if write_dequant else 0, ws.data_ptr(), ws.numel(), _stream(dev))
     _check("gptq_quantize_layer", st)
+    return o
+
+
+def greedy_workspace_bytes(m: int, n: int) -> int:
+    return int(_load().gptq_quantize_greedy_workspace_bytes(m, n))
+
+
+def quantize_greedy(W: torch.Tensor, U: torch.Tensor, bits: int, group_size: int, order: bool = True,
+                    loss: bool = True, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """OBQ's greedy-order quantization of W [m x n] (read only) against the
+    factor U.  Returns {'qcodes', 'scales', 'zeros'} in quantize_layer's
+    layout, plus 'order' [m x n] int32 (column quantized at each step) and
+    'loss' [m] float32 (sum of the chosen loss increases) when asked for."""
+    _require(W.is_cuda and U.is_cuda and W.device == U.device, "W and U must be on the same GPU")
+    _require(W.dim() == 2 and W.stride(1) == 1 and W.dtype in _DT, "W must be [m, n] fp16/bf16/fp32, unit column stride")
+    m, n = W.shape
+    _require(U.shape == (n, n) and U.dtype == torch.float32 and U.is_contiguous(), "U must be contiguous float32 [n, n]")
+    G = n_groups(n, group_size)
+    dev = W.device
+    o = dict(out or {})
+    if "qcodes" not in o:
+        o["qcodes"] = torch.empty((m, packed_words(n, bits)), dtype=torch.int32, device=dev)
+    if "scales" not in o:
+        o["scales"] = torch.empty((m, G), dtype=torch.float32, device=dev)
+    if "zeros" not in o:
+        o["zeros"] = torch.empty((m, G), dtype=torch.int32, device=dev)
+    if order and "order" not in o:
+        o["order"] = torch.empty((m, n), dtype=torch.int32, device=dev)
+    if loss and "loss" not in o:
+        o["loss"] = torch.empty((m,), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else _workspace(greedy_workspace_bytes(m, n), dev)
+    st = _load().gptq_quantize_greedy(W.data_ptr(), _DT[W.dtype], m, n, max(W.stride(0), n), U.data_ptr(), int(bits),
+                                      int(group_size), o["qcodes"].data_ptr(), o["scales"].data_ptr(),
+                                      o["zeros"].data_ptr(), _ptr(o.get("order")) if order else None,
+                                      _ptr(o.get("loss")) if loss else None, ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("gptq_quantize_greedy", st)
     return o
 
 

@@ -28,6 +28,11 @@ hipError_t rotate_hadamard(void* M, int dt, int64_t rows, int64_t n, int64_t ld,
 hipError_t swiglu(const void* G, const void* U, void* A, int dt, int64_t rows, int64_t cols, int64_t ld,
                   hipStream_t st);
 hipError_t residual_add(void* X, const void* Y, int dt, int64_t rows, int64_t cols, int64_t ld, hipStream_t st);
+bool greedy_supported(int64_t n, int64_t group);
+size_t greedy_workspace_bytes(int64_t m, int64_t n);
+hipError_t quantize_greedy(const void* W, int dt, int64_t m, int64_t n, int64_t ldw, const float* U, int bits,
+                           int64_t group, uint32_t* qcodes, float* S, int32_t* Z, int32_t* order, float* loss, void* ws,
+                           hipStream_t st);
 }  // namespace gptq
 
 namespace {
@@ -97,6 +102,21 @@ gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, 
   if (workspace == nullptr || ws_bytes < gptq::quantize_workspace_bytes(m, n, block_size)) return GPTQ_ERR_WORKSPACE;
   hipError_t e = gptq::quantize_layer(W, w_dtype, m, n, ldw, U, bits, group_size, block_size, qcodes, scales, zeros,
                                       err_sq, write_dequant, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+}
+
+size_t gptq_quantize_greedy_workspace_bytes(int64_t m, int64_t n) { return gptq::greedy_workspace_bytes(m, n); }
+
+gptq_status gptq_quantize_greedy(const void* W, int32_t w_dtype, int64_t m, int64_t n, int64_t ldw, const float* U,
+                                 int32_t bits, int64_t group_size, uint32_t* qcodes, float* scales, int32_t* zeros,
+                                 int32_t* order, float* loss, void* workspace, size_t ws_bytes, void* stream) {
+  if (m < 1 || n < 1 || ldw < n || !dtype_ok(w_dtype) || bits < 2 || bits > 8) return GPTQ_ERR_INVALID_ARG;
+  if (W == nullptr || U == nullptr || qcodes == nullptr || scales == nullptr || zeros == nullptr)
+    return GPTQ_ERR_INVALID_ARG;
+  if (!gptq::greedy_supported(n, group_size)) return GPTQ_ERR_UNSUPPORTED;
+  if (workspace == nullptr || ws_bytes < gptq::greedy_workspace_bytes(m, n)) return GPTQ_ERR_WORKSPACE;
+  hipError_t e = gptq::quantize_greedy(W, w_dtype, m, n, ldw, U, bits, group_size, qcodes, scales, zeros, order, loss,
+                                       workspace, (hipStream_t)stream);
   return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
 }
 

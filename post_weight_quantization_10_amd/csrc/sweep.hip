@@ -83,16 +83,6 @@ struct RowOps<4> {
   }
 };
 
-// Quantizer parameters (s, z) from the range [lo, hi] of a group or row:
-// x_lo = min(0, lo), x_hi = max(0, hi) (an all-zero range becomes [0, 1]),
-// s = (x_hi - x_lo) / maxq, z = rint(-x_lo / s).
-__device__ __forceinline__ void qparams(float lo, float hi, int maxq, float& s, float& z) {
-  lo = fminf(lo, 0.f);
-  hi = fmaxf(hi, 0.f);
-  if (hi == lo) { lo = 0.f; hi = 1.f; }
-  s = (hi - lo) / (float)maxq;
-  z = rintf(-lo / s);
-}
 
 struct GroupState {
   float s, inv_s, nz, mz;  // scale, 1/scale, -z, maxq - z

@@ -185,3 +185,35 @@ def test_swiglu_and_residual_reject():
     assert L.gptq_residual_add(P, P, pw.BF16, 4, 8, 4, None) == pw.GPTQ_ERR_INVALID_ARG
     assert L.gptq_residual_add(P, None, pw.BF16, 4, 8, 8, None) == pw.GPTQ_ERR_INVALID_ARG
     assert L.gptq_residual_add(None, None, pw.F16, 0, 8, 8, None) == pw.GPTQ_OK
+
+
+def _greedy(**kw):
+    a = dict(W=FAKE, dt=0, m=64, n=128, ldw=128, U=FAKE, bits=4, g=128, q=FAKE, s=FAKE, z=FAKE, o=None, l=None,
+             ws=FAKE, wsb=BIG)
+    a.update(kw)
+    return _lib().gptq_quantize_greedy(a["W"], a["dt"], a["m"], a["n"], a["ldw"], a["U"], a["bits"], a["g"], a["q"],
+                                       a["s"], a["z"], a["o"], a["l"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(m=0), "INVALID"), (dict(n=0), "INVALID"), (dict(ldw=100), "INVALID"), (dict(dt=7), "INVALID"),
+    (dict(bits=1), "INVALID"), (dict(bits=9), "INVALID"), (dict(W=None), "INVALID"), (dict(U=None), "INVALID"),
+    (dict(q=None), "INVALID"), (dict(s=None), "INVALID"), (dict(z=None), "INVALID"),
+    (dict(g=8), "UNSUPPORTED"), (dict(n=4097, ldw=4097), "UNSUPPORTED"),
+    (dict(ws=None), "WORKSPACE"), (dict(wsb=16), "WORKSPACE"),
+])
+def test_greedy_rejects(kw, expect):
+    """Host-side checks of gptq_quantize_greedy (no launch)."""
+    want = {"INVALID": pw.GPTQ_ERR_INVALID_ARG, "UNSUPPORTED": pw.GPTQ_ERR_UNSUPPORTED,
+            "WORKSPACE": pw.GPTQ_ERR_WORKSPACE}[expect]
+    assert _greedy(**kw) == want, kw
+
+
+def test_greedy_workspace_sizes():
+    tri = lambda n: n * (n + 1) // 2
+    al = lambda f: (f + 63) // 64 * 64
+    assert pw.greedy_workspace_bytes(10, 100) == 4 * al(tri(100))          # H^-1 stays in LDS
+    assert pw.greedy_workspace_bytes(10, 280) == 4 * al(tri(280))
+    assert pw.greedy_workspace_bytes(100, 300) == 4 * al(tri(300)) * 101   # one copy per workgroup
+    assert pw.greedy_workspace_bytes(5000, 300) == 4 * al(tri(300)) * 513  # at most 512 workgroups
+    assert pw.greedy_workspace_bytes(0, 300) == 0
