@@ -311,7 +311,7 @@ def bench_obq(args):
     flops = 2.0 * m * sum(R * (R - 1) / 2 for R in range(1, n + 1))
     tf_ev = flops / (ms_ev * 1e-3) / 1e12
     lds_bytes = 12.0 / 2.0 * flops  # per downdate entry: read and write it, read c_j (12 B per 2 flops)
-    path = "LDS-resident H^-1" if n <= 280 else "workspace-resident H^-1"
+    path = "LDS-resident H^-1" if n <= 272 else "workspace-resident H^-1"
     res = {
         "metric": f"ms per layer, OBQ greedy-order quantization ({m}x{n} fp16, 4-bit g{group or n})",
         "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": reps, "warmup": args.warmup,

@@ -7,7 +7,7 @@
 // Rows pick different weights, so each needs its own H^-1 ([OBQ] "Limitations
 // of OBQ", item 2): here one workgroup owns one row at a time and keeps that
 // row's H^-1 as a packed lower triangle, in LDS for rows of up to NL weights
-// (157 KB of the CU's 160 KB) and in a per-workgroup slice of the workspace
+// (145 KB of the CU's 160 KB) and in a per-workgroup slice of the workspace
 // beyond that.
 //
 // Unquantized weights always occupy positions 0..R-1: after weight p is
@@ -26,26 +26,34 @@
 namespace gptq {
 namespace {
 
-constexpr int GT = 256;     // threads per workgroup (4 waves)
-constexpr int GWV = GT / 64;
-constexpr int NL = 280;     // longest row whose packed H^-1 fits in LDS
+constexpr int NL = 272;     // longest row whose packed H^-1 fits in LDS
 constexpr int NMAX = 4096;  // longest row of the workspace-resident path
 constexpr int GMIN = 16;    // smallest group (bounds the per-group tables)
-constexpr int GRID_G = 512; // workgroups (and workspace slices) of the workspace path
+constexpr int GRID_G = 256; // workgroups (and workspace slices) of the workspace path
+constexpr int NT = 1024;    // threads per workgroup (16 waves)
+constexpr int NW = NT / 64;
+constexpr int RB = 4;       // full rows per downdate batch
 
 __host__ __device__ constexpr int tri(int i) { return i * (i + 1) / 2; }  // start of packed row i
 
+// Floats per packed copy of H^-1: the triangle, then 64 spare entries that
+// lanes past the end of a downdate row read and write instead of branching.
+__host__ __device__ constexpr int64_t slice_floats(int64_t n) { return ((n * (n + 1) / 2 + 64) + 63) & ~(int64_t)63; }
+
 template <int N, int TF>
 struct GreedySmem {
-  float T[TF > 0 ? TF : 1];  // packed lower triangle of the row's H^-1 (LDS path)
-  float w[N];                // current weights by position
-  float c[N];                // the eliminated weight's H^-1 column (downdate vector)
-  int perm[N];               // original column of each position
+  float T[TF > 0 ? TF + 64 : 1];  // packed lower triangle of the row's H^-1 (LDS path)
+  float w[N];                     // current weights by position
+  float c[N];                     // the eliminated weight's H^-1 column (downdate vector)
+  float e2[N];                    // squared rounding error of each position's weight
+  float ps[N], pis[N], pz[N];     // each position's grid: s, 1/s, z
+  int perm[N];                    // original column of each position
+  uint16_t ord[N];                // column quantized at each step
   float gs[N / GMIN + 1], gis[N / GMIN + 1], gz[N / GMIN + 1];  // per-group s, 1/s, z
-  uint64_t rkey[GWV];        // per-wave best candidate
-  float rerr[GWV], rd[GWV];
-  int rcode[GWV];
-  uint8_t code[N];           // chosen codes by original column
+  uint64_t rkey[NW];              // per-wave best candidate
+  float rerr[NW], rd[NW];
+  int rcode[NW];
+  uint8_t code[N];                // chosen codes by original column
 };
 
 struct GreedyArgs {
@@ -72,6 +80,118 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, ROWS, 0xF, false);
+}
+
+// Unsigned minimum over the 64 lanes by DPP (within quads, across each
+// 16-lane row, then row_bcast:15 and row_bcast:31 carry it to lane 63).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<0xB1, 0xF>(v, v));   // quad_perm [1,0,3,2]
+  v = min(v, dpp_u<0x4E, 0xF>(v, v));   // quad_perm [2,3,0,1]
+  v = min(v, dpp_u<0x124, 0xF>(v, v));  // row_ror:4
+  v = min(v, dpp_u<0x128, 0xF>(v, v));  // row_ror:8
+  v = min(v, dpp_u<0x142, 0xA>(v, v));  // row_bcast:15 into rows 1 and 3
+  v = min(v, dpp_u<0x143, 0xC>(v, v));  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Rounding of w on the grid (s, 1/s, z): returns what - w, sets the code.
+__device__ __forceinline__ float round_err(float w, float s, float is, float z, int maxq, int& code) {
+  const float qz = __builtin_amdgcn_fmed3f(rintf(w * is), -z, (float)maxq - z);
+  code = (int)(qz + z);
+  return s * qz - w;
+}
+
+// A score's bit pattern orders like the score for every non-negative value
+// (NaN after +inf); all ones is kept for "no candidate".
+__device__ __forceinline__ uint32_t score_bits(float e2, float d) {
+  return min(__float_as_uint(e2 * __builtin_amdgcn_rcpf(d)), 0xFFFFFFFEu);
+}
+
+// Candidate (score, column, position, H^-1 diagonal) of one lane.
+struct Cand {
+  uint32_t sc;
+  int col, pos;
+  float d;
+  __device__ __forceinline__ void init() {
+    sc = 0xFFFFFFFFu;
+    col = 0xFFFF;
+    pos = 0;
+    d = 1.f;
+  }
+  __device__ __forceinline__ void offer(uint32_t s, int c, int p, float dd) {
+    if (s < sc || (s == sc && c < col)) {
+      sc = s;
+      col = c;
+      pos = p;
+      d = dd;
+    }
+  }
+};
+
+// The wave's smallest (score, column); its lane posts it with the rounding
+// error and code of that position's weight.
+template <typename SM>
+__device__ __forceinline__ void post_wave_best(SM& sm, const Cand& b, int lane, int wv, int maxq) {
+  const uint32_t wmin = wave_min_u32(b.sc);
+  if (wmin == 0xFFFFFFFFu) {
+    if (lane == 0) sm.rkey[wv] = ~0ull;
+    return;
+  }
+  uint64_t tied = __ballot(b.sc == wmin);
+  int wl = __builtin_ctzll(tied);
+  if (tied & (tied - 1)) {  // equal scores: the smallest column
+    int wc = 0x10000;
+    while (tied) {
+      const int l = __builtin_ctzll(tied);
+      tied &= tied - 1;
+      const int cl = __builtin_amdgcn_readlane(b.col, l);
+      if (cl < wc) {
+        wc = cl;
+        wl = l;
+      }
+    }
+  }
+  if (lane == wl) {
+    const int k = b.pos;
+    int code;
+    const float err = round_err(sm.w[k], sm.ps[k], sm.pis[k], sm.pz[k], maxq, code);
+    sm.rkey[wv] = ((uint64_t)b.sc << 32) | ((uint64_t)b.col << 16) | (uint64_t)k;
+    sm.rerr[wv] = err;
+    sm.rd[wv] = b.d;
+    sm.rcode[wv] = code;
+  }
+}
+
+// Smallest of the NW per-wave posts: lanes 0..NW-1 hold one each and a DPP
+// minimum over the 16-lane row finds it; bw receives the posting wave.
+template <typename SM>
+__device__ __forceinline__ uint64_t min_post(SM& sm, int lane, int& bw) {
+  static_assert(NW == 16, "one 16-lane DPP row holds the posts");
+  const uint64_t mine = sm.rkey[lane & (NW - 1)];
+  uint32_t hi = (uint32_t)(mine >> 32), lo = (uint32_t)mine;
+#define GREEDY_MIN_STEP(CTRL)                                                                  \
+  {                                                                                          \
+    const uint32_t oh = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, CTRL, 0xF, 0xF, false);  \
+    const uint32_t ol = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, CTRL, 0xF, 0xF, false);  \
+    const bool take = oh < hi || (oh == hi && ol < lo);                                      \
+    hi = take ? oh : hi;                                                                     \
+    lo = take ? ol : lo;                                                                     \
+  }
+  GREEDY_MIN_STEP(0xB1)   // quad_perm [1,0,3,2]
+  GREEDY_MIN_STEP(0x4E)   // quad_perm [2,3,0,1]
+  GREEDY_MIN_STEP(0x124)  // row_ror:4
+  GREEDY_MIN_STEP(0x128)  // row_ror:8
+#undef GREEDY_MIN_STEP
+  const uint64_t kk = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 0) << 32) |
+                      (uint32_t)__builtin_amdgcn_readlane((int)lo, 0);
+  bw = __builtin_ctzll(__ballot(lane < NW && mine == kk) | (1ull << 63));
+  bw = bw > NW - 1 ? 0 : bw;
+  return kk;
+}
+
 // H^-1 = U^T U (U upper) as a packed lower triangle: Hp[tri(i) + j] for j <= i.
 __global__ __launch_bounds__(256) void hinv_pack_kernel(const float* __restrict__ U, int n, float* __restrict__ Hp) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -85,29 +205,38 @@ __global__ __launch_bounds__(256) void hinv_pack_kernel(const float* __restrict_
   Hp[e] = acc;
 }
 
+// One step is two phases separated by barriers: (1) every thread reads the
+// winner (position p) from the per-wave posts; the other weights are
+// compensated, p is swapped with the last unquantized position, and each
+// moved weight's squared rounding error is refreshed; (2) the rank-one
+// downdate of the leading (R-1)-triangle, in which the lane that updates a
+// diagonal entry also scores that position for the next step.  Lanes that
+// fall past the end of the triangle read and write spare entries instead of
+// branching.
 template <int DT, bool INLDS>
-__global__ __launch_bounds__(GT) void greedy_kernel(GreedyArgs a) {
+__global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
   constexpr int N = INLDS ? NL : NMAX;
   __shared__ __attribute__((aligned(16))) GreedySmem<N, INLDS ? tri(NL) : 0> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n, P = tri(n);
   const int maxq = (1 << a.bits) - 1;
+  const int spare = P + lane;  // where lanes past the end of a row read and write
   float* T;
   if constexpr (INLDS) {
     T = sm.T;
   } else {
-    T = a.Tws + (int64_t)blockIdx.x * (((int64_t)P + 63) & ~(int64_t)63);
+    T = a.Tws + (int64_t)blockIdx.x * slice_floats(n);
   }
 
   for (int64_t row = blockIdx.x; row < a.m; row += gridDim.x) {
-    for (int e = tid; e < P; e += GT) T[e] = a.Hp[e];
-    for (int k = tid; k < n; k += GT) {
+    for (int e = tid; e < P; e += NT) T[e] = a.Hp[e];
+    for (int k = tid; k < n; k += NT) {
       sm.w[k] = Elem<DT>::load(a.W, row * a.ldw + k);
       sm.perm[k] = k;
     }
     __syncthreads();
     // The grid of every group from the original row.
-    for (int g = wv; g < a.G; g += GWV) {
+    for (int g = wv; g < a.G; g += NW) {
       const int c0 = g * a.gsz, c1 = min(n, c0 + a.gsz);
       float lo = INFINITY, hi = -INFINITY;
       for (int c = c0 + lane; c < c1; c += 64) {
@@ -127,118 +256,130 @@ __global__ __launch_bounds__(GT) void greedy_kernel(GreedyArgs a) {
       }
     }
     __syncthreads();
+    // Each position's grid, and the scores of the first step.
+    Cand b;
+    b.init();
+    for (int k = tid; k < n; k += NT) {
+      const int g = k / a.gsz;
+      const float s = sm.gs[g], is = sm.gis[g], z = sm.gz[g];
+      sm.ps[k] = s;
+      sm.pis[k] = is;
+      sm.pz[k] = z;
+      int code;
+      const float err = round_err(sm.w[k], s, is, z, maxq, code);
+      sm.e2[k] = err * err;
+      const float d = T[tri(k) + k];
+      b.offer(score_bits(err * err, d), k, k, d);
+    }
+    post_wave_best(sm, b, lane, wv, maxq);
+    __syncthreads();
 
     double loss = 0.0;
     for (int R = n; R >= 1; --R) {
       const int last = R - 1;
-      // Scores of the unquantized weights; the smallest (score, column) wins.
-      uint64_t best = ~0ull;
-      float berr = 0.f, bd = 1.f;
-      int bcode = 0;
-      for (int k = tid; k < R; k += GT) {
-        const int col = sm.perm[k];
-        const int g = col / a.gsz;
-        const float s = sm.gs[g], z = sm.gz[g];
-        const float wk = sm.w[k];
-        const float qz = __builtin_amdgcn_fmed3f(rintf(wk * sm.gis[g]), -z, (float)maxq - z);
-        const float err = s * qz - wk;
-        const float d = T[tri(k) + k];
-        const float sc = err * err / d;
-        const uint64_t key = ((uint64_t)__float_as_uint(sc) << 32) | ((uint64_t)col << 16) | (uint64_t)k;
-        if (key < best) {
-          best = key;
-          berr = err;
-          bd = d;
-          bcode = (int)(qz + z);
-        }
-      }
-      uint64_t wmin = best;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const uint64_t t = __shfl_xor(wmin, o);
-        wmin = t < wmin ? t : wmin;
-      }
-      if (wmin == ~0ull) {
-        if (lane == 0) sm.rkey[wv] = ~0ull;
-      } else if (best == wmin) {  // the one lane holding the wave's winner
-        sm.rkey[wv] = wmin;
-        sm.rerr[wv] = berr;
-        sm.rd[wv] = bd;
-        sm.rcode[wv] = bcode;
-      }
-      __syncthreads();
-      int bw = 0;
-      uint64_t kk = sm.rkey[0];
-#pragma unroll
-      for (int i = 1; i < GWV; ++i) {
-        const uint64_t t = sm.rkey[i];
-        if (t < kk) {
-          kk = t;
-          bw = i;
-        }
-      }
+      int bw;
+      const uint64_t kk = min_post(sm, lane, bw);
       const int p = (int)(kk & 0xFFFF), colp = (int)((kk >> 16) & 0xFFFF);
       const float err = sm.rerr[bw], d = sm.rd[bw];
       if (tid == 0) {
         sm.code[colp] = (uint8_t)sm.rcode[bw];
-        if (a.order) a.order[row * n + (n - R)] = colp;
+        sm.ord[n - R] = (uint16_t)colp;
         loss += (double)(err * err / d);
       }
       // Compensation w_k += (what_p - w_p) H^-1_pk / H^-1_pp, and the swap of
       // positions p and R-1; c receives the H^-1 column of the eliminated weight.
       const float f = err / d;
-      for (int k = tid; k < R; k += GT) {
+      for (int k = tid; k < R; k += NT) {
         if (k == p) continue;
         const int ipk = p > k ? tri(p) + k : tri(k) + p;
         const float av = T[ipk];
+        int code;
         if (k != last) {
           if (p != last) {
             const int ilk = tri(last) + k;
             T[ipk] = T[ilk];
             T[ilk] = av;
           }
-          sm.w[k] += f * av;
+          const float wn = sm.w[k] + f * av;
+          sm.w[k] = wn;
           sm.c[k] = av;
+          const float e = round_err(wn, sm.ps[k], sm.pis[k], sm.pz[k], maxq, code);
+          sm.e2[k] = e * e;
         } else {  // position p takes over the last unquantized weight
-          sm.w[p] = sm.w[last] + f * av;
+          const float wn = sm.w[last] + f * av;
+          const float s = sm.ps[last], is = sm.pis[last], z = sm.pz[last];
+          sm.w[p] = wn;
           sm.perm[p] = sm.perm[last];
+          sm.ps[p] = s;
+          sm.pis[p] = is;
+          sm.pz[p] = z;
           T[tri(p) + p] = T[tri(last) + last];
           sm.c[p] = av;
+          const float e = round_err(wn, s, is, z, maxq, code);
+          sm.e2[p] = e * e;
         }
       }
       __syncthreads();
-      // Rank-one downdate of the leading (R-1)-triangle.  Rows r and R-2-r
-      // are paired (r + 1 and R-1-r entries, R in all) and one wave sweeps a
-      // pair with its lanes.
+      if (R == 1) break;
+      // Rank-one downdate of the leading (R-1)-triangle.  Lanes take columns
+      // (64 at a time), waves take rows round robin; the lane whose column
+      // meets the diagonal also scores that position for the next step.
       const int Rr = last;
       const float dinv = 1.f / d;
-      const int npair = (Rr + 1) / 2;
-      for (int r = wv; r < npair; r += GWV) {
-        const int r2 = Rr - 1 - r;
-        const int len = r == r2 ? r + 1 : Rr + 1;
-        const float cr = sm.c[r] * dinv, cr2 = sm.c[r2] * dinv;
-        const int b1 = tri(r), b2 = tri(r2) - r - 1;
-        for (int x0 = 0; x0 < len; x0 += 256) {
-          float tv[4], cv[4];
+      b.init();
+      for (int j0 = 0; j0 < Rr; j0 += 64) {
+        const int j = j0 + lane;
+        const bool jok = j < Rr;
+        const int jc = jok ? j : 0;
+        const float cj = sm.c[jc] * dinv;
+        const float e2j = sm.e2[jc];
+        const int pj = sm.perm[jc];
+        // Rows j0..j0+63 cross the diagonal (4 per wave): lanes right of it,
+        // and rows past the end, use the spare entries.
+        float dj = 0.f;  // new diagonal entry of column j, if this wave owns row j
+        {
+          float tv[4], ci[4];
           int ev[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int x = x0 + lane + 64 * u;
-            const bool first = x <= r;
-            const int j = first ? x : x - r - 1;
-            ev[u] = x < len ? (first ? b1 : b2) + x : -1;
-            cv[u] = x < len ? sm.c[j] * (first ? cr : cr2) : 0.f;
-            tv[u] = x < len ? T[ev[u]] : 0.f;
+            const int ii = j0 + wv + u * NW;
+            const bool ok = ii < Rr;
+            ci[u] = sm.c[ok ? ii : 0];
+            ev[u] = ok && j <= ii ? tri(ii) + j : spare;  // j <= ii < Rr: inside the triangle
+            tv[u] = T[ev[u]];
           }
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (ev[u] >= 0) T[ev[u]] = tv[u] - cv[u];
+          for (int u = 0; u < 4; ++u) {
+            const float nv = tv[u] - ci[u] * cj;
+            T[ev[u]] = nv;
+            dj = j == j0 + wv + u * NW ? nv : dj;
+          }
         }
+        // Full rows below: every lane is inside the triangle.
+        int i = j0 + 64 + wv;
+        for (; i + (RB - 1) * NW < Rr; i += RB * NW) {
+          float tv[RB], ci[RB];
+          int ev[RB];
+#pragma unroll
+          for (int u = 0; u < RB; ++u) {
+            ci[u] = sm.c[i + u * NW];
+            ev[u] = tri(i + u * NW) + j;
+            tv[u] = T[ev[u]];
+          }
+#pragma unroll
+          for (int u = 0; u < RB; ++u) T[ev[u]] = tv[u] - ci[u] * cj;
+        }
+        for (; i < Rr; i += NW) {
+          const int e = tri(i) + j;
+          T[e] = T[e] - sm.c[i] * cj;
+        }
+        if (jok && ((j - j0) & (NW - 1)) == wv) b.offer(score_bits(e2j, dj), pj, j, dj);
       }
+      post_wave_best(sm, b, lane, wv, maxq);
       __syncthreads();
     }
 
-    for (int wd = tid; wd < a.words; wd += GT) {
+    for (int wd = tid; wd < a.words; wd += NT) {
       const int b0 = wd * 32;
       const int j0 = b0 / a.bits, j1 = min(n - 1, (b0 + 31) / a.bits);
       uint64_t acc = 0;
@@ -249,21 +390,21 @@ __global__ __launch_bounds__(GT) void greedy_kernel(GreedyArgs a) {
       }
       a.Q[row * a.words + wd] = (uint32_t)acc;
     }
+    if (a.order)
+      for (int k = tid; k < n; k += NT) a.order[row * n + k] = sm.ord[k];
     if (tid == 0 && a.loss) a.loss[row] = (float)loss;
     __syncthreads();
   }
 }
 
-int64_t slice_floats(int64_t n) { return ((int64_t)tri((int)n) + 63) & ~(int64_t)63; }
-
 template <int DT>
 void launch_greedy(const GreedyArgs& a, hipStream_t st) {
   if (a.n <= NL) {
     const int grid = (int)std::min<int64_t>(a.m, 65535);
-    hipLaunchKernelGGL((greedy_kernel<DT, true>), dim3(grid), dim3(GT), 0, st, a);
+    hipLaunchKernelGGL((greedy_kernel<DT, true>), dim3(grid), dim3(NT), 0, st, a);
   } else {
     const int grid = (int)std::min<int64_t>(a.m, GRID_G);
-    hipLaunchKernelGGL((greedy_kernel<DT, false>), dim3(grid), dim3(GT), 0, st, a);
+    hipLaunchKernelGGL((greedy_kernel<DT, false>), dim3(grid), dim3(NT), 0, st, a);
   }
 }
 
