@@ -108,6 +108,24 @@ def test_greedy_resident_workgroups_take_every_row(m, n, rows):
     greedy_check(g, Wd, U32, Hd, 4, 0, rows, f"{m}x{n}")
 
 
+def test_greedy_bench_layer_sampled_rows():
+    """The layer `bench.py --kernel obq` times (4096 x 256 fp16, 4-bit g128,
+    H from 8192 lognormal-input fp16 tokens with two outlier channels), in the
+    same launch configuration, checked on sampled rows."""
+    m, n = 4096, 256
+    W, X = synth.small_layer(m, n, 4 * 2048, seed=41, law="lognormal", w_dtype="f16", x_dtype="f16",
+                             outlier_channels=2)
+    Hd, _ = O.damp(O.hessian([synth.as_float64(X, "f16")]), 0.01)
+    U_ref, info = O.inverse_cholesky_upper(Hd)
+    assert info == 0
+    U32 = U_ref.astype(np.float32)
+    g = run_gpu(W, "f16", U32, 4, 128)
+    assert np.all(np.sort(g["order"], axis=1) == np.arange(n)), "some row was not swept"
+    rows = [0, 1, 255, 256, 2047, 4094, 4095]
+    say(f"[greedy] bench layer {m}x{n}, sampled rows {rows}")
+    greedy_check(g, synth.as_float64(W, "f16"), U32, Hd, 4, 128, rows, f"{m}x{n}")
+
+
 def test_greedy_equals_rtn_for_identity_hessian():
     """U = I: nothing moves, so the codes are round-to-nearest of the original
     row (exact: the same fp32 products decide both sides up to near-ties)."""
