@@ -7,8 +7,9 @@
 // Rows pick different weights, so each needs its own H^-1 ([OBQ] "Limitations
 // of OBQ", item 2): here one workgroup owns one row at a time and keeps that
 // row's H^-1 as a packed lower triangle, in LDS for rows of up to NL weights
-// (145 KB of the CU's 160 KB) and in a per-workgroup slice of the workspace
-// beyond that.
+// (145 KB of the CU's 160 KB; rows of up to NS weights use 33 KB and four
+// workgroups share a CU) and in a per-workgroup slice of the workspace beyond
+// that.
 //
 // Unquantized weights always occupy positions 0..R-1: after weight p is
 // chosen it is swapped with position R-1 (row and column of the triangle,
@@ -27,12 +28,20 @@ namespace gptq {
 namespace {
 
 constexpr int NL = 272;     // longest row whose packed H^-1 fits in LDS
+constexpr int NS = 128;     // longest row of the small LDS variant (four workgroups per CU)
 constexpr int NMAX = 4096;  // longest row of the workspace-resident path
 constexpr int GMIN = 16;    // smallest group (bounds the per-group tables)
 constexpr int GRID_G = 256; // workgroups (and workspace slices) of the workspace path
-constexpr int NT = 1024;    // threads per workgroup (16 waves)
-constexpr int NW = NT / 64;
 constexpr int RB = 4;       // full rows per downdate batch
+
+// The three variants: H^-1 in LDS for n <= NS (256 threads, four rows per
+// CU at once), in LDS for n <= NL (1024 threads, one row per CU), in the
+// workspace beyond (1024 threads).
+enum { V_SMALL = 0, V_LDS = 1, V_WS = 2 };
+template <int V> struct Var;
+template <> struct Var<V_SMALL> { static constexpr int N = NS, NT = 256, TF = NS * (NS + 1) / 2; };
+template <> struct Var<V_LDS> { static constexpr int N = NL, NT = 1024, TF = NL * (NL + 1) / 2; };
+template <> struct Var<V_WS> { static constexpr int N = NMAX, NT = 1024, TF = 0; };
 
 __host__ __device__ constexpr int tri(int i) { return i * (i + 1) / 2; }  // start of packed row i
 
@@ -40,7 +49,7 @@ __host__ __device__ constexpr int tri(int i) { return i * (i + 1) / 2; }  // sta
 // lanes past the end of a downdate row read and write instead of branching.
 __host__ __device__ constexpr int64_t slice_floats(int64_t n) { return ((n * (n + 1) / 2 + 64) + 63) & ~(int64_t)63; }
 
-template <int N, int TF>
+template <int N, int TF, int NW>
 struct GreedySmem {
   float T[TF > 0 ? TF + 64 : 1];  // packed lower triangle of the row's H^-1 (LDS path)
   float w[N];                     // current weights by position
@@ -165,11 +174,12 @@ __device__ __forceinline__ void post_wave_best(SM& sm, const Cand& b, int lane, 
   }
 }
 
-// Smallest of the NW per-wave posts: lanes 0..NW-1 hold one each and a DPP
-// minimum over the 16-lane row finds it; bw receives the posting wave.
-template <typename SM>
+// Smallest of the NW per-wave posts: every 16-lane row holds them (repeated
+// when NW < 16) and a DPP minimum over the row finds it; bw receives the
+// posting wave.
+template <int NW, typename SM>
 __device__ __forceinline__ uint64_t min_post(SM& sm, int lane, int& bw) {
-  static_assert(NW == 16, "one 16-lane DPP row holds the posts");
+  static_assert(NW == 4 || NW == 8 || NW == 16, "the posts fit one 16-lane DPP row");
   const uint64_t mine = sm.rkey[lane & (NW - 1)];
   uint32_t hi = (uint32_t)(mine >> 32), lo = (uint32_t)mine;
 #define GREEDY_MIN_STEP(CTRL)                                                                  \
@@ -180,10 +190,10 @@ __device__ __forceinline__ uint64_t min_post(SM& sm, int lane, int& bw) {
     hi = take ? oh : hi;                                                                     \
     lo = take ? ol : lo;                                                                     \
   }
-  GREEDY_MIN_STEP(0xB1)   // quad_perm [1,0,3,2]
-  GREEDY_MIN_STEP(0x4E)   // quad_perm [2,3,0,1]
-  GREEDY_MIN_STEP(0x124)  // row_ror:4
-  GREEDY_MIN_STEP(0x128)  // row_ror:8
+  GREEDY_MIN_STEP(0xB1)                 // quad_perm [1,0,3,2]
+  GREEDY_MIN_STEP(0x4E)                 // quad_perm [2,3,0,1]
+  if constexpr (NW >= 8) GREEDY_MIN_STEP(0x124)   // row_ror:4
+  if constexpr (NW >= 16) GREEDY_MIN_STEP(0x128)  // row_ror:8
 #undef GREEDY_MIN_STEP
   const uint64_t kk = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 0) << 32) |
                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 0);
@@ -213,10 +223,11 @@ __global__ __launch_bounds__(256) void hinv_pack_kernel(const float* __restrict_
 // diagonal entry also scores that position for the next step.  Lanes that
 // fall past the end of the triangle read and write spare entries instead of
 // branching.
-template <int DT, bool INLDS>
-__global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
-  constexpr int N = INLDS ? NL : NMAX;
-  __shared__ __attribute__((aligned(16))) GreedySmem<N, INLDS ? tri(NL) : 0> sm;
+template <int DT, int V>
+__global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
+  constexpr int N = Var<V>::N, NT = Var<V>::NT, NW = NT / 64;
+  constexpr bool INLDS = V != V_WS;
+  __shared__ __attribute__((aligned(16))) GreedySmem<N, Var<V>::TF, NW> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n, P = tri(n);
   const int maxq = (1 << a.bits) - 1;
@@ -278,7 +289,7 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     for (int R = n; R >= 1; --R) {
       const int last = R - 1;
       int bw;
-      const uint64_t kk = min_post(sm, lane, bw);
+      const uint64_t kk = min_post<NW>(sm, lane, bw);
       const int p = (int)(kk & 0xFFFF), colp = (int)((kk >> 16) & 0xFFFF);
       const float err = sm.rerr[bw], d = sm.rd[bw];
       if (tid == 0) {
@@ -334,15 +345,16 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
         const float cj = sm.c[jc] * dinv;
         const float e2j = sm.e2[jc];
         const int pj = sm.perm[jc];
-        // Rows j0..j0+63 cross the diagonal (4 per wave): lanes right of it,
-        // and rows past the end, use the spare entries.
+        // Rows j0..j0+63 cross the diagonal (64 / NW per wave, 4 at a time):
+        // lanes right of it, and rows past the end, use the spare entries.
         float dj = 0.f;  // new diagonal entry of column j, if this wave owns row j
-        {
+#pragma unroll
+        for (int ub = 0; ub < 64 / NW; ub += 4) {
           float tv[4], ci[4];
           int ev[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int ii = j0 + wv + u * NW;
+            const int ii = j0 + wv + (ub + u) * NW;
             const bool ok = ii < Rr;
             ci[u] = sm.c[ok ? ii : 0];
             ev[u] = ok && j <= ii ? tri(ii) + j : spare;  // j <= ii < Rr: inside the triangle
@@ -352,7 +364,7 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
           for (int u = 0; u < 4; ++u) {
             const float nv = tv[u] - ci[u] * cj;
             T[ev[u]] = nv;
-            dj = j == j0 + wv + u * NW ? nv : dj;
+            dj = j == j0 + wv + (ub + u) * NW ? nv : dj;
           }
         }
         // Full rows below: every lane is inside the triangle.
@@ -399,13 +411,13 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
 
 template <int DT>
 void launch_greedy(const GreedyArgs& a, hipStream_t st) {
-  if (a.n <= NL) {
-    const int grid = (int)std::min<int64_t>(a.m, 65535);
-    hipLaunchKernelGGL((greedy_kernel<DT, true>), dim3(grid), dim3(NT), 0, st, a);
-  } else {
-    const int grid = (int)std::min<int64_t>(a.m, GRID_G);
-    hipLaunchKernelGGL((greedy_kernel<DT, false>), dim3(grid), dim3(NT), 0, st, a);
-  }
+  const int grid = (int)std::min<int64_t>(a.m, a.n <= NL ? 65535 : GRID_G);
+  if (a.n <= NS)
+    hipLaunchKernelGGL((greedy_kernel<DT, V_SMALL>), dim3(grid), dim3(Var<V_SMALL>::NT), 0, st, a);
+  else if (a.n <= NL)
+    hipLaunchKernelGGL((greedy_kernel<DT, V_LDS>), dim3(grid), dim3(Var<V_LDS>::NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((greedy_kernel<DT, V_WS>), dim3(grid), dim3(Var<V_WS>::NT), 0, st, a);
 }
 
 }  // namespace
