@@ -64,7 +64,7 @@ extern "C" {
 typedef enum {
   GPTQ_OK = 0,
   GPTQ_ERR_INVALID_ARG = 1,  /* bad size, pointer, dtype, bits, group/block */
-  GPTQ_ERR_UNSUPPORTED = 2,  /* valid request this build cannot run        */
+  GPTQ_ERR_UNSUPPORTED = 2,  /* valid request this library does not run    */
   GPTQ_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required     */
   GPTQ_ERR_HIP = 4           /* a HIP launch or runtime call failed         */
 } gptq_status;
