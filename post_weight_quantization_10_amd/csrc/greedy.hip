@@ -142,8 +142,8 @@ struct Cand {
 
 // The wave's smallest (score, column); its lane posts it with the rounding
 // error and code of that position's weight.
-template <typename SM>
-__device__ __forceinline__ void post_wave_best(SM& sm, const Cand& b, int lane, int wv, int maxq) {
+template <typename SM, typename ErrF>
+__device__ __forceinline__ void post_wave_best(SM& sm, const Cand& b, int lane, int wv, ErrF errf) {
   const uint32_t wmin = wave_min_u32(b.sc);
   if (wmin == 0xFFFFFFFFu) {
     if (lane == 0) sm.rkey[wv] = ~0ull;
@@ -166,7 +166,7 @@ __device__ __forceinline__ void post_wave_best(SM& sm, const Cand& b, int lane, 
   if (lane == wl) {
     const int k = b.pos;
     int code;
-    const float err = round_err(sm.w[k], sm.ps[k], sm.pis[k], sm.pz[k], maxq, code);
+    const float err = errf(k, code);
     sm.rkey[wv] = ((uint64_t)b.sc << 32) | ((uint64_t)b.col << 16) | (uint64_t)k;
     sm.rerr[wv] = err;
     sm.rd[wv] = b.d;
@@ -238,6 +238,7 @@ __global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
   } else {
     T = a.Tws + (int64_t)blockIdx.x * slice_floats(n);
   }
+  auto errf = [&](int k, int& code) { return round_err(sm.w[k], sm.ps[k], sm.pis[k], sm.pz[k], maxq, code); };
 
   for (int64_t row = blockIdx.x; row < a.m; row += gridDim.x) {
     for (int e = tid; e < P; e += NT) T[e] = a.Hp[e];
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
       const float d = T[tri(k) + k];
       b.offer(score_bits(err * err, d), k, k, d);
     }
-    post_wave_best(sm, b, lane, wv, maxq);
+    post_wave_best(sm, b, lane, wv, errf);
     __syncthreads();
 
     double loss = 0.0;
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
         }
         if (jok && ((j - j0) & (NW - 1)) == wv) b.offer(score_bits(e2j, dj), pj, j, dj);
       }
-      post_wave_best(sm, b, lane, wv, maxq);
+      post_wave_best(sm, b, lane, wv, errf);
       __syncthreads();
     }
 
@@ -409,6 +410,224 @@ __global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
   }
 }
 
+// Rows of NL < n <= NLZ weights keep H^-1 in the workspace, and the
+// rank-one downdates are deferred: the true H^-1 is the stored base minus
+// sum_t c_t c_t^T / d_t over the (at most KD) most recent eliminations,
+// whose columns c_t sit in LDS.  A step needs only the true row of the
+// chosen weight (base row minus the deferred terms) and the diagonal, which
+// is kept current in LDS; every KD steps the deferred columns are folded
+// into the base by one rank-KD update, so the base is read and written once
+// per KD steps instead of every step.  Positions are swapped as in
+// greedy_kernel: in the base, the deferred columns and the diagonal alike.
+constexpr int NLZ = 1024;  // longest row of the deferred-downdate path
+constexpr int KD = 8;      // downdates deferred per base update
+
+template <int N>
+struct LazySmem {
+  float w[N];         // current weights by position
+  float e2[N];        // squared rounding error of each position's weight
+  float dg[N];        // diagonal of the true H^-1 by position
+  float C[KD][N];     // deferred columns of H^-1 by position
+  float cdv[KD];      // 1 / d of each deferred column
+  int perm[N];        // original column of each position
+  uint16_t gpos[N];   // group of each position's weight
+  uint16_t ord[N];    // column quantized at each step
+  float gs[N / GMIN + 1], gis[N / GMIN + 1], gz[N / GMIN + 1];
+  uint64_t rkey[16];
+  float rerr[16], rd[16];
+  int rcode[16];
+  uint8_t code[N];    // chosen codes by original column
+};
+
+template <int DT>
+__global__ __launch_bounds__(1024) void greedy_lazy_kernel(GreedyArgs a) {
+  constexpr int N = NLZ, NT = 1024, NW = 16;
+  static_assert(N <= NT, "one position per thread");
+  __shared__ __attribute__((aligned(16))) LazySmem<N> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = a.n, P = tri(n);
+  const int maxq = (1 << a.bits) - 1;
+  const int spare = P + lane;
+  float* T = a.Tws + (int64_t)blockIdx.x * slice_floats(n);
+  auto errf = [&](int k, int& code) {
+    const int g = sm.gpos[k];
+    return round_err(sm.w[k], sm.gs[g], sm.gis[g], sm.gz[g], maxq, code);
+  };
+  const int j = tid;  // this thread's position
+
+  for (int64_t row = blockIdx.x; row < a.m; row += gridDim.x) {
+    for (int e = tid; e < P; e += NT) T[e] = a.Hp[e];
+    if (j < n) {
+      sm.w[j] = Elem<DT>::load(a.W, row * a.ldw + j);
+      sm.perm[j] = j;
+    }
+    __syncthreads();
+    for (int g = wv; g < a.G; g += NW) {
+      const int c0 = g * a.gsz, c1 = min(n, c0 + a.gsz);
+      float lo = INFINITY, hi = -INFINITY;
+      for (int c = c0 + lane; c < c1; c += 64) {
+        lo = fminf(lo, sm.w[c]);
+        hi = fmaxf(hi, sm.w[c]);
+      }
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+      float s, z;
+      qparams(lo, hi, maxq, s, z);
+      if (lane == 0) {
+        sm.gs[g] = s;
+        sm.gis[g] = 1.f / s;
+        sm.gz[g] = z;
+        a.S[row * a.G + g] = s;
+        a.Z[row * a.G + g] = (int32_t)z;
+      }
+    }
+    __syncthreads();
+    Cand b;
+    b.init();
+    if (j < n) {
+      sm.gpos[j] = (uint16_t)(j / a.gsz);
+      int code;
+      const float err = errf(j, code);
+      sm.e2[j] = err * err;
+      const float d = T[tri(j) + j];
+      sm.dg[j] = d;
+      b.offer(score_bits(err * err, d), j, j, d);
+    }
+    post_wave_best(sm, b, lane, wv, errf);
+    __syncthreads();
+
+    double loss = 0.0;
+    int kd = 0;  // deferred columns
+    for (int R = n; R >= 1; --R) {
+      const int last = R - 1;
+      int bw;
+      const uint64_t kk = min_post<NW>(sm, lane, bw);
+      const int p = (int)(kk & 0xFFFF), colp = (int)((kk >> 16) & 0xFFFF);
+      const float err = sm.rerr[bw], d = sm.rd[bw];
+      if (tid == 0) {
+        sm.code[colp] = (uint8_t)sm.rcode[bw];
+        sm.ord[n - R] = (uint16_t)colp;
+        loss += (double)(err * err / d);
+      }
+      // The true H^-1 entry (p, j), and the base entries the swap moves.
+      const bool mine = j < R && j != p;
+      float tp = 0.f, tl = 0.f, rp = 0.f;
+      if (mine) {
+        tp = T[p > j ? tri(p) + j : tri(j) + p];
+        tl = T[tri(last) + j];  // j == last: the base diagonal of the last position
+        rp = tp;
+        for (int t = 0; t < kd; ++t) rp -= sm.C[t][p] * sm.cdv[t] * sm.C[t][j];
+      }
+      __syncthreads();
+      const float f = err / d;
+      if (mine) {
+        int code;
+        if (j != last) {
+          if (p != last) {
+            T[p > j ? tri(p) + j : tri(j) + p] = tl;
+            T[tri(last) + j] = tp;
+          }
+          sm.w[j] += f * rp;
+          sm.dg[j] -= rp * rp / d;
+          sm.C[kd][j] = rp;
+          const float e = errf(j, code);
+          sm.e2[j] = e * e;
+        } else {  // position p takes over the last unquantized weight
+          sm.w[p] = sm.w[last] + f * rp;
+          sm.perm[p] = sm.perm[last];
+          sm.gpos[p] = sm.gpos[last];
+          sm.dg[p] = sm.dg[last] - rp * rp / d;
+          T[tri(p) + p] = tl;
+          for (int t = 0; t < kd; ++t) sm.C[t][p] = sm.C[t][last];
+          sm.C[kd][p] = rp;
+          const float e = errf(p, code);
+          sm.e2[p] = e * e;
+        }
+      }
+      if (tid == 0) sm.cdv[kd] = 1.f / d;
+      __syncthreads();
+      if (R == 1) break;
+      const int Rr = last;
+      ++kd;
+      if (kd == KD) {
+        // Fold the deferred columns into the base: lanes take columns, waves rows.
+        for (int j0 = 0; j0 < Rr; j0 += 64) {
+          const int jj = j0 + lane;
+          const int jc = jj < Rr ? jj : 0;
+          float cj[KD];
+#pragma unroll
+          for (int t = 0; t < KD; ++t) cj[t] = sm.C[t][jc] * sm.cdv[t];
+#pragma unroll
+          for (int ub = 0; ub < 64 / NW; ub += 4) {
+            float tv[4];
+            int ev[4], ic[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int ii = j0 + wv + (ub + u) * NW;
+              const bool ok = ii < Rr;
+              ic[u] = ok ? ii : 0;
+              ev[u] = ok && jj <= ii ? tri(ii) + jj : spare;  // jj <= ii < Rr: inside the triangle
+              tv[u] = T[ev[u]];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              float v = tv[u];
+#pragma unroll
+              for (int t = 0; t < KD; ++t) v -= sm.C[t][ic[u]] * cj[t];
+              T[ev[u]] = v;
+            }
+          }
+          int i = j0 + 64 + wv;
+          for (; i + (RB - 1) * NW < Rr; i += RB * NW) {
+            float tv[RB];
+            int ev[RB];
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+              ev[u] = tri(i + u * NW) + jj;
+              tv[u] = T[ev[u]];
+            }
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+              float v = tv[u];
+#pragma unroll
+              for (int t = 0; t < KD; ++t) v -= sm.C[t][i + u * NW] * cj[t];
+              T[ev[u]] = v;
+            }
+          }
+          for (; i < Rr; i += NW) {
+            const int e = tri(i) + jj;
+            float v = T[e];
+#pragma unroll
+            for (int t = 0; t < KD; ++t) v -= sm.C[t][i] * cj[t];
+            T[e] = v;
+          }
+        }
+        kd = 0;
+      }
+      // Scores for the next step from the kept diagonal.
+      b.init();
+      if (j < Rr) b.offer(score_bits(sm.e2[j], sm.dg[j]), sm.perm[j], j, sm.dg[j]);
+      post_wave_best(sm, b, lane, wv, errf);
+      __syncthreads();
+    }
+
+    for (int wd = tid; wd < a.words; wd += NT) {
+      const int b0 = wd * 32;
+      const int j0 = b0 / a.bits, j1 = min(n - 1, (b0 + 31) / a.bits);
+      uint64_t acc = 0;
+      for (int jj = j0; jj <= j1; ++jj) {
+        const int off = jj * a.bits - b0;
+        const uint64_t cv = sm.code[jj];
+        acc |= off >= 0 ? (cv << off) : (cv >> -off);
+      }
+      a.Q[row * a.words + wd] = (uint32_t)acc;
+    }
+    if (a.order && j < n) a.order[row * n + j] = sm.ord[j];
+    if (tid == 0 && a.loss) a.loss[row] = (float)loss;
+    __syncthreads();
+  }
+}
+
 template <int DT>
 void launch_greedy(const GreedyArgs& a, hipStream_t st) {
   const int grid = (int)std::min<int64_t>(a.m, a.n <= NL ? 65535 : GRID_G);
@@ -416,6 +635,8 @@ void launch_greedy(const GreedyArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((greedy_kernel<DT, V_SMALL>), dim3(grid), dim3(Var<V_SMALL>::NT), 0, st, a);
   else if (a.n <= NL)
     hipLaunchKernelGGL((greedy_kernel<DT, V_LDS>), dim3(grid), dim3(Var<V_LDS>::NT), 0, st, a);
+  else if (a.n <= NLZ)
+    hipLaunchKernelGGL((greedy_lazy_kernel<DT>), dim3(grid), dim3(1024), 0, st, a);
   else
     hipLaunchKernelGGL((greedy_kernel<DT, V_WS>), dim3(grid), dim3(Var<V_WS>::NT), 0, st, a);
 }
