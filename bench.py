@@ -310,8 +310,18 @@ def bench_obq(args):
     ms_ev = a.elapsed_time(b) / reps
     flops = 2.0 * m * sum(R * (R - 1) / 2 for R in range(1, n + 1))
     tf_ev = flops / (ms_ev * 1e-3) / 1e12
-    lds_bytes = 12.0 / 2.0 * flops  # per downdate entry: read and write it, read c_j (12 B per 2 flops)
-    path = "LDS-resident H^-1" if n <= 272 else "workspace-resident H^-1"
+    path = ("LDS-resident H^-1, four rows per CU" if n <= 128 else
+            "deferred downdates, base H^-1 in the workspace" if n <= 1024 else "workspace-resident H^-1")
+    if n <= 128:    # every downdate entry: read and write it in LDS, read c_j (12 B per 2 flops)
+        bound = {"peak": round(PEAK_LDS * 2 / 12 / 1e3, 2), "unit": "TFLOP/s",
+                 "source": "LDS bandwidth 128 B/clk/CU x 256 CU x 2.4 GHz, 12 B per 2 flops"}
+    elif n <= 1024:  # the base entry (8 B read + written) crosses HBM once per 8 downdates: 0.5 B per flop
+        bound = {"peak": round(PEAK_HBM / 0.5 / 1e3, 2), "unit": "TFLOP/s",
+                 "source": "HBM 8 TB/s, base H^-1 read and written once per 8 deferred downdates (0.5 B per flop)"}
+    else:            # every downdate reads and writes the base entry: 4 B per flop
+        bound = {"peak": round(PEAK_HBM / 4.0 / 1e3, 2), "unit": "TFLOP/s",
+                 "source": "HBM 8 TB/s, base H^-1 read and written every downdate (4 B per flop)"}
+    bound["frac"] = round(tf_ev / bound["peak"], 4)
     res = {
         "metric": f"ms per layer, OBQ greedy-order quantization ({m}x{n} fp16, 4-bit g{group or n})",
         "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
@@ -320,13 +330,11 @@ def bench_obq(args):
         "config": {"workload": f"OBQ greedy: W {m}x{n} fp16, H from 8192 lognormal-input tokens, "
                                f"4-bit g{group or n}, {path}",
                    "m": m, "n": n, "bits": bits, "group": group, "parallelism": "single GPU"},
-        "roofline": {"kernel": "gptq_quantize_greedy: greedy_kernel (+ hinv_pack_kernel)", "bound": "alu",
+        "roofline": {"kernel": "gptq_quantize_greedy: " + ("greedy_kernel" if n <= 128 or n > 1024 else
+                                                            "greedy_lazy_kernel") + " (+ hinv_pack_kernel)",
+                     "bound": "alu",
                      "achieved": round(tf_ev, 3), "peak": 157.3, "unit": "TFLOP/s",
-                     "frac": round(tf_ev / 157.3, 4), "traffic": None,
-                     "attainable": {"peak": round(PEAK_LDS * 2 / 12 / 1e3, 2), "unit": "TFLOP/s",
-                                    "frac": round(tf_ev / (PEAK_LDS * 2 / 12 / 1e3), 4),
-                                    "lds_GBps": round(lds_bytes / (ms_ev * 1e-3) / 1e9, 1),
-                                    "source": "LDS bandwidth 128 B/clk/CU x 256 CU x 2.4 GHz, 12 B per 2 flops"}},
+                     "frac": round(tf_ev / 157.3, 4), "traffic": None, "attainable": bound},
     }
     if not args.no_cpu_baseline:
         import oracle as O

@@ -6,10 +6,10 @@
 // H^-1 - H^-1_{:,p} H^-1_{p,:} / [H^-1]_pp ([OBQ] "The OBS / GPTQ Trick").
 // Rows pick different weights, so each needs its own H^-1 ([OBQ] "Limitations
 // of OBQ", item 2): here one workgroup owns one row at a time and keeps that
-// row's H^-1 as a packed lower triangle, in LDS for rows of up to NL weights
-// (145 KB of the CU's 160 KB; rows of up to NS weights use 33 KB and four
-// workgroups share a CU) and in a per-workgroup slice of the workspace beyond
-// that.
+// row's H^-1 as a packed lower triangle, in LDS for rows of up to NS weights
+// (33 KB; four workgroups share a CU) and in a per-workgroup slice of the
+// workspace beyond that, where rows of up to NLZ weights defer their
+// downdates (greedy_lazy_kernel).
 //
 // Unquantized weights always occupy positions 0..R-1: after weight p is
 // chosen it is swapped with position R-1 (row and column of the triangle,
@@ -27,20 +27,18 @@
 namespace gptq {
 namespace {
 
-constexpr int NL = 272;     // longest row whose packed H^-1 fits in LDS
-constexpr int NS = 128;     // longest row of the small LDS variant (four workgroups per CU)
+constexpr int NS = 128;     // longest row whose H^-1 stays in LDS (four workgroups per CU)
 constexpr int NMAX = 4096;  // longest row of the workspace-resident path
 constexpr int GMIN = 16;    // smallest group (bounds the per-group tables)
 constexpr int GRID_G = 256; // workgroups (and workspace slices) of the workspace path
 constexpr int RB = 4;       // full rows per downdate batch
 
-// The three variants: H^-1 in LDS for n <= NS (256 threads, four rows per
-// CU at once), in LDS for n <= NL (1024 threads, one row per CU), in the
-// workspace beyond (1024 threads).
-enum { V_SMALL = 0, V_LDS = 1, V_WS = 2 };
+// The two variants of greedy_kernel: H^-1 in LDS for n <= NS (256 threads,
+// four rows per CU at once) and in the workspace (1024 threads) for rows
+// longer than the deferred-downdate kernel takes.
+enum { V_SMALL = 0, V_WS = 2 };
 template <int V> struct Var;
 template <> struct Var<V_SMALL> { static constexpr int N = NS, NT = 256, TF = NS * (NS + 1) / 2; };
-template <> struct Var<V_LDS> { static constexpr int N = NL, NT = 1024, TF = NL * (NL + 1) / 2; };
 template <> struct Var<V_WS> { static constexpr int N = NMAX, NT = 1024, TF = 0; };
 
 __host__ __device__ constexpr int tri(int i) { return i * (i + 1) / 2; }  // start of packed row i
@@ -410,7 +408,7 @@ __global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
   }
 }
 
-// Rows of NL < n <= NLZ weights keep H^-1 in the workspace, and the
+// Rows of NS < n <= NLZ weights keep H^-1 in the workspace, and the
 // rank-one downdates are deferred: the true H^-1 is the stored base minus
 // sum_t c_t c_t^T / d_t over the (at most KD) most recent eliminations,
 // whose columns c_t sit in LDS.  A step needs only the true row of the
@@ -630,11 +628,9 @@ __global__ __launch_bounds__(1024) void greedy_lazy_kernel(GreedyArgs a) {
 
 template <int DT>
 void launch_greedy(const GreedyArgs& a, hipStream_t st) {
-  const int grid = (int)std::min<int64_t>(a.m, a.n <= NL ? 65535 : GRID_G);
+  const int grid = (int)std::min<int64_t>(a.m, a.n <= NS ? 65535 : GRID_G);
   if (a.n <= NS)
     hipLaunchKernelGGL((greedy_kernel<DT, V_SMALL>), dim3(grid), dim3(Var<V_SMALL>::NT), 0, st, a);
-  else if (a.n <= NL)
-    hipLaunchKernelGGL((greedy_kernel<DT, V_LDS>), dim3(grid), dim3(Var<V_LDS>::NT), 0, st, a);
   else if (a.n <= NLZ)
     hipLaunchKernelGGL((greedy_lazy_kernel<DT>), dim3(grid), dim3(1024), 0, st, a);
   else
@@ -647,7 +643,7 @@ bool greedy_supported(int64_t n, int64_t group) { return n <= NMAX && (group <= 
 
 size_t greedy_workspace_bytes(int64_t m, int64_t n) {
   if (m < 1 || n < 1 || n > NMAX) return 0;
-  const int64_t slices = n <= NL ? 0 : std::min<int64_t>(m, GRID_G);
+  const int64_t slices = n <= NS ? 0 : std::min<int64_t>(m, GRID_G);
   return (size_t)(slice_floats(n) * (1 + slices)) * sizeof(float);
 }
 

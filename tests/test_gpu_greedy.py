@@ -78,8 +78,8 @@ def greedy_check(g, Wd, U32, Hd, bits, group, rows, label):
     return ref
 
 
-# (m, n, bits, group, dtype): rows of up to 128 keep H^-1 in LDS with four rows per CU, up to 272
-# with one; longer ones use the workspace, with deferred downdates up to 1024.
+# (m, n, bits, group, dtype): rows of up to 128 keep H^-1 in LDS with four rows per CU; longer ones
+# use the workspace, with deferred downdates up to 1024.
 CASES = [
     (64, 96, 4, 0, "f16"), (48, 256, 4, 32, "bf16"), (32, 272, 3, 0, "f32"), (24, 273, 4, 64, "f16"),
     (16, 600, 4, 128, "f16"), (8, 1000, 2, 16, "f32"), (5, 40, 4, 128, "f16"), (3, 1, 4, 0, "f32"),
