@@ -311,10 +311,15 @@ def bench_obq(args):
     flops = 2.0 * m * sum(R * (R - 1) / 2 for R in range(1, n + 1))
     tf_ev = flops / (ms_ev * 1e-3) / 1e12
     path = ("LDS-resident H^-1, four rows per CU" if n <= 128 else
+            "deferred downdates, base H^-1 in LDS" if n <= 256 else
             "deferred downdates, base H^-1 in the workspace" if n <= 1024 else "workspace-resident H^-1")
     if n <= 128:    # every downdate entry: read and write it in LDS, read c_j (12 B per 2 flops)
         bound = {"peak": round(PEAK_LDS * 2 / 12 / 1e3, 2), "unit": "TFLOP/s",
                  "source": "LDS bandwidth 128 B/clk/CU x 256 CU x 2.4 GHz, 12 B per 2 flops"}
+    elif n <= 256:   # per 8 downdates of an entry (16 flops): 8 B of LDS for the base, under the ALU peak
+        bound = {"peak": 157.3, "unit": "TFLOP/s",
+                 "source": "fp32 vector peak: base and deferred columns in LDS, 0.5 B of LDS per flop "
+                           "(78.6 TB/s of LDS would allow 157 TFLOP/s)"}
     elif n <= 1024:  # the base entry (8 B read + written) crosses HBM once per 8 downdates: 0.5 B per flop
         bound = {"peak": round(PEAK_HBM / 0.5 / 1e3, 2), "unit": "TFLOP/s",
                  "source": "HBM 8 TB/s, base H^-1 read and written once per 8 deferred downdates (0.5 B per flop)"}

@@ -205,7 +205,7 @@ gptq_status gptq_quantize_layer(void* W, int32_t w_dtype, int64_t m, int64_t n, 
  *   loss       [m] float32 out, optional (NULL): the sum of the chosen dL_p,
  *              which equals (w - what)^T H_d (w - what) for the row.
  *   workspace, ws_bytes: at least gptq_quantize_greedy_workspace_bytes(m, n)
- *              bytes (the packed H^-1, and for n > 128 one packed copy per
+ *              bytes (the packed H^-1, and for n > 256 one packed copy per
  *              resident workgroup, at most 256).
  * This version runs n <= 4096 and group_size <= 0 or >= 16; other valid
  * requests return GPTQ_ERR_UNSUPPORTED.  Bad sizes, bits, dtype or NULL

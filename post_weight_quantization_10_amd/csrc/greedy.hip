@@ -7,9 +7,10 @@
 // Rows pick different weights, so each needs its own H^-1 ([OBQ] "Limitations
 // of OBQ", item 2): here one workgroup owns one row at a time and keeps that
 // row's H^-1 as a packed lower triangle, in LDS for rows of up to NS weights
-// (33 KB; four workgroups share a CU) and in a per-workgroup slice of the
-// workspace beyond that, where rows of up to NLZ weights defer their
-// downdates (greedy_lazy_kernel).
+// (33 KB; four workgroups share a CU); longer rows defer their downdates
+// (greedy_lazy_kernel, base in LDS up to NLB weights, else in a
+// per-workgroup slice of the workspace), and rows past NLZ downdate a
+// workspace slice every step.
 //
 // Unquantized weights always occupy positions 0..R-1: after weight p is
 // chosen it is swapped with position R-1 (row and column of the triangle,
@@ -408,9 +409,10 @@ __global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
   }
 }
 
-// Rows of NS < n <= NLZ weights keep H^-1 in the workspace, and the
-// rank-one downdates are deferred: the true H^-1 is the stored base minus
-// sum_t c_t c_t^T / d_t over the (at most KD) most recent eliminations,
+// Rows of NS < n <= NLZ weights defer the rank-one downdates, with the base
+// H^-1 in LDS up to NLB weights and in the workspace beyond: the true H^-1
+// is the stored base minus sum_t c_t c_t^T / d_t over the (at most KD) most
+// recent eliminations,
 // whose columns c_t sit in LDS.  A step needs only the true row of the
 // chosen weight (base row minus the deferred terms) and the diagonal, which
 // is kept current in LDS; every KD steps the deferred columns are folded
@@ -418,10 +420,12 @@ __global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
 // per KD steps instead of every step.  Positions are swapped as in
 // greedy_kernel: in the base, the deferred columns and the diagonal alike.
 constexpr int NLZ = 1024;  // longest row of the deferred-downdate path
+constexpr int NLB = 256;   // longest row whose base H^-1 stays in LDS on that path
 constexpr int KD = 8;      // downdates deferred per base update
 
-template <int N>
+template <int N, int TF>
 struct LazySmem {
+  float T[TF > 0 ? TF + 64 : 1];  // packed base H^-1 (+ 64 spare entries) when it fits in LDS
   float w[N];         // current weights by position
   float e2[N];        // squared rounding error of each position's weight
   float dg[N];        // diagonal of the true H^-1 by position
@@ -437,16 +441,21 @@ struct LazySmem {
   uint8_t code[N];    // chosen codes by original column
 };
 
-template <int DT>
+template <int DT, bool BASE_LDS>
 __global__ __launch_bounds__(1024) void greedy_lazy_kernel(GreedyArgs a) {
-  constexpr int N = NLZ, NT = 1024, NW = 16;
+  constexpr int N = BASE_LDS ? NLB : NLZ, NT = 1024, NW = 16;
   static_assert(N <= NT, "one position per thread");
-  __shared__ __attribute__((aligned(16))) LazySmem<N> sm;
+  __shared__ __attribute__((aligned(16))) LazySmem<N, BASE_LDS ? NLB * (NLB + 1) / 2 : 0> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n, P = tri(n);
   const int maxq = (1 << a.bits) - 1;
   const int spare = P + lane;
-  float* T = a.Tws + (int64_t)blockIdx.x * slice_floats(n);
+  float* T;
+  if constexpr (BASE_LDS) {
+    T = sm.T;
+  } else {
+    T = a.Tws + (int64_t)blockIdx.x * slice_floats(n);
+  }
   auto errf = [&](int k, int& code) {
     const int g = sm.gpos[k];
     return round_err(sm.w[k], sm.gs[g], sm.gis[g], sm.gz[g], maxq, code);
@@ -628,11 +637,13 @@ __global__ __launch_bounds__(1024) void greedy_lazy_kernel(GreedyArgs a) {
 
 template <int DT>
 void launch_greedy(const GreedyArgs& a, hipStream_t st) {
-  const int grid = (int)std::min<int64_t>(a.m, a.n <= NS ? 65535 : GRID_G);
+  const int grid = (int)std::min<int64_t>(a.m, a.n <= NLB ? 65535 : GRID_G);
   if (a.n <= NS)
     hipLaunchKernelGGL((greedy_kernel<DT, V_SMALL>), dim3(grid), dim3(Var<V_SMALL>::NT), 0, st, a);
+  else if (a.n <= NLB)
+    hipLaunchKernelGGL((greedy_lazy_kernel<DT, true>), dim3(grid), dim3(1024), 0, st, a);
   else if (a.n <= NLZ)
-    hipLaunchKernelGGL((greedy_lazy_kernel<DT>), dim3(grid), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL((greedy_lazy_kernel<DT, false>), dim3(grid), dim3(1024), 0, st, a);
   else
     hipLaunchKernelGGL((greedy_kernel<DT, V_WS>), dim3(grid), dim3(Var<V_WS>::NT), 0, st, a);
 }
@@ -643,7 +654,7 @@ bool greedy_supported(int64_t n, int64_t group) { return n <= NMAX && (group <= 
 
 size_t greedy_workspace_bytes(int64_t m, int64_t n) {
   if (m < 1 || n < 1 || n > NMAX) return 0;
-  const int64_t slices = n <= NS ? 0 : std::min<int64_t>(m, GRID_G);
+  const int64_t slices = n <= NLB ? 0 : std::min<int64_t>(m, GRID_G);
   return (size_t)(slice_floats(n) * (1 + slices)) * sizeof(float);
 }
 

@@ -212,7 +212,7 @@ def test_greedy_rejects(kw, expect):
 def test_greedy_workspace_sizes():
     al = lambda n: (n * (n + 1) // 2 + 64 + 63) // 64 * 64   # packed triangle + 64 spare floats
     assert pw.greedy_workspace_bytes(10, 100) == 4 * al(100)          # H^-1 stays in LDS
-    assert pw.greedy_workspace_bytes(10, 128) == 4 * al(128)
-    assert pw.greedy_workspace_bytes(100, 129) == 4 * al(129) * 101   # one copy per workgroup
+    assert pw.greedy_workspace_bytes(10, 256) == 4 * al(256)
+    assert pw.greedy_workspace_bytes(100, 257) == 4 * al(257) * 101   # one copy per workgroup
     assert pw.greedy_workspace_bytes(5000, 300) == 4 * al(300) * 257  # at most 256 workgroups
     assert pw.greedy_workspace_bytes(0, 300) == 0
