@@ -262,10 +262,6 @@ def bench_rotate(args):
     print(json.dumps(res), flush=True)
 
 
-# LDS bandwidth of the chip: 128 bytes per clock per CU, 256 CUs, 2.4 GHz.
-PEAK_LDS = 128 * 256 * 2.4e9 / 1e9  # GB/s
-
-
 def bench_obq(args):
     """gptq_quantize_greedy (OBQ's greedy order) on a 4096 x n fp16 layer,
     4-bit g128 (per-row grid when n < 128), against the factor U of a
@@ -310,13 +306,10 @@ def bench_obq(args):
     ms_ev = a.elapsed_time(b) / reps
     flops = 2.0 * m * sum(R * (R - 1) / 2 for R in range(1, n + 1))
     tf_ev = flops / (ms_ev * 1e-3) / 1e12
-    path = ("LDS-resident H^-1, four rows per CU" if n <= 128 else
+    path = ("deferred downdates, base H^-1 in LDS, four rows per CU" if n <= 128 else
             "deferred downdates, base H^-1 in LDS" if n <= 256 else
             "deferred downdates, base H^-1 in the workspace" if n <= 1024 else "workspace-resident H^-1")
-    if n <= 128:    # every downdate entry: read and write it in LDS, read c_j (12 B per 2 flops)
-        bound = {"peak": round(PEAK_LDS * 2 / 12 / 1e3, 2), "unit": "TFLOP/s",
-                 "source": "LDS bandwidth 128 B/clk/CU x 256 CU x 2.4 GHz, 12 B per 2 flops"}
-    elif n <= 256:   # per 8 downdates of an entry (16 flops): 8 B of LDS for the base, under the ALU peak
+    if n <= 256:     # per 8 downdates of an entry (16 flops): 8 B of LDS for the base, under the ALU peak
         bound = {"peak": 157.3, "unit": "TFLOP/s",
                  "source": "fp32 vector peak: base and deferred columns in LDS, 0.5 B of LDS per flop "
                            "(78.6 TB/s of LDS would allow 157 TFLOP/s)"}
@@ -335,8 +328,8 @@ def bench_obq(args):
         "config": {"workload": f"OBQ greedy: W {m}x{n} fp16, H from 8192 lognormal-input tokens, "
                                f"4-bit g{group or n}, {path}",
                    "m": m, "n": n, "bits": bits, "group": group, "parallelism": "single GPU"},
-        "roofline": {"kernel": "gptq_quantize_greedy: " + ("greedy_kernel" if n <= 128 or n > 1024 else
-                                                            "greedy_lazy_kernel") + " (+ hinv_pack_kernel)",
+        "roofline": {"kernel": "gptq_quantize_greedy: " + ("greedy_kernel" if n > 1024 else "greedy_lazy_kernel") +
+                               " (+ hinv_pack_kernel)",
                      "bound": "alu",
                      "achieved": round(tf_ev, 3), "peak": 157.3, "unit": "TFLOP/s",
                      "frac": round(tf_ev / 157.3, 4), "traffic": None, "attainable": bound},

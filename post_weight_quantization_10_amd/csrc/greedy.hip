@@ -6,11 +6,11 @@
 // H^-1 - H^-1_{:,p} H^-1_{p,:} / [H^-1]_pp ([OBQ] "The OBS / GPTQ Trick").
 // Rows pick different weights, so each needs its own H^-1 ([OBQ] "Limitations
 // of OBQ", item 2): here one workgroup owns one row at a time and keeps that
-// row's H^-1 as a packed lower triangle, in LDS for rows of up to NS weights
-// (33 KB; four workgroups share a CU); longer rows defer their downdates
-// (greedy_lazy_kernel, base in LDS up to NLB weights, else in a
-// per-workgroup slice of the workspace), and rows past NLZ downdate a
-// workspace slice every step.
+// row's H^-1 as a packed lower triangle.  Rows of up to NLZ weights defer
+// their downdates (greedy_lazy_kernel; the base in LDS up to NLB weights,
+// with four rows per CU up to NS, else in a per-workgroup slice of the
+// workspace); longer rows downdate a workspace slice every step
+// (greedy_kernel).
 //
 // Unquantized weights always occupy positions 0..R-1: after weight p is
 // chosen it is swapped with position R-1 (row and column of the triangle,
@@ -28,18 +28,16 @@
 namespace gptq {
 namespace {
 
-constexpr int NS = 128;     // longest row whose H^-1 stays in LDS (four workgroups per CU)
+constexpr int NS = 128;     // longest row of the four-rows-per-CU variant
 constexpr int NMAX = 4096;  // longest row of the workspace-resident path
 constexpr int GMIN = 16;    // smallest group (bounds the per-group tables)
 constexpr int GRID_G = 256; // workgroups (and workspace slices) of the workspace path
 constexpr int RB = 4;       // full rows per downdate batch
 
-// The two variants of greedy_kernel: H^-1 in LDS for n <= NS (256 threads,
-// four rows per CU at once) and in the workspace (1024 threads) for rows
-// longer than the deferred-downdate kernel takes.
-enum { V_SMALL = 0, V_WS = 2 };
+// greedy_kernel downdates every step; it takes the rows longer than the
+// deferred-downdate kernel does, with H^-1 in the workspace (1024 threads).
+enum { V_WS = 2 };
 template <int V> struct Var;
-template <> struct Var<V_SMALL> { static constexpr int N = NS, NT = 256, TF = NS * (NS + 1) / 2; };
 template <> struct Var<V_WS> { static constexpr int N = NMAX, NT = 1024, TF = 0; };
 
 __host__ __device__ constexpr int tri(int i) { return i * (i + 1) / 2; }  // start of packed row i
@@ -409,7 +407,7 @@ __global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
   }
 }
 
-// Rows of NS < n <= NLZ weights defer the rank-one downdates, with the base
+// Rows of up to NLZ weights defer the rank-one downdates, with the base
 // H^-1 in LDS up to NLB weights and in the workspace beyond: the true H^-1
 // is the stored base minus sum_t c_t c_t^T / d_t over the (at most KD) most
 // recent eliminations,
@@ -423,7 +421,15 @@ constexpr int NLZ = 1024;  // longest row of the deferred-downdate path
 constexpr int NLB = 256;   // longest row whose base H^-1 stays in LDS on that path
 constexpr int KD = 8;      // downdates deferred per base update
 
-template <int N, int TF>
+// Deferred-downdate variants: rows of up to NS weights, base in LDS, 4 waves
+// (four rows per CU); up to NLB, base in LDS, 16 waves; up to NLZ, base in
+// the workspace, 16 waves.
+template <int LV> struct LVar;
+template <> struct LVar<0> { static constexpr int N = NS, NT = 256, TF = NS * (NS + 1) / 2; };
+template <> struct LVar<1> { static constexpr int N = NLB, NT = 1024, TF = NLB * (NLB + 1) / 2; };
+template <> struct LVar<2> { static constexpr int N = NLZ, NT = 1024, TF = 0; };
+
+template <int N, int TF, int NW>
 struct LazySmem {
   float T[TF > 0 ? TF + 64 : 1];  // packed base H^-1 (+ 64 spare entries) when it fits in LDS
   float w[N];         // current weights by position
@@ -435,17 +441,18 @@ struct LazySmem {
   uint16_t gpos[N];   // group of each position's weight
   uint16_t ord[N];    // column quantized at each step
   float gs[N / GMIN + 1], gis[N / GMIN + 1], gz[N / GMIN + 1];
-  uint64_t rkey[16];
-  float rerr[16], rd[16];
-  int rcode[16];
+  uint64_t rkey[NW];
+  float rerr[NW], rd[NW];
+  int rcode[NW];
   uint8_t code[N];    // chosen codes by original column
 };
 
-template <int DT, bool BASE_LDS>
-__global__ __launch_bounds__(1024) void greedy_lazy_kernel(GreedyArgs a) {
-  constexpr int N = BASE_LDS ? NLB : NLZ, NT = 1024, NW = 16;
+template <int DT, int LV>
+__global__ __launch_bounds__(LVar<LV>::NT) void greedy_lazy_kernel(GreedyArgs a) {
+  constexpr int N = LVar<LV>::N, NT = LVar<LV>::NT, NW = NT / 64;
+  constexpr bool BASE_LDS = LVar<LV>::TF > 0;
   static_assert(N <= NT, "one position per thread");
-  __shared__ __attribute__((aligned(16))) LazySmem<N, BASE_LDS ? NLB * (NLB + 1) / 2 : 0> sm;
+  __shared__ __attribute__((aligned(16))) LazySmem<N, LVar<LV>::TF, NW> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n, P = tri(n);
   const int maxq = (1 << a.bits) - 1;
@@ -639,11 +646,11 @@ template <int DT>
 void launch_greedy(const GreedyArgs& a, hipStream_t st) {
   const int grid = (int)std::min<int64_t>(a.m, a.n <= NLB ? 65535 : GRID_G);
   if (a.n <= NS)
-    hipLaunchKernelGGL((greedy_kernel<DT, V_SMALL>), dim3(grid), dim3(Var<V_SMALL>::NT), 0, st, a);
+    hipLaunchKernelGGL((greedy_lazy_kernel<DT, 0>), dim3(grid), dim3(LVar<0>::NT), 0, st, a);
   else if (a.n <= NLB)
-    hipLaunchKernelGGL((greedy_lazy_kernel<DT, true>), dim3(grid), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL((greedy_lazy_kernel<DT, 1>), dim3(grid), dim3(LVar<1>::NT), 0, st, a);
   else if (a.n <= NLZ)
-    hipLaunchKernelGGL((greedy_lazy_kernel<DT, false>), dim3(grid), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL((greedy_lazy_kernel<DT, 2>), dim3(grid), dim3(LVar<2>::NT), 0, st, a);
   else
     hipLaunchKernelGGL((greedy_kernel<DT, V_WS>), dim3(grid), dim3(Var<V_WS>::NT), 0, st, a);
 }
