@@ -84,7 +84,8 @@ CASES = [
     (64, 96, 4, 0, "f16"), (48, 256, 4, 32, "bf16"), (32, 272, 3, 0, "f32"), (24, 273, 4, 64, "f16"),
     (16, 600, 4, 128, "f16"), (8, 1000, 2, 16, "f32"), (5, 40, 4, 128, "f16"), (3, 1, 4, 0, "f32"),
     (1, 17, 8, 0, "bf16"), (40, 130, 3, 16, "f16"), (20, 128, 4, 32, "bf16"), (20, 129, 3, 0, "f16"),
-    (300, 100, 4, 0, "f32"), (3, 1100, 4, 128, "f16"),
+    (300, 100, 4, 0, "f32"), (3, 1100, 4, 128, "f16"), (12, 257, 3, 32, "f32"), (10, 400, 4, 64, "bf16"),
+    (2, 1024, 4, 128, "bf16"),
 ]
 
 
