@@ -34,11 +34,6 @@ constexpr int GMIN = 16;    // smallest group (bounds the per-group tables)
 constexpr int GRID_G = 256; // workgroups (and workspace slices) of the workspace path
 constexpr int RB = 4;       // full rows per downdate batch
 
-// greedy_kernel downdates every step; it takes the rows longer than the
-// deferred-downdate kernel does, with H^-1 in the workspace (1024 threads).
-enum { V_WS = 2 };
-template <int V> struct Var;
-template <> struct Var<V_WS> { static constexpr int N = NMAX, NT = 1024, TF = 0; };
 
 __host__ __device__ constexpr int tri(int i) { return i * (i + 1) / 2; }  // start of packed row i
 
@@ -46,9 +41,8 @@ __host__ __device__ constexpr int tri(int i) { return i * (i + 1) / 2; }  // sta
 // lanes past the end of a downdate row read and write instead of branching.
 __host__ __device__ constexpr int64_t slice_floats(int64_t n) { return ((n * (n + 1) / 2 + 64) + 63) & ~(int64_t)63; }
 
-template <int N, int TF, int NW>
+template <int N, int NW>
 struct GreedySmem {
-  float T[TF > 0 ? TF + 64 : 1];  // packed lower triangle of the row's H^-1 (LDS path)
   float w[N];                     // current weights by position
   float c[N];                     // the eliminated weight's H^-1 column (downdate vector)
   float e2[N];                    // squared rounding error of each position's weight
@@ -220,21 +214,18 @@ __global__ __launch_bounds__(256) void hinv_pack_kernel(const float* __restrict_
 // diagonal entry also scores that position for the next step.  Lanes that
 // fall past the end of the triangle read and write spare entries instead of
 // branching.
-template <int DT, int V>
-__global__ __launch_bounds__(Var<V>::NT) void greedy_kernel(GreedyArgs a) {
-  constexpr int N = Var<V>::N, NT = Var<V>::NT, NW = NT / 64;
-  constexpr bool INLDS = V != V_WS;
-  __shared__ __attribute__((aligned(16))) GreedySmem<N, Var<V>::TF, NW> sm;
+//
+// It takes the rows longer than the deferred-downdate kernel does, with the
+// row's H^-1 in a workspace slice (1024 threads).
+template <int DT>
+__global__ __launch_bounds__(1024) void greedy_kernel(GreedyArgs a) {
+  constexpr int N = NMAX, NT = 1024, NW = NT / 64;
+  __shared__ __attribute__((aligned(16))) GreedySmem<N, NW> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n, P = tri(n);
   const int maxq = (1 << a.bits) - 1;
   const int spare = P + lane;  // where lanes past the end of a row read and write
-  float* T;
-  if constexpr (INLDS) {
-    T = sm.T;
-  } else {
-    T = a.Tws + (int64_t)blockIdx.x * slice_floats(n);
-  }
+  float* T = a.Tws + (int64_t)blockIdx.x * slice_floats(n);
   auto errf = [&](int k, int& code) { return round_err(sm.w[k], sm.ps[k], sm.pis[k], sm.pz[k], maxq, code); };
 
   for (int64_t row = blockIdx.x; row < a.m; row += gridDim.x) {
@@ -652,7 +643,7 @@ void launch_greedy(const GreedyArgs& a, hipStream_t st) {
   else if (a.n <= NLZ)
     hipLaunchKernelGGL((greedy_lazy_kernel<DT, 2>), dim3(grid), dim3(LVar<2>::NT), 0, st, a);
   else
-    hipLaunchKernelGGL((greedy_kernel<DT, V_WS>), dim3(grid), dim3(Var<V_WS>::NT), 0, st, a);
+    hipLaunchKernelGGL((greedy_kernel<DT>), dim3(grid), dim3(1024), 0, st, a);
 }
 
 }  // namespace
