@@ -313,9 +313,9 @@ def bench_obq(args):
         bound = {"peak": 157.3, "unit": "TFLOP/s",
                  "source": "fp32 vector peak: base and deferred columns in LDS, 0.5 B of LDS per flop "
                            "(78.6 TB/s of LDS would allow 157 TFLOP/s)"}
-    elif n <= 1024:  # the base entry (8 B read + written) crosses HBM once per 8 downdates: 0.5 B per flop
-        bound = {"peak": round(PEAK_HBM / 0.5 / 1e3, 2), "unit": "TFLOP/s",
-                 "source": "HBM 8 TB/s, base H^-1 read and written once per 8 deferred downdates (0.5 B per flop)"}
+    elif n <= 1024:  # the base entry (8 B read + written) crosses HBM once per 16 downdates: 0.25 B per flop
+        bound = {"peak": round(PEAK_HBM / 0.25 / 1e3, 2), "unit": "TFLOP/s",
+                 "source": "HBM 8 TB/s, base H^-1 read and written once per 16 deferred downdates (0.25 B per flop)"}
     else:            # every downdate reads and writes the base entry: 4 B per flop
         bound = {"peak": round(PEAK_HBM / 4.0 / 1e3, 2), "unit": "TFLOP/s",
                  "source": "HBM 8 TB/s, base H^-1 read and written every downdate (4 B per flop)"}

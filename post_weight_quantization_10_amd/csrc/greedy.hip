@@ -410,17 +410,18 @@ __global__ __launch_bounds__(1024) void greedy_kernel(GreedyArgs a) {
 // greedy_kernel: in the base, the deferred columns and the diagonal alike.
 constexpr int NLZ = 1024;  // longest row of the deferred-downdate path
 constexpr int NLB = 256;   // longest row whose base H^-1 stays in LDS on that path
-constexpr int KD = 8;      // downdates deferred per base update
 
 // Deferred-downdate variants: rows of up to NS weights, base in LDS, 4 waves
 // (four rows per CU); up to NLB, base in LDS, 16 waves; up to NLZ, base in
 // the workspace, 16 waves.
 template <int LV> struct LVar;
-template <> struct LVar<0> { static constexpr int N = NS, NT = 256, TF = NS * (NS + 1) / 2; };
-template <> struct LVar<1> { static constexpr int N = NLB, NT = 1024, TF = NLB * (NLB + 1) / 2; };
-template <> struct LVar<2> { static constexpr int N = NLZ, NT = 1024, TF = 0; };
+// KD downdates are deferred per base update: 8 with the base in LDS, 16 with
+// it in the workspace, where each base update is a pass over HBM.
+template <> struct LVar<0> { static constexpr int N = NS, NT = 256, TF = NS * (NS + 1) / 2, KD = 8; };
+template <> struct LVar<1> { static constexpr int N = NLB, NT = 1024, TF = NLB * (NLB + 1) / 2, KD = 8; };
+template <> struct LVar<2> { static constexpr int N = NLZ, NT = 1024, TF = 0, KD = 16; };
 
-template <int N, int TF, int NW>
+template <int N, int TF, int NW, int KD>
 struct LazySmem {
   float T[TF > 0 ? TF + 64 : 1];  // packed base H^-1 (+ 64 spare entries) when it fits in LDS
   float w[N];         // current weights by position
@@ -440,10 +441,10 @@ struct LazySmem {
 
 template <int DT, int LV>
 __global__ __launch_bounds__(LVar<LV>::NT) void greedy_lazy_kernel(GreedyArgs a) {
-  constexpr int N = LVar<LV>::N, NT = LVar<LV>::NT, NW = NT / 64;
+  constexpr int N = LVar<LV>::N, NT = LVar<LV>::NT, NW = NT / 64, KD = LVar<LV>::KD;
   constexpr bool BASE_LDS = LVar<LV>::TF > 0;
   static_assert(N <= NT, "one position per thread");
-  __shared__ __attribute__((aligned(16))) LazySmem<N, LVar<LV>::TF, NW> sm;
+  __shared__ __attribute__((aligned(16))) LazySmem<N, LVar<LV>::TF, NW, KD> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n, P = tri(n);
   const int maxq = (1 << a.bits) - 1;
