@@ -77,13 +77,18 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 
 // Quantizer parameters (s, z) from the range [lo, hi] of a group or row:
 // x_lo = min(0, lo), x_hi = max(0, hi) (an all-zero range becomes [0, 1]),
-// s = (x_hi - x_lo) / maxq, z = rint(-x_lo / s).
+// s = (x_hi - x_lo) / maxq, z = rint(-x_lo / s).  Taken in fp64 (s then
+// rounded to fp32): for 16-bit weights the extremes of a row or group are
+// often exact negatives of each other, and then -x_lo / s is exactly the
+// half-integer maxq / 2 in exact arithmetic, so the integer z would be
+// decided by the last bit of the division; fp64 takes that decision the same
+// way as an fp64 computation of the same formula does.
 __device__ __forceinline__ void qparams(float lo, float hi, int maxq, float& s, float& z) {
-  lo = fminf(lo, 0.f);
-  hi = fmaxf(hi, 0.f);
-  if (hi == lo) { lo = 0.f; hi = 1.f; }
-  s = (hi - lo) / (float)maxq;
-  z = rintf(-lo / s);
+  double l = fmin((double)lo, 0.0), h = fmax((double)hi, 0.0);
+  if (h == l) { l = 0.0; h = 1.0; }
+  const double s64 = (h - l) / (double)maxq;
+  s = (float)s64;
+  z = (float)rint(-l / s64);
 }
 
 

@@ -29,7 +29,7 @@ def _to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(a).to(DEV)
 
 
-def run_job(workload: str, job_index: int, sample_rows: int = 128, sample_cols: int = 48,
+def run_job(workload: str, job_index: int, sample_rows: int = 1024, sample_cols: int = 48,
             host_prepare_max_n: int = 12288, tokens: int = 0) -> Dict[str, float]:
     import post_weight_quantization_10_amd as pw
     wl = synth.workloads()[workload]
