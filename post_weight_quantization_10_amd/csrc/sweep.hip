@@ -32,6 +32,40 @@ constexpr int BMAX = 128;  // widest block
 constexpr int LA = 2;          // blocks per lazy flush on the look-ahead path
 constexpr int ELD = LA * BMAX;  // leading dimension of the E buffer: the errors of LA consecutive blocks
 
+// Layout of a block's factor rows for the sweep kernel.  Lane lr (of the LPR
+// lanes that share a weight row) holds the block columns c = lr + LPR j,
+// j = 0..7, in register j, so step p (column p) changes only registers
+// j >= J = p / LPR: the columns left of p are final.  Row p of the factor
+// block (divided by its diagonal, zero on and left of it) keeps just those
+// registers, cut into the segments one load each reads (4, 2 or 1 floats:
+// registers 0-3 / 4-7 as float4 where all four are needed, else the pairs and
+// singles that remain), every segment stored as LPR consecutive vectors (lane
+// lr's at lr * len): the LPR lanes of a row read consecutive bytes
+// (bank-conflict-free, the same addresses for every row of the wave), and no
+// load brings a register the step does not use.
+template <int LPR>
+struct BlockLayout {
+  static constexpr int NSTEP = 8 * LPR;           // columns per block
+  static constexpr int USZ = 36 * LPR * LPR;      // floats: sum over rows of LPR (8 - J)
+  static constexpr int STRIDE = USZ + NSTEP;      // per block in the workspace: the rows, then 1/U_pp
+  // segments of a row with first live register J: (first register, length)
+  static constexpr int NSEG[8] = {2, 3, 2, 2, 1, 2, 1, 1};
+  static constexpr int SEG[8][3][2] = {{{0, 4}, {4, 4}, {0, 0}}, {{1, 1}, {2, 2}, {4, 4}}, {{2, 2}, {4, 4}, {0, 0}},
+                                       {{3, 1}, {4, 4}, {0, 0}}, {{4, 4}, {0, 0}, {0, 0}}, {{5, 1}, {6, 2}, {0, 0}},
+                                       {{6, 2}, {0, 0}, {0, 0}}, {{7, 1}, {0, 0}, {0, 0}}};
+  __host__ __device__ static constexpr int row_off(int p) {
+    const int K = p / LPR, t = p % LPR;
+    return LPR * (LPR * (8 * K - K * (K - 1) / 2) + t * (8 - K));
+  }
+  // offset of segment s of row p (lane 0)
+  __host__ __device__ static constexpr int seg_off(int p, int s) {
+    const int J = p / LPR;
+    int o = row_off(p);
+    for (int k = 0; k < s; ++k) o += LPR * SEG[J][k][1];
+    return o;
+  }
+};
+
 struct SweepArgs {
   const float* U;
   float* V;
@@ -43,10 +77,16 @@ struct SweepArgs {
   int64_t G;
   float* S;
   int32_t* Z;
-  uint8_t* Q8;    // [m x n] codes
-  float* E;       // [m x 128] scaled errors of this block
+  uint8_t* Q8;    // [m x n] codes, or null when the codes are packed here
+  uint32_t* Qw;   // packed codes [m x words] (bit-streams), or null
+  int64_t words;  // uint32 words per row of Qw
+  int bits;
+  void* Wout;     // dequantized weights written here (W's dtype), or null
+  int wdt;
+  int64_t ldw;
+  float* E;       // scaled errors of this block (leading dimension ELD)
   float* err_sq;  // [m] or null
-  const float* Dblk;  // this block's factor rows divided by their diagonal ([NSTEP][NSTEP]), then 1/U_pp [NSTEP]
+  const float* Dblk;  // this block's factor rows in BlockLayout order, then 1/U_pp [NSTEP]
   // look-ahead: errors of the kpend columns swept since the last flush
   // (E buffer from column 0) and the factor rows of those columns restricted
   // to this block's columns (U + r * n + i, leading dimension n)
@@ -62,9 +102,17 @@ struct RowOps;
 template <>
 struct RowOps<16> {
   template <int SRC>
-  __device__ __forceinline__ static float bcast(float v) { return row_bcast<SRC>(v); }
+  __device__ __forceinline__ static float bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xF, 0xF, false));
+  }
   __device__ __forceinline__ static float rmin(float v) { return row_min16(v); }
   __device__ __forceinline__ static float rmax(float v) { return row_max16(v); }
+  __device__ __forceinline__ static float rsum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  }
 };
 template <>
 struct RowOps<4> {
@@ -81,34 +129,44 @@ struct RowOps<4> {
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
     return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
   }
+  __device__ __forceinline__ static float rsum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  }
 };
-
 
 struct GroupState {
   float s, inv_s, nz, mz;  // scale, 1/scale, -z, maxq - z
   float z;
 };
 
-// Range of columns [c0, c1) of this lane's 8 values (block-local column of
-// value k is 8*lane + k), reduced over the row's lanes, then (s, z).
+__device__ __forceinline__ GroupState make_group(float s, float z, int maxq) {
+  GroupState g;
+  g.s = s;
+  g.z = z;
+  g.inv_s = 1.f / s;
+  g.nz = -z;
+  g.mz = (float)maxq - z;
+  return g;
+}
+
+// (s, z) of block columns [c0, c1) of the row: this lane's values there
+// (column of register k: lr + LPR k), reduced over the row's lanes.
 template <int LPR>
 __device__ __forceinline__ GroupState group_params(const float (&v)[8], int lr, int c0, int c1, int maxq) {
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int c = 8 * lr + k;
+    const int c = lr + LPR * k;
     const bool in = c >= c0 && c < c1;
     lo = fminf(lo, in ? v[k] : INFINITY);
     hi = fmaxf(hi, in ? v[k] : -INFINITY);
   }
   lo = RowOps<LPR>::rmin(lo);
   hi = RowOps<LPR>::rmax(hi);
-  GroupState g;
-  qparams(lo, hi, maxq, g.s, g.z);
-  g.inv_s = 1.f / g.s;
-  g.nz = -g.z;
-  g.mz = (float)maxq - g.z;
-  return g;
+  float s, z;
+  qparams(lo, hi, maxq, s, z);
+  return make_group(s, z, maxq);
 }
 
 template <int LPR>
@@ -128,167 +186,186 @@ __device__ __forceinline__ void store_params(const SweepArgs& a, const GroupStat
   }
 }
 
-// GMODE: 0 = (s, z) fixed for the whole block (per-row, or a group spanning
-// several blocks); 8..128 = group size known at compile time, groups start
-// inside the block; -1 = any other in-block group size (runtime).
+__device__ __forceinline__ void store_w(void* W, int dt, int64_t idx, float v) {
+  if (dt == 0) ((_Float16*)W)[idx] = (_Float16)v;
+  else if (dt == 1) ((uint16_t*)W)[idx] = f32_to_bf16(v);
+  else ((float*)W)[idx] = v;
+}
+
 // The errors of the pending columns (swept since the last flush) applied to
 // this block's 128 columns for the workgroup's 16 rows, with
-// v_mfma_f32_16x16x4f32: wave w computes output column blocks 2w, 2w+1; the
-// factor rows stream through the Up buffer (64 at a time, pitch 144, which
-// keeps the operand reads bank-conflict-free).  The result lands in upd
-// (16 x 132) for the lanes' V loads.
-constexpr int KPMAX = (LA - 1) * BMAX;
-constexpr int EPITCH = KPMAX + 4;
-constexpr int CPITCH = 144;
-__device__ __forceinline__ void pending_update(const SweepArgs& a, int64_t r0, float* chunk, float* sE, float* upd) {
+// v_mfma_f32_16x16x4f32: wave w computes output column blocks 2w, 2w+1.  The
+// sum over the KP pending columns is taken in an order that gives every lane
+// contiguous errors: at MFMA step t, lane quarter g takes k = (KP / 4) g + t.
+// Every operand is loaded straight from global memory (the errors as float4
+// runs, the factor rows one float per lane, 16 lanes per 64-byte row piece),
+// all of them before the first MFMA, so the workgroup waits for one round of
+// loads.  The result lands in `upd` (16 x 132 in LDS).
+constexpr int UPITCH = BMAX + 4;
+template <int KP>
+__device__ __forceinline__ void pending_update(const SweepArgs& a, int64_t r0, float* upd) {
+  constexpr int K4 = KP / 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g16 = lane >> 4;
-  const int kp = a.kpend;
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  // 64 factor rows x 128 columns per chunk, 8 float4 per thread; the next
-  // chunk is loaded while the current one is multiplied
-  f32x4 xr[8];
-  auto load_chunk = [&](int k0) {
+  const int64_t erow = min<int64_t>(r0 + l16, a.m - 1);  // rows past m: results never used
+  const f32x4* __restrict__ ep = (const f32x4*)(a.Ep + erow * ELD + K4 * g16);
+  f32x4 ev[K4 / 4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + 256 * u;
-      const int kr = e >> 5, c4 = 4 * (e & 31);  // w is a multiple of 4 on this path
-      xr[u] = c4 < a.w ? *(const f32x4*)&a.Upend[(int64_t)(k0 + kr) * a.n + c4] : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < K4 / 4; ++u) ev[u] = ep[u];
+  // w is a multiple of 4 on this path, so a column block is either inside the block or past it
+  float bv[2][K4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int col = 16 * (2 * wave + q) + l16;
+    const bool in = col < a.w;
+    const float* __restrict__ up = a.Upend + (int64_t)(K4 * g16) * a.n + (in ? col : 0);
+#pragma unroll
+    for (int t = 0; t < K4; ++t) bv[q][t] = up[(int64_t)t * a.n];
+    if (!in) {
+#pragma unroll
+      for (int t = 0; t < K4; ++t) bv[q][t] = 0.f;
     }
-  };
-  load_chunk(0);
-  for (int e = tid; e < 16 * kp; e += 256) {
-    const int rr = e / kp, k = e % kp;
-    const int64_t row = min<int64_t>(r0 + rr, a.m - 1);  // rows past m: their results are never used
-    sE[rr * EPITCH + k] = a.Ep[row * ELD + k];
   }
-  for (int k0 = 0; k0 < kp; k0 += 64) {
-    __syncthreads();  // the previous chunk is consumed (and sE is written)
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + 256 * u;
-      *(f32x4*)&chunk[(e >> 5) * CPITCH + 4 * (e & 31)] = xr[u];
-    }
-    if (k0 + 64 < kp) load_chunk(k0 + 64);
-    __syncthreads();
+  for (int t = 0; t < K4; ++t) {
+    const float av = ev[t / 4][t % 4];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float av = sE[l16 * EPITCH + k0 + 4 * kk + g16];
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, chunk[(4 * kk + g16) * CPITCH + 16 * (2 * wave + q) + l16],
-                                                       acc[q], 0, 0, 0);
-    }
+    for (int q = 0; q < 2; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[q][t], acc[q], 0, 0, 0);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) upd[(4 * g16 + rr) * (BMAX + 4) + 16 * (2 * wave + q) + l16] = acc[q][rr];
-  __syncthreads();  // upd complete; chunk (the Up buffer) free
+    for (int rr = 0; rr < 4; ++rr) upd[(4 * g16 + rr) * UPITCH + 16 * (2 * wave + q) + l16] = acc[q][rr];
+  __syncthreads();  // upd complete
 }
 
+// One block of the sweep.  GMODE: 0 = (s, z) fixed for the whole block
+// (per-row, or a group spanning several blocks); 8..128 = group size known at
+// compile time, groups start inside the block; -1 = any other in-block group
+// size (runtime).  Codes and errors of a lane's columns are taken after the
+// last step from the registers, which keep each column's value from its own
+// step on (the factor row of a later step is zero there); groups narrower than
+// the lanes of a row, and runtime group sizes, capture them at their step.
 template <int LPR, int GMODE, bool LOOK>
 __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
-  constexpr int NSTEP = 8 * LPR;
-  constexpr int PITCH = NSTEP + 4;
+  using LY = BlockLayout<LPR>;
+  constexpr int NSTEP = LY::NSTEP;
   constexpr int ROWS = 256 / LPR;
-  static_assert(!LOOK || (LPR == 16 && 64 * CPITCH <= NSTEP * PITCH), "look-ahead needs the 128-column layout");
-  __shared__ __attribute__((aligned(16))) float Up[NSTEP * PITCH];
+  constexpr bool CAPTURE = GMODE < 0 || (GMODE > 0 && GMODE < LPR);
+  constexpr int NG = (GMODE > 0 && !CAPTURE) ? NSTEP / GMODE : 1;  // groups of the block kept for the end
+  constexpr int USZ = LY::USZ;
+  static_assert(!LOOK || (LPR == 16 && 16 * UPITCH <= USZ), "look-ahead needs the 128-column layout");
+  __shared__ __attribute__((aligned(16))) float Us[USZ];
   __shared__ float invd[NSTEP];
-  __shared__ __attribute__((aligned(16))) float sE[LOOK ? 16 * EPITCH : 1];
-  __shared__ float upd[LOOK ? 16 * (BMAX + 4) : 1];
+  __shared__ uint8_t codes8[ROWS][NSTEP];
   const int tid = threadIdx.x;
   const int lr = tid & (LPR - 1);
-  const int64_t r = (int64_t)blockIdx.x * ROWS + tid / LPR;
+  const int rl = tid / LPR;  // row within the workgroup
+  const int64_t r = (int64_t)blockIdx.x * ROWS + rl;
   const bool active = r < a.m;
   const int w = a.w;
   const int64_t i = a.i;
-  const float* __restrict__ U = a.U;
-  if constexpr (LOOK) {
-    if (a.kpend > 0) pending_update(a, (int64_t)blockIdx.x * ROWS, Up, sE, upd);
-  }
-
-  // this block's factor rows divided by their diagonal (zero on and below it)
-  // and 1/U_pp, prepared once per layer by diag_blocks_kernel
+  // this block's factor rows and 1/U_pp (prepared once per layer by
+  // diag_blocks_kernel) and the rows' values: every load of the kernel's
+  // start in flight at once
+  constexpr int Q4 = LY::USZ / 4, NQ = (Q4 + 255) / 256;
+  f32x4 ublk[NQ];
   {
-    constexpr int Q = NSTEP * NSTEP / 4;  // float4 groups
     const f32x4* src = (const f32x4*)a.Dblk;
-    f32x4 t[Q / 256];
 #pragma unroll
-    for (int u = 0; u < Q / 256; ++u) t[u] = src[tid + 256 * u];
-#pragma unroll
-    for (int u = 0; u < Q / 256; ++u) {
+    for (int u = 0; u < NQ; ++u) {
       const int q = tid + 256 * u;
-      const int p = q / (NSTEP / 4), j4 = q % (NSTEP / 4);
-      *(f32x4*)&Up[p * PITCH + 4 * j4] = t[u];
+      ublk[u] = (Q4 % 256 == 0 || q < Q4) ? src[q] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (tid < NSTEP) invd[tid] = a.Dblk[NSTEP * NSTEP + tid];
   }
-  (void)U;
-
-  float v[8], ek[8], qk[8];
-  const bool vec = ((a.n | i) & 3) == 0;  // 16-byte aligned rows of V
-  if (vec && active && 8 * lr + 8 <= w) {
-    const f32x4 x0 = *(const f32x4*)&a.V[r * a.n + i + 8 * lr];
-    const f32x4 x1 = *(const f32x4*)&a.V[r * a.n + i + 8 * lr + 4];
-    v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
-    v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
-  } else {
+  const float invd_t = tid < NSTEP ? a.Dblk[LY::USZ + tid] : 0.f;
+  float v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = 8 * lr + k;
-      v[k] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
-    }
+  for (int k = 0; k < 8; ++k) {
+    const int c = lr + LPR * k;
+    v[k] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
   }
   if constexpr (LOOK) {
     if (a.kpend > 0) {
+      if (a.kpend == BMAX) pending_update<BMAX>(a, (int64_t)blockIdx.x * ROWS, Us);
+      else pending_update<BMAX / 2>(a, (int64_t)blockIdx.x * ROWS, Us);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int c = 8 * lr + k;
-        if (c < w) v[k] -= upd[(tid / LPR) * (BMAX + 4) + c];
-      }
+      for (int k = 0; k < 8; ++k) v[k] -= Us[rl * UPITCH + lr + LPR * k];
+      __syncthreads();  // upd consumed before the factor block overwrites it
     }
   }
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const int q = tid + 256 * u;
+    if (Q4 % 256 == 0 || q < Q4) ((f32x4*)Us)[q] = ublk[u];
+  }
+  if (tid < NSTEP) invd[tid] = invd_t;
+
+  GroupState g = make_group(1.f, 0.f, a.maxq);
+  if (GMODE == 0 && active) {
+    const int64_t gi = a.group <= 0 ? 0 : i / a.group;
+    g = make_group(a.S[r * a.G + gi], (float)a.Z[r * a.G + gi], a.maxq);
+  }
+  GroupState gk[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) gk[k] = g;
+  float ek[8], qk[8], sk[8], zk[8];  // CAPTURE only: error, qz, scale and zero point of the column
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     ek[k] = 0.f;
     qk[k] = 0.f;
+    sk[k] = 1.f;
+    zk[k] = 0.f;
   }
-  GroupState g;
-  g.s = 1.f;
-  g.z = 0.f;
-  if (GMODE == 0 && active) {
-    const int64_t gi = a.group <= 0 ? 0 : i / a.group;
-    g.s = a.S[r * a.G + gi];
-    g.z = (float)a.Z[r * a.G + gi];
-  }
-  g.inv_s = 1.f / g.s;
-  g.nz = -g.z;
-  g.mz = (float)a.maxq - g.z;
   int next_group = 0;  // GMODE == -1: block-local column of the next group start
   const bool writer = active && lr == 0;
   __syncthreads();
 
-  // factor row p of this lane's 8 columns, prefetched two columns ahead
-  f32x4 ua[3], ub[3];
-  ua[0] = *(const f32x4*)&Up[0 * PITCH + 8 * lr];
-  ub[0] = *(const f32x4*)&Up[0 * PITCH + 8 * lr + 4];
-  ua[1] = *(const f32x4*)&Up[1 * PITCH + 8 * lr];
-  ub[1] = *(const f32x4*)&Up[1 * PITCH + 8 * lr + 4];
+  // factor rows prefetched D steps ahead into a ring of registers (only the
+  // live registers J..7 of each row)
+  constexpr int D = 4;
+  float u[D + 1][8];
+  auto load_row = [&](auto PC) {
+    constexpr int P = decltype(PC)::value;
+    constexpr int J = P / LPR;
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      (
+          [&] {
+            constexpr int R0 = LY::SEG[J][S][0], LEN = LY::SEG[J][S][1];
+            constexpr int O = LY::seg_off(P, S);
+            if constexpr (LEN == 4) {
+              const f32x4 x = *(const f32x4*)&Us[O + 4 * lr];
+              u[P % (D + 1)][R0] = x[0]; u[P % (D + 1)][R0 + 1] = x[1];
+              u[P % (D + 1)][R0 + 2] = x[2]; u[P % (D + 1)][R0 + 3] = x[3];
+            } else if constexpr (LEN == 2) {
+              const float2 x = *(const float2*)&Us[O + 2 * lr];
+              u[P % (D + 1)][R0] = x.x; u[P % (D + 1)][R0 + 1] = x.y;
+            } else {
+              u[P % (D + 1)][R0] = Us[O + lr];
+            }
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, LY::NSEG[J]>{});
+  };
+  [&]<int... P>(std::integer_sequence<int, P...>) {
+    (load_row(std::integral_constant<int, P>{}), ...);
+  }(std::make_integer_sequence<int, D>{});
 
   // one column per step, fully unrolled so that register and DPP lane
   // indices are compile-time constants
   [&]<int... P>(std::integer_sequence<int, P...>) {
     (
         [&] {
-          if constexpr (P + 2 < NSTEP) {
-            ua[(P + 2) % 3] = *(const f32x4*)&Up[(P + 2) * PITCH + 8 * lr];
-            ub[(P + 2) % 3] = *(const f32x4*)&Up[(P + 2) * PITCH + 8 * lr + 4];
-          }
+          if constexpr (P + D < NSTEP) load_row(std::integral_constant<int, P + D>{});
+          // keep the prefetch where it is: the scheduler would otherwise sink
+          // the loads next to their use, D steps later
+          __builtin_amdgcn_sched_barrier(0);
           if constexpr (GMODE > 0) {
             if constexpr (P % GMODE == 0) {
               g = group_params<LPR>(v, lr, P, P + GMODE < w ? P + GMODE : w, a.maxq);
               store_params(a, g, r, i + P, writer && P < w);
+              if constexpr (!CAPTURE) gk[P / GMODE] = g;
             }
           } else if constexpr (GMODE < 0) {
             if (P == next_group && P < w) {
@@ -298,103 +375,138 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
               next_group += (int)a.group;
             }
           }
-          const float vp = RowOps<LPR>::template bcast<(P >> 3)>(v[P & 7]);
+          constexpr int J = P / LPR;  // register of column P (registers below are final)
+          const float vp = RowOps<LPR>::template bcast<P % LPR>(v[J]);
           const float qz = __builtin_amdgcn_fmed3f(rintf(vp * g.inv_s), g.nz, g.mz);
           const float err = fmaf(-g.s, qz, vp);
-          if (lr == (P >> 3)) {  // the owner keeps the error and the code of its column
-            ek[P & 7] = err;
-            qk[P & 7] = qz + g.z;
+          if constexpr (CAPTURE) {
+            if (lr == P % LPR) {
+              ek[J] = err;
+              qk[J] = qz;
+              sk[J] = g.s;
+              zk[J] = g.z;
+            }
           }
-          const f32x4 u0 = ua[P % 3], u1 = ub[P % 3];
-          v[0] = fmaf(-err, u0[0], v[0]);
-          v[1] = fmaf(-err, u0[1], v[1]);
-          v[2] = fmaf(-err, u0[2], v[2]);
-          v[3] = fmaf(-err, u0[3], v[3]);
-          v[4] = fmaf(-err, u1[0], v[4]);
-          v[5] = fmaf(-err, u1[1], v[5]);
-          v[6] = fmaf(-err, u1[2], v[6]);
-          v[7] = fmaf(-err, u1[3], v[7]);
+#pragma unroll
+          for (int k = J; k < 8; ++k) v[k] = fmaf(-err, u[P % (D + 1)][k], v[k]);
         }(),
         ...);
   }(std::make_integer_sequence<int, NSTEP>{});
 
-  // scaled errors e = err / U_pp of this lane's columns, their squares summed over the row
+  // codes, errors and dequantized weights of this lane's columns
   float eacc = 0.f;
+  float ws_[8], qz_[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    ek[k] *= invd[8 * lr + k];
-    eacc = fmaf(ek[k], ek[k], eacc);
-  }
-  if constexpr (LPR == 16) {
-    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0xB1, 0xF, 0xF, false));
-    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0x4E, 0xF, 0xF, false));
-    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0x124, 0xF, 0xF, false));
-    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0x128, 0xF, 0xF, false));
-  } else {
-    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0xB1, 0xF, 0xF, false));
-    eacc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, eacc), 0x4E, 0xF, 0xF, false));
-  }
-
-  if (active) {
-    if (8 * lr + 8 <= w) {
-      *(f32x4*)&a.E[r * ELD + 8 * lr] = f32x4{ek[0], ek[1], ek[2], ek[3]};
-      *(f32x4*)&a.E[r * ELD + 8 * lr + 4] = f32x4{ek[4], ek[5], ek[6], ek[7]};
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        lo |= (uint32_t)(int)qk[k] << (8 * k);
-        hi |= (uint32_t)(int)qk[k + 4] << (8 * k);
-      }
-      uint8_t* q = a.Q8 + r * a.n + i + 8 * lr;
-      if ((((uintptr_t)q) & 7) == 0) {
-        *(uint2*)q = make_uint2(lo, hi);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) q[k] = (uint8_t)(int)qk[k];
-      }
+    const int c = lr + LPR * k;
+    float err, qz, s;
+    if constexpr (CAPTURE) {
+      err = ek[k];
+      qz = qk[k];
+      s = sk[k];
     } else {
+      const GroupState& gc = gk[GMODE > 0 ? (LPR * k) / GMODE : 0];
+      qz = __builtin_amdgcn_fmed3f(rintf(v[k] * gc.inv_s), gc.nz, gc.mz);
+      err = fmaf(-gc.s, qz, v[k]);
+      s = gc.s;
+    }
+    const float e = err * invd[c];
+    ek[k] = e;
+    qz_[k] = qz;
+    ws_[k] = s;
+    eacc = fmaf(e, e, eacc);
+  }
+  eacc = RowOps<LPR>::rsum(eacc);
+  if (active) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int c = 8 * lr + k;
-        if (c < w) {
-          a.E[r * ELD + c] = ek[k];
-          a.Q8[r * a.n + i + c] = (uint8_t)(int)qk[k];
-        }
+    for (int k = 0; k < 8; ++k) {
+      const int c = lr + LPR * k;
+      if (c < w) {
+        a.E[r * ELD + c] = ek[k];
+        if (a.Wout) store_w(a.Wout, a.wdt, r * a.ldw + i + c, ws_[k] * qz_[k]);
       }
     }
-    if (lr == 0 && a.err_sq) a.err_sq[r] += eacc;
+    // blocks run one launch after another, so each row's sum is taken in block order
+    if (lr == 0 && a.err_sq) atomicAdd(a.err_sq + r, eacc);
+  }
+  // codes: q = qz + z, as bytes (fallback layout) or packed per row
+  float zc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if constexpr (CAPTURE) {
+      zc[k] = zk[k];
+    } else {
+      zc[k] = gk[GMODE > 0 ? (LPR * k) / GMODE : 0].z;
+    }
+  }
+  if (a.Qw == nullptr) {
+    if (active) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = lr + LPR * k;
+        if (c < w) a.Q8[r * a.n + i + c] = (uint8_t)(int)(qz_[k] + zc[k]);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) codes8[rl][lr + LPR * k] = (uint8_t)(int)(qz_[k] + zc[k]);
+  // the row's codes were written by lanes of this wave only: wait for the
+  // wave's LDS writes before its lanes read each other's bytes
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  if (!active) return;
+  // lane lr packs words lr and lr + LPR of the block (a block of NSTEP codes
+  // of at most 8 bits is at most NSTEP / 4 = 2 LPR words); a word touches at
+  // most 17 codes (2-bit codes, one straddling in), all read at once
+  const int bits = a.bits;
+  const int nwords = (w * bits + 31) / 32;
+  uint32_t* dst = a.Qw + r * a.words + (i * bits) / 32;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int wd = lr + LPR * h;
+    const int bit0 = 32 * wd;
+    const int j0 = bit0 / bits;
+    constexpr int MAXC = 17;
+    uint32_t q[MAXC];
+#pragma unroll
+    for (int t = 0; t < MAXC; ++t) q[t] = codes8[rl][min(j0 + t, NSTEP - 1)];
+    uint32_t word = 0;
+#pragma unroll
+    for (int t = 0; t < MAXC; ++t) {
+      const int j = j0 + t;
+      const int sh = j * bits - bit0;
+      if (j < w && sh < 32) word |= sh >= 0 ? (q[t] << sh) : (q[t] >> (-sh));
+    }
+    if (wd < nwords) dst[wd] = word;
   }
 }
 
-// Per block of B columns starting at i = blk * B: rows p of U[i:i+w, i:i+w]
-// divided by U_pp, zero on and below the diagonal, padded to NSTEP x NSTEP,
-// followed by 1/U_pp (0 past w).
-template <int NSTEP>
-// One workgroup per (block, 8 rows of it): every load of the workgroup in
-// flight at once.
+// Per block of B columns starting at i = blk * B: the factor rows p of
+// U[i:i+w, i:i+w] divided by U_pp, zero on and left of the diagonal, in
+// BlockLayout<LPR> order, then 1/U_pp (0 past w).  One thread per (row p,
+// lane lr), writing the row's live registers of that lane.
+template <int LPR>
 __global__ __launch_bounds__(256) void diag_blocks_kernel(const float* U, int64_t n, int64_t B, float* out) {
+  using LY = BlockLayout<LPR>;
   const int64_t i = (int64_t)blockIdx.x * B;
   const int w = (int)std::min<int64_t>(B, n - i);
-  float* dst = out + (int64_t)blockIdx.x * (NSTEP * NSTEP + NSTEP);
-  const int p0 = 8 * blockIdx.y;
-  constexpr int PER = 8 * NSTEP / 256;  // elements per thread
-  float u[PER], d[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int idx = threadIdx.x + 256 * k;
-    const int p = p0 + idx / NSTEP, j = idx % NSTEP;
-    const bool in = p < w && j < w && j > p;
-    u[k] = in ? U[(i + p) * n + i + j] : 0.f;
-    d[k] = in ? U[(i + p) * n + i + p] : 1.f;
-  }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int idx = threadIdx.x + 256 * k;
-    dst[(p0 + idx / NSTEP) * NSTEP + idx % NSTEP] = u[k] / d[k];
-  }
-  if (threadIdx.x < 8) {
-    const int p = p0 + threadIdx.x;
-    dst[NSTEP * NSTEP + p] = (p < w) ? 1.f / U[(i + p) * n + i + p] : 0.f;
+  float* dst = out + (int64_t)blockIdx.x * LY::STRIDE;
+  const int t = blockIdx.y * 256 + threadIdx.x;
+  const int p = t / LPR, lr = t % LPR;
+  if (p < LY::NSTEP) {
+    const int J = p / LPR;
+    const bool prow = p < w;
+    const float d = prow ? U[(i + p) * n + i + p] : 1.f;
+    for (int s = 0; s < LY::NSEG[J]; ++s) {
+      const int r0 = LY::SEG[J][s][0], len = LY::SEG[J][s][1];
+      const int o = LY::seg_off(p, s) + len * lr;
+      for (int k = 0; k < len; ++k) {
+        const int c = lr + LPR * (r0 + k);
+        dst[o + k] = (prow && c < w && c > p) ? U[(i + p) * n + i + c] / d : 0.f;
+      }
+    }
+    if (lr == 0) dst[LY::USZ + p] = prow ? 1.f / d : 0.f;
   }
 }
 
@@ -502,57 +614,6 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* Q8, int64_t m,
   }
 }
 
-// W <- s (q - z) in W's dtype.
-template <int DT>
-__global__ __launch_bounds__(256) void dequant_kernel(void* W, int64_t ldw, const uint8_t* Q8, const float* S,
-                                                      const int32_t* Z, int64_t m, int64_t n, int64_t group,
-                                                      int64_t G) {
-  for (int64_t r = blockIdx.y; r < m; r += gridDim.y)
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n; c += (int64_t)gridDim.x * 256) {
-    const int64_t g = group <= 0 ? 0 : c / group;
-    const float s = S[r * G + g];
-    const float z = (float)Z[r * G + g];
-    Elem<DT>::store(W, r * ldw + c, s * ((float)Q8[r * n + c] - z));
-  }
-}
-
-// The same, 8 elements per thread (n % 8 == 0, ldw % 8 == 0, 16-byte aligned W).
-template <int DT>
-__global__ __launch_bounds__(256) void dequant_x8_kernel(void* W, int64_t ldw, const uint8_t* Q8, const float* S,
-                                                         const int32_t* Z, int64_t m, int64_t n, int64_t group,
-                                                         int64_t G) {
-  for (int64_t r = blockIdx.y; r < m; r += gridDim.y)
-    for (int64_t c = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x); c < n; c += (int64_t)gridDim.x * 2048) {
-      const uint2 q = *(const uint2*)(Q8 + r * n + c);
-      float y[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int64_t g = group <= 0 ? 0 : (c + k) / group;
-        const uint32_t qb = ((k < 4 ? q.x : q.y) >> (8 * (k & 3))) & 0xFFu;
-        y[k] = S[r * G + g] * ((float)qb - (float)Z[r * G + g]);
-      }
-      if (DT == 2) {
-        *(f32x4*)((float*)W + r * ldw + c) = f32x4{y[0], y[1], y[2], y[3]};
-        *(f32x4*)((float*)W + r * ldw + c + 4) = f32x4{y[4], y[5], y[6], y[7]};
-      } else {
-        uint32_t wv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint16_t lo, hi;
-          if (DT == 0) {
-            lo = __builtin_bit_cast(uint16_t, (_Float16)y[2 * k]);
-            hi = __builtin_bit_cast(uint16_t, (_Float16)y[2 * k + 1]);
-          } else {
-            lo = f32_to_bf16(y[2 * k]);
-            hi = f32_to_bf16(y[2 * k + 1]);
-          }
-          wv[k] = (uint32_t)lo | ((uint32_t)hi << 16);
-        }
-        *(uint4*)((uint16_t*)W + r * ldw + c) = uint4{wv[0], wv[1], wv[2], wv[3]};
-      }
-    }
-}
-
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 dim3 rows_grid(int64_t cols, int64_t rows) {
@@ -561,13 +622,11 @@ dim3 rows_grid(int64_t cols, int64_t rows) {
 
 }  // namespace
 
-// Workspace: fp32 working copy V [m x n], codes [m x n] bytes, E [m x 128],
-// then the prepared diagonal factor blocks.
-inline int nstep_for(int64_t B) { return B <= 32 ? 32 : BMAX; }
-inline size_t dblk_bytes(int64_t n, int64_t B) {
-  const int64_t ns = nstep_for(B);
-  return (size_t)cdiv(n, B) * (size_t)(ns * ns + ns) * 4;
-}
+// Workspace: fp32 working copy V [m x n], codes [m x n] bytes (used only when
+// a block's codes do not fill whole 32-bit words), E [m x 256], then the
+// prepared diagonal factor blocks.
+inline int64_t dstride_for(int64_t B) { return B <= 32 ? BlockLayout<4>::STRIDE : BlockLayout<16>::STRIDE; }
+inline size_t dblk_bytes(int64_t n, int64_t B) { return (size_t)cdiv(n, B) * (size_t)dstride_for(B) * 4; }
 
 size_t quantize_workspace_bytes(int64_t m, int64_t n, int64_t B) {
   if (m < 1 || n < 1 || B < 1) return 0;
@@ -585,8 +644,10 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   float* E = (float*)p;
   p += align256((size_t)m * ELD * 4);
   float* Dblk = (float*)p;
-  const int nstep = nstep_for(B);
-  const int64_t dstride = (int64_t)nstep * nstep + nstep;
+  const int64_t dstride = dstride_for(B);
+  // every block starts on a word boundary of the packed rows: the sweep packs its own codes
+  const bool packed = (B * bits) % 32 == 0;
+  const int64_t words = cdiv(n * bits, 32);
 
   const int maxq = (1 << bits) - 1;
   const int64_t G = group <= 0 ? 1 : cdiv(n, group);
@@ -610,8 +671,12 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   if (err_sq)
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(m, 256), 1024)), dim3(256), 0, st,
                        err_sq, m);
-  if (nstep == 32) hipLaunchKernelGGL((diag_blocks_kernel<32>), dim3((unsigned)cdiv(n, B), 32 / 8), dim3(256), 0, st, U, n, B, Dblk);
-  else hipLaunchKernelGGL((diag_blocks_kernel<BMAX>), dim3((unsigned)cdiv(n, B), BMAX / 8), dim3(256), 0, st, U, n, B, Dblk);
+  if (B <= 32)
+    hipLaunchKernelGGL((diag_blocks_kernel<4>), dim3((unsigned)cdiv(n, B), (unsigned)cdiv(32 * 4, 256)), dim3(256), 0,
+                       st, U, n, B, Dblk);
+  else
+    hipLaunchKernelGGL((diag_blocks_kernel<16>), dim3((unsigned)cdiv(n, B), (unsigned)cdiv(128 * 16, 256)), dim3(256),
+                       0, st, U, n, B, Dblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -622,7 +687,8 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
     if (group > B && i % group == 0)
       hipLaunchKernelGGL(row_params_kernel, dim3(prow), dim3(256), 0, st, (const float*)V, m, n, i, group, maxq, S,
                          Z, G, i / group);
-    SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, Q8, E + eoff, err_sq, Dblk + (i / B) * dstride,
+    SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, packed ? nullptr : Q8, packed ? qcodes : nullptr, words,
+                bits, write_dequant ? W : nullptr, dt, ldw, E + eoff, err_sq, Dblk + (i / B) * dstride,
                 E, (int)(i - g0), U + g0 * n + i};
     if (B <= 32) launch_sweep<4, false>(a, gmode, st);
     else if (look) launch_sweep<16, true>(a, gmode, st);
@@ -666,16 +732,8 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
       if ((e = flush(i, w, i + w, n - i - w)) != hipSuccess) return e;
     }
   }
-  const int64_t words = cdiv(n * bits, 32);
-  hipLaunchKernelGGL(pack_kernel, rows_grid(words, m), dim3(256), 0, st, (const uint8_t*)Q8, m, n, bits, qcodes, words);
-  if (write_dequant) {
-    if (x8 && dt == 0) hipLaunchKernelGGL((dequant_x8_kernel<0>), rg8, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
-    else if (x8 && dt == 1) hipLaunchKernelGGL((dequant_x8_kernel<1>), rg8, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
-    else if (x8) hipLaunchKernelGGL((dequant_x8_kernel<2>), rg8, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
-    else if (dt == 0) hipLaunchKernelGGL((dequant_kernel<0>), rg, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
-    else if (dt == 1) hipLaunchKernelGGL((dequant_kernel<1>), rg, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
-    else hipLaunchKernelGGL((dequant_kernel<2>), rg, dim3(256), 0, st, W, ldw, (const uint8_t*)Q8, (const float*)S, (const int32_t*)Z, m, n, group, G);
-  }
+  if (!packed)
+    hipLaunchKernelGGL(pack_kernel, rows_grid(words, m), dim3(256), 0, st, (const uint8_t*)Q8, m, n, bits, qcodes, words);
   return hipGetLastError();
 }
 

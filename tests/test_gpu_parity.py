@@ -144,6 +144,10 @@ SWEEP_CASES = [
     (16, 200, 4, 4, 8, "f32"),
     (64, 1000, 4, 64, 64, "f16"),     # look-ahead path, B = 64, ragged last group and block
     (130, 2048, 4, 128, 128, "bf16"),  # look-ahead path, four full groups of four blocks
+    (20, 300, 4, 0, 100, "f16"),      # 100-column blocks: codes do not fill whole words per block
+    (24, 500, 3, 0, 96, "f32"),       # 96-column blocks, 3-bit codes packed inside the sweep
+    (40, 384, 4, 8, 128, "f16"),      # groups narrower than a row's lanes: captured at their step
+    (36, 640, 5, 32, 128, "bf16"),    # four groups per block, 5-bit codes straddling words
 ]
 
 
