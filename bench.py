@@ -8,6 +8,21 @@ synth/ and resident in HBM before timing.  A step is the whole path:
 restore W, zero H, gptq_hessian_accumulate, gptq_prepare_hinv,
 gptq_quantize_layer (with the dequantized weights written back).
 
+--workload picks another layer shape: tiny (64x128 fp32), mlp_up / mlp_down
+(11008x4096 / 4096x11008, 3-bit per row, 262144 tokens), qkv / o / gate_up /
+down7b (a 7B block's jobs over 65536 tokens: q/k/v stacked to 12288 rows and
+gate/up to 22016 rows, each on one shared Hessian), fc1 / fc2 (a 175B-class
+FFN shard, 3-bit g128, 262144 tokens).
+
+Beside the whole-step time the line carries, per phase, the median and the
+minimum of the HIP-event times over the timed steps and the phase's roofline
+fraction from its algorithmic work: SYRK n(n+1)T flops against dense fp16
+MFMA; the inverse factor 4n^3/3 flops (the route run here executes 2n^3/3)
+against fp32 MFMA; the trailing update's GEMM kernels the flops they perform of
+m n (n - B) against fp32 MFMA; the sweep kernel m n (4 + 4 + b/8) + 8 m G +
+4 n B bytes against HBM.  The two quantize-phase splits come from GPU kernel
+durations recorded by torch.profiler over one further step.
+
 Prints one JSON line (rank 0).  Multi-GPU runs are not supported.
 
 --kernel w4a16 instead times the runtime use of a packed layer,
@@ -47,17 +62,25 @@ PEAK_TF16 = 2500.0     # MI355X dense fp16 MFMA, TFLOP/s
 PEAK_TF32 = 157.3      # MI355X fp32 MFMA, TFLOP/s
 PEAK_HBM = 8000.0      # GB/s
 # measured on one MI355X by `bench.py --kernel peaks` (profiles/attainable_peaks.md):
-# fp16 MFMA stream with random operands, HBM read stream
+# fp16 MFMA stream with random operands, fp32 MFMA stream, HBM read stream
 ATTAIN_TF16 = 1726.4
+ATTAIN_TF32 = 155.0
 ATTAIN_HBM_READ = 6390.2
+
+# --workload name -> (synth workload, job index)
+LAYERS = {
+    "tiny": ("tiny", 0), "attn": ("attn", 0), "mlp_up": ("mlp", 0), "mlp_down": ("mlp", 1),
+    "qkv": ("block7b", 0), "o": ("block7b", 1), "gate_up": ("block7b", 2), "down7b": ("block7b", 3),
+    "fc1": ("ffn175b", 0), "fc2": ("ffn175b", 1),
+}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="attn", choices=["attn", "tiny"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="attn", choices=sorted(LAYERS))
     ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "rotate", "stack", "peaks", "obq"],
                     help="layer: the quantization path (default); w4a16: the packed layer at run time; "
                          "rotate: the Hadamard rotation before GPTQ; peaks: measured attainable MFMA and HBM rates")
@@ -69,18 +92,51 @@ def parse():
     return ap.parse_args()
 
 
+def host_info():
+    """CPU model, memory and the BLAS numpy calls, for the CPU-baseline record."""
+    import platform
+
+    import numpy as np
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    ram = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    ram = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        b = np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name')} {b.get('version')}"
+    except Exception:  # noqa: BLE001 - older numpy: no dict form
+        pass
+    return {"cpu": cpu, "logical_cpus": os.cpu_count(), "ram_gib": ram, "blas": blas}
+
+
 def cpu_baseline(W16, X16, job, U_gpu):
     """The fp64 oracle timed on a bounded sample of the same layer, scaled to
-    one full layer: H over 32 of the 128 token chunks (x4), the inverse factor
-    at full size (x1), the sweep over 1024 of the 4096 rows (x4)."""
+    one full layer: H over a whole number of 2048-token chunks (about 65536
+    tokens at n = 4096, fewer for wider layers), the inverse factor at full
+    size, the sweep over a subset of rows (about 4 M weights)."""
     import numpy as np
 
     import oracle as O
     T = X16.shape[0]
     n = W16.shape[1]
     m = W16.shape[0]
-    tok = min(T, 32 * 2048)
-    rows = min(m, 1024)
+    tok = max(2048, min(T, int(65536 * (4096 / n) ** 2) // 2048 * 2048))
+    rows = max(8, min(m, int(4 * 2 ** 20 // n)))
     t0 = time.perf_counter()
     H = O.hessian([X16[c:c + 2048] for c in range(0, tok, 2048)])
     t1 = time.perf_counter()
@@ -93,9 +149,9 @@ def cpu_baseline(W16, X16, job, U_gpu):
     est = (t1 - t0) * (T / tok) + (t2 - t1) + (t3 - t2) * (m / rows)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(est * 1e3, 1), "unit": "ms per layer (estimated from the sample)", "cores": threads,
-            "kind": "oracle",
-            "sample": f"fp64 oracle: Hessian over {tok} of {T} tokens (x{T // tok}), full {n}x{n} inverse factor, "
-                      f"sweep of {rows} of {m} rows (x{m // rows}); stage seconds "
+            "kind": "oracle", "host": host_info(),
+            "sample": f"fp64 oracle: Hessian over {tok} of {T} tokens (x{T / tok:g}), full {n}x{n} inverse factor, "
+                      f"sweep of {rows} of {m} rows (x{m / rows:.2f}); stage seconds "
                       f"{t1 - t0:.2f}/{t2 - t1:.2f}/{t3 - t2:.2f}"}
 
 
@@ -512,6 +568,72 @@ def main():
     if args.kernel == "obq":
         bench_obq(args)
         return
+    bench_layer(args)
+
+
+def trailing_schedule(m: int, n: int, B: int, group: int):
+    """Flops of the trailing update m n (n - B) split as gptq_quantize_layer
+    runs it: (flops in the GEMM kernels, flops applied inside the sweep
+    kernel).  With B a multiple of 64 and groups no wider than a block the
+    blocks go in pairs: the second block of a pair takes the first one's
+    errors on its own columns inside the sweep, then one GEMM with K = 2B
+    updates the columns after the pair."""
+    look = B % 64 == 0 and (group <= 0 or group <= B) and n % 4 == 0
+    gemm = in_sweep = 0.0
+    if look:
+        g0 = 0
+        while g0 < n:
+            w1 = min(B, n - g0)
+            w2 = min(B, n - g0 - w1)
+            in_sweep += 2.0 * m * w1 * w2
+            i = g0 + w1 + w2
+            gemm += 2.0 * m * (i - g0) * (n - i)
+            g0 = i
+    else:
+        for i in range(0, n, B):
+            w = min(B, n - i)
+            gemm += 2.0 * m * w * (n - i - w)
+    return gemm, in_sweep
+
+
+def kernel_ms(fn, groups):
+    """GPU durations (ms) of the kernels fn() launches, summed per group of
+    kernel-name substrings, from torch.profiler's device activity; None when
+    the profiler gives no device events."""
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        fn()
+        torch.cuda.synchronize()
+    tot = {g: 0.0 for g in groups}
+    seen = 0
+    for e in prof.key_averages():
+        us = getattr(e, "device_time_total", None)
+        if us is None:
+            us = getattr(e, "cuda_time_total", 0.0)
+        if not us:
+            continue
+        for g, subs in groups.items():
+            if any(k in e.key for k in subs):
+                tot[g] += us / 1e3
+                seen += 1
+                break
+    return tot if seen else None
+
+
+def _phase(ms_list, work, unit, peak, attain=None, attain_src=None, scale=1e12):
+    import numpy as np
+    med, mn = float(np.median(ms_list)), float(np.min(ms_list))
+    rate = work / (med * 1e-3) / scale
+    d = {"ms_median": round(med, 4), "ms_min": round(mn, 4), "work": work, "achieved": round(rate, 2),
+         "unit": unit, "peak": peak, "frac": round(rate / peak, 4)}
+    if attain:
+        d["attainable"] = {"peak": attain, "frac": round(rate / attain, 4), "source": attain_src}
+    return d
+
+
+def bench_layer(args):
     import numpy as np
     import torch
 
@@ -519,42 +641,57 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
-    wl = synth.workloads()[args.workload]
-    job = wl.jobs[0]
+    wkey, jidx = LAYERS[args.workload]
+    wl = synth.workloads()[wkey]
+    job = wl.jobs[jidx]
     t_gen = time.perf_counter()
     W_np = synth.stacked_weight(job, wl.seed, wl.wid)
     X_np = synth.x_full(job.x, wl.seed, wl.wid)
     t_gen = time.perf_counter() - t_gen
     m, n = W_np.shape
     T = X_np.shape[0]
+    B, bits, group = job.block, job.bits, job.group
     W0 = torch.from_numpy(W_np).to(dev)
     X = torch.from_numpy(X_np).to(dev)
+    keep_host = not args.no_cpu_baseline
+    if not keep_host:
+        del X_np
     Wk = W0.clone()
     H = torch.zeros((n, n), dtype=torch.float32, device=dev)
     U = torch.empty_like(H)
     hws = torch.empty(max(pw.hessian_workspace_bytes(n, T), 1), dtype=torch.uint8, device=dev)
     pws = torch.empty(pw.prepare_workspace_bytes(n), dtype=torch.uint8, device=dev)
-    qws = torch.empty(pw.quantize_workspace_bytes(m, n, job.block), dtype=torch.uint8, device=dev)
+    qws = torch.empty(pw.quantize_workspace_bytes(m, n, B), dtype=torch.uint8, device=dev)
+    G = pw.n_groups(n, group)
     out = {
-        "qcodes": torch.empty((m, pw.packed_words(n, job.bits)), dtype=torch.int32, device=dev),
-        "scales": torch.empty((m, pw.n_groups(n, job.group)), dtype=torch.float32, device=dev),
-        "zeros": torch.empty((m, pw.n_groups(n, job.group)), dtype=torch.int32, device=dev),
+        "qcodes": torch.empty((m, pw.packed_words(n, bits)), dtype=torch.int32, device=dev),
+        "scales": torch.empty((m, G), dtype=torch.float32, device=dev),
+        "zeros": torch.empty((m, G), dtype=torch.int32, device=dev),
         "err_sq": torch.empty((m,), dtype=torch.float32, device=dev),
     }
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     phase = {"hessian": [], "prepare": [], "quantize": []}
     info_t = None
 
-    def step(record: bool):
+    def hess():
+        pw.hessian_accumulate(H, X, workspace=hws)
+
+    def prep():
         nonlocal info_t
+        _, _, info_t = pw.prepare_hinv(H, job.damp, U=U, workspace=pws)
+
+    def quant():
+        pw.quantize_layer(Wk, U, bits, group, B, write_dequant=True, workspace=qws, out=out)
+
+    def step(record: bool):
         Wk.copy_(W0)
         H.zero_()
         ev[0].record()
-        pw.hessian_accumulate(H, X, workspace=hws)
+        hess()
         ev[1].record()
-        _, _, info_t = pw.prepare_hinv(H, job.damp, U=U, workspace=pws)
+        prep()
         ev[2].record()
-        pw.quantize_layer(Wk, U, job.bits, job.group, job.block, write_dequant=True, workspace=qws, out=out)
+        quant()
         ev[3].record()
         if record:
             torch.cuda.synchronize()
@@ -565,7 +702,7 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    print(f"# inputs generated in {t_gen:.1f}s; warmup done", file=sys.stderr, flush=True)
+    print(f"# {args.workload}: inputs generated in {t_gen:.1f}s; warmup done", file=sys.stderr, flush=True)
     # timed region: exactly K steps, synchronized on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -573,17 +710,65 @@ def main():
         step(False)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    # per-phase HIP-event timings over K further steps (same stream as the kernels)
-    for _ in range(args.steps):
+    # per-phase HIP-event timings over max(K, 20) further steps (same stream as the kernels)
+    for _ in range(max(args.steps, 20)):
         step(True)
     assert int(info_t.item()) == 0, "damped Hessian not positive definite"
-    ph = {k: float(np.mean(v)) for k, v in phase.items()}
+    print("# timed; splitting the quantize phase", file=sys.stderr, flush=True)
 
-    flops_syrk = float(n) * (n + 1) * T
-    achieved = flops_syrk / (ph["hessian"] * 1e-3) / 1e12
-    traffic = traffic_bytes(args.traffic)
+    # the quantize phase's kernels, by GPU duration (one further step of it)
+    split = None
+    try:
+        Wk.copy_(W0)
+        split = kernel_ms(quant, {"sweep": ("sweep_block_kernel",),
+                                  "trailing_gemm": ("gemm_nn_dma_kernel", "gemm_f32_kernel", "gemm_split_reduce"),
+                                  "other": ("to_f32", "diag_blocks", "row_params", "pack_kernel", "dequant",
+                                            "zero_f32")})
+    except Exception as exc:  # noqa: BLE001 - the split is reported as missing, the rest stands
+        print(f"# quantize-phase split unavailable: {exc}", file=sys.stderr, flush=True)
+
+    syrk_flop = float(n) * (n + 1) * T
+    prep_flop = 4.0 * n ** 3 / 3
+    gemm_flop, in_sweep_flop = trailing_schedule(m, n, B, group)
+    sweep_bytes = m * n * (4 + 4 + bits / 8) + 8.0 * m * G + 4.0 * n * B
+    ph = {
+        "syrk": _phase(phase["hessian"], syrk_flop, "TFLOP/s", PEAK_TF16, ATTAIN_TF16,
+                       "bench.py --kernel peaks (fp16 MFMA stream, random operands)"),
+        "prepare": _phase(phase["prepare"], prep_flop, "TFLOP/s", PEAK_TF32, ATTAIN_TF32,
+                          "bench.py --kernel peaks (fp32 MFMA stream)"),
+        "quantize": {"ms_median": round(float(np.median(phase["quantize"])), 4),
+                     "ms_min": round(float(np.min(phase["quantize"])), 4)},
+    }
+    ph["prepare"]["work_note"] = (f"4n^3/3 algorithmic flops; the route run here executes 2n^3/3 "
+                                  f"({2.0 * n ** 3 / 3:.4g}), frac on that basis "
+                                  f"{ph['prepare']['frac'] / 2:.4f}")
+    if split:
+        g_ms, s_ms = split["trailing_gemm"], split["sweep"]
+        if g_ms > 0:
+            rate = gemm_flop / (g_ms * 1e-3) / 1e12
+            ph["trailing_gemm"] = {"ms": round(g_ms, 4), "work": gemm_flop, "achieved": round(rate, 2),
+                                   "unit": "TFLOP/s", "peak": PEAK_TF32, "frac": round(rate / PEAK_TF32, 4),
+                                   "attainable": {"peak": ATTAIN_TF32, "frac": round(rate / ATTAIN_TF32, 4),
+                                                  "source": "bench.py --kernel peaks (fp32 MFMA stream)"},
+                                   "work_note": f"flops the GEMM kernels perform of m n (n - B) = "
+                                                f"{float(m) * n * (n - B):.4g}; {in_sweep_flop:.4g} more are "
+                                                f"applied inside the sweep kernel"}
+        if s_ms > 0:
+            rate = sweep_bytes / (s_ms * 1e-3) / 1e9
+            ph["sweep"] = {"ms": round(s_ms, 4), "work": sweep_bytes, "achieved": round(rate, 1), "unit": "GB/s",
+                           "peak": PEAK_HBM, "frac": round(rate / PEAK_HBM, 4),
+                           "attainable": {"peak": ATTAIN_HBM_READ, "frac": round(rate / ATTAIN_HBM_READ, 4),
+                                          "source": "bench.py --kernel peaks (HBM read stream)"},
+                           "latency_floor_us": [round(n * c / 2.4e3, 1) for c in (20, 50)],
+                           "work_note": "m n (4 + 4 + b/8) + 8 m G + 4 n B bytes: V read, E written, codes, "
+                                        "scales and zeros, the factor's diagonal blocks"}
+        ph["quantize"]["other_ms"] = round(split["other"], 4)
+    achieved = ph["syrk"]["achieved"]
+    traffic = traffic_bytes(args.traffic) if args.workload == "attn" else None
+    med_total = sum(ph[k]["ms_median"] for k in ("syrk", "prepare", "quantize"))
     res = {
-        "metric": "ms per 4096x4096 4-bit g128 GPTQ layer (incl. H^-1) + % MFMA/HBM roofline",
+        "metric": "ms per 4096x4096 4-bit g128 GPTQ layer (incl. H^-1) + % MFMA/HBM roofline"
+                  if args.workload == "attn" else f"ms per GPTQ layer ({args.workload}, incl. H and H^-1)",
         "value": round(ms_step, 3),
         "unit": "ms",
         "n_gpus": 1,
@@ -597,22 +782,25 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: W {m}x{n} {job.weights[0].dtype}, X {T} tokens x {n} {job.x.dtype}, "
-                        f"{job.bits}-bit, group {job.group}, block {job.block}, damp {job.damp}",
-            "tokens": T, "m": m, "n": n, "bits": job.bits, "group": job.group, "block": job.block,
+                        f"{bits}-bit, group {group}, block {B}, damp {job.damp}",
+            "tokens": T, "m": m, "n": n, "bits": bits, "group": group, "block": B,
             "parallelism": "single GPU",
         },
-        "phases_ms": {k: round(v, 4) for k, v in ph.items()},
-        "ms_layer_incl_hinv": round(ph["prepare"] + ph["quantize"], 4),
+        "phases_ms": {"hessian": ph["syrk"]["ms_median"], "prepare": ph["prepare"]["ms_median"],
+                      "quantize": ph["quantize"]["ms_median"]},
+        "ms_layer_incl_hinv": round(ph["prepare"]["ms_median"] + ph["quantize"]["ms_median"], 4),
+        "ms_layer_incl_hinv_min": round(ph["prepare"]["ms_min"] + ph["quantize"]["ms_min"], 4),
+        "ms_step_event_median": round(med_total, 4),
         "roofline": {
             "kernel": "gptq_hessian_accumulate, H += 2 X^T X: syrk16_dma_kernel (MFMA fp16) + syrk_reduce_kernel",
             "bound": "mfma",
-            "achieved": round(achieved, 2),
+            "achieved": achieved,
             "peak": PEAK_TF16,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_TF16, 4),
+            "frac": ph["syrk"]["frac"],
             "traffic": traffic,
-            "attainable": {"peak": ATTAIN_TF16, "frac": round(achieved / ATTAIN_TF16, 4),
-                           "source": "bench.py --kernel peaks (fp16 MFMA stream, random operands)"},
+            "attainable": ph["syrk"]["attainable"],
+            "phases": ph,
         },
     }
     if not args.no_cpu_baseline:
