@@ -21,6 +21,8 @@
  *
  *   gptq_dequant_matmul      Y = X What^T with the packed codes unpacked and
  *                            dequantized next to 16-bit activations
+ *                            (gptq_dequant_matmul_static: the same without a
+ *                            workspace, for callers that cannot allocate)
  *
  * and one that prepares a layer for it with a fixed rotation:
  *
@@ -40,7 +42,8 @@
  * Conventions for every call:
  *   - Array arguments are DEVICE pointers owned by the caller; the library
  *     allocates no memory and keeps no state between calls.  Scratch memory
- *     is passed in as `workspace`, sized by the matching *_workspace_bytes().
+ *     is passed in as `workspace`, sized by the matching *_workspace_bytes()
+ *     (gptq_dequant_matmul_static alone uses a fixed buffer of its own).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work on it and return without synchronizing.
  *   - Matrices are row-major with an explicit leading dimension.
@@ -66,7 +69,9 @@ typedef enum {
   GPTQ_ERR_INVALID_ARG = 1,  /* bad size, pointer, dtype, bits, group/block */
   GPTQ_ERR_UNSUPPORTED = 2,  /* valid request this library does not run    */
   GPTQ_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required     */
-  GPTQ_ERR_HIP = 4           /* a HIP launch or runtime call failed         */
+  GPTQ_ERR_HIP = 4,          /* a HIP launch or runtime call failed         */
+  GPTQ_ERR_SCRATCH_LIMIT = 5 /* needs more than the fixed scratch buffer of
+                                gptq_dequant_matmul_static                 */
 } gptq_status;
 
 typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype;
@@ -255,6 +260,33 @@ gptq_status gptq_dequant_matmul(const void* X, int32_t x_dtype, int64_t tokens, 
                                 const uint32_t* qcodes, const float* scales, const int32_t* zeros,
                                 int64_t m, int64_t n, int32_t bits, int64_t group_size, void* Y,
                                 int64_t ldy, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gptq_dequant_matmul_static: gptq_dequant_matmul without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc).
+ *
+ * Arguments, results, errors and supported cases are those of
+ * gptq_dequant_matmul.  The fp32 partial sums of the K ranges go to a fixed
+ * buffer inside the library instead: gptq_static_scratch_bytes() bytes
+ * (32 MiB) per GPU, reserved when the library is loaded on that GPU and held
+ * until the process ends.  Nothing is allocated by the call.
+ *   - A request whose gptq_dequant_matmul_workspace_bytes(tokens, m, n)
+ *     exceeds that size returns GPTQ_ERR_SCRATCH_LIMIT (nothing enqueued);
+ *     e.g. 16 tokens with m x (number of 1024-column K ranges) up to 131072.
+ *   - Every call on one GPU uses the same buffer, and the buffer keeps the
+ *     last call's partial sums (each call writes every partial it reads, so
+ *     nothing needs clearing).  Calls that overlap in time on one GPU (two
+ *     streams, or two host threads) race on it and give wrong results: the
+ *     caller serializes them, e.g. on one stream.
+ *   - The first call on a GPU looks up the buffer's device address (a host
+ *     call, no allocation); later calls reuse it.
+ * ---------------------------------------------------------------------- */
+size_t gptq_static_scratch_bytes(void);
+gptq_status gptq_dequant_matmul_static(const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx,
+                                       const uint32_t* qcodes, const float* scales, const int32_t* zeros,
+                                       int64_t m, int64_t n, int32_t bits, int64_t group_size, void* Y,
+                                       int64_t ldy, void* stream);
 
 /* ------------------------------------------------------------------------
  * Fixed rotation before GPTQ ("OptRot: Mitigating Weight Outliers via

@@ -24,7 +24,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgptq_mi355x.so")
 
-GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_UNSUPPORTED, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP = range(5)
+GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_UNSUPPORTED, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP, GPTQ_ERR_SCRATCH_LIMIT = range(6)
 F16, BF16, F32 = 0, 1, 2
 _DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 
@@ -67,6 +67,10 @@ def _load() -> ctypes.CDLL:
     L.gptq_dequant_matmul_workspace_bytes.restype = sz
     L.gptq_dequant_matmul.argtypes = [vp, i32, i64, i64, vp, vp, vp, i64, i64, i32, i64, vp, i64, vp, sz, vp]
     L.gptq_dequant_matmul.restype = i32
+    L.gptq_static_scratch_bytes.argtypes = []
+    L.gptq_static_scratch_bytes.restype = sz
+    L.gptq_dequant_matmul_static.argtypes = [vp, i32, i64, i64, vp, vp, vp, i64, i64, i32, i64, vp, i64, vp]
+    L.gptq_dequant_matmul_static.restype = i32
     L.gptq_rotate_hadamard.argtypes = [vp, i32, i64, i64, i64, i64, vp]
     L.gptq_rotate_hadamard.restype = i32
     L.gptq_swiglu.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp]
@@ -296,6 +300,36 @@ def dequant_matmul(X: torch.Tensor, qcodes: torch.Tensor, scales: torch.Tensor, 
                                      Y.data_ptr(), max(Y.stride(0), m), _ptr(ws), 0 if ws is None else ws.numel(),
                                      _stream(dev))
     _check("gptq_dequant_matmul", st)
+    return Y
+
+
+def static_scratch_bytes() -> int:
+    return int(_load().gptq_static_scratch_bytes())
+
+
+def dequant_matmul_static(X: torch.Tensor, qcodes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                          bits: int, group_size: int, Y: torch.Tensor) -> torch.Tensor:
+    """dequant_matmul without a workspace: the partial sums go to the
+    library's fixed per-GPU buffer, so the call allocates nothing (Y must be
+    given).  Calls that overlap in time on one GPU race on that buffer."""
+    _require(X.is_cuda and X.dim() == 2 and X.stride(1) == 1 and X.dtype in (torch.float16, torch.bfloat16),
+             "X must be a [tokens, n] fp16/bf16 CUDA tensor with unit column stride")
+    m = qcodes.shape[0]
+    T, n = X.shape
+    dev = X.device
+    _require(qcodes.device == dev and qcodes.dtype == torch.int32 and qcodes.is_contiguous()
+             and qcodes.shape == (m, packed_words(n, bits)), "qcodes must be contiguous int32 [m, words]")
+    G = n_groups(n, group_size)
+    _require(scales.shape == (m, G) and scales.dtype == torch.float32 and scales.is_contiguous()
+             and scales.device == dev, "scales must be contiguous float32 [m, G]")
+    _require(zeros.shape == (m, G) and zeros.dtype == torch.int32 and zeros.is_contiguous() and zeros.device == dev,
+             "zeros must be contiguous int32 [m, G]")
+    _require(Y.dtype == X.dtype and Y.dim() == 2 and Y.shape == (T, m) and Y.stride(1) == 1 and Y.device == dev,
+             "Y must be [tokens, m] in X's dtype with unit column stride")
+    st = _load().gptq_dequant_matmul_static(X.data_ptr(), _DT[X.dtype], T, max(X.stride(0), n), qcodes.data_ptr(),
+                                            scales.data_ptr(), zeros.data_ptr(), m, n, int(bits), int(group_size),
+                                            Y.data_ptr(), max(Y.stride(0), m), _stream(dev))
+    _check("gptq_dequant_matmul_static", st)
     return Y
 
 

@@ -49,6 +49,7 @@ const char* gptq_status_string(int32_t s) {
     case GPTQ_ERR_UNSUPPORTED: return "GPTQ_ERR_UNSUPPORTED";
     case GPTQ_ERR_WORKSPACE: return "GPTQ_ERR_WORKSPACE";
     case GPTQ_ERR_HIP: return "GPTQ_ERR_HIP";
+    case GPTQ_ERR_SCRATCH_LIMIT: return "GPTQ_ERR_SCRATCH_LIMIT";
     default: return "GPTQ_UNKNOWN_STATUS";
   }
 }
@@ -124,10 +125,11 @@ size_t gptq_dequant_matmul_workspace_bytes(int64_t tokens, int64_t m, int64_t n)
   return gptq::dequant_matmul_workspace_bytes(tokens, m, n);
 }
 
-gptq_status gptq_dequant_matmul(const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx, const uint32_t* qcodes,
-                                const float* scales, const int32_t* zeros, int64_t m, int64_t n, int32_t bits,
-                                int64_t group_size, void* Y, int64_t ldy, void* workspace, size_t ws_bytes,
-                                void* stream) {
+// Argument checks shared by the two dequant-matmul entry points; GPTQ_OK
+// means "run it" (tokens > 0).
+static gptq_status dequant_matmul_check(const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx,
+                                        const uint32_t* qcodes, const float* scales, const int32_t* zeros, int64_t m,
+                                        int64_t n, int32_t bits, int64_t group_size, void* Y, int64_t ldy) {
   if (m < 1 || n < 1 || tokens < 0 || tokens > ((int64_t)1 << 31) || ldx < n || ldy < m ||
       !(x_dtype == GPTQ_F16 || x_dtype == GPTQ_BF16) || bits < 2 || bits > 8)
     return GPTQ_ERR_INVALID_ARG;
@@ -140,10 +142,39 @@ gptq_status gptq_dequant_matmul(const void* X, int32_t x_dtype, int64_t tokens, 
   if (!gptq::dequant_matmul_supported(bits, n, group_size, tokens) || ldx % 8 != 0 || !al16(X) || !al16(qcodes) ||
       (int64_t)64 * n * 4 >= lim || m * G * 4 >= lim || (int64_t)16 * ldx * 2 >= lim)
     return GPTQ_ERR_UNSUPPORTED;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_dequant_matmul(const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx, const uint32_t* qcodes,
+                                const float* scales, const int32_t* zeros, int64_t m, int64_t n, int32_t bits,
+                                int64_t group_size, void* Y, int64_t ldy, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  const gptq_status c = dequant_matmul_check(X, x_dtype, tokens, ldx, qcodes, scales, zeros, m, n, bits, group_size,
+                                             Y, ldy);
+  if (c != GPTQ_OK || tokens == 0) return c;
   const size_t need = gptq::dequant_matmul_workspace_bytes(tokens, m, n);
   if (need > 0 && (workspace == nullptr || ws_bytes < need)) return GPTQ_ERR_WORKSPACE;
   hipError_t e = gptq::dequant_matmul(X, x_dtype, tokens, ldx, qcodes, bits, scales, zeros, m, n, group_size, Y, ldy,
                                       workspace, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+}
+
+size_t gptq_static_scratch_bytes(void) { return gptq::kStaticScratchBytes; }
+
+gptq_status gptq_dequant_matmul_static(const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx,
+                                       const uint32_t* qcodes, const float* scales, const int32_t* zeros, int64_t m,
+                                       int64_t n, int32_t bits, int64_t group_size, void* Y, int64_t ldy,
+                                       void* stream) {
+  const gptq_status c = dequant_matmul_check(X, x_dtype, tokens, ldx, qcodes, scales, zeros, m, n, bits, group_size,
+                                             Y, ldy);
+  if (c != GPTQ_OK || tokens == 0) return c;
+  const size_t need = gptq::dequant_matmul_workspace_bytes(tokens, m, n);
+  if (need > gptq::kStaticScratchBytes) return GPTQ_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  hipError_t e = gptq::static_scratch((hipStream_t)stream, &ws);
+  if (e != hipSuccess) return GPTQ_ERR_HIP;
+  e = gptq::dequant_matmul(X, x_dtype, tokens, ldx, qcodes, bits, scales, zeros, m, n, group_size, Y, ldy, ws,
+                           (hipStream_t)stream);
   return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
 }
 

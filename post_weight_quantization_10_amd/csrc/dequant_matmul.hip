@@ -36,9 +36,17 @@
 //     outputs of the K sets are summed by a second kernel in a fixed order
 //     (deterministic) and converted to X's dtype.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "internal.hpp"
+
+// Fixed device buffer for the partial sums of dequant_matmul_static (callers
+// that cannot allocate).  Each GPU the library runs on holds its own copy
+// until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[gptq::kStaticScratchBytes];
 
 namespace gptq {
 
@@ -689,4 +697,41 @@ hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const u
   return hipGetLastError();
 }
 
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of `scratch` on the device `stream` belongs to (the current
+// device for the null stream), looked up once per device with that device
+// current and kept.
+hipError_t static_scratch(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    if ((e = hipStreamGetDevice(stream, &d)) != hipSuccess) return e;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace gptq
+

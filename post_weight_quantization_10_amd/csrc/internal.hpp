@@ -5,6 +5,12 @@
 
 namespace gptq {
 
+// Size of the fixed partial-sum buffer behind gptq_dequant_matmul_static.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+
+// Device address of that buffer on the device of `stream`.
+hipError_t static_scratch(hipStream_t stream, void** out);
+
 // Flags for gemm_f32.
 enum : int {
   GEMM_LOWER_TILES = 1,  // C square; only 128x128 tiles on or below the diagonal are computed

@@ -216,3 +216,23 @@ def test_greedy_workspace_sizes():
     assert pw.greedy_workspace_bytes(100, 257) == 4 * al(257) * 101   # one copy per workgroup
     assert pw.greedy_workspace_bytes(5000, 300) == 4 * al(300) * 257  # at most 256 workgroups
     assert pw.greedy_workspace_bytes(0, 300) == 0
+
+
+def test_static_dequant_matmul_limits():
+    """The no-workspace variant rejects, before any HIP call, what the plain
+    entry point rejects, and requests larger than its fixed buffer."""
+    L = _lib()
+    assert pw.static_scratch_bytes() == 32 << 20
+    m, n, T = 1 << 20, 8192, 16
+    assert pw.dequant_matmul_workspace_bytes(T, m, n) > pw.static_scratch_bytes()
+    r = L.gptq_dequant_matmul_static(FAKE, pw.F16, T, n, FAKE, FAKE, FAKE, m, n, 4, 128, FAKE, m, None)
+    assert r == pw.GPTQ_ERR_SCRATCH_LIMIT
+    assert pw.status_string(r) == "GPTQ_ERR_SCRATCH_LIMIT"
+    assert L.gptq_dequant_matmul_static(FAKE, pw.F32, T, n, FAKE, FAKE, FAKE, 64, n, 4, 128, FAKE, 64,
+                                        None) == pw.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_dequant_matmul_static(None, pw.F16, T, n, FAKE, FAKE, FAKE, 64, n, 4, 128, FAKE, 64,
+                                        None) == pw.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_dequant_matmul_static(FAKE, pw.F16, 0, n, None, None, None, 64, n, 4, 128, None, 64,
+                                        None) == pw.GPTQ_OK
+    assert L.gptq_dequant_matmul_static(FAKE, pw.F16, T, n, FAKE, FAKE, FAKE, 64, n, 5, 128, FAKE, 64,
+                                        None) == pw.GPTQ_ERR_UNSUPPORTED
