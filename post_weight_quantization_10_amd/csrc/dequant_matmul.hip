@@ -6,8 +6,9 @@
 // ends on the same point: the artifact needs a packed INT4 kernel for the
 // target device).
 //
-// How (4-bit codes, and 3-bit codes for up to 16 tokens; fp16 or bf16
-// activations):
+// How (4-bit and 3-bit codes, fp16 or bf16 activations; 3-bit rows are
+// bit-streams whose codes straddle words, turned into the 4-bit layout in
+// registers right after their load):
 //   * Up to 16 tokens (decode): a workgroup takes 64 rows of W over one K
 //     range of 512 or 1024 columns; each wave requests all of its codes at
 //     once while the workgroup stages X and the group parameters in LDS.
@@ -82,7 +83,27 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h, int dt) {
   return dt == 0 ? (float)__builtin_bit_cast(_Float16, (uint16_t)h) : __builtin_bit_cast(float, h << 16);
 }
 
-template <int DT>
+// 32 3-bit codes (a little-endian 96-bit stream w0 w1 w2, code c at bit 3c)
+// as four words of eight 4-bit codes (code 8i + k at bits 4k of word i): the
+// layout the 4-bit path unpacks.  Per word, the 24-bit window of its eight
+// codes is spread 3 -> 4 bits in three mask-and-shift steps.
+__device__ __forceinline__ u32x4 spread3(uint32_t w0, uint32_t w1, uint32_t w2) {
+  const uint32_t win[4] = {w0 & 0xFFFFFFu, __builtin_amdgcn_alignbit(w1, w0, 24) & 0xFFFFFFu,
+                           __builtin_amdgcn_alignbit(w2, w1, 16) & 0xFFFFFFu, w2 >> 8};
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = win[i];
+    const uint32_t x = (t & 0xFFFu) | ((t & 0xFFF000u) << 4);         // codes 0-3 | 4-7 at bits 0 | 16, 3 apart
+    const uint32_t y = (x & 0x003F003Fu) | ((x & 0x0FC00FC0u) << 2);  // pairs at bits 0 | 8 | 16 | 24, 3 apart
+    out[i] = (y & 0x07070707u) | ((y & 0x38383838u) << 1);           // 4 apart
+  }
+  return out;
+}
+
+// BITS = 3: a lane's 32 codes of a piece are three words (a 12-byte load),
+// turned into the 4-bit layout by spread3.
+template <int DT, int BITS>
 __global__ __launch_bounds__(256, 2) void dqmm4_kernel(DqArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[DQ_TOK * DQ_XP];
   __shared__ float xsum[DQ_TOK][DQ_KR / 128];
@@ -119,11 +140,19 @@ __global__ __launch_bounds__(256, 2) void dqmm4_kernel(DqArgs a) {
   const int64_t nslices = cdiv(a.n, DQ_KR);
   for (int64_t ks = blockIdx.y; ks < nslices; ks += a.KS) {
     const int64_t k0 = ks * DQ_KR;
-    // this lane's words: k0/8 + 16p + 4 g4 .. +3 for the four pieces p
+    // this lane's words of the four pieces p: 4 bits: k0/8 + 16p + 4 g4 .. +3;
+    // 3 bits: 3 k0/32 + 12p + 3 g4 .. +2, spread to the 4-bit layout
     u32x4 qw[4];
-    const uint32_t qoff = (qrow + (uint32_t)(k0 / 8) + 4u * g4) * 4u;
+    const uint32_t qoff = (qrow + (uint32_t)(k0 * BITS / 32) + (uint32_t)BITS * g4) * 4u;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) qw[p] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 64u * p, 0, 0);
+    for (int p = 0; p < 4; ++p) {
+      if constexpr (BITS == 4) {
+        qw[p] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 64u * p, 0, 0);
+      } else {
+        const u32x3 c = __builtin_amdgcn_raw_buffer_load_b96(qrs, qoff + 48u * p, 0, 0);
+        qw[p] = spread3(c.x, c.y, c.z);
+      }
+    }
 
     // stage X[t0 .. t0+63][k0 .. k0+511] with the pair order of the unpacked
     // codes inside each 8-column word, and the sum of every 128-column piece
@@ -245,24 +274,6 @@ __device__ __forceinline__ uint32_t hsub(uint32_t a, uint32_t b) {
 // rows hold: they only reach output columns that are never written.  Columns
 // past n are staged as zeros, so the codes there (another row's, or zeros
 // past the buffer) add nothing.
-// 32 3-bit codes (a little-endian 96-bit stream w0 w1 w2, code c at bit 3c)
-// as four words of eight 4-bit codes (code 8i + k at bits 4k of word i): the
-// layout the 4-bit path unpacks.  Per word, the 24-bit window of its eight
-// codes is spread 3 -> 4 bits in three mask-and-shift steps.
-__device__ __forceinline__ u32x4 spread3(uint32_t w0, uint32_t w1, uint32_t w2) {
-  const uint32_t win[4] = {w0 & 0xFFFFFFu, __builtin_amdgcn_alignbit(w1, w0, 24) & 0xFFFFFFu,
-                           __builtin_amdgcn_alignbit(w2, w1, 16) & 0xFFFFFFu, w2 >> 8};
-  u32x4 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t t = win[i];
-    const uint32_t x = (t & 0xFFFu) | ((t & 0xFFF000u) << 4);         // codes 0-3 | 4-7 at bits 0 | 16, 3 apart
-    const uint32_t y = (x & 0x003F003Fu) | ((x & 0x0FC00FC0u) << 2);  // pairs at bits 0 | 8 | 16 | 24, 3 apart
-    out[i] = (y & 0x07070707u) | ((y & 0x38383838u) << 1);           // 4 apart
-  }
-  return out;
-}
-
 // BITS = 3: each lane's 32 codes of a piece are three words (a 12-byte load)
 // turned into the 4-bit layout by spread3; everything else as for 4 bits.
 template <int DT, bool G128, int KR, int TT, int BITS>
@@ -439,6 +450,7 @@ __global__ __launch_bounds__(256) void dqmm4_task_kernel(DqArgs a) {
 constexpr int GM = 128, GN = 128, GK = 64;
 constexpr int GXP = GK + 8;  // LDS pitch of a staged X row (halves): 144 bytes
 
+template <int BITS>
 __global__ __launch_bounds__(256, 2) void dqmm4_gemm_kernel(DqArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][GM * GXP];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -458,7 +470,7 @@ __global__ __launch_bounds__(256, 2) void dqmm4_gemm_kernel(DqArgs a) {
   int64_t zrow[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    qoff[nb] = ((uint32_t)(32 * nb + l32) * (uint32_t)a.W + 4u * g) * 4u;
+    qoff[nb] = ((uint32_t)(32 * nb + l32) * (uint32_t)a.W + (uint32_t)BITS * g) * 4u;
     zrow[nb] = min<int64_t>(rw + 32 * nb + l32, a.m - 1);
   }
   // X staging: thread -> (token tid / 2, 32-column half tid % 2), four words
@@ -481,10 +493,19 @@ __global__ __launch_bounds__(256, 2) void dqmm4_gemm_kernel(DqArgs a) {
       *(u32x4*)&xs[buf][xt * GXP + 32 * xh + 8 * w] = e;
     }
   };
+  // a step's 64 columns are 8 words at 4 bits (lane half g: 4 g .. 4 g + 3) and
+  // 6 at 3 bits (3 g .. 3 g + 2, spread to the 4-bit layout)
   auto load_q = [&](int64_t k0, u32x4 (&q)[2]) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      q[nb] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff[nb] + (uint32_t)(k0 / 8) * 4u, 0, 0);
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t off = qoff[nb] + (uint32_t)(k0 * BITS / 32) * 4u;
+      if constexpr (BITS == 4) {
+        q[nb] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
+      } else {
+        const u32x3 c = __builtin_amdgcn_raw_buffer_load_b96(qrs, off, 0, 0);
+        q[nb] = spread3(c.x, c.y, c.z);
+      }
+    }
   };
 
   f32x16 acc[2][2], tot[2][2];
@@ -659,7 +680,7 @@ size_t dequant_matmul_workspace_bytes(int64_t tokens, int64_t m, int64_t n) {
 }
 
 bool dequant_matmul_supported(int bits, int64_t n, int64_t group, int64_t tokens) {
-  return (bits == 4 || (bits == 3 && tokens <= 16)) && n % 32 == 0 && (group <= 0 || group % 128 == 0);
+  return (bits == 4 || bits == 3) && n % 32 == 0 && (group <= 0 || group % 128 == 0);
 }
 
 hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const uint32_t* Q, int bits, const float* S,
@@ -678,16 +699,19 @@ hipError_t dequant_matmul(const void* X, int dt, int64_t T, int64_t ldx, const u
     const dim3 grid((unsigned)(cdiv(m, 64) * a.KS));
     if (dt == 0) launch_task<0>(a, group == 128, bits, sp.kr, T, grid, st);
     else launch_task<1>(a, group == 128, bits, sp.kr, T, grid, st);
-  } else if (dt == 0 && bits == 4 && cdiv(T, GM) * cdiv(m, GN) >= 128) {
+  } else if (dt == 0 && cdiv(T, GM) * cdiv(m, GN) >= 128) {
     // enough 128 x 128 tiles to fill the GPU without cutting K
     a.KS = 1;
     a.P = nullptr;
     const dim3 grid((unsigned)cdiv(T, GM), (unsigned)cdiv(m, GN));
-    hipLaunchKernelGGL(dqmm4_gemm_kernel, grid, dim3(256), 0, st, a);
+    if (bits == 4) hipLaunchKernelGGL((dqmm4_gemm_kernel<4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dqmm4_gemm_kernel<3>), grid, dim3(256), 0, st, a);
   } else {
     const dim3 grid((unsigned)cdiv(m, DQ_ROWS), (unsigned)a.KS, (unsigned)cdiv(T, DQ_TOK));
-    if (dt == 0) hipLaunchKernelGGL(dqmm4_kernel<0>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(dqmm4_kernel<1>, grid, dim3(256), 0, st, a);
+    if (dt == 0 && bits == 4) hipLaunchKernelGGL((dqmm4_kernel<0, 4>), grid, dim3(256), 0, st, a);
+    else if (dt == 0) hipLaunchKernelGGL((dqmm4_kernel<0, 3>), grid, dim3(256), 0, st, a);
+    else if (bits == 4) hipLaunchKernelGGL((dqmm4_kernel<1, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dqmm4_kernel<1, 3>), grid, dim3(256), 0, st, a);
   }
   if (a.KS > 1) {
     const dim3 rg((unsigned)cdiv(m, 1024), (unsigned)std::min<int64_t>(T, 65535));

@@ -120,7 +120,7 @@ def test_dequant_matmul_rejects(kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(bits=3, T=17), dict(bits=2), dict(bits=8), dict(g=64), dict(g=32), dict(n=240, ldx=240), dict(ldx=260),
+    dict(bits=2), dict(bits=8), dict(g=64), dict(g=32), dict(n=240, ldx=240), dict(ldx=260),
     dict(X=ctypes.c_void_p(0x1008)), dict(q=ctypes.c_void_p(0x1004)),
 ])
 def test_dequant_matmul_unsupported(kw):

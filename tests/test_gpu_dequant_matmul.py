@@ -82,7 +82,7 @@ DQ_CASES = [
     (2, 8192, 8192, 0, "bf16"),      # 1024-column ranges, one group per row across ranges
     (9, 16320, 4160, 128, "bf16"),   # 1024-column ranges, ragged rows, a 64-column last range and group
 ]
-# 3-bit codes (a per-row bit-stream: codes straddle words), decode sizes only
+# 3-bit codes (a per-row bit-stream: codes straddle words)
 DQ3_CASES = [
     (1, 64, 256, 0, "f16"),
     (1, 4096, 4096, 0, "f16"),       # the MLP recipe's per-row 3-bit layer shape, one token
@@ -90,6 +90,11 @@ DQ3_CASES = [
     (16, 4096, 11008, 0, "f16"),     # 11008 columns: 344 words per row, a 768-column last range
     (7, 16320, 4160, 128, "f16"),    # 1024-column ranges, ragged rows, a 64-column last range
     (2, 8192, 8192, 256, "bf16"),
+    (17, 256, 1024, 128, "f16"),     # past decode sizes: staged kernel, K cut into sets
+    (100, 1000, 2080, 0, "bf16"),    # staged kernel, ragged tokens and rows, a 32-column last piece
+    (512, 4096, 4096, 128, "f16"),   # GEMM-shaped kernel (>= 128 tiles of 128 x 128)
+    (400, 4160, 992, 0, "f16"),      # GEMM-shaped, ragged tiles, a 32-column last K step
+    (64, 2048, 12288, 128, "bf16"),  # the 175B shard's fc1 input width
 ]
 
 
@@ -167,9 +172,8 @@ def test_dequant_matmul_unsupported_on_device():
     z = torch.zeros((8, 1), dtype=torch.int32, device=DEV)
     with pytest.raises(pw.GPTQError):
         pw.dequant_matmul(X[:, :90], torch.zeros((8, 12), dtype=torch.int32, device=DEV), s, z, 4, 0)
-    with pytest.raises(pw.GPTQError):  # 3-bit codes: decode batches (up to 16 tokens) only
-        pw.dequant_matmul(torch.zeros((17, 96), dtype=torch.float16, device=DEV),
-                          torch.zeros((8, 9), dtype=torch.int32, device=DEV), s, z, 3, 0)
+    with pytest.raises(pw.GPTQError):  # 5-bit codes are not run at all
+        pw.dequant_matmul(X, torch.zeros((8, 15), dtype=torch.int32, device=DEV), s, z, 5, 0)
     Y3 = pw.dequant_matmul(X, torch.zeros((8, 9), dtype=torch.int32, device=DEV), s, z, 3, 0)
     torch.cuda.synchronize()
     assert torch.all(Y3 == 0)
