@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
   static_assert(!LOOK || (LPR == 16 && 16 * UPITCH <= USZ), "look-ahead needs the 128-column layout");
   __shared__ __attribute__((aligned(16))) float Us[USZ];
   __shared__ float invd[NSTEP];
-  __shared__ uint8_t codes8[ROWS][NSTEP];
+  __shared__ __attribute__((aligned(8))) uint8_t codes8[ROWS][NSTEP];
   const int tid = threadIdx.x;
   const int lr = tid & (LPR - 1);
   const int rl = tid / LPR;  // row within the workgroup
@@ -449,36 +449,64 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
     }
     return;
   }
+  // the row's codes as bytes (0 past w), then each lane packs 8 consecutive
+  // codes into one dense segment of 8 bits: the row's bit-stream is the
+  // segments of its LPR lanes in order
 #pragma unroll
-  for (int k = 0; k < 8; ++k) codes8[rl][lr + LPR * k] = (uint8_t)(int)(qz_[k] + zc[k]);
+  for (int k = 0; k < 8; ++k) {
+    const int c = lr + LPR * k;
+    codes8[rl][c] = c < w ? (uint8_t)(int)(qz_[k] + zc[k]) : (uint8_t)0;
+  }
   // the row's codes were written by lanes of this wave only: wait for the
   // wave's LDS writes before its lanes read each other's bytes
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
-  if (!active) return;
-  // lane lr packs words lr and lr + LPR of the block (a block of NSTEP codes
-  // of at most 8 bits is at most NSTEP / 4 = 2 LPR words); a word touches at
-  // most 17 codes (2-bit codes, one straddling in), all read at once
   const int bits = a.bits;
+  uint64_t seg = 0;
+  {
+    const uint64_t b8 = *(const uint64_t*)&codes8[rl][8 * lr];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) seg |= ((b8 >> (8 * k)) & 0xFFu) << (bits * k);
+  }
   const int nwords = (w * bits + 31) / 32;
   uint32_t* dst = a.Qw + r * a.words + (i * bits) / 32;
+  if (bits == 4 || bits == 8) {  // a segment is whole words: store it
+    if (active) {
+      if (bits == 4) {
+        if (lr < nwords) dst[lr] = (uint32_t)seg;
+      } else {
+        if (2 * lr < nwords) dst[2 * lr] = (uint32_t)seg;
+        if (2 * lr + 1 < nwords) dst[2 * lr + 1] = (uint32_t)(seg >> 32);
+      }
+    }
+    return;
+  }
+  // the segments replace the row's bytes (NSTEP bytes = LPR segments); the
+  // wave's read of the bytes is issued before this write
+  uint64_t* segs = (uint64_t*)&codes8[rl][0];
+  segs[lr] = seg;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  if (!active) return;
+  // word wd = bits [32 wd, 32 wd + 32) of the row: the segments of 8 bits
+  // each that overlap it (at most 3 for bits >= 2)
+  const int sb = 8 * bits;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int wd = lr + LPR * h;
     const int bit0 = 32 * wd;
-    const int j0 = bit0 / bits;
-    constexpr int MAXC = 17;
-    uint32_t q[MAXC];
+    const int s0 = bit0 / sb;
+    uint64_t word = 0;
 #pragma unroll
-    for (int t = 0; t < MAXC; ++t) q[t] = codes8[rl][min(j0 + t, NSTEP - 1)];
-    uint32_t word = 0;
-#pragma unroll
-    for (int t = 0; t < MAXC; ++t) {
-      const int j = j0 + t;
-      const int sh = j * bits - bit0;
-      if (j < w && sh < 32) word |= sh >= 0 ? (q[t] << sh) : (q[t] >> (-sh));
+    for (int t = 0; t < 3; ++t) {
+      const int sg = s0 + t;
+      const int off = sg * sb - bit0;  // position of the segment's bit 0 in the word
+      if (sg < LPR && off < 32) {
+        const uint64_t v = segs[sg];
+        word |= off >= 0 ? (v << off) : (v >> (-off));
+      }
     }
-    if (wd < nwords) dst[wd] = word;
+    if (wd < nwords) dst[wd] = (uint32_t)word;
   }
 }
 
