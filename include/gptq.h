@@ -29,9 +29,10 @@
  *   gptq_rotate_hadamard     M <- M R (block-diagonal Hadamard), applied to
  *                            the weights and the activations alike
  *
- * and the elementwise steps of the network-level loop over MLP blocks:
+ * and the steps of the network-level loop over transformer blocks that are
+ * not products:
  *
- *   gptq_swiglu, gptq_residual_add
+ *   gptq_attention, gptq_swiglu, gptq_residual_add
  *
  * Sources (web pages describing the method):
  *   [OBQ]    "Part 2: Adaptive Rounding: Optimal Brain Quantizer (OBQ)"
@@ -336,6 +337,29 @@ gptq_status gptq_swiglu(const void* G, const void* Uo, void* A, int32_t dtype, i
                         int64_t f, int64_t ld, void* stream);
 gptq_status gptq_residual_add(void* X, const void* Y, int32_t dtype, int64_t tokens, int64_t d,
                               int64_t ld, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gptq_attention: the attention of a transformer block in the network-level
+ * loop, between its quantized q/k/v and o projections ("Part 3: Adaptive
+ * Rounding: GPTQ", 'Algorithm GPTQ': each layer's calibration inputs are
+ * computed by the network as quantized so far).  Causal multi-head softmax
+ * attention over sequences of seq_len consecutive tokens:
+ *   O[i, h] = sum_{j <= i in i's sequence} softmax_j(Q[i,h] . K[j,h] / sqrt(dh)) V[j,h]
+ * with head h the columns [h dh, (h + 1) dh).  fp32 arithmetic, one rounding
+ * of O to dtype.
+ *   Q, K, V, O  [tokens x heads * head_dim] device, row-major, common leading
+ *               dimension ld >= heads * head_dim; dtype GPTQ_F16 or
+ *               GPTQ_BF16.  O must not alias Q, K or V.
+ *   tokens      a multiple of seq_len (0 is a no-op).
+ * This version runs head_dim 64 or 128, seq_len a multiple of 64, ld % 8 == 0
+ * and 16-byte aligned pointers; other valid requests return
+ * GPTQ_ERR_UNSUPPORTED.  Errors: tokens < 0 or not a multiple of seq_len,
+ * seq_len / heads / head_dim < 1, ld too small, dtype not 16-bit, NULL
+ * pointers (tokens > 0) -> GPTQ_ERR_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_attention(const void* Q, const void* K, const void* V, void* O, int32_t dtype,
+                           int64_t tokens, int64_t seq_len, int64_t heads, int64_t head_dim,
+                           int64_t ld, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,8 @@ describe the method.  Short names used in the citations below:
 Beyond the per-layer path, dequant_matmul is the runtime consumer of the
 packed layer (weights unpacked and dequantized next to 16-bit activations),
 hadamard_rotate is the fixed rotation applied before GPTQ that [OptRot]
-uses as its baseline, and quantize_mlp_stack is the network-level loop
+uses as its baseline, and quantize_transformer_stack / quantize_mlp_stack
+are the network-level loop
 ([GPTQ] "Algorithm GPTQ": one layer at a time, each layer's calibration
 inputs taken from the network as quantized so far; [SOQ] "Calibration for a
 multimodal or VLA backbone": later blocks see activations already changed by
@@ -62,11 +63,21 @@ the design notes):
       ([OptRot] Figure 1, "fusible" rotations); H' = 2 X'^T X' = R^T H R.
       Weight incoherence (the quantity [OptRot] Theorem 3.1 bounds the error
       with) is read as mu_W = sqrt(m n) max |W_ij| / ||W||_F.
-  R13 The network the loop runs through is a stack of MLP blocks shaped like
-      a 7B transformer's: x <- x + W_down (silu(W_gate x) * (W_up x)),
-      silu(v) = v / (1 + e^-v); gate and up share one Hessian (same input),
-      down gets its own from the block's hidden activations.  The pages fix
-      neither the block nor normalisation; attention and norms are left out.
+  R13 The network the loop runs through is a stack of transformer blocks
+      shaped like a 7B model's, without normalisation (the pages fix neither
+      the block nor its norms):
+        x <- x + W_o attn(W_q x, W_k x, W_v x)
+        x <- x + W_down (silu(W_gate x) * (W_up x)),  silu(v) = v / (1 + e^-v)
+      attn is causal multi-head softmax attention over sequences of
+      consecutive tokens, head h the columns [h dh, (h+1) dh), scores scaled
+      by 1/sqrt(dh).  q, k and v share one Hessian (same input) and are swept
+      as one stacked layer, as are gate and up; o and down get their own from
+      the attention output and the hidden activations.  quantize_mlp_stack is
+      the same loop over MLP blocks alone.
+  R16 Activation precision in the network loop: the GPU network stores every
+      activation in fp16 (each a single rounding of an fp32 result), so the
+      oracle network can round the same values at the same points
+      (act_dtype="f16"); its arithmetic between the roundings stays fp64.
   R14 OBQ's greedy order ([OBQ] "Greedy Search"; the loss-increase formula
       there is lost from the text): the score of an unquantized weight p is
       dL_p = (what_p - w_p)^2 / [H^-1]_pp with what_p its rounding on the grid
@@ -650,4 +661,152 @@ def quantize_mlp_stack(blocks, X0: np.ndarray, bits: int, group: int, block: int
         rd = gptq_quantize(np.asarray(Wd, np.float64), U2, bits, group, block)
         out.append({"gate": rg, "up": ru, "down": rd, "X": X, "A": A, "U": U, "U2": U2})
         X = X + A @ rd["What"].T
+    return out, X
+
+
+# ----------------------------------------------------------------------------- transformer blocks
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, seq_len: int, heads: int) -> np.ndarray:
+    """Causal multi-head softmax attention (reading R13): for every sequence of
+    seq_len consecutive tokens and every head h (columns [h dh, (h+1) dh)),
+    O_i = sum_{j <= i} softmax_j(Q_i . K_j / sqrt(dh)) V_j.  fp64."""
+    Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+    T, dm = Q.shape
+    dh = dm // heads
+    O = np.zeros_like(Q)
+    mask = np.tril(np.ones((seq_len, seq_len), dtype=bool))
+    for s0 in range(0, T, seq_len):
+        for h in range(heads):
+            c = slice(h * dh, (h + 1) * dh)
+            S = Q[s0:s0 + seq_len, c] @ K[s0:s0 + seq_len, c].T / math.sqrt(dh)
+            S = np.where(mask, S, -np.inf)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            O[s0:s0 + seq_len, c] = P @ V[s0:s0 + seq_len, c]
+    return O
+
+
+def attention_error_bound(Q, K, V, O, seq_len: int, heads: int) -> np.ndarray:
+    """Per-element bound on how far an fp32 computation of attention(Q, K, V)
+    can be from O (exact products of 16-bit inputs; an fp32 dot product of dh
+    terms errs by at most (dh + 16) 2^-24 sum_d |q_d k_d| / sqrt(dh) in a
+    score, which moves output i by at most sum_j p_ij d_ij |v_j - O_i|; the
+    exponentials, the normalisation and the weighted sum add a few relative
+    2^-24 of sum_j p_ij |v_j|)."""
+    Q, K, V, O = (np.asarray(a, dtype=np.float64) for a in (Q, K, V, O))
+    T, dm = Q.shape
+    dh = dm // heads
+    B = np.zeros_like(Q)
+    mask = np.tril(np.ones((seq_len, seq_len), dtype=bool))
+    for s0 in range(0, T, seq_len):
+        for h in range(heads):
+            c = slice(h * dh, (h + 1) * dh)
+            S = Q[s0:s0 + seq_len, c] @ K[s0:s0 + seq_len, c].T / math.sqrt(dh)
+            S = np.where(mask, S, -np.inf)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            Dsc = (dh + 16) * 2.0 ** -24 * (np.abs(Q[s0:s0 + seq_len, c]) @ np.abs(K[s0:s0 + seq_len, c]).T) \
+                / math.sqrt(dh)
+            PD = P * Dsc
+            Va = np.abs(V[s0:s0 + seq_len, c])
+            B[s0:s0 + seq_len, c] = PD @ Va + PD.sum(axis=1, keepdims=True) * np.abs(O[s0:s0 + seq_len, c]) \
+                + 2.0 ** -21 * (P @ Va)
+    return B + 2.0 ** -40
+
+
+def round_activations(y: np.ndarray, act_dtype: Optional[str], other: Optional[np.ndarray] = None,
+                      tol: Optional[np.ndarray] = None) -> Tuple[np.ndarray, int]:
+    """Round fp64 values to the activation dtype (reading R16; round to
+    nearest even), or keep them when act_dtype is None.  other, tol compare
+    against a network that computes the values in another precision, with an
+    error of at most tol: where the other side stored the rounding of some
+    value within tol of y (fp16(y - tol) <= other <= fp16(y + tol); rounding
+    is monotone), its value is taken (it is a correct rounding of a result the
+    other precision may produce; everything downstream depends on it).
+    Returns (values, number of values taken over that differ from the own
+    rounding)."""
+    y = np.asarray(y, dtype=np.float64)
+    if act_dtype is None:
+        return y, 0
+    if act_dtype != "f16":
+        raise ValueError("only fp16 activations are modelled")
+    own = y.astype(np.float16)
+    if other is None:
+        return own.astype(np.float64), 0
+    g = np.asarray(other).astype(np.float16)
+    t = np.asarray(tol, dtype=np.float64)
+    lo = (y - t).astype(np.float16)
+    hi = (y + t).astype(np.float16)
+    ok = (g >= lo) & (g <= hi) & (g != own)
+    return np.where(ok, g, own).astype(np.float64), int(ok.sum())
+
+
+def _matmul_tol(X: np.ndarray, What: np.ndarray) -> np.ndarray:
+    """Bound on an fp32 computation of X What^T with exact products: a sum of K
+    terms, each rounding relative 2^-24 of a partial sum of at most sum |x w|."""
+    K = X.shape[1]
+    return 2.0 ** -24 * (K + 64) * (np.abs(X) @ np.abs(What).T)
+
+
+def quantize_transformer_stack(blocks, X0: np.ndarray, seq_len: int, heads: int, bits: int, group: int,
+                               block: int, damp_rel: float, act_dtype: Optional[str] = None,
+                               follow=None, tie: float = 0.0):
+    """The network-level loop over transformer blocks (reading R13; [GPTQ]
+    "Algorithm GPTQ": one layer at a time, each layer's calibration inputs
+    computed by the network as quantized so far).  blocks: list of (W_q, W_k,
+    W_v, W_o, W_gate, W_up, W_down).  Per block: H of x, q/k/v swept as one
+    stacked layer with its factor; QKV = x What_qkv^T; A = attention; H of A,
+    o swept; x += A What_o^T; H of x, gate/up swept together; A2 = swiglu; H of
+    A2, down swept; x += A2 What_down^T.
+
+    act_dtype="f16" rounds every activation where a 16-bit network stores it
+    (reading R16).  follow (one dict per block with that network's "QKV", "A",
+    "Yo", "X_mid", "GU", "A2", "Yd", "X_out" and the (q, z) of its four sweeps
+    "qkv", "o", "gate_up", "down") and tie compare against such a network: its
+    codes and zero points are taken at near-ties (gptq_quantize's follow) and
+    its activations where they are roundings of a value within the error
+    bound of an fp32 computation of that value (round_activations).  Returns
+    (per-block dicts, final x)."""
+    X, _ = round_activations(X0, act_dtype)
+    out = []
+    for b, (Wq, Wk, Wv, Wo, Wg, Wu, Wd) in enumerate(blocks):
+        fb = follow[b] if follow is not None else {}
+        rec = {"X": X, "followed_act": 0}
+
+        def act(name, y, tol):
+            v, k = round_activations(y, act_dtype, fb.get(name), tol)
+            rec["followed_act"] += k
+            rec[name] = v
+            return v
+
+        def sweep(W, Xin, name):
+            H = hessian([Xin])
+            U, info = inverse_cholesky_upper(damp(H, damp_rel)[0])
+            if info:
+                raise ValueError(f"{name}: Hessian not positive definite")
+            fq = fb.get(name)
+            r = gptq_quantize(np.asarray(W, np.float64), U, bits, group, block, follow=fq,
+                              tie=tie if fq is not None else 0.0)
+            rec[name] = r
+            rec["U_" + name] = U
+            return r
+
+        d = X.shape[1]
+        r = sweep(np.concatenate([Wq, Wk, Wv], axis=0), X, "qkv")
+        QKV = act("QKV", X @ r["What"].T, _matmul_tol(X, r["What"]))
+        Q, K_, V = QKV[:, :d], QKV[:, d:2 * d], QKV[:, 2 * d:]
+        A0 = attention(Q, K_, V, seq_len, heads)
+        A = act("A", A0, attention_error_bound(Q, K_, V, A0, seq_len, heads))
+        r = sweep(Wo, A, "o")
+        Yo = act("Yo", A @ r["What"].T, _matmul_tol(A, r["What"]))
+        Xm = act("X_mid", X + Yo, 2.0 ** -23 * np.abs(X + Yo))
+        r = sweep(np.concatenate([Wg, Wu], axis=0), Xm, "gate_up")
+        GU = act("GU", Xm @ r["What"].T, _matmul_tol(Xm, r["What"]))
+        f = np.asarray(Wg).shape[0]
+        A2y = swiglu(GU[:, :f], GU[:, f:])
+        A2 = act("A2", A2y, 2.0 ** -20 * np.abs(A2y) + 2.0 ** -40)
+        r = sweep(Wd, A2, "down")
+        Yd = act("Yd", A2 @ r["What"].T, _matmul_tol(A2, r["What"]))
+        X = act("X_out", Xm + Yd, 2.0 ** -23 * np.abs(Xm + Yd))
+        out.append(rec)
     return out, X

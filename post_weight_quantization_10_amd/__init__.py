@@ -77,6 +77,8 @@ def _load() -> ctypes.CDLL:
     L.gptq_swiglu.restype = i32
     L.gptq_residual_add.argtypes = [vp, vp, i32, i64, i64, i64, vp]
     L.gptq_residual_add.restype = i32
+    L.gptq_attention.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, vp]
+    L.gptq_attention.restype = i32
     L.gptq_quantize_greedy_workspace_bytes.argtypes = [i64, i64]
     L.gptq_quantize_greedy_workspace_bytes.restype = sz
     L.gptq_quantize_greedy.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -377,6 +379,87 @@ def residual_add(X: torch.Tensor, Y: torch.Tensor) -> torch.Tensor:
                                    _stream(X.device))
     _check("gptq_residual_add", st)
     return X
+
+
+def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_len: int, heads: int,
+              O: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal multi-head softmax attention over sequences of seq_len
+    consecutive tokens; Q, K, V [tokens, heads * head_dim] fp16/bf16 with a
+    common row stride.  Returns O in the same layout."""
+    _rows16(Q, "Q")
+    for t, nm in ((K, "K"), (V, "V")):
+        _require(t.shape == Q.shape and t.dtype == Q.dtype and t.stride() == Q.stride() and t.device == Q.device,
+                 f"{nm} must match Q")
+    T, dm = Q.shape
+    _require(heads >= 1 and dm % heads == 0, "the row width must be heads * head_dim")
+    if O is None:
+        O = torch.empty_strided(Q.shape, Q.stride(), dtype=Q.dtype, device=Q.device)
+    _require(O.shape == Q.shape and O.dtype == Q.dtype and O.stride() == Q.stride(), "O must match Q")
+    st = _load().gptq_attention(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), _DT[Q.dtype], T,
+                                int(seq_len), int(heads), dm // heads, max(Q.stride(0), dm), _stream(Q.device))
+    _check("gptq_attention", st)
+    return O
+
+
+def quantize_transformer_stack(blocks, X0: torch.Tensor, seq_len: int, heads: int, bits: int = 4,
+                               group_size: int = 128, block_size: int = 128, damp: float = 0.01,
+                               keep_inputs: bool = False):
+    """The network-level loop over transformer blocks (no normalization):
+        x <- x + W_o attn(W_q x, W_k x, W_v x);  x <- x + W_down (silu(W_gate x) * (W_up x))
+    one layer at a time, each layer's calibration inputs computed by the
+    network as quantized so far.  blocks: list of (W_q, W_k, W_v, W_o, W_gate,
+    W_up, W_down) CUDA tensors (fp16/bf16, not modified; q/k/v and o are
+    [d, d], gate/up [f, d], down [d, f]).  X0: [tokens, d] activations in the
+    same dtype, tokens grouped in sequences of seq_len.  Per block: H of x
+    (shared by q, k, v: their rows are swept together), Q/K/V through
+    gptq_dequant_matmul, A = attention, H of A and the o sweep, x += A W_o^T;
+    then H of x (shared by gate and up), G and Uo, A2 = swiglu, H of A2 and the
+    down sweep, x += A2 W_down^T.  Returns (per-block dicts with the four
+    quantize_layer results and factors, plus every activation when
+    keep_inputs, final x)."""
+    X = X0.clone()
+    out = []
+
+    def factor(Xa):
+        n = Xa.shape[1]
+        H = torch.zeros((n, n), dtype=torch.float32, device=Xa.device)
+        hessian_accumulate(H, Xa)
+        U, _, info = prepare_hinv(H, damp)
+        return U, info
+
+    def product(Xa, r):
+        return dequant_matmul(Xa, r["qcodes"], r["scales"], r["zeros"], bits, group_size)
+
+    for Wq, Wk, Wv, Wo, Wg, Wu, Wd in blocks:
+        d = X.shape[1]
+        rec = {}
+        X_in = X.clone() if keep_inputs else None
+        U1, i1 = factor(X)
+        rqkv = quantize_layer(torch.cat([Wq, Wk, Wv], dim=0), U1, bits, group_size, block_size, write_dequant=False)
+        qkv = product(X, rqkv)                               # [tokens, 3d]: Q | K | V
+        Q, K, V = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+        A = attention(Q, K, V, seq_len, heads)
+        U2, i2 = factor(A)
+        ro = quantize_layer(Wo.clone(), U2, bits, group_size, block_size, write_dequant=False)
+        Yo = product(A, ro)
+        X = residual_add(X, Yo)
+        X_mid = X.clone() if keep_inputs else None
+        U3, i3 = factor(X)
+        rgu = quantize_layer(torch.cat([Wg, Wu], dim=0), U3, bits, group_size, block_size, write_dequant=False)
+        GU = product(X, rgu)                                 # [tokens, 2f]: G | Uo
+        f = Wg.shape[0]
+        A2 = swiglu(GU[:, :f], GU[:, f:])
+        U4, i4 = factor(A2)
+        rd = quantize_layer(Wd.clone(), U4, bits, group_size, block_size, write_dequant=False)
+        Yd = product(A2, rd)
+        X = residual_add(X, Yd)
+        if any(int(t.item()) != 0 for t in (i1, i2, i3, i4)):
+            raise GPTQError("gptq_prepare_hinv (a block's Hessian is not positive definite)", GPTQ_ERR_INVALID_ARG)
+        rec.update({"qkv": rqkv, "o": ro, "gate_up": rgu, "down": rd, "U": (U1, U2, U3, U4)})
+        if keep_inputs:
+            rec.update({"X": X_in, "QKV": qkv, "A": A, "Yo": Yo, "X_mid": X_mid, "GU": GU, "A2": A2, "Yd": Yd})
+        out.append(rec)
+    return out, X
 
 
 def quantize_mlp_stack(blocks, X0: torch.Tensor, bits: int = 4, group_size: int = 128, block_size: int = 128,

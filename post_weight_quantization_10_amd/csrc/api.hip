@@ -28,6 +28,9 @@ hipError_t rotate_hadamard(void* M, int dt, int64_t rows, int64_t n, int64_t ld,
 hipError_t swiglu(const void* G, const void* U, void* A, int dt, int64_t rows, int64_t cols, int64_t ld,
                   hipStream_t st);
 hipError_t residual_add(void* X, const void* Y, int dt, int64_t rows, int64_t cols, int64_t ld, hipStream_t st);
+bool attention_supported(int64_t seq_len, int64_t head_dim);
+hipError_t attention(const void* Q, const void* K, const void* V, void* O, int dt, int64_t T, int64_t S,
+                     int64_t heads, int64_t dh, int64_t ld, hipStream_t st);
 bool greedy_supported(int64_t n, int64_t group);
 size_t greedy_workspace_bytes(int64_t m, int64_t n);
 hipError_t quantize_greedy(const void* W, int dt, int64_t m, int64_t n, int64_t ldw, const float* U, int bits,
@@ -208,6 +211,21 @@ gptq_status gptq_residual_add(void* X, const void* Y, int32_t dtype, int64_t tok
   if (tokens == 0) return GPTQ_OK;
   if (X == nullptr || Y == nullptr || tokens * (ld / d + 1) * d >= ((int64_t)1 << 40)) return GPTQ_ERR_INVALID_ARG;
   hipError_t e = gptq::residual_add(X, Y, dtype, tokens, d, ld, (hipStream_t)stream);
+  return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+}
+
+gptq_status gptq_attention(const void* Q, const void* K, const void* V, void* O, int32_t dtype, int64_t tokens,
+                           int64_t seq_len, int64_t heads, int64_t head_dim, int64_t ld, void* stream) {
+  if (tokens < 0 || seq_len < 1 || heads < 1 || head_dim < 1 || ld < heads * head_dim ||
+      !(dtype == GPTQ_F16 || dtype == GPTQ_BF16) || (tokens > 0 && tokens % seq_len != 0) ||
+      heads > 65535 || tokens >= ((int64_t)1 << 37))
+    return GPTQ_ERR_INVALID_ARG;
+  if (tokens == 0) return GPTQ_OK;
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return GPTQ_ERR_INVALID_ARG;
+  const auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (!gptq::attention_supported(seq_len, head_dim) || ld % 8 != 0 || !al16(Q) || !al16(K) || !al16(V) || !al16(O))
+    return GPTQ_ERR_UNSUPPORTED;
+  hipError_t e = gptq::attention(Q, K, V, O, dtype, tokens, seq_len, heads, head_dim, ld, (hipStream_t)stream);
   return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
 }
 

@@ -236,3 +236,20 @@ def test_static_dequant_matmul_limits():
                                         None) == pw.GPTQ_OK
     assert L.gptq_dequant_matmul_static(FAKE, pw.F16, T, n, FAKE, FAKE, FAKE, 64, n, 5, 128, FAKE, 64,
                                         None) == pw.GPTQ_ERR_UNSUPPORTED
+
+
+def test_attention_rejects_on_host():
+    L = _lib()
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dt=0, T=256, S=64, h=2, dh=64, ld=128)
+
+    def call(**kw):
+        b = dict(a)
+        b.update(kw)
+        return L.gptq_attention(b["Q"], b["K"], b["V"], b["O"], b["dt"], b["T"], b["S"], b["h"], b["dh"], b["ld"],
+                                None)
+    for kw in (dict(T=-1), dict(T=100), dict(S=0), dict(h=0), dict(dh=0), dict(ld=100), dict(dt=2), dict(Q=None),
+               dict(O=None)):
+        assert call(**kw) == pw.GPTQ_ERR_INVALID_ARG, kw
+    for kw in (dict(dh=32, ld=64), dict(S=32, T=256), dict(ld=130), dict(K=ctypes.c_void_p(0x1008))):
+        assert call(**kw) == pw.GPTQ_ERR_UNSUPPORTED, kw
+    assert call(T=0, Q=None, K=None, V=None, O=None) == pw.GPTQ_OK

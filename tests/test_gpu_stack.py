@@ -13,6 +13,15 @@ the GPU's own inputs to that step, so the chain is verified link by link:
   * the next block's input X + Y within u |X + Y| + (1 + u) 2^-24 |X + Y|
     + 2^-25 (one fp32 add, one rounding).
 The oracle's own fp64 stack from the same X0 is reported beside it.
+
+test_transformer_stack_end_to_end runs the loop over transformer blocks
+(attention with q/k/v on one shared Hessian, o, then the MLP) and the oracle's
+network with its activations rounded to fp16 where the GPU stores them; the
+oracle follows the GPU only where both are correct (a code or zero point
+within 1e-4 steps of a rounding boundary; an activation that is the fp16
+rounding of a value within the fp32 error bound of the exact result), after
+which every activation, code and zero point of every block must be identical
+and every scale within 1e-5.
 """
 import numpy as np
 import pytest
@@ -98,3 +107,46 @@ def test_mlp_stack_link_by_link():
     # not a parity bar: the fp64 network carries unrounded activations, so its
     # Hessians and then its decisions drift from the fp16 network's
     assert rel < 0.1
+
+
+def test_transformer_stack_end_to_end():
+    d, f, T, seq, heads, L, bits, group, B = 512, 1024, 2048, 256, 4, 2, 4, 128, 128
+    blocks_np = []
+    for l in range(L):
+        ws = []
+        for k, (r, c) in enumerate([(d, d)] * 4 + [(f, d), (f, d), (d, f)]):
+            ws.append(synth.small_layer(r, c, 16, seed=400 + 7 * l + k, w_dtype="f16", outlier_frac=0.001)[0])
+        blocks_np.append(tuple(ws))
+    X0 = synth.activations(T, d, "f16", seed=41)
+    blocks = [tuple(torch.from_numpy(w).to(DEV) for w in blk) for blk in blocks_np]
+    res, XL = pw.quantize_transformer_stack(blocks, torch.from_numpy(X0).to(DEV), seq, heads, bits, group, B, 0.01,
+                                            keep_inputs=True)
+    torch.cuda.synchronize()
+    names = ("QKV", "A", "Yo", "X_mid", "GU", "A2", "Yd")
+    widths = {"qkv": d, "o": d, "gate_up": d, "down": f}
+    fol = []
+    for l, r in enumerate(res):
+        fb = {k: _h64(r[k]) for k in names}
+        fb["X_out"] = _h64(res[l + 1]["X"]) if l + 1 < L else _h64(XL)
+        for k, n in widths.items():
+            q, s_, z = _codes(r[k], n, bits)
+            fb[k] = (q, z)
+            fb["s_" + k] = s_
+        fol.append(fb)
+    ores, oX = O.quantize_transformer_stack([tuple(w.astype(np.float64) for w in blk) for blk in blocks_np],
+                                            X0.astype(np.float64), seq, heads, bits, group, B, 0.01,
+                                            act_dtype="f16", follow=fol, tie=1e-4)
+    for l, (r, fb) in enumerate(zip(ores, fol)):
+        ncode = sum(r[k]["followed"] for k in widths)
+        say(f"[transformer stack] block {l}: followed {r['followed_act']} activation roundings, {ncode} codes")
+        for k in names + ("X_out",):
+            bad = np.argwhere(r[k] != fb[k])
+            assert not len(bad), f"block {l} {k}: {len(bad)} values differ after following, first {bad[0]}: " \
+                                 f"gpu {fb[k][tuple(bad[0])]} oracle {r[k][tuple(bad[0])]}"
+        for k in widths:
+            q, z = fb[k]
+            assert np.array_equal(r[k]["q"], q), f"block {l} {k}: codes differ away from near-ties"
+            assert np.array_equal(r[k]["z"].astype(np.int64), z.astype(np.int64)), f"block {l} {k}: zero points"
+            srel = float(np.max(np.abs(fb["s_" + k] - r[k]["s"]) / np.abs(r[k]["s"])))
+            assert srel <= 1e-5, f"block {l} {k}: scale rel err {srel:.2e}"
+    np.testing.assert_array_equal(oX, _h64(XL))
