@@ -97,7 +97,11 @@ def run_job(workload: str, job_index: int, sample_rows: int = 1024, sample_cols:
     r = Hd @ (Ug.T @ (Ug @ v)) - v
     out["u_resid"] = float(np.linalg.norm(r) / np.linalg.norm(v))
     say(f"  ||U^T U H_d v - v|| / ||v|| = {out['u_resid']:.3e}")
-    assert out["u_resid"] <= 1e-2
+    # measured 2.6e-7 (n = 4096) up to 4.4e-5 (n = 11008 at 65536 tokens,
+    # cond(H_d) 3e5); 2e-4 leaves room for box-to-box rounding order and
+    # catches a regression of the large-n factor, which for n above the
+    # host-prepare limit has no element-wise comparison with the oracle
+    assert out["u_resid"] <= 2e-4
 
     # ---- sweep on sampled rows
     rows = np.sort(rng.choice(m, size=min(sample_rows, m), replace=False))
