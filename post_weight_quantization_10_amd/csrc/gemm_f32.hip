@@ -385,6 +385,130 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_dma_kernel(GemmDesc d, int nsp
       }
 }
 
+// ---------------------------------------------------------------------------- NN, 64 x 64 tiles
+//
+// The same staging for products whose 128 x 128 tile grid would leave the GPU
+// under-filled, such as the doubling products of a triangular inverse, where a
+// triangular operand also gives the tiles K ranges from 64 to K: 64 x 64
+// tiles, four waves of 32 x 32 (2 x 2 blocks of v_mfma_f32_16x16x4f32), a ring
+// of three 32-deep K stages with one barrier per stage.  One linear grid over
+// (tile, batch entry) is ordered longest K range first, so the short tiles
+// fill in behind the long ones and no split-K partial sums are needed.
+
+constexpr int SB = 64, SNS = 3;
+constexpr int SSTAGE_F = 2 * SB * DBK;  // floats per stage (A then B): 16 KiB
+__device__ __forceinline__ int swzB4(int k) { return (k & 3) << 2; }  // chunk XOR for the 64-wide B rows
+
+__global__ __launch_bounds__(256, 2) void gemm_nn_dma64_kernel(GemmDesc d, int tM, int tN) {
+  if (d.info && *d.info != 0) return;
+  __shared__ __attribute__((aligned(1024))) float stg[SNS * SSTAGE_F];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int z = (int)(blockIdx.x % (unsigned)d.batch), rank = (int)(blockIdx.x / (unsigned)d.batch);
+  int tm, tn;
+  if (d.flags & GEMM_A_LOWER) {  // the K range grows with the tile row
+    tm = tM - 1 - rank / tN;
+    tn = rank % tN;
+  } else if (d.flags & GEMM_B_LOWER) {  // and shrinks with the tile column
+    tn = rank / tM;
+    tm = rank % tM;
+  } else {
+    tm = rank / tN;
+    tn = rank % tN;
+  }
+  const int r0 = tm * SB, c0 = tn * SB;
+  const float* A = d.A + z * d.strideA;
+  const float* B = d.B + z * d.strideB;
+  float* C = d.C + z * d.strideC;
+  int kLo = 0, kHi = d.K;
+  if (d.flags & GEMM_A_LOWER) kHi = min(kHi, r0 + SB);
+  if (d.flags & GEMM_B_LOWER) kLo = c0;
+  const int nst = kHi > kLo ? (kHi - kLo) / DBK : 0;
+  const int mrows = min(SB, d.M - r0), ncols = min(SB, d.N - c0);
+
+  // this lane's copies of one stage: A rows 16w + 8q + l/8 (eight 16-byte
+  // chunks each), B rows 8w + 4q + l/16 (sixteen chunks each)
+  int voffA[2], voffB[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int ra = 16 * wave + 8 * q + (lane >> 3);
+    voffA[q] = (int)((int64_t)ra * d.lda * 4) + (((lane & 7) ^ swzA(ra)) << 4);
+    const int rb = 8 * wave + 4 * q + (lane >> 4);
+    voffB[q] = (int)((int64_t)rb * d.ldb * 4) + (((lane & 15) ^ swzB4(rb)) << 4);
+  }
+  const uint32_t aBytes = (uint32_t)(((int64_t)(mrows - 1) * d.lda + DBK) * 4);
+  const uint32_t bBytes = (uint32_t)(((int64_t)(DBK - 1) * d.ldb + ncols) * 4);
+  auto issue = [&](int st) {
+    const int kc = kLo + st * DBK;
+    const i32x4 ra = make_rsrc(A + (int64_t)r0 * d.lda + kc, aBytes);
+    const i32x4 rb = make_rsrc(B + (int64_t)kc * d.ldb + c0, bBytes);
+    const uint32_t sb = (uint32_t)(uintptr_t)((float LDS_AS*)(stg + (st % SNS) * SSTAGE_F));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dma16(ra, sb + (uint32_t)((16 * wave + 8 * q) * DBK * 4), voffA[q]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dma16(rb, sb + (uint32_t)((SB * DBK + (8 * wave + 4 * q) * SB) * 4), voffB[q]);
+  };
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // v_mfma_f32_16x16x4f32: lane l gives A[l%16][k] and B[k][l%16] with
+  // k = 4kk + l/16; result register r is row 4(l/16) + r, column l%16
+  const int l16 = lane & 15, kq = lane >> 4;
+  auto compute = [&](const float* s) {
+    const float* sA = s;
+    const float* sB = s + SB * DBK;
+#pragma unroll
+    for (int kk = 0; kk < DBK / 4; ++kk) {
+      const int k = 4 * kk + kq;
+      float a[2], b[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = 32 * wr + 16 * mb + l16;
+        a[mb] = sA[row * DBK + ((kk ^ swzA(row)) << 2) + kq];
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = 32 * wc + 16 * nb + l16;
+        b[nb] = sB[k * SB + (((col >> 2) ^ swzB4(k)) << 2) + (col & 3)];
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+    }
+  };
+
+  // three-stage ring: stages st + 1 and st + 2 are in flight while st computes
+  if (nst > 0) issue(0);
+  if (nst > 1) issue(1);
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) wait_vmcnt<4>(); else wait_vmcnt<0>();
+    stage_barrier();  // stage st visible to every wave; every wave is done with stage st - 1
+    if (st + 2 < nst) issue(st + 2);
+    compute(stg + (st % SNS) * SSTAGE_F);
+  }
+
+  const float alpha = d.alpha, beta = d.beta;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 32 * wr + 16 * mb + 4 * kq + r, col = c0 + 32 * wc + 16 * nb + l16;
+        if (row < d.M && col < d.N) {
+          float* pc = C + (int64_t)row * d.ldc + col;
+          const float v = alpha * acc[mb][nb][r];
+          *pc = (beta == 0.f) ? v : fmaf(beta, *pc, v);
+        }
+      }
+}
+
 // C tile = alpha * (sum of its chunks in chunk order) + beta * C; chunks past
 // the tile's K range were never computed and are skipped.
 __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmDesc d, int nsplit, int chunk, const float* part) {
@@ -441,7 +565,10 @@ hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s) 
   const int tM = (int)cdiv(d.M, BM), tN = (int)cdiv(d.N, BN);
   if (d.flags & GEMM_LOWER_TILES) grid = dim3((unsigned)(tM * (tM + 1) / 2), 1, (unsigned)d.batch);
   else grid = dim3((unsigned)tM, (unsigned)tN, (unsigned)d.batch);
-  if (!transA && !transB && nn_dma_ok(d)) {
+  if (!transA && !transB && (d.flags & GEMM_SMALL_TILES) && nn_dma_ok(d)) {
+    const int sM = (int)cdiv(d.M, SB), sN = (int)cdiv(d.N, SB);
+    hipLaunchKernelGGL(gemm_nn_dma64_kernel, dim3((unsigned)((int64_t)sM * sN * d.batch)), dim3(256), 0, s, d, sM, sN);
+  } else if (!transA && !transB && nn_dma_ok(d)) {
     // split K when the tiles alone would give fewer than about four work
     // items per CU (the triangular products have K ranges from 128 to K, so
     // balance needs more items than workgroup slots) and K is long: chunks of

@@ -16,6 +16,8 @@ enum : int {
   GEMM_LOWER_TILES = 1,  // C square; only 128x128 tiles on or below the diagonal are computed
   GEMM_A_LOWER = 2,      // op(A)[i][k] == 0 for k > i (skip those K chunks)
   GEMM_B_LOWER = 4,      // op(B)[k][j] == 0 for k < j (skip those K chunks)
+  GEMM_SMALL_TILES = 8,  // NN products on 64x64 tiles, longest K range first, never split (for grids of few
+                         // 128x128 tiles with triangular operands)
 };
 
 struct GemmDesc {
