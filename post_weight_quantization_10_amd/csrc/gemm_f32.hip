@@ -549,6 +549,24 @@ bool nn_dma_ok(const GemmDesc& d) {
          (int64_t)(BM - 1) * d.lda * 4 + 4096 < ((int64_t)1 << 31) && (int64_t)(DBK - 1) * d.ldb * 4 + 4096 < ((int64_t)1 << 31);
 }
 
+// Whether 64 x 64 tiles finish a full-K product (no triangular operand) in
+// fewer rounds of resident workgroups than 128 x 128 tiles: a 128-tile does
+// four times the work of a 64-tile, two of either fit on a CU, and a round of
+// 64-tiles is taken as 15 % less efficient (more operand traffic per flop).
+// True for the narrow late flushes of a sweep, whose 128-tile grid leaves
+// most CUs idle.
+bool small_tiles_pay(const GemmDesc& d, int tM, int tN, int sM, int sN) {
+  if (d.flags & (GEMM_A_LOWER | GEMM_B_LOWER)) return false;
+  static const int64_t slots = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    return (int64_t)2 * cus;
+  }();
+  const int64_t r128 = cdiv((int64_t)tM * tN * d.batch, slots), r64 = cdiv((int64_t)sM * sN * d.batch, slots);
+  return 20 * r64 < 17 * 4 * r128;
+}
+
 template <bool TA, bool TB>
 void launch(const GemmDesc& d, dim3 grid, hipStream_t s) {
   const bool vec = d.lda % 4 == 0 && d.ldb % 4 == 0 && d.strideA % 4 == 0 && d.strideB % 4 == 0 &&
@@ -565,8 +583,8 @@ hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s) 
   const int tM = (int)cdiv(d.M, BM), tN = (int)cdiv(d.N, BN);
   if (d.flags & GEMM_LOWER_TILES) grid = dim3((unsigned)(tM * (tM + 1) / 2), 1, (unsigned)d.batch);
   else grid = dim3((unsigned)tM, (unsigned)tN, (unsigned)d.batch);
-  if (!transA && !transB && (d.flags & GEMM_SMALL_TILES) && nn_dma_ok(d)) {
-    const int sM = (int)cdiv(d.M, SB), sN = (int)cdiv(d.N, SB);
+  const int sM = (int)cdiv(d.M, SB), sN = (int)cdiv(d.N, SB);
+  if (!transA && !transB && nn_dma_ok(d) && ((d.flags & GEMM_SMALL_TILES) || small_tiles_pay(d, tM, tN, sM, sN))) {
     hipLaunchKernelGGL(gemm_nn_dma64_kernel, dim3((unsigned)((int64_t)sM * sN * d.batch)), dim3(256), 0, s, d, sM, sN);
   } else if (!transA && !transB && nn_dma_ok(d)) {
     // split K when the tiles alone would give fewer than about four work
