@@ -12,15 +12,20 @@
 // inverse (2n^3/3 flops) instead of four factor-sized steps (4n^3/3).
 //
 //   1. reversed copy + damping  A = J H J + lambda I             (HBM-bound)
-//   2. blocked right-looking Cholesky of A in NB = 64 column blocks, one
-//      kernel per block column k.  Workgroup 0 takes the next diagonal block:
-//      it applies the update from block column k to it, factors it and
-//      inverts the factor (Dinv_{k+1}).  Every other workgroup owns a 128 x 128
-//      lower tile of the trailing matrix: it solves the two panel slabs it
-//      needs on the fly, L21 = A21 Dinv_k^T (MFMA, fp32), applies
-//      A22 <- A22 - L21 L21^T (MFMA, fp32), and the tiles of the first tile
-//      column store their slab of L21.  So the next diagonal block is factored
-//      while the rest of the trailing update runs, one launch per block.
+//   2. blocked Cholesky of A in NB = 64 column blocks, two levels: panels of
+//      PB = 4 blocks.  One launch per block column k of a panel: workgroup 0
+//      takes the next diagonal block (it applies the update from block column
+//      k to it, factors it and inverts the factor, Dinv_{k+1}); the other
+//      workgroups own 128 x 128 lower tiles of the panel's remaining columns:
+//      they solve the slabs they need on the fly, L21 = A21 Dinv_k^T (MFMA,
+//      fp32), apply A22 <- A22 - L21 L21^T (MFMA, fp32), and the tiles of the
+//      first tile column store their slab of L21 to L.  After the panel, one
+//      rank-256 update from the stored panel of L: the launch that factors the
+//      next panel's first diagonal block (its update taken from L) applies it
+//      to the next panel's columns, and the rest of it is dealt out over the
+//      next panel's launches.  So each diagonal block is factored while tiles
+//      run, and the trailing matrix moves through memory once per 256
+//      columns instead of once per 64.
 //   3. triangular inverse in place by recursive doubling: with the NB-block
 //      inverses on the diagonal, for block sizes s = NB, 2NB, ...:
 //        L21^{-} = -L22^{-1} (L21 L11^{-1})   (two batched MFMA GEMMs)
@@ -87,7 +92,8 @@ __global__ __launch_bounds__(256) void reverse_damp4_kernel(const float* H, floa
 }
 
 constexpr int TB = 128;          // trailing-update tile
-constexpr int PRE_TILES = 256;   // above this many tiles a step solves its panel slabs in a kernel of their own
+constexpr int PB = 4;            // block columns per panel of the two-level Cholesky
+constexpr int64_t TWO_LEVEL_MIN = 4096;  // trailing columns below which a panel runs to the end
 constexpr int LP = 65;           // LDS pitch of 64-column leaf matrices (floats)
 constexpr int LLP = 68;          // LDS pitch of the leaf factor: 16-byte aligned rows
 constexpr int PP = 68;           // LDS pitch of the leaf's product operands: 16-byte aligned rows
@@ -108,7 +114,10 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 // If kp >= 0, first the update from block column K = [kp, kp + NB):
 //   Lrow = A[J, K] Dinv_K^T   (the rows J of that block column of the factor)
 //   D    = A[J, J] - Lrow Lrow^T
-// (two 64 x 64 x 64 MFMA products), else D = A[J, J].  Then D = L L^T and
+// (two 64 x 64 x 64 MFMA products).  If lnk > 0 instead, the update from lnk
+// block columns of the factor stored in L from column lk0 on:
+//   D    = A[J, J] - sum_c L[J, lk0 + 64c] L[J, lk0 + 64c]^T
+// (one 64 x 64 x 64 product per slab).  Else D = A[J, J].  Then D = L L^T and
 // Dinv_J = L^{-1}, written to dinv_out (NB x NB, zero outside the kb x kb
 // lower triangle).  Rows and columns past kb are padded with the identity.
 //
@@ -124,7 +133,8 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 // work that is not on the column chain goes to the matrix cores.)
 __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t n, int64_t j0, int64_t kp,
                                         const float* __restrict__ dinv_prev, float* __restrict__ dinv_out,
-                                        int32_t* info, float* smem) {
+                                        int32_t* info, float* smem, const float* __restrict__ Lsrc = nullptr,
+                                        int64_t lk0 = 0, int lnk = 0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = (int)min<int64_t>(NB, n - j0);
@@ -195,13 +205,37 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
   if (tid == 0) *failed = 0;
   __syncthreads();
 
-  // The two products with v_mfma_f32_16x16x4f32 (lane l: A[l%16][l/16],
+  // The products with v_mfma_f32_16x16x4f32 (lane l: A[l%16][l/16],
   // B[l/16][l%16]; result register r is row 4(l/16) + r, column l%16) on
   // 16 x 16 output blocks.  MFMA step 4t + q of a K = 64 sum gives lane
   // quarter kq = l/16 the index k = 16t + 4kq + q: one 16-byte read per
   // operand and group t, and a block that needs only k < 16(t+1) stops there.
+  const int i16 = lane & 15, kq = lane >> 4;
+  // D -= S S^T for the 64 x 64 slab S in sP, on the ten lower 16 x 16 blocks:
+  // 3, 3, 2, 2 of them per wave.  Blocks (bi, bj): wave 0 (0,0) (1,0) (1,1);
+  // wave 1 (2,0) (2,1) (2,2); wave 2 (3,0) (3,1); wave 3 (3,2) (3,3)
+  auto dupd = [&]() {
+    const int nblk = wave < 2 ? 3 : 2;
+    const int bi0 = wave == 0 ? 0 : (wave == 1 ? 2 : 3);
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      if (b < nblk) {
+        const int bi = wave == 0 ? (b == 0 ? 0 : 1) : bi0;
+        const int bj = wave == 0 ? (b == 0 ? 0 : b - 1) : (wave == 3 ? 2 + b : b);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f32x4 av = *(const f32x4*)&sP[(16 * bi + i16) * PP + 16 * t + 4 * kq];
+          const f32x4 bv = *(const f32x4*)&sP[(16 * bj + i16) * PP + 16 * t + 4 * kq];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sD[(16 * bi + 4 * kq + r) * LP + 16 * bj + i16] -= acc[r];
+      }
+    }
+  };
   if (kp >= 0) {
-    const int i16 = lane & 15, kq = lane >> 4;
     {  // Lrow rows 16w.. = P[16w.., :] Dinv_K^T; column block bj needs k < 16(bj+1) (Dinv_K is lower)
       f32x4 acc[4];
 #pragma unroll
@@ -223,27 +257,31 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
         for (int r = 0; r < 4; ++r) sP[(16 * wave + 4 * kq + r) * PP + 16 * bj + i16] = acc[bj][r];
     }
     __syncthreads();
-    {  // D -= Lrow Lrow^T on the ten lower 16 x 16 blocks: 3, 3, 2, 2 of them per wave
-      // blocks (bi, bj): wave 0 (0,0) (1,0) (1,1); wave 1 (2,0) (2,1) (2,2); wave 2 (3,0) (3,1); wave 3 (3,2) (3,3)
-      const int nblk = wave < 2 ? 3 : 2;
-      const int bi0 = wave == 0 ? 0 : (wave == 1 ? 2 : 3);
+    dupd();
+    __syncthreads();
+  }
+  if (lnk > 0) {
+    // the slabs L[J, lk0 + 64c] in turn through sP (rows past kb zero)
+    const bool v16 = (n & 3) == 0;
+    for (int c = 0; c < lnk; ++c) {
+      const float* src = Lsrc + lk0 + (int64_t)NB * c;
+      f32x4 lv[4];
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
-        if (b < nblk) {
-          const int bi = wave == 0 ? (b == 0 ? 0 : 1) : bi0;
-          const int bj = wave == 0 ? (b == 0 ? 0 : b - 1) : (wave == 3 ? 2 + b : b);
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const f32x4 av = *(const f32x4*)&sP[(16 * bi + i16) * PP + 16 * t + 4 * kq];
-            const f32x4 bv = *(const f32x4*)&sP[(16 * bj + i16) * PP + 16 * t + 4 * kq];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sD[(16 * bi + 4 * kq + r) * LP + 16 * bj + i16] -= acc[r];
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int e = tid + 256 * u;
+        const int r = e >> 4, c4 = 4 * (e & 15);
+        const float* q = src + (j0 + min(r, kb - 1)) * n + c4;
+        lv[u] = v16 ? *(const f32x4*)q : f32x4{q[0], q[1], q[2], q[3]};
       }
+      if (c > 0) __syncthreads();  // every wave is done with the previous slab
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = tid + 256 * u;
+        const int r = e >> 4, c4 = 4 * (e & 15);
+        *(f32x4*)&sP[r * PP + c4] = r < kb ? lv[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      __syncthreads();
+      dupd();
     }
     __syncthreads();
   }
@@ -445,53 +483,61 @@ __device__ __forceinline__ void panel_solve(const float* S, const float* sD, int
   }
 }
 
-// One 128 x 128 lower tile t of the trailing matrix [R0, n)^2, R0 = k0 + NB.
-// PRE: the panel slabs were solved beforehand (panel_solve_kernel wrote every
-// slab of L21 for this block column), so the tile loads its two slabs of L
-// instead of A21 and Dinv_k and goes straight to the rank update.
-template <bool VEC, bool PRE>
+// Tile lists.  A region [R0, n) x [R0, cend) of the trailing matrix is cut
+// into 128 x 128 tiles, nr tile rows and nc <= nr tile columns; its lower
+// tiles (tm >= tn) are listed column by column, so column j starts at
+// C(j) = j nr - j (j - 1) / 2.
+__device__ __forceinline__ void region_tile(int t, int nr, int& tm, int& tn) {
+  const float b = 2.f * (float)nr + 1.f;
+  int j = (int)((b - sqrtf(fmaxf(b * b - 8.f * (float)t, 0.f))) * 0.5f);
+  auto C = [nr](int c) { return c * nr - c * (c - 1) / 2; };
+  while (j > 0 && C(j) > t) --j;
+  while (C(j + 1) <= t) ++j;
+  tn = j;
+  tm = j + (t - C(j));
+}
+
+// One 128 x 128 lower tile (tm, tn) of the region [R0, n) x [R0, cend):
+//   C -= sum over slabs S of S[rows] S[cols]^T,
+// S a 64-column block column of the factor.  SOLVE: one slab, solved here
+// from A's block column at k0 (S = A21 Dinv_k^T, MFMA fp32), and the tiles of
+// the first tile column store their rows of it to L.  Else nk slabs read from
+// L's columns k0 + 64 c, the next slab's loads in flight while the current
+// one's MFMAs run.  skip00: the first 64 x 64 quadrant of tile (0, 0) is a
+// diagonal block that workgroup 0 updates itself.
+template <bool VEC, bool SOLVE>
 __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __restrict__ L,
-                                            const float* __restrict__ dinv_k, int64_t n, int64_t k0, int t,
-                                            float* smem) {
+                                            const float* __restrict__ dinv_k, int64_t n, int64_t k0, int nk,
+                                            int64_t R0, int64_t cend, int tm, int tn, bool skip00, float* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  float* sD = smem;            // 64 x 64: Dinv_k
-  float* sR = sD + 64 * 64;    // 128 x 64: rows of the tile's row slab, A21 then L21
+  float* sD = smem;            // 64 x 64: Dinv_k (SOLVE)
+  float* sR = sD + 64 * 64;    // 128 x 64: the tile's row slab (SOLVE: A21, then L21)
   float* sC = sR + 128 * 64;   // 128 x 64: the same for the column slab
-  int tm = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
-  while ((tm + 1) * (tm + 2) / 2 <= t) ++tm;
-  while (tm * (tm + 1) / 2 > t) --tm;
-  const int tn = t - tm * (tm + 1) / 2;
-  const int64_t R0 = k0 + NB;
   const int64_t r0 = R0 + (int64_t)tm * TB, c0 = R0 + (int64_t)tn * TB;
   const bool dg = tm == tn;
   const int wr = wave >> 1, wc = wave & 1;
-  // A quadrant of a diagonal tile above the diagonal has nothing to do, and
-  // neither has the first quadrant of tile 0: that is the next diagonal block,
-  // which workgroup 0 updates itself.
-  const bool active = !(dg && wr < wc) && !(tm == 0 && wr == 0 && wc == 0);
+  // Nothing to do for a quadrant of a diagonal tile above the diagonal, for
+  // one whose columns all lie past cend, and for the skipped diagonal block.
+  const bool active =
+      !(dg && wr < wc) && c0 + 64 * wc < cend && !(skip00 && tm == 0 && tn == 0 && wr == 0 && wc == 0);
   const uint32_t n32 = (uint32_t)n;
+  const float* P = SOLVE ? (const float*)A : (const float*)L;
 
-  // Panel rows and Dinv_k (PRE: the solved rows of L): all loads in flight
-  // together, then to LDS.  Rows past n are clamped: they only reach outputs
-  // that are never stored.
-  {
-    const float* P = PRE ? L : A;
-    f32x4 pr[8], pc[8], dv[4];
+  // Rows of the tile's row and column slabs at column col, all loads in
+  // flight together.  Rows past n are clamped: they only reach outputs that
+  // are never stored.
+  f32x4 pr[8], pc[8];
+  auto load_slabs = [&](int64_t col) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = tid + 256 * u;
       const int r = e >> 4, g = 4 * (e & 15);
-      pr[u] = ld4<VEC>(P + min(r0 + r, n - 1) * n + k0 + g);
-      if (!dg) pc[u] = ld4<VEC>(P + min(c0 + r, n - 1) * n + k0 + g);
+      pr[u] = ld4<VEC>(P + min(r0 + r, n - 1) * n + col + g);
+      if (!dg) pc[u] = ld4<VEC>(P + min(c0 + r, n - 1) * n + col + g);
     }
-    if (!PRE) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = tid + 256 * u;
-        dv[u] = *(const f32x4*)&dinv_k[(e >> 4) * NB + 4 * (e & 15)];
-      }
-    }
+  };
+  auto store_slabs = [&]() {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = tid + 256 * u;
@@ -499,39 +545,111 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
       *(f32x4*)&sR[pidx(r, g)] = pr[u];
       if (!dg) *(f32x4*)&sC[pidx(r, g)] = pc[u];
     }
-    if (!PRE) {
+  };
+  const int cl = lane & 31, kr = lane >> 5;
+
+  // C of this wave's 64 x 64 quadrant through a buffer resource over the
+  // tile's rows inside the matrix and 32-bit lane offsets (the tile spans
+  // fewer than 128 n elements, n < 2^22).  Loads past the last row read as
+  // zero and entries past n or cend are never stored, so edge tiles need no
+  // clamping; a store that must not happen gets an offset past the buffer and
+  // is dropped, so no store is behind a branch.
+  const bool interior = r0 + TB <= n && c0 + TB <= cend;
+  const uint32_t lr0 = (uint32_t)(64 * wr + 4 * (lane >> 5)), lc0 = (uint32_t)(64 * wc + (lane & 31));
+  const uint32_t rlim = (uint32_t)(min<int64_t>(TB, n - r0) - 1), clim = (uint32_t)(min<int64_t>(TB, cend - c0) - 1);
+  const __amdgpu_buffer_rsrc_t trs =
+      __builtin_amdgcn_make_buffer_rsrc(A + (r0 * n + c0), 0, (int)((rlim + 1) * n32 * 4u), 0x00020000);
+  const uint32_t loff = (lr0 * n32 + lc0) * 4u;
+  auto coff = [&](int mb, int nb, int r) {
+    return loff + ((uint32_t)(32 * mb + 8 * (r >> 2) + (r & 3)) * n32 + (uint32_t)(32 * nb)) * 4u;
+  };
+  f32x16 cp[2][2];
+  auto load_c = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        cp[mb][nb] = zero16();
+        if (active) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            cp[mb][nb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(trs, coff(mb, nb, r), 0, 0));
+        }
+      }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
+  const float* sB = dg ? sR : sC;
+  // acc += (rows of sR) (rows of sB)^T over the slab's 64 columns; the
+  // operands of steps 4g+4.. are read while the MFMAs of steps 4g.. run
+  auto rank_update = [&]() {
+    f32x4 a0[2], a1[2], b0[2], b1[2];
+    auto ld = [&](int g, int b) {
+      const int k = kgroup(g, kr);
+      a0[b] = *(const f32x4*)&sR[pidx(64 * wr + cl, k)];
+      a1[b] = *(const f32x4*)&sR[pidx(64 * wr + 32 + cl, k)];
+      b0[b] = *(const f32x4*)&sB[pidx(64 * wc + cl, k)];
+      b1[b] = *(const f32x4*)&sB[pidx(64 * wc + 32 + cl, k)];
+    };
+    ld(0, 0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int b = g & 1;
+      if (g + 1 < 8) ld(g + 1, b ^ 1);
+      __builtin_amdgcn_sched_barrier(0);  // keeps the reads ahead of this group's MFMAs
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[0][0] = mfma_f32(a0[b][q], b0[b][q], acc[0][0]);
+        acc[0][1] = mfma_f32(a0[b][q], b1[b][q], acc[0][1]);
+        acc[1][0] = mfma_f32(a1[b][q], b0[b][q], acc[1][0]);
+        acc[1][1] = mfma_f32(a1[b][q], b1[b][q], acc[1][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if constexpr (SOLVE) {
+    {
+      f32x4 dv[4];
+      load_slabs(k0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = tid + 256 * u;
+        dv[u] = *(const f32x4*)&dinv_k[(e >> 4) * NB + 4 * (e & 15)];
+      }
+      store_slabs();
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = tid + 256 * u;
         *(f32x4*)&sD[pidx(e >> 4, 4 * (e & 15))] = dv[u];
       }
     }
-  }
-  __syncthreads();
-
-  // L21 slabs; each wave reads and then overwrites only its own 32 rows
-  // the first tile column stores its slab of L21: rows past n fall outside
-  // this buffer and are dropped
-  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-      L + (r0 * n + k0), 0, (int)((uint32_t)min<int64_t>(TB, n - r0) * n32 * 4u), 0x00020000);
-  const int cl = lane & 31, kr = lane >> 5;
-  // The solved rows go back in place.  Output register r of a 32 x 32 block
-  // is row 32w + 4kr + 8(r/4) + r%4 (column cl), so its swizzled LDS index is
-  // a lane term plus a constant: (row & 15) = 4kr | (8(r/4 % 2) + r%4).
-  auto put = [&](float* S, const f32x16 (&v)[2]) {
+    __syncthreads();
+    // L21 slabs; each wave reads and then overwrites only its own 32 rows.
+    // The first tile column stores its slab of L21: rows past n fall outside
+    // this buffer and are dropped.
+    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+        L + (r0 * n + k0), 0, (int)((uint32_t)min<int64_t>(TB, n - r0) * n32 * 4u), 0x00020000);
+    // The solved rows go back in place.  Output register r of a 32 x 32 block
+    // is row 32w + 4kr + 8(r/4) + r%4 (column cl), so its swizzled LDS index is
+    // a lane term plus a constant: (row & 15) = 4kr | (8(r/4 % 2) + r%4).
+    auto put = [&](float* S, const f32x16 (&v)[2]) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int lc = (32 * nb + cl) ^ (kr << 4);
-      float* base = S + (32 * wave + 4 * kr) * 64;
+      for (int nb = 0; nb < 2; ++nb) {
+        const int lc = (32 * nb + cl) ^ (kr << 4);
+        float* base = S + (32 * wave + 4 * kr) * 64;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rc = 8 * (r >> 2) + (r & 3);
-        base[rc * 64 + (lc ^ ((rc & 15) << 2))] = v[nb][r];
+        for (int r = 0; r < 16; ++r) {
+          const int rc = 8 * (r >> 2) + (r & 3);
+          base[rc * 64 + (lc ^ ((rc & 15) << 2))] = v[nb][r];
+        }
       }
-    }
-  };
-  f32x16 o[2];
-  if (!PRE) {
+    };
+    f32x16 o[2];
     panel_solve(sR, sD, wave, lane, o);
     put(sR, o);
     if (tn == 0) {  // row 32w + 4kr + rc of the slab: a lane term plus a uniform multiple of n
@@ -549,72 +667,29 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
       panel_solve(sC, sD, wave, lane, o);
       put(sC, o);
     }
+    load_c();  // fetched only now, so that it is not live during the panel solves
+    __syncthreads();
+    if (active) rank_update();
+  } else {
+    // the next slab's loads (or, with the last slab, C's) in flight during
+    // the current slab's MFMAs: never both sets of registers live at once
+    load_slabs(k0);
+    for (int c = 0; c + 1 < nk; ++c) {
+      if (c > 0) __syncthreads();  // every wave is done with the previous slabs
+      store_slabs();
+      __syncthreads();
+      load_slabs(k0 + (int64_t)NB * (c + 1));
+      if (active) rank_update();
+    }
+    if (nk > 1) __syncthreads();
+    store_slabs();
+    __syncthreads();
+    load_c();
+    if (active) rank_update();
   }
-  // C of this wave's 64 x 64 quadrant, fetched only now (so it is not live
-  // during the panel solves) and consumed after the rank update's MFMAs
-  const bool interior = r0 + TB <= n && c0 + TB <= n;
-  f32x16 cp[2][2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) cp[mb][nb] = zero16();
-  // A buffer resource over the tile's rows inside the matrix and 32-bit lane
-  // offsets (the tile spans fewer than 128 n elements, n < 2^22).  Loads past
-  // the last row read as zero and entries past n are never stored, so edge
-  // tiles need no clamping; a store that must not happen gets an offset past
-  // the buffer and is dropped, so no store is behind a branch.
-  const uint32_t lr0 = (uint32_t)(64 * wr + 4 * (lane >> 5)), lc0 = (uint32_t)(64 * wc + (lane & 31));
-  const uint32_t rlim = (uint32_t)(min<int64_t>(TB, n - r0) - 1), clim = (uint32_t)(min<int64_t>(TB, n - c0) - 1);
-  const __amdgpu_buffer_rsrc_t trs =
-      __builtin_amdgcn_make_buffer_rsrc(A + (r0 * n + c0), 0, (int)((rlim + 1) * n32 * 4u), 0x00020000);
-  const uint32_t loff = (lr0 * n32 + lc0) * 4u;
-  auto coff = [&](int mb, int nb, int r) {
-    return loff + ((uint32_t)(32 * mb + 8 * (r >> 2) + (r & 3)) * n32 + (uint32_t)(32 * nb)) * 4u;
-  };
-  if (active) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          cp[mb][nb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(trs, coff(mb, nb, r), 0, 0));
-  }
-  __syncthreads();
   if (!active) return;
 
-  const float* sB = dg ? sR : sC;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
-  // the operands of steps 4g+4.. read while the MFMAs of steps 4g.. run
-  f32x4 a0[2], a1[2], b0[2], b1[2];
-  auto ld = [&](int g, int b) {
-    const int k = kgroup(g, kr);
-    a0[b] = *(const f32x4*)&sR[pidx(64 * wr + cl, k)];
-    a1[b] = *(const f32x4*)&sR[pidx(64 * wr + 32 + cl, k)];
-    b0[b] = *(const f32x4*)&sB[pidx(64 * wc + cl, k)];
-    b1[b] = *(const f32x4*)&sB[pidx(64 * wc + 32 + cl, k)];
-  };
-  ld(0, 0);
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int b = g & 1;
-    if (g + 1 < 8) ld(g + 1, b ^ 1);
-    __builtin_amdgcn_sched_barrier(0);  // keeps the reads ahead of this group's MFMAs
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[0][0] = mfma_f32(a0[b][q], b0[b][q], acc[0][0]);
-      acc[0][1] = mfma_f32(a0[b][q], b1[b][q], acc[0][1]);
-      acc[1][0] = mfma_f32(a1[b][q], b0[b][q], acc[1][0]);
-      acc[1][1] = mfma_f32(a1[b][q], b1[b][q], acc[1][1]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // lower part only; the next diagonal block is left to workgroup 0, which
-  // reads it before the update
+  // lower part only
   if (interior && !dg) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -633,42 +708,24 @@ __device__ __forceinline__ void tile_update(float* __restrict__ A, float* __rest
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const uint32_t lr = lr0 + (uint32_t)(32 * mb + 8 * (r >> 2) + (r & 3)), lc = lc0 + (uint32_t)(32 * nb);
-        // inside the matrix, and on or below the diagonal of a diagonal tile
-        // (there r0 = c0, and tile 0's first quadrant is inactive)
+        // inside the matrix and the region, and on or below the diagonal of
+        // a diagonal tile (there r0 = c0)
         const bool st = lr <= rlim && lc <= clim && (!dg || lc <= lr);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, cp[mb][nb][r] - acc[mb][nb][r]), trs,
                                               st ? coff(mb, nb, r) : 0x80000000u, 0, 0);
       }
 }
 
-// Block column k at k0 (n - k0 > NB): workgroup 0 factors diagonal block
-// k + 1, workgroups 1.. update the lower tiles of the trailing matrix.
-template <bool VEC, bool PRE>
-__global__ __launch_bounds__(256, 2) void chol_step_kernel(float* A, float* L, float* dinv, int64_t n, int64_t k0,
-                                                           int32_t* info) {
-  if (*info != 0) return;
-  __shared__ __attribute__((aligned(16))) float smem[SMEM];
-  const int64_t kbk = k0 / NB;
-  if (blockIdx.x == 0)
-    leaf_block(A, n, k0 + NB, k0, dinv + kbk * NB * NB, dinv + (kbk + 1) * NB * NB, info, smem);
-  else
-    tile_update<VEC, PRE>(A, L, dinv + kbk * NB * NB, n, k0, (int)blockIdx.x - 1, smem);
-}
-
-// Every 128-row slab of block column k of the factor, L21 = A21 Dinv_k^T
-// (the solve each tile would otherwise repeat for its two slabs), written to
-// L; one workgroup per slab.  Used when the trailing matrix has more tiles
-// than the GPU runs at once, so the tiles of the step only load their slabs.
+// Rows [r0, r0 + 128) of the block column at k0 of the factor,
+// L21 = A21 Dinv_k^T, written to L (rows past n dropped).
 template <bool VEC>
-__global__ __launch_bounds__(256) void panel_solve_kernel(const float* A, float* L, const float* dinv, int64_t n,
-                                                          int64_t k0, const int32_t* info) {
-  if (*info != 0) return;
-  __shared__ __attribute__((aligned(16))) float sD[64 * 64];
-  __shared__ __attribute__((aligned(16))) float sR[128 * 64];
+__device__ __forceinline__ void solve_slab(const float* __restrict__ A, float* __restrict__ L,
+                                           const float* __restrict__ dinv_k, int64_t n, int64_t k0, int64_t r0,
+                                           float* smem) {
+  float* sD = smem;          // 64 x 64
+  float* sR = sD + 64 * 64;  // 128 x 64
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t r0 = k0 + NB + (int64_t)blockIdx.x * TB;
-  const float* dinv_k = dinv + (k0 / NB) * NB * NB;
   {
     f32x4 pr[8], dv[4];
 #pragma unroll
@@ -695,7 +752,6 @@ __global__ __launch_bounds__(256) void panel_solve_kernel(const float* A, float*
   __syncthreads();
   f32x16 o[2];
   panel_solve(sR, sD, wave, lane, o);
-  // rows past n fall outside this buffer and are dropped
   const uint32_t n32 = (uint32_t)n;
   const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
       L + (r0 * n + k0), 0, (int)((uint32_t)min<int64_t>(TB, n - r0) * n32 * 4u), 0x00020000);
@@ -709,6 +765,65 @@ __global__ __launch_bounds__(256) void panel_solve_kernel(const float* A, float*
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), lrs,
                                             (lb + (uint32_t)(8 * (r >> 2) + (r & 3)) * n32 + 32u * nb) * 4u, 0, 0);
     }
+}
+
+// One launch of the blocked Cholesky, three kinds of workgroup:
+//  - workgroup 0 factors the diagonal block at leaf_j0 (leaf_mode 1: after
+//    the update from the block column at leaf_kp, from A and that block's
+//    inverse; 2: after the update from leaf_nk block columns of L starting at
+//    column leaf_kp; 0: no leaf in this launch);
+//  - nstrip workgroups update the tiles of [sk0 + 64, n) x [sk0 + 64, send)
+//    (the rest of a panel's columns) from the block column at sk0, solving it
+//    on the fly and storing it to L; or, with no strip, nsolve workgroups
+//    solve and store that block column's 128-row slabs;
+//  - the rest update tiles [lt0, lt1) of the lower tile list of
+//    [lR0, n) x [lR0, lcend) from lnk block columns of L starting at lk0
+//    (lskip00: not the diagonal block at lR0, which workgroup 0 updates).
+struct StepArgs {
+  float* A;
+  float* L;
+  float* dinv;
+  int32_t* info;
+  int64_t n;
+  int64_t leaf_j0, leaf_kp;
+  int leaf_mode, leaf_nk;
+  int64_t sk0, send;
+  int s_nr, nstrip, nsolve;
+  int64_t lk0, lR0, lcend;
+  int lnk, l_nr, lt0, lt1, lskip00;
+};
+
+template <bool VEC>
+__global__ __launch_bounds__(256, 2) void chol_step_kernel(StepArgs a) {
+  if (*a.info != 0) return;
+  __shared__ __attribute__((aligned(16))) float smem[SMEM];
+  int b = (int)blockIdx.x;
+  if (b == 0) {
+    if (a.leaf_mode == 1)
+      leaf_block(a.A, a.n, a.leaf_j0, a.leaf_kp, a.dinv + (a.leaf_kp / NB) * NB * NB,
+                 a.dinv + (a.leaf_j0 / NB) * NB * NB, a.info, smem);
+    else if (a.leaf_mode == 2)
+      leaf_block(a.A, a.n, a.leaf_j0, -1, nullptr, a.dinv + (a.leaf_j0 / NB) * NB * NB, a.info, smem, a.L,
+                 a.leaf_kp, a.leaf_nk);
+    return;
+  }
+  b -= 1;
+  const float* dk = a.dinv + (a.sk0 / NB) * NB * NB;
+  if (b < a.nstrip) {
+    int tm, tn;
+    region_tile(b, a.s_nr, tm, tn);
+    tile_update<VEC, true>(a.A, a.L, dk, a.n, a.sk0, 1, a.sk0 + NB, a.send, tm, tn, true, smem);
+    return;
+  }
+  b -= a.nstrip;
+  if (b < a.nsolve) {
+    solve_slab<VEC>(a.A, a.L, dk, a.n, a.sk0, a.sk0 + NB + (int64_t)TB * b, smem);
+    return;
+  }
+  b -= a.nsolve;
+  int tm, tn;
+  region_tile(a.lt0 + b, a.l_nr, tm, tn);
+  tile_update<VEC, false>(a.A, a.L, nullptr, a.n, a.lk0, a.lnk, a.lR0, a.lcend, tm, tn, a.lskip00 != 0, smem);
 }
 
 // Zero the strict upper triangle and put the NB-block inverses on the diagonal.
@@ -813,29 +928,73 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // blocked right-looking Cholesky of A (lower): the factor's off-diagonal
-  // blocks go to L, the inverses of its diagonal blocks to dinv
+  // Blocked Cholesky of A (lower), two levels while the trailing matrix is
+  // large: panels of PB block columns of NB.  Inside a panel, block column k
+  // is applied (right-looking) only to the panel's later columns while
+  // workgroup 0 factors block k + 1; at the panel's end one rank-PB*NB update
+  // reads the panel back from L.  Its part on the next panel's columns runs
+  // in the launch that factors the next panel's first block; the rest of it
+  // is dealt out over the next panel's launches, where it fills the CUs the
+  // serial diagonal blocks leave idle (it touches neither that panel's
+  // columns nor its diagonal blocks).  So the trailing matrix moves through
+  // memory once per PB*NB columns instead of once per NB.  Once fewer than
+  // TWO_LEVEL_MIN columns would remain after a panel, the last panel runs to
+  // the end: one launch per block column updating the whole trailing matrix,
+  // where a launch is bound by the diagonal block's factorization rather
+  // than by memory and a rank-256 tile (at least 14 us of MFMA on one CU)
+  // would only lengthen it.  The factor's off-diagonal blocks go to L, the
+  // inverses of its diagonal blocks to dinv.
   hipLaunchKernelGGL(chol_first_kernel, dim3(1), dim3(256), 0, s, (const float*)w.A, n, w.dinv, info);
-  const bool vec = n % 4 == 0;
-  for (int64_t k0 = 0; k0 + NB < n; k0 += NB) {
-    const int64_t nt = cdiv(n - k0 - NB, TB);
-    const unsigned grid = (unsigned)(1 + nt * (nt + 1) / 2);
-    // more tiles than CUs: solve the slabs once (PRE), else in the tiles
-    if (grid - 1 > PRE_TILES) {
-      if (vec) {
-        hipLaunchKernelGGL((panel_solve_kernel<true>), dim3((unsigned)nt), dim3(256), 0, s, (const float*)w.A, w.L,
-                           (const float*)w.dinv, n, k0, (const int32_t*)info);
-        hipLaunchKernelGGL((chol_step_kernel<true, true>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
-      } else {
-        hipLaunchKernelGGL((panel_solve_kernel<false>), dim3((unsigned)nt), dim3(256), 0, s, (const float*)w.A, w.L,
-                           (const float*)w.dinv, n, k0, (const int32_t*)info);
-        hipLaunchKernelGGL((chol_step_kernel<false, true>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0,
-                           info);
+  {
+    const int64_t nb = cdiv(n, NB);
+    const bool vec = n % 4 == 0;
+    auto lower_tiles = [](int64_t nr, int64_t nc) { return nc * nr - nc * (nc - 1) / 2; };  // nc <= nr
+    auto panel_end = [&](int64_t b0) {
+      const int64_t b1 = std::min(b0 + PB, nb);
+      return n - b1 * NB < TWO_LEVEL_MIN ? nb : b1;
+    };
+    auto launch = [&](const StepArgs& a, int64_t grid) {
+      if (vec) hipLaunchKernelGGL((chol_step_kernel<true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((chol_step_kernel<false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    };
+    StepArgs base{};
+    base.A = w.A; base.L = w.L; base.dinv = w.dinv; base.info = info; base.n = n;
+    int64_t far_R0 = 0, far_k0 = 0, far_tiles = 0;  // the previous panel's update past this panel
+    for (int64_t b0 = 0; b0 < nb;) {
+      const int64_t b1 = panel_end(b0), np = b1 - b0;
+      for (int64_t k = b0; k < b1 && k + 1 < nb; ++k) {
+        StepArgs a = base;
+        a.sk0 = k * NB;
+        if (k + 1 < b1) {
+          a.leaf_mode = 1; a.leaf_j0 = (k + 1) * NB; a.leaf_kp = k * NB;
+          a.send = std::min(b1 * NB, n);
+          const int64_t nr = cdiv(n - (k + 1) * NB, TB), nc = cdiv(a.send - (k + 1) * NB, TB);
+          a.s_nr = (int)nr; a.nstrip = (int)lower_tiles(nr, nc);
+        } else {
+          a.nsolve = (int)cdiv(n - (k + 1) * NB, TB);
+        }
+        if (far_tiles > 0) {
+          a.lk0 = far_k0; a.lnk = PB; a.lR0 = far_R0; a.lcend = n; a.l_nr = (int)cdiv(n - far_R0, TB);
+          a.lt0 = (int)(far_tiles * (k - b0) / np); a.lt1 = (int)(far_tiles * (k - b0 + 1) / np);
+        }
+        launch(a, 1 + (int64_t)a.nstrip + a.nsolve + (a.lt1 - a.lt0));
       }
-    } else if (vec) {
-      hipLaunchKernelGGL((chol_step_kernel<true, false>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
-    } else {
-      hipLaunchKernelGGL((chol_step_kernel<false, false>), dim3(grid), dim3(256), 0, s, w.A, w.L, w.dinv, n, k0, info);
+      far_tiles = 0;
+      if (b1 < nb) {  // the panel's update: block b1 factored, the next panel's columns updated
+        const int64_t nb1 = panel_end(b1);
+        StepArgs a = base;
+        a.leaf_mode = 2; a.leaf_j0 = b1 * NB; a.leaf_kp = b0 * NB; a.leaf_nk = (int)np;
+        a.lk0 = b0 * NB; a.lnk = (int)np; a.lR0 = b1 * NB; a.lcend = std::min(nb1 * NB, n); a.lskip00 = 1;
+        const int64_t nr = cdiv(n - a.lR0, TB), nc = cdiv(a.lcend - a.lR0, TB);
+        a.l_nr = (int)nr; a.lt0 = 0; a.lt1 = (int)lower_tiles(nr, nc);
+        launch(a, 1 + (int64_t)a.lt1);
+        if (nb1 < nb) {
+          far_R0 = nb1 * NB; far_k0 = b0 * NB;
+          const int64_t nt = cdiv(n - far_R0, TB);
+          far_tiles = lower_tiles(nt, nt);
+        }
+      }
+      b0 = b1;
     }
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -79,7 +79,7 @@ def _h_case(n, T, seed):
     return O.hessian([X.astype(np.float64)]).astype(np.float32)
 
 
-@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129, 200, 513, 1024, 3000, 4100])
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129, 200, 513, 1024, 3000, 4100, 4417, 6000])
 def test_prepare_parity(n):
     say(f"[prepare] n={n}")
     H32 = _h_case(n, max(2 * n, 64), seed=1000 + n)
