@@ -726,6 +726,16 @@ def bench_layer(args):
                                             "zero_f32")})
     except Exception as exc:  # noqa: BLE001 - the split is reported as missing, the rest stands
         print(f"# quantize-phase split unavailable: {exc}", file=sys.stderr, flush=True)
+    if split:
+        # the kernel durations of one quantize step must add up to about the
+        # event-timed phase; under an outside profiler torch's own can attribute
+        # them wrongly, and then no split is reported
+        q_med = float(np.median(phase["quantize"]))
+        tot = sum(split.values())
+        if not 0.6 * q_med <= tot <= 1.3 * q_med:
+            print(f"# quantize-phase split dropped: kernels sum to {tot:.3f} ms against a {q_med:.3f} ms phase",
+                  file=sys.stderr, flush=True)
+            split = None
 
     syrk_flop = float(n) * (n + 1) * T
     prep_flop = 4.0 * n ** 3 / 3
