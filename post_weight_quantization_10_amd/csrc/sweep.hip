@@ -247,8 +247,11 @@ __device__ __forceinline__ void pending_update(const SweepArgs& a, int64_t r0, f
 // last step from the registers, which keep each column's value from its own
 // step on (the factor row of a later step is zero there); groups narrower than
 // the lanes of a row, and runtime group sizes, capture them at their step.
+// Three workgroups per CU for the look-ahead kernel (at most 168 VGPRs, which
+// its pending update's operands otherwise just exceed); the narrow-group
+// variants hold several groups' state and would spill, so they keep one.
 template <int LPR, int GMODE, bool LOOK>
-__global__ __launch_bounds__(256) void sweep_block_kernel(SweepArgs a) {
+__global__ __launch_bounds__(256, (LOOK && (GMODE <= 0 || GMODE >= 64)) ? 3 : 1) void sweep_block_kernel(SweepArgs a) {
   using LY = BlockLayout<LPR>;
   constexpr int NSTEP = LY::NSTEP;
   constexpr int ROWS = 256 / LPR;
