@@ -576,8 +576,9 @@ def trailing_schedule(m: int, n: int, B: int, group: int):
     runs it: (flops in the GEMM kernels, flops applied inside the sweep
     kernel).  With B a multiple of 64 and groups no wider than a block the
     blocks go in pairs: the second block of a pair takes the first one's
-    errors on its own columns inside the sweep, then one GEMM with K = 2B
-    updates the columns after the pair."""
+    errors on its own columns inside the sweep, then GEMMs update the columns
+    after the pair (those of its 1024-column superblock at once, the rest
+    after the superblock with K = 1024; the same flops either way)."""
     look = B % 64 == 0 and (group <= 0 or group <= B) and n % 4 == 0
     gemm = in_sweep = 0.0
     if look:

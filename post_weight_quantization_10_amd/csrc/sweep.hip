@@ -30,7 +30,8 @@ namespace {
 
 constexpr int BMAX = 128;  // widest block
 constexpr int LA = 2;          // blocks per lazy flush on the look-ahead path
-constexpr int ELD = LA * BMAX;  // leading dimension of the E buffer: the errors of LA consecutive blocks
+constexpr int SBW = 8 * BMAX;  // columns per superblock of the look-ahead path's two-level flush
+constexpr int ELD = SBW;       // leading dimension of the E buffer: the errors of one superblock
 
 // Layout of a block's factor rows for the sweep kernel.  Lane lr (of the LPR
 // lanes that share a weight row) holds the block columns c = lr + LPR j,
@@ -712,25 +713,25 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   if (e != hipSuccess) return e;
 
   // sweep one block [i, i + w) with its errors written at column eoff of E;
-  // on the look-ahead path the kpend columns before it (from column g0) are
-  // still to be applied to it
-  auto sweep_block = [&](int64_t i, int w, int eoff, bool look, int64_t g0) -> hipError_t {
+  // on the look-ahead path the kpend columns before it (from column g0, their
+  // errors at column epair of E) are still to be applied to it
+  auto sweep_block = [&](int64_t i, int w, int eoff, bool look, int64_t g0, int epair) -> hipError_t {
     if (group > B && i % group == 0)
       hipLaunchKernelGGL(row_params_kernel, dim3(prow), dim3(256), 0, st, (const float*)V, m, n, i, group, maxq, S,
                          Z, G, i / group);
     SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, packed ? nullptr : Q8, packed ? qcodes : nullptr, words,
                 bits, write_dequant ? W : nullptr, dt, ldw, E + eoff, err_sq, Dblk + (i / B) * dstride,
-                E, (int)(i - g0), U + g0 * n + i};
+                E + epair, (int)(i - g0), U + g0 * n + i};
     if (B <= 32) launch_sweep<4, false>(a, gmode, st);
     else if (look) launch_sweep<16, true>(a, gmode, st);
     else launch_sweep<16, false>(a, gmode, st);
     return hipGetLastError();
   };
-  // V[:, c0:c0+N] -= E[:, 0:K] U[r0:r0+K, c0:c0+N]
-  auto flush = [&](int64_t r0, int K, int64_t c0, int64_t N) -> hipError_t {
+  // V[:, c0:c0+N] -= E[:, ec:ec+K] U[r0:r0+K, c0:c0+N]
+  auto flush = [&](int ec, int64_t r0, int K, int64_t c0, int64_t N) -> hipError_t {
     if (N <= 0) return hipSuccess;
     GemmDesc g{};
-    g.A = E; g.lda = ELD;
+    g.A = E + ec; g.lda = ELD;
     g.B = U + r0 * n + c0; g.ldb = n;
     g.C = V + c0; g.ldc = n;
     g.M = (int)m; g.N = (int)N; g.K = K; g.batch = 1;
@@ -743,24 +744,32 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
     // Look-ahead: LA blocks per flush.  Block t of a group first takes the
     // errors of blocks 0..t-1 of its group (inside the sweep kernel, K = t B,
     // on MFMA), then is swept; after the group, one GEMM with K = LA B brings
-    // the rest of the row up to date: a quarter of the passes over V and long
-    // K per GEMM tile.  (Groups wider than a block would need V updated past
-    // the block before their scales are taken, so they stay on the path below.)
-    for (int64_t g0 = 0; g0 < n;) {
-      int64_t i = g0;
-      for (int t = 0; t < LA && i < n; ++t) {
-        const int w = (int)std::min<int64_t>(B, n - i);
-        if ((e = sweep_block(i, w, (int)(i - g0), true, g0)) != hipSuccess) return e;
-        i += w;
+    // the rest of its superblock (SBW columns) up to date, and after the
+    // superblock one GEMM with K = SBW the rest of the row: a quarter of the
+    // passes over V of flushing every group to the end, and long K for most
+    // of the flops.  Every column still gets each earlier column's error once
+    // before it is swept.  (Groups wider than a block would need V updated
+    // past the block before their scales are taken, so they stay on the path
+    // below.)
+    for (int64_t s0 = 0; s0 < n; s0 += SBW) {
+      const int64_t s1 = std::min<int64_t>(s0 + SBW, n);  // SBW is a multiple of B: no block straddles
+      for (int64_t g0 = s0; g0 < s1;) {
+        int64_t i = g0;
+        for (int t = 0; t < LA && i < s1; ++t) {
+          const int w = (int)std::min<int64_t>(B, s1 - i);
+          if ((e = sweep_block(i, w, (int)(i - s0), true, g0, (int)(g0 - s0))) != hipSuccess) return e;
+          i += w;
+        }
+        if ((e = flush((int)(g0 - s0), g0, (int)(i - g0), i, s1 - i)) != hipSuccess) return e;
+        g0 = i;
       }
-      if ((e = flush(g0, (int)(i - g0), i, n - i)) != hipSuccess) return e;
-      g0 = i;
+      if ((e = flush(0, s0, (int)(s1 - s0), s1, n - s1)) != hipSuccess) return e;
     }
   } else {
     for (int64_t i = 0; i < n; i += B) {
       const int w = (int)std::min<int64_t>(B, n - i);
-      if ((e = sweep_block(i, w, 0, false, i)) != hipSuccess) return e;
-      if ((e = flush(i, w, i + w, n - i - w)) != hipSuccess) return e;
+      if ((e = sweep_block(i, w, 0, false, i, 0)) != hipSuccess) return e;
+      if ((e = flush(0, i, w, i + w, n - i - w)) != hipSuccess) return e;
     }
   }
   if (!packed)

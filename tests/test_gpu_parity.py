@@ -148,6 +148,8 @@ SWEEP_CASES = [
     (24, 500, 3, 0, 96, "f32"),       # 96-column blocks, 3-bit codes packed inside the sweep
     (40, 384, 4, 8, 128, "f16"),      # groups narrower than a row's lanes: captured at their step
     (36, 640, 5, 32, 128, "bf16"),    # four groups per block, 5-bit codes straddling words
+    (70, 1400, 4, 64, 64, "f16"),     # look-ahead path over a full and a partial 1024-column superblock
+    (40, 2600, 3, 0, 128, "f32"),     # three superblocks, the last one ragged (a 40-column block)
 ]
 
 
