@@ -81,9 +81,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="attn", choices=sorted(LAYERS))
-    ap.add_argument("--kernel", default="layer", choices=["layer", "w4a16", "rotate", "stack", "peaks", "obq"],
+    ap.add_argument("--kernel", default="layer",
+                    choices=["layer", "w4a16", "rotate", "stack", "tstack", "peaks", "obq"],
                     help="layer: the quantization path (default); w4a16: the packed layer at run time; "
-                         "rotate: the Hadamard rotation before GPTQ; peaks: measured attainable MFMA and HBM rates")
+                         "rotate: the Hadamard rotation before GPTQ; stack / tstack: the network-level loop over "
+                         "MLP / transformer blocks; peaks: measured attainable MFMA and HBM rates")
     ap.add_argument("--bits", type=int, default=4, choices=[3, 4], help="code width for --kernel w4a16")
     ap.add_argument("--obq-n", type=int, default=256, help="row length for --kernel obq (m = 4096 rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -483,6 +485,101 @@ def bench_stack(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_tstack(args):
+    """quantize_transformer_stack over 2 transformer blocks of a 7B shape
+    (d 4096, f 11008, 32 heads of 128, no normalisation; weights N(0, 1/fan-in)
+    with 0.1 % x10 outliers, fp16), 8192 calibration tokens of the
+    attention-projection recipe in sequences of 2048; a step is the whole loop.
+    Phase times of one block from HIP events between the same calls the loop
+    makes: hessian (four), prepare (four), sweeps (q/k/v stacked, o, gate/up
+    stacked, down), attention, the rest of the forward (the quantized
+    products, SwiGLU, the residuals)."""
+    import torch
+
+    import post_weight_quantization_10_amd as pw
+    import synth
+    d, f, heads, seq, T, L, bits, group, B = 4096, 11008, 32, 2048, 8192, 2, 4, 128, 128
+    dev = torch.device("cuda:0")
+    blocks = []
+    # weights of std 1/sqrt(fan-in): with no normalisation between blocks,
+    # 0.02 (the single-layer recipe) grows the residual stream ~50x a block
+    # and overflows fp16 in the second block's SwiGLU
+    for l in range(L):
+        shapes = [(d, d)] * 4 + [(f, d), (f, d), (d, f)]
+        ws = [synth.small_layer(r, c, 16, seed=400 + 7 * l + k, w_dtype="f16", sigma=c ** -0.5,
+                                outlier_frac=0.001)[0]
+              for k, (r, c) in enumerate(shapes)]
+        blocks.append(tuple(torch.from_numpy(w).to(dev) for w in ws))
+    X0 = torch.from_numpy(synth.activations(T, d, "f16", seed=401)).to(dev)
+    for _ in range(max(args.warmup, 1)):
+        pw.quantize_transformer_stack(blocks, X0, seq, heads, bits, group, B, 0.01)
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pw.quantize_transformer_stack(blocks, X0, seq, heads, bits, group, B, 0.01)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    # one block by hand, HIP events between the calls the loop makes
+    Wq, Wk, Wv, Wo, Wg, Wu, Wd = blocks[0]
+    acc = {"hessian": 0.0, "prepare": 0.0, "sweeps": 0.0, "attention": 0.0, "forward": 0.0}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(key, fn):
+        ev[0].record()
+        r = fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        acc[key] += ev[0].elapsed_time(ev[1])
+        return r
+
+    def factor(Xa):
+        n = Xa.shape[1]
+        H = torch.zeros((n, n), dtype=torch.float32, device=dev)
+        timed("hessian", lambda: pw.hessian_accumulate(H, Xa))
+        return timed("prepare", lambda: pw.prepare_hinv(H, 0.01))[0]
+
+    def product(Xa, r):
+        return pw.dequant_matmul(Xa, r["qcodes"], r["scales"], r["zeros"], bits, group)
+
+    X = X0.clone()
+    U1 = factor(X)
+    Wqkv = torch.cat([Wq, Wk, Wv], dim=0)
+    rqkv = timed("sweeps", lambda: pw.quantize_layer(Wqkv, U1, bits, group, B, write_dequant=False))
+    qkv = timed("forward", lambda: product(X, rqkv))
+    A = timed("attention", lambda: pw.attention(qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:], seq, heads))
+    U2 = factor(A)
+    ro = timed("sweeps", lambda: pw.quantize_layer(Wo.clone(), U2, bits, group, B, write_dequant=False))
+    timed("forward", lambda: pw.residual_add(X, product(A, ro)))
+    U3 = factor(X)
+    Wgu = torch.cat([Wg, Wu], dim=0)
+    rgu = timed("sweeps", lambda: pw.quantize_layer(Wgu, U3, bits, group, B, write_dequant=False))
+    A2 = timed("forward", lambda: (lambda GU: pw.swiglu(GU[:, :f], GU[:, f:]))(product(X, rgu)))
+    U4 = factor(A2)
+    rd = timed("sweeps", lambda: pw.quantize_layer(Wd.clone(), U4, bits, group, B, write_dequant=False))
+    timed("forward", lambda: pw.residual_add(X, product(A2, rd)))
+    att_flops = 4.0 * d * T * (seq + 1) / 2  # QK and PV, causal: (seq + 1) / 2 keys per query on average
+    att_ms = acc["attention"]
+    res = {
+        "metric": "ms per 7B-shaped transformer block of the network-level loop (d 4096, f 11008, 32 heads, "
+                  "8192 tokens in sequences of 2048, 4-bit g128)",
+        "value": round(ms / L, 3), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 MFMA (H, products) / fp32", "data": "synthetic",
+        "config": {"workload": f"{L} transformer blocks d {d} f {f} heads {heads}, X0 {T}x{d} fp16 "
+                               f"(sequences of {seq}), {bits}-bit g{group} B{B}",
+                   "tokens": T, "d": d, "f": f, "heads": heads, "seq_len": seq, "blocks": L,
+                   "parallelism": "single GPU"},
+        "phases_ms_one_block": {k: round(v, 3) for k, v in acc.items()},
+        "roofline": {"kernel": "gptq_attention (attention_kernel: causal softmax attention, fp32 VALU)",
+                     "bound": "alu", "achieved": round(att_flops / (att_ms * 1e-3) / 1e12, 2), "peak": PEAK_TF32,
+                     "unit": "TFLOP/s", "frac": round(att_flops / (att_ms * 1e-3) / 1e12 / PEAK_TF32, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_peaks(args):
     """Attainable peaks, each the best of a few timed launches on the current
     stream (HIP events): MFMA streams of 1024 workgroups x 4 waves, eight
@@ -564,6 +661,9 @@ def main():
         return
     if args.kernel == "stack":
         bench_stack(args)
+        return
+    if args.kernel == "tstack":
+        bench_tstack(args)
         return
     if args.kernel == "obq":
         bench_obq(args)

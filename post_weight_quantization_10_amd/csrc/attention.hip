@@ -9,16 +9,22 @@
 //   p_ij = softmax_j (Q[i, h] . K[j, h] / sqrt(dh))
 //
 // for every head h (columns h dh .. h dh + dh - 1 of the activations).  fp32
-// throughout, one rounding of O to the activations' dtype.
+// accuracy throughout, one rounding of O to the activations' dtype.
 //
-// One wave per 64 (64-dim heads) or 32 (128-dim heads) consecutive queries of
-// one head (a query block never straddles a sequence: the sequence length is a
-// multiple of 64); a lane owns 64 dims of one query's scaled query and output
-// rows in registers (16-byte loads and stores: 16-byte aligned rows).  Keys and
-// values stream through LDS in tiles of 32 (fp32); per tile every lane takes
-// its 32 scores (masked past its own position), rescales its output once by
-// e^(m_old - m_new) with the tile's running maximum (the online softmax), and
-// adds p V.  VALU-bound: 2 dh FMAs per (query, key) pair.
+// On the matrix cores: a workgroup takes 64 consecutive queries of one head
+// (a query block never straddles a sequence: the sequence length is a multiple
+// of 64) and walks the sequence's keys in tiles of 64 up to its diagonal.
+// Wave (wq, wk) owns queries 32 wq .. and keys 32 wk .. of each tile:
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_{f16,bf16}: 16-bit inputs, so every
+//     product is exact and the sums are fp32; a lane holds one query's scores
+//     for 16 keys (its query's Q operand stays in registers for all tiles);
+//   * online softmax in fp32: the tile's maximum per query over both key
+//     halves through LDS, the output rescaled once per tile;
+//   * O += P V with v_mfma_f32_32x32x2f32 (fp32 probabilities, V converted
+//     exactly from 16 bits, staged per tile in LDS as fp32): the MFMA step
+//     that lane half h feeds key 8 (s / 4) + 4 h + s % 4 takes the lane's own
+//     probability register s, so P never moves between lanes.
+// The two key halves' outputs and sums meet in LDS at the end.
 #include <cmath>
 
 #include "common.hpp"
@@ -28,9 +34,6 @@ namespace gptq {
 
 namespace {
 
-constexpr int AQ = 64;  // queries per workgroup (one wave)
-constexpr int AK = 32;  // keys per LDS tile
-
 struct AttnArgs {
   const void* Q;
   const void* K;
@@ -39,7 +42,7 @@ struct AttnArgs {
   int64_t T, S, heads, ld;
 };
 
-// 8 16-bit values (one 16-byte word) <-> floats
+// 8 16-bit values (one 16-byte word) -> floats
 template <int DT>
 __device__ __forceinline__ void h8_to_f(u32x4 v, float* f) {
 #pragma unroll
@@ -54,142 +57,163 @@ __device__ __forceinline__ void h8_to_f(u32x4 v, float* f) {
     }
   }
 }
+
 template <int DT>
-__device__ __forceinline__ u32x4 f_to_h8(const float* f) {
-  u32x4 v;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint16_t lo, hi;
-    if (DT == 0) {
-      lo = __builtin_bit_cast(uint16_t, (_Float16)f[2 * e]);
-      hi = __builtin_bit_cast(uint16_t, (_Float16)f[2 * e + 1]);
-    } else {
-      lo = f32_to_bf16(f[2 * e]);
-      hi = f32_to_bf16(f[2 * e + 1]);
-    }
-    v[e] = (uint32_t)lo | ((uint32_t)hi << 16);
-  }
-  return v;
+__device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, const f32x16& c) {
+  if constexpr (DT == 0)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
 }
 
-// LQ = DH / 64 adjacent lanes per query (a 128-dim head is split over two
-// lanes, 64 dims each, their partial scores added with one DPP swap), so a
-// lane holds 64 query and 64 output values; a wave takes 64 / LQ queries.
 template <int DT, int DH>
-__global__ __launch_bounds__(AQ) void attention_kernel(AttnArgs a) {
-  constexpr int LQ = DH / 64, DL = DH / LQ, QW = AQ / LQ;  // lanes per query, dims per lane, queries per wave
-  __shared__ __attribute__((aligned(16))) float ks[AK][DH];
-  __shared__ __attribute__((aligned(16))) float vs[AK][DH];
-  const int lane = threadIdx.x;
-  const int64_t q0 = (int64_t)blockIdx.x * QW;
+__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+  constexpr int NS = DH / 16;  // S^T MFMA steps over the head's dims
+  constexpr int NB = DH / 32;  // 32-dim blocks of the output
+  constexpr int VP = DH + 4;   // LDS pitch of a staged V row (floats)
+  static_assert(2 * NB * 16 * 64 <= 64 * VP, "the end's exchange fits over the V tile");
+  __shared__ __attribute__((aligned(16))) float vs[64 * VP];
+  __shared__ float mx[2][2][32];  // [wq][wk][query]: a tile's maximum of each key half
+  __shared__ float cb[4][32];     // per wave: this tile's rescale factor of each query
+  __shared__ float lb[2][32];     // [wq][query]: the second key half's sum of p
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave >> 1, wk = wave & 1;
+  const int lq = lane & 31, h = lane >> 5;
+  const int64_t q0 = (int64_t)blockIdx.x * 64;
   const int64_t hc = (int64_t)blockIdx.y * DH;  // first column of the head
-  const int64_t i = q0 + lane / LQ;
-  const int dl0 = DL * (lane % LQ);  // this lane's first dim of the head
-  const bool valid = i < a.T;
   const int64_t seq0 = (q0 / a.S) * a.S;
+  const int64_t myq = q0 + 32 * wq + lq;  // this lane's query (a column of S^T)
   const float scale = 1.f / sqrtf((float)DH);
   const uint16_t* Qp = (const uint16_t*)a.Q;
   const uint16_t* Kp = (const uint16_t*)a.K;
   const uint16_t* Vp = (const uint16_t*)a.V;
 
-  float q[DL], o[DL];
-  {
-    const int64_t ii = valid ? i : a.T - 1;
+  // B operand of S^T = K Q^T: lane l gives Q^T[dims 16 s + 8 h .. + 7][query lq]
+  u32x4 qop[NS];
 #pragma unroll
-    for (int d = 0; d < DL; d += 8) h8_to_f<DT>(*(const u32x4*)(Qp + ii * a.ld + hc + dl0 + d), q + d);
+  for (int s = 0; s < NS; ++s) qop[s] = *(const u32x4*)(Qp + myq * a.ld + hc + 16 * s + 8 * h);
+
+  f32x16 o[NB];
 #pragma unroll
-    for (int d = 0; d < DL; ++d) {
-      q[d] *= scale;
-      o[d] = 0.f;
+  for (int b = 0; b < NB; ++b) o[b] = zero16();
+  float m = -INFINITY, lsum = 0.f;  // running maximum of this lane's query; this lane's share of the sum
+  for (int64_t kb = seq0; kb <= q0; kb += 64) {
+    // A operand: lane l gives K[key kb + 32 wk + lq][dims 16 s + 8 h .. + 7]
+    u32x4 kop[NS];
+    const int64_t mykey = kb + 32 * wk + lq;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kop[s] = *(const u32x4*)(Kp + mykey * a.ld + hc + 16 * s + 8 * h);
+    // the tile of V, 16-byte words
+    constexpr int VW = 64 * DH / 8 / 256;  // words per thread
+    u32x4 vv[VW];
+#pragma unroll
+    for (int u = 0; u < VW; ++u) {
+      const int e = tid + 256 * u;
+      vv[u] = *(const u32x4*)(Vp + (kb + e / (DH / 8)) * a.ld + hc + 8 * (e % (DH / 8)));
     }
-  }
-  float m = -INFINITY, l = 0.f;
-  const int64_t kend = min<int64_t>(q0 + QW, a.T);  // keys past the block's last query are masked for all
-  for (int64_t kb = seq0; kb < kend; kb += AK) {
-    __syncthreads();  // the previous tile is consumed
-    // tile: AK keys x DH of K and of V, 16-byte words, AK * DH / 8 / AQ per lane each
+    __syncthreads();  // every wave is done with the previous tile's V and maxima
 #pragma unroll
-    for (int u = 0; u < AK * DH / 8 / AQ; ++u) {
-      const int e = lane + AQ * u;
-      const int jj = e / (DH / 8), d = 8 * (e % (DH / 8));
-      const int64_t j = min<int64_t>(kb + jj, a.T - 1);  // keys past T are masked below
+    for (int u = 0; u < VW; ++u) {
+      const int e = tid + 256 * u;
       float f[8];
-      h8_to_f<DT>(*(const u32x4*)(Kp + j * a.ld + hc + d), f);
-      *(f32x4*)&ks[jj][d] = f32x4{f[0], f[1], f[2], f[3]};
-      *(f32x4*)&ks[jj][d + 4] = f32x4{f[4], f[5], f[6], f[7]};
-      h8_to_f<DT>(*(const u32x4*)(Vp + j * a.ld + hc + d), f);
-      *(f32x4*)&vs[jj][d] = f32x4{f[0], f[1], f[2], f[3]};
-      *(f32x4*)&vs[jj][d + 4] = f32x4{f[4], f[5], f[6], f[7]};
+      h8_to_f<DT>(vv[u], f);
+      float* dst = vs + (e / (DH / 8)) * VP + 8 * (e % (DH / 8));
+      *(f32x4*)dst = f32x4{f[0], f[1], f[2], f[3]};
+      *(f32x4*)(dst + 4) = f32x4{f[4], f[5], f[6], f[7]};
     }
-    __syncthreads();
-    float s[AK];
+    // scores: st[r] = S^T[key kb + 32 wk + 8 (r / 4) + 4 h + r % 4][query myq]
+    f32x16 st = zero16();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) st = mfma_qk<DT>(kop[s], qop[s], st);
     float mt = -INFINITY;
 #pragma unroll
-    for (int jj = 0; jj < AK; ++jj) {
-      float dot = 0.f;
-#pragma unroll
-      for (int d = 0; d < DL; d += 4) {
-        const f32x4 k4 = *(const f32x4*)&ks[jj][dl0 + d];
-        dot = fmaf(q[d], k4[0], dot);
-        dot = fmaf(q[d + 1], k4[1], dot);
-        dot = fmaf(q[d + 2], k4[2], dot);
-        dot = fmaf(q[d + 3], k4[3], dot);
-      }
-      if constexpr (LQ == 2)  // the partner lane's half (lanes 2q, 2q + 1)
-        dot += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, dot), 0xB1, 0xF, 0xF, false));
-      s[jj] = (kb + jj <= i) ? dot : -INFINITY;
-      mt = fmaxf(mt, s[jj]);
+    for (int r = 0; r < 16; ++r) {
+      const int64_t key = kb + 32 * wk + 8 * (r >> 2) + 4 * h + (r & 3);
+      st[r] = key <= myq ? st[r] * scale : -INFINITY;
+      mt = fmaxf(mt, st[r]);
     }
-    // the first tile always holds a visible key (key seq0 <= i), so after it
-    // the running maximum is finite; before it c = e^-inf = 0
-    const float mn = fmaxf(m, mt);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));  // the query's other 16 keys of this key half
+    if (h == 0) mx[wq][wk][lq] = mt;
+    __syncthreads();  // V staged, both key halves' maxima published
+    // every query of the block sees key seq0 <= itself, so after the first tile
+    // the maximum is finite; before it the factor is e^-inf = 0
+    const float mn = fmaxf(m, fmaxf(mt, mx[wq][wk ^ 1][lq]));
     const float c = expf(m - mn);
     float ps = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < AK; ++jj) {
-      s[jj] = expf(s[jj] - mn);  // masked keys: e^-inf = 0
-      ps += s[jj];
+    for (int r = 0; r < 16; ++r) {
+      st[r] = expf(st[r] - mn);  // masked keys: e^-inf = 0
+      ps += st[r];
     }
-    l = fmaf(l, c, ps);
-#pragma unroll
-    for (int d = 0; d < DL; ++d) o[d] *= c;
-#pragma unroll
-    for (int jj = 0; jj < AK; ++jj) {
-#pragma unroll
-      for (int d = 0; d < DL; d += 4) {
-        const f32x4 v4 = *(const f32x4*)&vs[jj][dl0 + d];
-        o[d] = fmaf(s[jj], v4[0], o[d]);
-        o[d + 1] = fmaf(s[jj], v4[1], o[d + 1]);
-        o[d + 2] = fmaf(s[jj], v4[2], o[d + 2]);
-        o[d + 3] = fmaf(s[jj], v4[3], o[d + 3]);
-      }
-    }
+    lsum = fmaf(lsum, c, ps);
     m = mn;
-  }
-  if (!valid) return;
-  const float inv = 1.f / l;
+    // the output's registers hold queries 8 (r / 4) + 4 h + r % 4: their factors through LDS
+    if (h == 0) cb[wave][lq] = c;  // read back by this wave only, in order
 #pragma unroll
-  for (int d = 0; d < DL; ++d) o[d] *= inv;
+    for (int r = 0; r < 16; ++r) {
+      const float cr = cb[wave][8 * (r >> 2) + 4 * h + (r & 3)];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b][r] *= cr;
+    }
+    // O += P V: step s takes key 8 (s / 4) + 4 h + s % 4 of this key half from
+    // lane half h (A[query lq][h] = its probability register s) and the
+    // matching row of V (B[h][dim 32 b + lq])
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const float* vrow = vs + (32 * wk + 8 * (s >> 2) + 4 * h + (s & 3)) * VP + lq;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(st[s], vrow[32 * b], o[b], 0, 0, 0);
+    }
+  }
+
+  // the two key halves: O = (o_0 + o_1) / (l_0 + l_1), with the same running
+  // maxima on both sides
+  const float lw = lsum + __shfl_xor(lsum, 32);  // this wave's sum for query lq
+  __syncthreads();  // the last tile's V is consumed: its space takes the exchange
+  float* ox = vs + wq * (NB * 16 * 64);
+  if (wk == 1) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ox[(b * 16 + r) * 64 + lane] = o[b][r];
+    if (h == 0) lb[wq][lq] = lw;
+  }
+  __syncthreads();
+  if (wk == 1) return;
+  if (h == 0) cb[wave][lq] = lw + lb[wq][lq];  // the query's whole sum (read back by this wave)
   uint16_t* Op = (uint16_t*)a.O;
 #pragma unroll
-  for (int d = 0; d < DL; d += 8) *(u32x4*)(Op + i * a.ld + hc + dl0 + d) = f_to_h8<DT>(o + d);
+  for (int r = 0; r < 16; ++r) {
+    const int ql = 8 * (r >> 2) + 4 * h + (r & 3);
+    const float inv = 1.f / cb[wave][ql];
+    const int64_t q = q0 + 32 * wq + ql;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float v = (o[b][r] + ox[(b * 16 + r) * 64 + lane]) * inv;
+      Op[q * a.ld + hc + 32 * b + lq] = DT == 0 ? __builtin_bit_cast(uint16_t, (_Float16)v) : f32_to_bf16(v);
+    }
+  }
 }
 
 }  // namespace
 
 bool attention_supported(int64_t seq_len, int64_t head_dim) {
-  return (head_dim == 64 || head_dim == 128) && seq_len % AQ == 0;
+  return (head_dim == 64 || head_dim == 128) && seq_len % 64 == 0;
 }
 
 hipError_t attention(const void* Q, const void* K, const void* V, void* O, int dt, int64_t T, int64_t S,
                      int64_t heads, int64_t dh, int64_t ld, hipStream_t st) {
   if (T == 0) return hipSuccess;
   AttnArgs a{Q, K, V, O, T, S, heads, ld};
-  const dim3 grid((unsigned)cdiv(T, AQ / (dh / 64)), (unsigned)heads);
-  if (dt == 0 && dh == 64) hipLaunchKernelGGL((attention_kernel<0, 64>), grid, dim3(AQ), 0, st, a);
-  else if (dt == 0) hipLaunchKernelGGL((attention_kernel<0, 128>), grid, dim3(AQ), 0, st, a);
-  else if (dh == 64) hipLaunchKernelGGL((attention_kernel<1, 64>), grid, dim3(AQ), 0, st, a);
-  else hipLaunchKernelGGL((attention_kernel<1, 128>), grid, dim3(AQ), 0, st, a);
+  const dim3 grid((unsigned)(T / 64), (unsigned)heads);  // T is a multiple of S, itself a multiple of 64
+  if (dt == 0 && dh == 64) hipLaunchKernelGGL((attention_kernel<0, 64>), grid, dim3(256), 0, st, a);
+  else if (dt == 0) hipLaunchKernelGGL((attention_kernel<0, 128>), grid, dim3(256), 0, st, a);
+  else if (dh == 64) hipLaunchKernelGGL((attention_kernel<1, 64>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attention_kernel<1, 128>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
