@@ -312,7 +312,6 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
 #pragma unroll
     for (int r = 0; r < 4; ++r) sD[(16 * bi + 4 * g16 + r) * LP + 16 * bj + l16] -= acc[r];
   };
-  int badcol = -1;  // wave 0: first column whose pivot is not positive and finite (uniform)
 #pragma unroll 1
   for (int p = 0; p < NB / PW; ++p) {
     const int c0 = PW * p;
@@ -321,25 +320,30 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
       float a[PW];
 #pragma unroll
       for (int k = 0; k < PW; ++k) a[k] = sD[lane * LP + c0 + k];
-      float myrs = 0.f, mypiv = 1.f;  // lane c0 + jj keeps column jj's pivot and its 1/sqrt
+      // Per column only the pivot's readlane, its 1/sqrt and the scaling sit
+      // on the chain.  Rows above the pivot are scaled too: those entries (the
+      // upper part of the panel's own 16 x 16 block; rows of earlier panels
+      // stay exactly 0) are never read, as later panels, the substitution and
+      // the doubling products read only the strictly lower part of that block.
+      // The next column's pivot is taken from pn = a[jj+1] - l^2, which in
+      // lane c0 + jj + 1 is exactly that lane's updated a[jj+1] (there the
+      // broadcast l is its own), so no readlane of l sits on the chain.
+      float rsv[PW];
+      float piv = readlane_f(a[0], c0);
 #pragma unroll
       for (int jj = 0; jj < PW; ++jj) {
-        const int j = c0 + jj;
-        const float piv = readlane_f(a[jj], j);
         const float rs = __builtin_amdgcn_rsqf(piv);  // not finite after a failure: the rest is discarded
-        // lane j holds the pivot itself (piv rs = sqrt(piv)); rows above it get 0
-        const float l = lane >= j ? a[jj] * rs : 0.f;
-        myrs = lane == j ? rs : myrs;
-        mypiv = lane == j ? piv : mypiv;
+        rsv[jj] = rs;
+        const float l = a[jj] * rs;  // lane c0 + jj: piv rs = sqrt(piv)
         a[jj] = l;
+        if (jj + 1 < PW) piv = readlane_f(fmaf(-l, l, a[jj + 1]), c0 + jj + 1);
 #pragma unroll
         for (int k = jj + 1; k < PW; ++k) a[k] = fmaf(-l, readlane_f(l, c0 + k), a[k]);
       }
-      // the panel's first column whose pivot is not positive and finite
-      const bool inpan = lane >= c0 && lane < c0 + PW;
-      const uint64_t badm = __ballot(inpan && !(mypiv > 0.f && mypiv < INFINITY));
-      if (badcol < 0 && badm != 0) badcol = (int)__builtin_ctzll(badm);
-      if (inpan) rinv[lane] = myrs;
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < PW; k += 4) *(f32x4*)&rinv[c0 + k] = f32x4{rsv[k], rsv[k + 1], rsv[k + 2], rsv[k + 3]};
+      }
 #pragma unroll
       for (int k = 0; k < PW; ++k) sL[lane * LLP + c0 + k] = a[k];
     } else if (p > 0) {
@@ -354,9 +358,16 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
     }
     __syncthreads();
   }
-  if (wave == 0 && badcol >= 0 && lane == 0) {
-    atomicCAS(info, 0, (int32_t)(n - (j0 + badcol)));
-    *failed = 1;
+  // the first column whose pivot is not positive and finite, i.e. whose
+  // 1/sqrt is not positive and finite (0 for an infinite pivot, infinite for
+  // 0, NaN below 0); padding columns past kb have pivot 1
+  if (wave == 0) {
+    const float r = rinv[lane];
+    const uint64_t badm = __ballot(!(r > 0.f && r < INFINITY));
+    if (badm != 0 && lane == 0) {
+      atomicCAS(info, 0, (int32_t)(n - (j0 + (int)__builtin_ctzll(badm))));
+      *failed = 1;
+    }
   }
 
   // ---- inverse.  The four 16 x 16 diagonal blocks: lane = (block g16,
