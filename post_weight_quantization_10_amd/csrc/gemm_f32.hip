@@ -557,12 +557,7 @@ bool nn_dma_ok(const GemmDesc& d) {
 // most CUs idle.
 bool small_tiles_pay(const GemmDesc& d, int tM, int tN, int sM, int sN) {
   if (d.flags & (GEMM_A_LOWER | GEMM_B_LOWER)) return false;
-  static const int64_t slots = [] {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    return (int64_t)2 * cus;
-  }();
+  const int64_t slots = (int64_t)2 * device_cus();
   const int64_t r128 = cdiv((int64_t)tM * tN * d.batch, slots), r64 = cdiv((int64_t)sM * sN * d.batch, slots);
   return 20 * r64 < 17 * 4 * r128;
 }
@@ -576,6 +571,16 @@ void launch(const GemmDesc& d, dim3 grid, hipStream_t s) {
 }
 
 }  // namespace
+
+int device_cus() {
+  static const int cus = [] {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    return c;
+  }();
+  return cus;
+}
 
 hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0 || d.batch <= 0) return hipSuccess;

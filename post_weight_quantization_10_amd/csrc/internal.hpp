@@ -44,4 +44,7 @@ struct GemmDesc {
 // then reads all of its A rows before writing them).
 hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s);
 
+// Compute units of the current device (256 if the query fails), read once.
+int device_cus();
+
 }  // namespace gptq

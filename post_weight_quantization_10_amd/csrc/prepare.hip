@@ -141,7 +141,7 @@ __device__ __forceinline__ void leaf_block(const float* __restrict__ A, int64_t 
   float* sD = smem;              // 64 x LP
   float* sP = sD + 64 * LP;      // 64 x PP
   float* sQ = sP + 64 * PP;      // 64 x PP
-  float* sL = sQ + 64 * PP;      // 64 x LLP: the factor, zero above the diagonal
+  float* sL = sQ + 64 * PP;      // 64 x LLP: the factor (above the diagonal only zeros and unread values)
   float* sX = sP;                // 64 x LLP over sP and sQ once the update is applied: the inverse
   float* sT = sP + 64 * LLP;     // 32 x 33: products of the doubling steps
   float* rinv = sL + 64 * LLP;   // 64: 1 / L[j][j]
@@ -778,18 +778,19 @@ __device__ __forceinline__ void solve_slab(const float* __restrict__ A, float* _
     }
 }
 
-// One launch of the blocked Cholesky, three kinds of workgroup:
+// One launch of the blocked Cholesky, three kinds of workgroup, in this
+// order of blockIdx:
 //  - workgroup 0 factors the diagonal block at leaf_j0 (leaf_mode 1: after
 //    the update from the block column at leaf_kp, from A and that block's
 //    inverse; 2: after the update from leaf_nk block columns of L starting at
 //    column leaf_kp; 0: no leaf in this launch);
+//  - lt1 - lt0 workgroups update tiles [lt0, lt1) of the lower tile list of
+//    [lR0, n) x [lR0, lcend) from lnk block columns of L starting at lk0
+//    (lskip00: not the diagonal block at lR0, which workgroup 0 updates);
 //  - nstrip workgroups update the tiles of [sk0 + 64, n) x [sk0 + 64, send)
 //    (the rest of a panel's columns) from the block column at sk0, solving it
 //    on the fly and storing it to L; or, with no strip, nsolve workgroups
-//    solve and store that block column's 128-row slabs;
-//  - the rest update tiles [lt0, lt1) of the lower tile list of
-//    [lR0, n) x [lR0, lcend) from lnk block columns of L starting at lk0
-//    (lskip00: not the diagonal block at lR0, which workgroup 0 updates).
+//    solve and store that block column's 128-row slabs.
 struct StepArgs {
   float* A;
   float* L;
@@ -818,7 +819,17 @@ __global__ __launch_bounds__(256, 2) void chol_step_kernel(StepArgs a) {
                  a.leaf_kp, a.leaf_nk);
     return;
   }
+  // The longest workgroups go out first: the rank-256 tiles from L (about
+  // three times a strip tile), then the strip tiles, then the slab solves,
+  // which fill the CUs the long tiles leave idle at the launch's end.
   b -= 1;
+  if (b < a.lt1 - a.lt0) {
+    int tm, tn;
+    region_tile(a.lt0 + b, a.l_nr, tm, tn);
+    tile_update<VEC, false>(a.A, a.L, nullptr, a.n, a.lk0, a.lnk, a.lR0, a.lcend, tm, tn, a.lskip00 != 0, smem);
+    return;
+  }
+  b -= a.lt1 - a.lt0;
   const float* dk = a.dinv + (a.sk0 / NB) * NB * NB;
   if (b < a.nstrip) {
     int tm, tn;
@@ -827,14 +838,7 @@ __global__ __launch_bounds__(256, 2) void chol_step_kernel(StepArgs a) {
     return;
   }
   b -= a.nstrip;
-  if (b < a.nsolve) {
-    solve_slab<VEC>(a.A, a.L, dk, a.n, a.sk0, a.sk0 + NB + (int64_t)TB * b, smem);
-    return;
-  }
-  b -= a.nsolve;
-  int tm, tn;
-  region_tile(a.lt0 + b, a.l_nr, tm, tn);
-  tile_update<VEC, false>(a.A, a.L, nullptr, a.n, a.lk0, a.lnk, a.lR0, a.lcend, tm, tn, a.lskip00 != 0, smem);
+  if (b < a.nsolve) solve_slab<VEC>(a.A, a.L, dk, a.n, a.sk0, a.sk0 + NB + (int64_t)TB * b, smem);
 }
 
 // Zero the strict upper triangle and put the NB-block inverses on the diagonal.
@@ -970,6 +974,44 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
     };
     StepArgs base{};
     base.A = w.A; base.L = w.L; base.dinv = w.dinv; base.info = info; base.n = n;
+    // Workgroups of the launch for block column k of the panel ending at b1
+    // besides its share of the previous panel's far update: strip tiles
+    // (k + 1 < b1) or slab solves (the panel's last column).
+    auto own_tiles = [&](int64_t k, int64_t b1, int64_t& nstrip, int64_t& nsolve) {
+      nstrip = nsolve = 0;
+      if (k + 1 < b1) {
+        const int64_t send = std::min(b1 * NB, n);
+        nstrip = lower_tiles(cdiv(n - (k + 1) * NB, TB), cdiv(send - (k + 1) * NB, TB));
+      } else {
+        nsolve = cdiv(n - (k + 1) * NB, TB);
+      }
+    };
+    // The far update's tiles are dealt over the panel's launches so that
+    // every launch but the last fills whole rounds of one tile per CU (two
+    // share a CU at half speed each): an even split leaves each launch with a
+    // partly filled last round.  Counted in far-tile times: a strip tile
+    // (rank 64 with its slab solves) about 2/3, a slab solve 1/4, the
+    // diagonal block one.
+    const int64_t cus = device_cus();
+    int64_t far_cut[PB + 1] = {};
+    auto deal_far = [&](int64_t p0, int64_t p1, int64_t F) {
+      const int64_t m = p1 - p0;
+      int64_t own[PB];
+      int64_t total = 3 * F;  // in thirds of a far tile
+      for (int64_t i = 0; i < m; ++i) {
+        int64_t ns, nv;
+        own_tiles(p0 + i, p1, ns, nv);
+        own[i] = 3 + 2 * ns + cdiv(3 * nv, 4);
+        total += own[i];
+      }
+      const int64_t rounds = cdiv(total, 3 * cus);
+      far_cut[0] = 0;
+      for (int64_t i = 0; i < m; ++i) {
+        const int64_t h = rounds / m + (i < rounds % m ? 1 : 0);
+        const int64_t f = i + 1 < m ? std::max<int64_t>(0, (3 * cus * h - own[i]) / 3) : F;
+        far_cut[i + 1] = std::min(F, far_cut[i] + f);
+      }
+    };
     int64_t far_R0 = 0, far_k0 = 0, far_tiles = 0;  // the previous panel's update past this panel
     for (int64_t b0 = 0; b0 < nb;) {
       const int64_t b1 = panel_end(b0), np = b1 - b0;
@@ -986,7 +1028,7 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
         }
         if (far_tiles > 0) {
           a.lk0 = far_k0; a.lnk = PB; a.lR0 = far_R0; a.lcend = n; a.l_nr = (int)cdiv(n - far_R0, TB);
-          a.lt0 = (int)(far_tiles * (k - b0) / np); a.lt1 = (int)(far_tiles * (k - b0 + 1) / np);
+          a.lt0 = (int)far_cut[k - b0]; a.lt1 = (int)far_cut[k - b0 + 1];
         }
         launch(a, 1 + (int64_t)a.nstrip + a.nsolve + (a.lt1 - a.lt0));
       }
@@ -1003,6 +1045,7 @@ hipError_t prepare_hinv(const float* H, int64_t n, float damp, float* U, int32_t
           far_R0 = nb1 * NB; far_k0 = b0 * NB;
           const int64_t nt = cdiv(n - far_R0, TB);
           far_tiles = lower_tiles(nt, nt);
+          deal_far(b1, nb1, far_tiles);
         }
       }
       b0 = b1;
