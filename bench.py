@@ -822,7 +822,7 @@ def bench_layer(args):
     try:
         Wk.copy_(W0)
         split = kernel_ms(quant, {"sweep": ("sweep_block_kernel",),
-                                  "trailing_gemm": ("gemm_nn_dma_kernel", "gemm_nn_dma64_kernel", "gemm_nn_big_kernel", "gemm_f32_kernel", "gemm_split_reduce"),
+                                  "trailing_gemm": ("gemm_nn_dma_kernel", "gemm_nn_dma64_kernel", "gemm_f32_kernel", "gemm_split_reduce"),
                                   "other": ("to_f32", "diag_blocks", "row_params", "pack_kernel", "dequant",
                                             "zero_f32")})
     except Exception as exc:  # noqa: BLE001 - the split is reported as missing, the rest stands

@@ -542,192 +542,6 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmDesc d, int 
   }
 }
 
-// ---------------------------------------------------------------------------- NN, 256 x 256 tiles
-//
-// For products with many tiles (the trailing updates of layers with many
-// rows): one workgroup of four wave64s per CU, each wave a 128 x 128 block
-// (4 x 4 accumulators of v_mfma_f32_32x32x2f32), K in 16-deep stages moved
-// HBM -> LDS with buffer_load_dwordx4 ... lds through a ring of five stages
-// (all 160 KiB of LDS): four stages in flight while one is consumed, one
-// barrier per stage.  Per flop a tile moves half the operand bytes of a
-// 128 x 128 tile.  The products go into the accumulators in the same K order
-// (k pairs 0-1, 2-3, ...) and C takes the same final fma as in the other NN
-// kernels, so the results are bit-identical to theirs.
-
-constexpr int GT = 256;                // tile edge
-constexpr int GK = 16;                 // K per stage
-constexpr int GNS = 5;                 // stages in the ring
-constexpr int GSTG = 2 * GT * GK * 4;  // bytes per stage: A 256 x 16, then B 16 x 256 (32 KiB)
-constexpr int GGROUP = 16;             // tile rows per group of the grid order
-
-// LDS layouts.  A: row r of a stage is 64 B (four 16-byte chunks); its slot s
-// holds chunk s ^ gswa(r), so the 32 rows one MFMA operand read touches fall
-// on 16 distinct (row mod 4, slot) bank groups.  B: row k is 1 KiB; odd rows
-// are rotated by eight chunks, so the two k rows of one read (lane halves)
-// land on different banks.
-__device__ __forceinline__ int gswa(int row) { return (row >> 2) & 3; }
-__device__ __forceinline__ int gswb(int k) { return (k & 1) << 3; }
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_nn_big_kernel(GemmDesc d, int ntm, int ntn) {
-  if (d.info && *d.info != 0) return;
-  __shared__ __attribute__((aligned(1024))) char ring[GNS * GSTG];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
-  // Grid order: groups of GGROUP tile rows, column by column inside a group,
-  // so the workgroups resident at one time share few A and B panels.
-  const int pid = blockIdx.x;
-  const int per_group = GGROUP * ntn;
-  const int grp = pid / per_group;
-  const int tm0 = grp * GGROUP;
-  const int gsz = min(ntm - tm0, GGROUP);
-  const int within = pid - grp * per_group;
-  const int tm = tm0 + within % gsz, tn = within / gsz;
-  const int r0 = tm * GT, c0 = tn * GT;
-  const int64_t z = blockIdx.y;
-  const float* A = d.A + z * d.strideA;
-  const float* B = d.B + z * d.strideB;
-  float* C = d.C + z * d.strideC;
-  const int mrows = min(GT, d.M - r0), ncols = min(GT, d.N - c0);
-  const int nst = d.K / GK;
-
-  // this lane's copies of one stage: A rows 16(4w + q) + l/4 (chunk l % 4),
-  // B row 4w + q (chunk l); byte offsets relative to the stage's buffer bases
-  int voffA[4], voffB[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int ra = 16 * (4 * wave + q) + (lane >> 2);
-    voffA[q] = (int)((int64_t)ra * d.lda * 4) + ((((lane & 3) ^ gswa(ra))) << 4);
-    const int kb = 4 * wave + q;
-    voffB[q] = (int)((int64_t)kb * d.ldb * 4) + (((lane ^ gswb(kb))) << 4);
-  }
-  // rows past M and the K range's end read as zero; columns past N only
-  // reach outputs that are never stored
-  const uint32_t aBytes = (uint32_t)(((int64_t)(mrows - 1) * d.lda + GK) * 4);
-  const uint32_t bBytes = (uint32_t)(((int64_t)(GK - 1) * d.ldb + ncols) * 4);
-  const uint32_t ring0 = (uint32_t)(uintptr_t)((char LDS_AS*)ring);
-  auto issue = [&](int st) {
-    const int kc = st * GK;
-    const i32x4 ra = make_rsrc(A + (int64_t)r0 * d.lda + kc, aBytes);
-    const i32x4 rb = make_rsrc(B + (int64_t)kc * d.ldb + c0, bBytes);
-    const uint32_t sb = ring0 + (uint32_t)((st % GNS) * GSTG);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dma16(ra, sb + (uint32_t)((4 * wave + q) * 1024), voffA[q]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dma16(rb, sb + (uint32_t)(GT * GK * 4 + (4 * wave + q) * 1024), voffB[q]);
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = zero16();
-  const int kr = lane >> 5, cl = lane & 31;
-  auto compute = [&](const float* sA) {
-    const float* sB = sA + GT * GK;
-    // operands of k pair kk (k = 2 kk + kr) in slot kk % 2, read one pair
-    // (sixteen MFMAs) ahead
-    float fa[2][4], fb[2][4];
-    auto rd = [&](int kk, int sl) {
-      const int k = 2 * kk + kr;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int row = wr * 128 + mb * 32 + cl;
-        fa[sl][mb] = sA[row * GK + ((((k >> 2) ^ gswa(row))) << 2) + (k & 3)];
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = wc * 128 + nb * 32 + cl;
-        fb[sl][nb] = sB[k * GT + ((((col >> 2) ^ gswb(k))) << 2) + (col & 3)];
-      }
-    };
-    rd(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < GK / 2; ++kk) {
-      const int sl = kk & 1;
-      if (kk + 1 < GK / 2) rd(kk + 1, sl ^ 1);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[sl][mb], fb[sl][nb], acc[mb][nb], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the first pair's reads
-#pragma unroll
-    for (int kk = 0; kk + 1 < GK / 2; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-  };
-
-  if (nst > 0) {
-#pragma unroll
-    for (int st = 0; st < GNS - 1; ++st)
-      if (st < nst) issue(st);
-    for (int st = 0; st < nst; ++st) {
-      // stage st landed for this wave's copies, later stages still in flight
-      const int ahead = min(GNS - 2, nst - 1 - st);
-      if (ahead >= 3) wait_vmcnt<24>(); else if (ahead == 2) wait_vmcnt<16>(); else if (ahead == 1) wait_vmcnt<8>();
-      else wait_vmcnt<0>();
-      stage_barrier();  // stage st visible; stage st - 1 no longer read by anyone
-      if (st + GNS - 1 < nst) issue(st + GNS - 1);
-      compute((const float*)(ring + (st % GNS) * GSTG));
-    }
-  }
-
-  // C through a buffer over the tile's rows with 32-bit offsets (the lane's
-  // base plus a term uniform per register), in eight chunks of two 32 x 32
-  // blocks, each chunk fetched while the one before it is written.  An entry
-  // past M or N gets an offset past the buffer: its load reads zero and its
-  // store is dropped, so edge tiles need no branches.
-  const float alpha = d.alpha, beta = d.beta;
-  const bool use_c = beta != 0.f;
-  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-      C + ((int64_t)r0 * d.ldc + c0), 0, (int)(((int64_t)(mrows - 1) * d.ldc + ncols) * 4), 0x00020000);
-  const uint32_t ldc4 = (uint32_t)d.ldc * 4u;
-  const uint32_t lb = (uint32_t)(wr * 128 + 4 * kr) * ldc4 + (uint32_t)(wc * 128 + cl) * 4u;
-  const int rlim = mrows - (wr * 128 + 4 * kr), clim = ncols - (wc * 128 + cl);
-  auto off = [&](int mb, int nb, int r) {
-    const int ro = mb * 32 + 8 * (r >> 2) + (r & 3);
-    const uint32_t o = lb + (uint32_t)ro * ldc4 + (uint32_t)(nb * 128);
-    return (ro < rlim && nb * 32 < clim) ? o : 0x80000000u;
-  };
-  f32x16 cq[2][2];
-  auto ld = [&](int ch, int sl) {
-    const int mb = ch >> 1, nb0 = 2 * (ch & 1);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      cq[sl][j] = zero16();
-      if (use_c) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          cq[sl][j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(crs, off(mb, nb0 + j, r), 0, 0));
-      }
-    }
-  };
-  auto st = [&](int ch, int sl) {
-    const int mb = ch >> 1, nb0 = 2 * (ch & 1);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float v = alpha * acc[mb][nb0 + j][r];
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, use_c ? fmaf(beta, cq[sl][j][r], v) : v), crs,
-                                              off(mb, nb0 + j, r), 0, 0);
-      }
-  };
-  ld(0, 0);
-#pragma unroll
-  for (int ch = 0; ch < 8; ++ch) {
-    if (ch + 1 < 8) ld(ch + 1, (ch + 1) & 1);
-    st(ch, ch & 1);
-  }
-}
-
 bool nn_dma_ok(const GemmDesc& d) {
   const auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   return d.K % DBK == 0 && d.lda % 4 == 0 && d.ldb % 4 == 0 && d.N % 4 == 0 && d.strideA % 4 == 0 &&
@@ -746,24 +560,6 @@ bool small_tiles_pay(const GemmDesc& d, int tM, int tN, int sM, int sN) {
   const int64_t slots = (int64_t)2 * device_cus();
   const int64_t r128 = cdiv((int64_t)tM * tN * d.batch, slots), r64 = cdiv((int64_t)sM * sN * d.batch, slots);
   return 20 * r64 < 17 * 4 * r128;
-}
-
-// Whether a plain NN product takes the 256 x 256 tiles.  Inside their K loops
-// both tile kernels keep the matrix pipe busy at the clock the chip holds
-// (measured: 88 % of the 256-tile loop's cycles, 98 % for two 128-tiles
-// sharing a CU); what differs is how often each operand panel is fetched.
-// That matters once the panels no longer stay in the last-level cache (256
-// MiB): then the 128-tiles' second fetch of each panel comes from HBM.  So
-// 256-tiles when A's and B's panels together exceed half that cache and the
-// grid fills every CU at least once.
-constexpr int64_t kPanelCacheBytes = (int64_t)128 << 20;
-bool big_tiles_pay(const GemmDesc& d) {
-  if (d.flags || d.K % GK || (int64_t)(GT - 1) * d.lda * 4 + 4096 >= ((int64_t)1 << 31) ||
-      (int64_t)(GK - 1) * d.ldb * 4 + 4096 >= ((int64_t)1 << 31) ||
-      (int64_t)(GT - 1) * d.ldc * 4 + 4096 >= ((int64_t)1 << 31))
-    return false;
-  const int64_t tiles = cdiv(d.M, GT) * cdiv(d.N, GT) * d.batch;
-  return tiles >= device_cus() && ((int64_t)d.M + d.N) * d.K * 4 * d.batch > kPanelCacheBytes;
 }
 
 template <bool TA, bool TB>
@@ -793,10 +589,7 @@ hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s) 
   if (d.flags & GEMM_LOWER_TILES) grid = dim3((unsigned)(tM * (tM + 1) / 2), 1, (unsigned)d.batch);
   else grid = dim3((unsigned)tM, (unsigned)tN, (unsigned)d.batch);
   const int sM = (int)cdiv(d.M, SB), sN = (int)cdiv(d.N, SB);
-  if (!transA && !transB && nn_dma_ok(d) && big_tiles_pay(d)) {
-    const int gM = (int)cdiv(d.M, GT), gN = (int)cdiv(d.N, GT);
-    hipLaunchKernelGGL(gemm_nn_big_kernel, dim3((unsigned)(gM * gN), (unsigned)d.batch), dim3(256), 0, s, d, gM, gN);
-  } else if (!transA && !transB && nn_dma_ok(d) && ((d.flags & GEMM_SMALL_TILES) || small_tiles_pay(d, tM, tN, sM, sN))) {
+  if (!transA && !transB && nn_dma_ok(d) && ((d.flags & GEMM_SMALL_TILES) || small_tiles_pay(d, tM, tN, sM, sN))) {
     hipLaunchKernelGGL(gemm_nn_dma64_kernel, dim3((unsigned)((int64_t)sM * sN * d.batch)), dim3(256), 0, s, d, sM, sN);
   } else if (!transA && !transB && nn_dma_ok(d)) {
     // split K when the tiles alone would give fewer than about four work

@@ -189,6 +189,42 @@ def test_sweep_parity(m, n, bits, group, block, wdt):
     assert np.all(diff <= 1e-3 * fr["err_sq"] + 1e-4 * expect)
 
 
+def test_sweep_parity_large_rows_ragged_tiles():
+    """A tall layer whose trailing updates leave partial tiles in both
+    directions (33000 rows; the flush past the first 1024-column superblock
+    writes 1152 columns with K = 1024), with more rows than the GPU holds
+    workgroups of the sweep at once.  The oracle checks 512 rows, among them
+    128 of the last 232 rows."""
+    m, n, bits, group, block = 33000, 2176, 4, 128, 128
+    say(f"[sweep, large] m={m} n={n} bits={bits} group={group} block={block} W=f16")
+    W, X = synth.small_layer(m, n, 4 * n, seed=33000, law="lognormal", w_dtype="f16", x_dtype="f32",
+                             outlier_frac=0.002, outlier_channels=2)
+    H = O.hessian([X.astype(np.float64)])
+    Hd, _ = O.damp(H, 0.01)
+    U_ref, _ = O.inverse_cholesky_upper(Hd)
+    U32 = U_ref.astype(np.float32)
+    Wt = to_dev(W, "f16")
+    res = pw.quantize_layer(Wt, torch.from_numpy(U32).to(DEV), bits, group, block, write_dequant=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.sort(np.concatenate([rng.choice(32768, 384, replace=False), rng.choice(np.arange(32768, m), 128, replace=False)]))
+    Wr = W[rows].astype(np.float64)
+    U64 = U32.astype(np.float64)
+    ref = O.gptq_quantize(Wr, U64, bits, group, block)
+    q = O.unpack_codes(res["qcodes"][rows].cpu().numpy().view(np.uint32), bits, n)
+    sc = res["scales"][rows].cpu().numpy()
+    z = res["zeros"][rows].cpu().numpy()
+    rep = compare_codes(q, sc, z, ref, group)
+    say(f"  same {rep['same_frac']:.6f} diverged rows {rep['rows_diverged']} scale rel {rep['scale_rel_max']:.2e}")
+    assert_codes(rep, "sweep-large")
+    follow_check(q, sc, z, Wr, U64, bits, group, block, "sweep-large")
+    lr = loss_rel(Wr, H, q, sc, z, ref, group)
+    assert lr <= LOSS_RTOL, f"loss rel {lr:.3e}"
+    Wh = O.dequant_from(q, sc, z, group)
+    got = Wt[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
+    assert np.allclose(got, Wh, rtol=1e-3, atol=1e-3 * np.abs(Wh).max())
+
+
 def test_sweep_block_invariance_on_gpu():
     """B = 1, 32 and 128 give the same codes except at near-ties."""
     m, n, bits, group = 64, 384, 4, 128
