@@ -94,6 +94,12 @@ struct SweepArgs {
   const float* Ep;
   int kpend;
   const float* Upend;
+  // superblock launches: nblk consecutive blocks of width w (the last one
+  // wlast wide) swept by one launch, each first taking the errors of the
+  // launch's earlier blocks (Upend: the factor rows from the launch's first
+  // column, at this block's columns)
+  int nblk;
+  int wlast;
 };
 
 // Lanes-per-row variants: 16 lanes (one DPP row) x 8 columns = 128 columns,
@@ -241,6 +247,62 @@ __device__ __forceinline__ void pending_update(const SweepArgs& a, int64_t r0, f
   __syncthreads();  // upd complete
 }
 
+// The same for a block inside a superblock launch: the errors of the
+// launch's earlier blocks (K = kpend columns, a multiple of 64) come from LDS
+// (Elds, this workgroup's 16 rows, pitch ELP), the factor rows from global
+// memory in chunks of 64 rows, the next chunk's loads in flight while the
+// current chunk's 32 MFMAs per wave run.  The same k order inside a chunk:
+// lane quarter g takes k = 64 c + 16 g + t at step t.
+constexpr int ELP = SBW + 4;
+__device__ __forceinline__ void pending_update_sb(const SweepArgs& a, const float* Elds, float* upd) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g16 = lane >> 4;
+  const int nch = a.kpend / 64;
+  int colq[2];
+  bool inq[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    colq[q] = 16 * (2 * wave + q) + l16;
+    inq[q] = colq[q] < a.w;
+  }
+  auto load_u = [&](int c, float (&u)[2][16]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float* __restrict__ up = a.Upend + (int64_t)(64 * c + 16 * g16) * a.n + (inq[q] ? colq[q] : 0);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) u[q][t] = up[(int64_t)t * a.n];
+    }
+  };
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  auto chunk = [&](int c, const float (&u)[2][16]) {
+    f32x4 e4[4];
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) e4[v4] = *(const f32x4*)&Elds[l16 * ELP + 64 * c + 16 * g16 + 4 * v4];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(e4[t / 4][t % 4], u[q][t], acc[q], 0, 0, 0);
+    }
+  };
+  float ua[2][16], ub[2][16];
+  load_u(0, ua);
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) load_u(c + 1, ub);
+    chunk(c, ua);
+    if (c + 1 < nch) {
+      if (c + 2 < nch) load_u(c + 2, ua);
+      chunk(c + 1, ub);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (!inq[q]) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};  // columns past the block: never read
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) upd[(4 * g16 + rr) * UPITCH + 16 * (2 * wave + q) + l16] = acc[q][rr];
+  }
+  __syncthreads();  // upd complete
+}
+
 // One block of the sweep.  GMODE: 0 = (s, z) fixed for the whole block
 // (per-row, or a group spanning several blocks); 8..128 = group size known at
 // compile time, groups start inside the block; -1 = any other in-block group
@@ -251,18 +313,29 @@ __device__ __forceinline__ void pending_update(const SweepArgs& a, int64_t r0, f
 // Three workgroups per CU for the look-ahead kernel (at most 168 VGPRs, which
 // its pending update's operands otherwise just exceed); the narrow-group
 // variants hold several groups' state and would spill, so they keep one.
-template <int LPR, int GMODE, bool LOOK>
-__global__ __launch_bounds__(256, (LOOK && (GMODE <= 0 || GMODE >= 64)) ? 3 : 1) void sweep_block_kernel(SweepArgs a) {
+template <int LPR>
+struct SweepSmem {
+  using LY = BlockLayout<LPR>;
+  float* Us;                                        // LY::USZ floats, 16-byte aligned
+  float* invd;                                      // LY::NSTEP
+  uint8_t (*codes8)[LY::NSTEP];                     // [256 / LPR][NSTEP], 8-byte aligned
+  float* Elds;                                      // superblock launches: [16][ELP] errors, else null
+};
+
+// SBM: the block is block `sbt` of a superblock launch (its pending errors
+// from Elds, its own errors also kept there at column sbt * w).
+template <int LPR, int GMODE, bool LOOK, bool SBM>
+__device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const SweepSmem<LPR>& sm, int ecol) {
   using LY = BlockLayout<LPR>;
   constexpr int NSTEP = LY::NSTEP;
   constexpr int ROWS = 256 / LPR;
   constexpr bool CAPTURE = GMODE < 0 || (GMODE > 0 && GMODE < LPR);
   constexpr int NG = (GMODE > 0 && !CAPTURE) ? NSTEP / GMODE : 1;  // groups of the block kept for the end
   constexpr int USZ = LY::USZ;
-  static_assert(!LOOK || (LPR == 16 && 16 * UPITCH <= USZ), "look-ahead needs the 128-column layout");
-  __shared__ __attribute__((aligned(16))) float Us[USZ];
-  __shared__ float invd[NSTEP];
-  __shared__ __attribute__((aligned(8))) uint8_t codes8[ROWS][NSTEP];
+  static_assert(!(LOOK || SBM) || (LPR == 16 && 16 * UPITCH <= USZ), "look-ahead needs the 128-column layout");
+  float* const Us = sm.Us;
+  float* const invd = sm.invd;
+  uint8_t (*const codes8)[NSTEP] = sm.codes8;
   const int tid = threadIdx.x;
   const int lr = tid & (LPR - 1);
   const int rl = tid / LPR;  // row within the workgroup
@@ -290,9 +363,10 @@ __global__ __launch_bounds__(256, (LOOK && (GMODE <= 0 || GMODE >= 64)) ? 3 : 1)
     const int c = lr + LPR * k;
     v[k] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
   }
-  if constexpr (LOOK) {
+  if constexpr (LOOK || SBM) {
     if (a.kpend > 0) {
-      if (a.kpend == BMAX) pending_update<BMAX>(a, (int64_t)blockIdx.x * ROWS, Us);
+      if constexpr (SBM) pending_update_sb(a, sm.Elds, Us);
+      else if (a.kpend == BMAX) pending_update<BMAX>(a, (int64_t)blockIdx.x * ROWS, Us);
       else pending_update<BMAX / 2>(a, (int64_t)blockIdx.x * ROWS, Us);
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] -= Us[rl * UPITCH + lr + LPR * k];
@@ -427,6 +501,7 @@ __global__ __launch_bounds__(256, (LOOK && (GMODE <= 0 || GMODE >= 64)) ? 3 : 1)
       const int c = lr + LPR * k;
       if (c < w) {
         a.E[r * ELD + c] = ek[k];
+        if constexpr (SBM) sm.Elds[rl * ELP + ecol + c] = ek[k];
         if (a.Wout) store_w(a.Wout, a.wdt, r * a.ldw + i + c, ws_[k] * qz_[k]);
       }
     }
@@ -514,6 +589,44 @@ __global__ __launch_bounds__(256, (LOOK && (GMODE <= 0 || GMODE >= 64)) ? 3 : 1)
   }
 }
 
+template <int LPR, int GMODE, bool LOOK>
+__global__ __launch_bounds__(256, (LOOK && (GMODE <= 0 || GMODE >= 64)) ? 3 : 1) void sweep_block_kernel(SweepArgs a) {
+  using LY = BlockLayout<LPR>;
+  __shared__ __attribute__((aligned(16))) float Us[LY::USZ];
+  __shared__ float invd[LY::NSTEP];
+  __shared__ __attribute__((aligned(8))) uint8_t codes8[256 / LPR][LY::NSTEP];
+  const SweepSmem<LPR> sm{Us, invd, codes8, nullptr};
+  sweep_block_body<LPR, GMODE, LOOK, false>(a, sm, 0);
+}
+
+// A whole superblock (up to SBW columns) in one launch, one workgroup per CU:
+// block t first takes the errors of blocks 0..t-1 of the launch (kept in LDS)
+// on MFMA, then is swept.  Rows are independent, so nothing is exchanged
+// between workgroups; what the launch replaces is one launch per block and
+// the product flushes inside the superblock.
+template <int GMODE>
+__global__ __launch_bounds__(256, 1) void sweep_superblock_kernel(SweepArgs a) {
+  using LY = BlockLayout<16>;
+  __shared__ __attribute__((aligned(16))) float Us[LY::USZ];
+  __shared__ float invd[LY::NSTEP];
+  __shared__ __attribute__((aligned(8))) uint8_t codes8[16][LY::NSTEP];
+  __shared__ __attribute__((aligned(16))) float Elds[16 * ELP];
+  const SweepSmem<16> sm{Us, invd, codes8, Elds};
+  for (int t = 0; t < a.nblk; ++t) {
+    SweepArgs b = a;
+    b.i = a.i + (int64_t)t * a.w;
+    b.w = t + 1 < a.nblk ? a.w : a.wlast;
+    b.E = a.E + (int64_t)t * a.w;
+    b.Dblk = a.Dblk + (int64_t)t * LY::STRIDE;
+    b.kpend = t * a.w;
+    b.Upend = a.Upend + (int64_t)t * a.w;
+    // the previous block's reads of the LDS buffers are done and its errors
+    // are in Elds
+    if (t > 0) __syncthreads();
+    sweep_block_body<16, GMODE, false, true>(b, sm, t * a.w);
+  }
+}
+
 // Per block of B columns starting at i = blk * B: the factor rows p of
 // U[i:i+w, i:i+w] divided by U_pp, zero on and left of the diagonal, in
 // BlockLayout<LPR> order, then 1/U_pp (0 past w).  One thread per (row p,
@@ -539,6 +652,19 @@ __global__ __launch_bounds__(256) void diag_blocks_kernel(const float* U, int64_
       }
     }
     if (lr == 0) dst[LY::USZ + p] = prow ? 1.f / d : 0.f;
+  }
+}
+
+void launch_sweep_sb(const SweepArgs& a, int gmode, hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(a.m, 16)), block(256);
+  switch (gmode) {
+    case 0: hipLaunchKernelGGL((sweep_superblock_kernel<0>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((sweep_superblock_kernel<8>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((sweep_superblock_kernel<16>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((sweep_superblock_kernel<32>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((sweep_superblock_kernel<64>), grid, block, 0, st, a); break;
+    case 128: hipLaunchKernelGGL((sweep_superblock_kernel<128>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((sweep_superblock_kernel<-1>), grid, block, 0, st, a);
   }
 }
 
@@ -721,7 +847,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
                          Z, G, i / group);
     SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, packed ? nullptr : Q8, packed ? qcodes : nullptr, words,
                 bits, write_dequant ? W : nullptr, dt, ldw, E + eoff, err_sq, Dblk + (i / B) * dstride,
-                E + epair, (int)(i - g0), U + g0 * n + i};
+                E + epair, (int)(i - g0), U + g0 * n + i, 1, w};
     if (B <= 32) launch_sweep<4, false>(a, gmode, st);
     else if (look) launch_sweep<16, true>(a, gmode, st);
     else launch_sweep<16, false>(a, gmode, st);
@@ -740,7 +866,24 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   };
   // (pending K = t B is a multiple of the 64-row chunks; rows of V 16-byte aligned)
   const bool look = B % 64 == 0 && (group <= 0 || group <= B) && n % 4 == 0;
-  if (look) {
+  // Superblock launches while the rows fit the GPU in one round of one
+  // workgroup (16 rows) per CU: each superblock of SBW columns is swept by one
+  // launch (every block taking the errors of the superblock's earlier blocks
+  // inside the kernel), then one product brings the rest of the row up to
+  // date.
+  const bool sb = look && cdiv(m, 16) <= device_cus();
+  if (sb) {
+    for (int64_t s0 = 0; s0 < n; s0 += SBW) {
+      const int64_t s1 = std::min<int64_t>(s0 + SBW, n);
+      const int nblk = (int)cdiv(s1 - s0, B);
+      SweepArgs a{U, V, n, m, s0, (int)B, maxq, group, G, S, Z, packed ? nullptr : Q8, packed ? qcodes : nullptr,
+                  words, bits, write_dequant ? W : nullptr, dt, ldw, E, err_sq, Dblk + (s0 / B) * dstride,
+                  nullptr, 0, U + s0 * n + s0, nblk, (int)(s1 - s0 - (int64_t)(nblk - 1) * B)};
+      launch_sweep_sb(a, gmode, st);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = flush(0, s0, (int)(s1 - s0), s1, n - s1)) != hipSuccess) return e;
+    }
+  } else if (look) {
     // Look-ahead: LA blocks per flush.  Block t of a group first takes the
     // errors of blocks 0..t-1 of its group (inside the sweep kernel, K = t B,
     // on MFMA), then is swept; after the group, one GEMM with K = LA B brings
