@@ -247,60 +247,69 @@ __device__ __forceinline__ void pending_update(const SweepArgs& a, int64_t r0, f
   __syncthreads();  // upd complete
 }
 
-// The same for a block inside a superblock launch: the errors of the
-// launch's earlier blocks (K = kpend columns, a multiple of 64) come from LDS
-// (Elds, this workgroup's 16 rows, pitch ELP), the factor rows from global
-// memory in chunks of 64 rows, the next chunk's loads in flight while the
-// current chunk's 32 MFMAs per wave run.  The same k order inside a chunk:
+// Inside a superblock launch the pending updates run on four waves of their
+// own (waves 4..7 of a 512-thread workgroup) while waves 0..3 sweep: wave
+// 4 + w accumulates output column blocks 2w, 2w + 1 of
+//   acc += E[:, k0 : k0 + 64 nch] U[s0 + k0 .., ib + (0..wblk)]
+// for the workgroup's 16 rows, the errors from LDS (Elds, pitch ELP), the
+// factor rows from global memory in chunks of 64 rows with the next chunk's
+// loads in flight while the current chunk's 32 MFMAs run.  Inside a chunk,
 // lane quarter g takes k = 64 c + 16 g + t at step t.
 constexpr int ELP = SBW + 4;
-__device__ __forceinline__ void pending_update_sb(const SweepArgs& a, const float* Elds, float* upd) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g16 = lane >> 4;
-  const int nch = a.kpend / 64;
-  int colq[2];
-  bool inq[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    colq[q] = 16 * (2 * wave + q) + l16;
-    inq[q] = colq[q] < a.w;
-  }
-  auto load_u = [&](int c, float (&u)[2][16]) {
+struct PendingOps {
+  const float* Elds;
+  const float* ubase;  // factor row a.i + k0, column ib
+  int64_t n;
+  int k0;
+  uint32_t loff[2];    // per-lane byte offsets: the lane's k quarter and column
+  int l16, g16;
+  // per-lane offsets from a row pointer that is the same for the whole wave,
+  // so the loads take a scalar base and one 32-bit offset register each
+  __device__ __forceinline__ PendingOps(const SweepArgs& a, const float* E_, int k0_, int64_t ib, int wblk)
+      : Elds(E_), ubase(a.U + (a.i + k0_) * a.n + ib), n(a.n), k0(k0_) {
+    const int lane = threadIdx.x & 63, wq = (threadIdx.x >> 6) - 4;
+    l16 = lane & 15;
+    g16 = lane >> 4;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const float* __restrict__ up = a.Upend + (int64_t)(64 * c + 16 * g16) * a.n + (inq[q] ? colq[q] : 0);
-#pragma unroll
-      for (int t = 0; t < 16; ++t) u[q][t] = up[(int64_t)t * a.n];
+      const int col = 16 * (2 * wq + q) + l16;
+      loff[q] = (uint32_t)((16 * g16 * n + (col < wblk ? col : 0)) * 4);  // past the block: computed, never read
     }
-  };
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  auto chunk = [&](int c, const float (&u)[2][16]) {
+  }
+  __device__ __forceinline__ void load(int c, float (&u)[2][16]) const {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const char* __restrict__ row = (const char*)(ubase + (int64_t)(64 * c + t) * n);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) u[q][t] = *(const float*)(row + loff[q]);
+    }
+  }
+  __device__ __forceinline__ void mul(int c, const float (&u)[2][16], f32x4 (&acc)[2]) const {
     f32x4 e4[4];
 #pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) e4[v4] = *(const f32x4*)&Elds[l16 * ELP + 64 * c + 16 * g16 + 4 * v4];
+    for (int v4 = 0; v4 < 4; ++v4) e4[v4] = *(const f32x4*)&Elds[l16 * ELP + k0 + 64 * c + 16 * g16 + 4 * v4];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(e4[t / 4][t % 4], u[q][t], acc[q], 0, 0, 0);
     }
-  };
+  }
+};
+
+__device__ __forceinline__ void pending_acc(const SweepArgs& a, const float* Elds, int k0, int nch, int64_t ib,
+                                            int wblk, f32x4 (&acc)[2]) {
+  if (nch <= 0) return;
+  const PendingOps op(a, Elds, k0, ib, wblk);
   float ua[2][16], ub[2][16];
-  load_u(0, ua);
+  op.load(0, ua);
   for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) load_u(c + 1, ub);
-    chunk(c, ua);
+    if (c + 1 < nch) op.load(c + 1, ub);
+    op.mul(c, ua, acc);
     if (c + 1 < nch) {
-      if (c + 2 < nch) load_u(c + 2, ua);
-      chunk(c + 1, ub);
+      if (c + 2 < nch) op.load(c + 2, ua);
+      op.mul(c + 1, ub, acc);
     }
   }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (!inq[q]) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};  // columns past the block: never read
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) upd[(4 * g16 + rr) * UPITCH + 16 * (2 * wave + q) + l16] = acc[q][rr];
-  }
-  __syncthreads();  // upd complete
 }
 
 // One block of the sweep.  GMODE: 0 = (s, z) fixed for the whole block
@@ -320,6 +329,7 @@ struct SweepSmem {
   float* invd;                                      // LY::NSTEP
   uint8_t (*codes8)[LY::NSTEP];                     // [256 / LPR][NSTEP], 8-byte aligned
   float* Elds;                                      // superblock launches: [16][ELP] errors, else null
+  float* upd;                                       // superblock launches: [16][UPITCH] pending update
 };
 
 // SBM: the block is block `sbt` of a superblock launch (its pending errors
@@ -363,10 +373,9 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
     const int c = lr + LPR * k;
     v[k] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
   }
-  if constexpr (LOOK || SBM) {
+  if constexpr (LOOK && !SBM) {
     if (a.kpend > 0) {
-      if constexpr (SBM) pending_update_sb(a, sm.Elds, Us);
-      else if (a.kpend == BMAX) pending_update<BMAX>(a, (int64_t)blockIdx.x * ROWS, Us);
+      if (a.kpend == BMAX) pending_update<BMAX>(a, (int64_t)blockIdx.x * ROWS, Us);
       else pending_update<BMAX / 2>(a, (int64_t)blockIdx.x * ROWS, Us);
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] -= Us[rl * UPITCH + lr + LPR * k];
@@ -379,6 +388,17 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
     if (Q4 % 256 == 0 || q < Q4) ((f32x4*)Us)[q] = ublk[u];
   }
   if (tid < NSTEP) invd[tid] = invd_t;
+  if constexpr (SBM) {
+    // B1: the factor block is in LDS and the MFMA waves have put this block's
+    // pending update in `upd` (they take the same barrier whether or not
+    // anything is pending; they write `upd` again only after the next block's
+    // B0, when every sweeping wave has read it)
+    __syncthreads();
+    if (a.kpend > 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] -= sm.upd[rl * UPITCH + lr + LPR * k];
+    }
+  }
 
   GroupState g = make_group(1.f, 0.f, a.maxq);
   if (GMODE == 0 && active) {
@@ -398,7 +418,7 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
   }
   int next_group = 0;  // GMODE == -1: block-local column of the next group start
   const bool writer = active && lr == 0;
-  __syncthreads();
+  if constexpr (!SBM) __syncthreads();
 
   // factor rows prefetched D steps ahead into a ring of registers (only the
   // live registers J..7 of each row)
@@ -595,35 +615,76 @@ __global__ __launch_bounds__(256, (LOOK && (GMODE <= 0 || GMODE >= 64)) ? 3 : 1)
   __shared__ __attribute__((aligned(16))) float Us[LY::USZ];
   __shared__ float invd[LY::NSTEP];
   __shared__ __attribute__((aligned(8))) uint8_t codes8[256 / LPR][LY::NSTEP];
-  const SweepSmem<LPR> sm{Us, invd, codes8, nullptr};
+  const SweepSmem<LPR> sm{Us, invd, codes8, nullptr, nullptr};
   sweep_block_body<LPR, GMODE, LOOK, false>(a, sm, 0);
 }
 
-// A whole superblock (up to SBW columns) in one launch, one workgroup per CU:
-// block t first takes the errors of blocks 0..t-1 of the launch (kept in LDS)
-// on MFMA, then is swept.  Rows are independent, so nothing is exchanged
-// between workgroups; what the launch replaces is one launch per block and
-// the product flushes inside the superblock.
+// A whole superblock (up to SBW columns) in one launch, one workgroup per CU,
+// 512 threads.  Waves 0..3 sweep the blocks one after another (16 rows, as
+// above); waves 4..7 apply the pending updates on the matrix cores beside
+// them: while block t is swept they accumulate the errors of blocks 0..t-1
+// onto block t + 1's columns, and once block t's errors are in LDS they add
+// those and hand the update over.  Rows are independent, so nothing is
+// exchanged between workgroups; what the launch replaces is one launch per
+// block and the product flushes inside the superblock.
+//
+// Barriers per block, taken by all eight waves: B0 (t > 0: block t - 1
+// swept, its errors in Elds; the MFMA waves' partial sums done) and B1 (the
+// update in `upd`, the factor block in LDS).
 template <int GMODE>
-__global__ __launch_bounds__(256, 1) void sweep_superblock_kernel(SweepArgs a) {
+__global__ __launch_bounds__(512, 1) void sweep_superblock_kernel(SweepArgs a) {
   using LY = BlockLayout<16>;
   __shared__ __attribute__((aligned(16))) float Us[LY::USZ];
   __shared__ float invd[LY::NSTEP];
   __shared__ __attribute__((aligned(8))) uint8_t codes8[16][LY::NSTEP];
   __shared__ __attribute__((aligned(16))) float Elds[16 * ELP];
-  const SweepSmem<16> sm{Us, invd, codes8, Elds};
-  for (int t = 0; t < a.nblk; ++t) {
-    SweepArgs b = a;
-    b.i = a.i + (int64_t)t * a.w;
-    b.w = t + 1 < a.nblk ? a.w : a.wlast;
-    b.E = a.E + (int64_t)t * a.w;
-    b.Dblk = a.Dblk + (int64_t)t * LY::STRIDE;
-    b.kpend = t * a.w;
-    b.Upend = a.Upend + (int64_t)t * a.w;
-    // the previous block's reads of the LDS buffers are done and its errors
-    // are in Elds
-    if (t > 0) __syncthreads();
-    sweep_block_body<16, GMODE, false, true>(b, sm, t * a.w);
+  __shared__ __attribute__((aligned(16))) float upd[16 * UPITCH];
+  const SweepSmem<16> sm{Us, invd, codes8, Elds, upd};
+  const int B = a.w;
+  if (threadIdx.x < 256) {
+    for (int t = 0; t < a.nblk; ++t) {
+      SweepArgs b = a;
+      b.i = a.i + (int64_t)t * B;
+      b.w = t + 1 < a.nblk ? B : a.wlast;
+      b.E = a.E + (int64_t)t * B;
+      b.Dblk = a.Dblk + (int64_t)t * LY::STRIDE;
+      b.kpend = t * B;
+      if (t > 0) __syncthreads();  // B0
+      sweep_block_body<16, GMODE, false, true>(b, sm, t * B);
+    }
+  } else {
+    const int lane = threadIdx.x & 63, wq = (threadIdx.x >> 6) - 4;
+    const int l16 = lane & 15, g16 = lane >> 4;
+    const int nb = B / 64;  // 64-row chunks per block (1 or 2)
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float bu[2][2][16];     // factor rows of the previous block, for its errors onto this one (loaded early)
+    for (int t = 0; t < a.nblk; ++t) {
+      const int wt = t + 1 < a.nblk ? B : a.wlast;  // width of block t
+      if (t > 0) {
+        __syncthreads();  // B0: block t - 1's errors are in Elds
+        const PendingOps op(a, Elds, (t - 1) * B, a.i + (int64_t)t * B, wt);
+        op.mul(0, bu[0], acc);
+        if (nb > 1) op.mul(1, bu[1], acc);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            upd[(4 * g16 + rr) * UPITCH + 16 * (2 * wq + q) + l16] = 16 * (2 * wq + q) + l16 < wt ? acc[q][rr] : 0.f;
+      }
+      __syncthreads();  // B1
+      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t + 1 < a.nblk) {
+        // while block t is swept: blocks 0..t-1 onto block t + 1, then the
+        // factor rows of block t for block t + 1's columns (its errors follow)
+        const int wn = t + 2 < a.nblk ? B : a.wlast;
+        const int64_t ibn = a.i + (int64_t)(t + 1) * B;
+        pending_acc(a, Elds, 0, t * nb, ibn, wn, acc);
+        const PendingOps op(a, Elds, t * B, ibn, wn);
+        op.load(0, bu[0]);
+        if (nb > 1) op.load(1, bu[1]);
+      }
+    }
   }
 }
 
@@ -656,7 +717,7 @@ __global__ __launch_bounds__(256) void diag_blocks_kernel(const float* U, int64_
 }
 
 void launch_sweep_sb(const SweepArgs& a, int gmode, hipStream_t st) {
-  const dim3 grid((unsigned)cdiv(a.m, 16)), block(256);
+  const dim3 grid((unsigned)cdiv(a.m, 16)), block(512);
   switch (gmode) {
     case 0: hipLaunchKernelGGL((sweep_superblock_kernel<0>), grid, block, 0, st, a); break;
     case 8: hipLaunchKernelGGL((sweep_superblock_kernel<8>), grid, block, 0, st, a); break;
