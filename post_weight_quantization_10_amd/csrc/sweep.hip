@@ -193,12 +193,6 @@ __device__ __forceinline__ void store_params(const SweepArgs& a, const GroupStat
   }
 }
 
-__device__ __forceinline__ void store_w(void* W, int dt, int64_t idx, float v) {
-  if (dt == 0) ((_Float16*)W)[idx] = (_Float16)v;
-  else if (dt == 1) ((uint16_t*)W)[idx] = f32_to_bf16(v);
-  else ((float*)W)[idx] = v;
-}
-
 // The errors of the pending columns (swept since the last flush) applied to
 // this block's 128 columns for the workgroup's 16 rows, with
 // v_mfma_f32_16x16x4f32: wave w computes output column blocks 2w, 2w+1.  The
@@ -322,6 +316,43 @@ __device__ __forceinline__ void pending_acc(const SweepArgs& a, const float* Eld
 // Three workgroups per CU for the look-ahead kernel (at most 168 VGPRs, which
 // its pending update's operands otherwise just exceed); the narrow-group
 // variants hold several groups' state and would spill, so they keep one.
+// A barrier that orders only LDS: global stores and loads in flight (the
+// previous block's outputs, the next block's operands) stay in flight.  The
+// waves of a superblock launch hand each other data through LDS only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// What a block's sweep reads from global memory first: its factor rows and
+// 1/U_pp (prepared once per layer by diag_blocks_kernel) and the rows' values.
+template <int LPR>
+struct BlockLoads {
+  using LY = BlockLayout<LPR>;
+  static constexpr int Q4 = LY::USZ / 4, NQ = (Q4 + 255) / 256;
+  f32x4 ublk[NQ];
+  float invd_t;
+  float v[8];
+  __device__ __forceinline__ void load(const SweepArgs& a) {
+    const int tid = threadIdx.x, lr = tid & (LPR - 1);
+    const int64_t r = (int64_t)blockIdx.x * (256 / LPR) + tid / LPR;
+    const bool active = r < a.m;
+    const f32x4* src = (const f32x4*)a.Dblk;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int q = tid + 256 * u;
+      ublk[u] = (Q4 % 256 == 0 || q < Q4) ? src[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    invd_t = tid < LY::NSTEP ? a.Dblk[LY::USZ + tid] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = lr + LPR * k;
+      v[k] = (active && c < a.w) ? a.V[r * a.n + a.i + c] : 0.f;
+    }
+  }
+};
+
 template <int LPR>
 struct SweepSmem {
   using LY = BlockLayout<LPR>;
@@ -335,7 +366,8 @@ struct SweepSmem {
 // SBM: the block is block `sbt` of a superblock launch (its pending errors
 // from Elds, its own errors also kept there at column sbt * w).
 template <int LPR, int GMODE, bool LOOK, bool SBM>
-__device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const SweepSmem<LPR>& sm, int ecol) {
+__device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const SweepSmem<LPR>& sm, int ecol,
+                                                 BlockLoads<LPR>* pre = nullptr, const SweepArgs* next = nullptr) {
   using LY = BlockLayout<LPR>;
   constexpr int NSTEP = LY::NSTEP;
   constexpr int ROWS = 256 / LPR;
@@ -353,26 +385,15 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
   const bool active = r < a.m;
   const int w = a.w;
   const int64_t i = a.i;
-  // this block's factor rows and 1/U_pp (prepared once per layer by
-  // diag_blocks_kernel) and the rows' values: every load of the kernel's
-  // start in flight at once
-  constexpr int Q4 = LY::USZ / 4, NQ = (Q4 + 255) / 256;
-  f32x4 ublk[NQ];
-  {
-    const f32x4* src = (const f32x4*)a.Dblk;
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int q = tid + 256 * u;
-      ublk[u] = (Q4 % 256 == 0 || q < Q4) ? src[q] : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  const float invd_t = tid < NSTEP ? a.Dblk[LY::USZ + tid] : 0.f;
-  float v[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int c = lr + LPR * k;
-    v[k] = (active && c < w) ? a.V[r * a.n + i + c] : 0.f;
-  }
+  // every load of the block's start in flight at once (in a superblock
+  // launch they were issued during the previous block)
+  constexpr int Q4 = BlockLoads<LPR>::Q4, NQ = BlockLoads<LPR>::NQ;
+  BlockLoads<LPR> ld;
+  if constexpr (SBM) ld = *pre;
+  else ld.load(a);
+  f32x4 (&ublk)[NQ] = ld.ublk;
+  const float invd_t = ld.invd_t;
+  float (&v)[8] = ld.v;
   if constexpr (LOOK && !SBM) {
     if (a.kpend > 0) {
       if (a.kpend == BMAX) pending_update<BMAX>(a, (int64_t)blockIdx.x * ROWS, Us);
@@ -393,7 +414,7 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
     // pending update in `upd` (they take the same barrier whether or not
     // anything is pending; they write `upd` again only after the next block's
     // B0, when every sweeping wave has read it)
-    __syncthreads();
+    lds_barrier();
     if (a.kpend > 0) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] -= sm.upd[rl * UPITCH + lr + LPR * k];
@@ -491,6 +512,9 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
         ...);
   }(std::make_integer_sequence<int, NSTEP>{});
 
+  if constexpr (SBM) {
+    if (next) pre->load(*next);  // the next block's operands arrive while this one is written out
+  }
   // codes, errors and dequantized weights of this lane's columns
   float eacc = 0.f;
   float ws_[8], qz_[8];
@@ -515,17 +539,48 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
     eacc = fmaf(e, e, eacc);
   }
   eacc = RowOps<LPR>::rsum(eacc);
+  if constexpr (SBM) {
+    // the errors go to LDS first: from the barrier on, the MFMA waves apply
+    // them to the next block while this one is written out
+    if (active) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = lr + LPR * k;
+        if (c < w) sm.Elds[rl * ELP + ecol + c] = ek[k];
+      }
+    }
+    if (next) lds_barrier();  // B0 of the next block
+  }
   if (active) {
+    // one branch on the output type for the whole row, not one per column
+    const bool full = w == NSTEP;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int c = lr + LPR * k;
-      if (c < w) {
-        a.E[r * ELD + c] = ek[k];
-        if constexpr (SBM) sm.Elds[rl * ELP + ecol + c] = ek[k];
-        if (a.Wout) store_w(a.Wout, a.wdt, r * a.ldw + i + c, ws_[k] * qz_[k]);
+      if (full || c < w) a.E[r * ELD + c] = ek[k];
+    }
+    if (a.Wout) {
+      if (a.wdt == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = lr + LPR * k;
+          if (full || c < w) ((_Float16*)a.Wout)[r * a.ldw + i + c] = (_Float16)(ws_[k] * qz_[k]);
+        }
+      } else if (a.wdt == 1) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = lr + LPR * k;
+          if (full || c < w) ((uint16_t*)a.Wout)[r * a.ldw + i + c] = f32_to_bf16(ws_[k] * qz_[k]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = lr + LPR * k;
+          if (full || c < w) ((float*)a.Wout)[r * a.ldw + i + c] = ws_[k] * qz_[k];
+        }
       }
     }
-    // blocks run one launch after another, so each row's sum is taken in block order
+    // blocks run one after another, so each row's sum is taken in block order
     if (lr == 0 && a.err_sq) atomicAdd(a.err_sq + r, eacc);
   }
   // codes: q = qz + z, as bytes (fallback layout) or packed per row
@@ -628,9 +683,10 @@ __global__ __launch_bounds__(256, (LOOK && (GMODE <= 0 || GMODE >= 64)) ? 3 : 1)
 // exchanged between workgroups; what the launch replaces is one launch per
 // block and the product flushes inside the superblock.
 //
-// Barriers per block, taken by all eight waves: B0 (t > 0: block t - 1
-// swept, its errors in Elds; the MFMA waves' partial sums done) and B1 (the
-// update in `upd`, the factor block in LDS).
+// Barriers per block, taken by all eight waves: B0 (t > 0: block t - 1's
+// errors in Elds, taken by the sweeping waves before they write that block
+// out; the MFMA waves' partial sums done) and B1 (the update in `upd`, the
+// factor block in LDS).
 template <int GMODE>
 __global__ __launch_bounds__(512, 1) void sweep_superblock_kernel(SweepArgs a) {
   using LY = BlockLayout<16>;
@@ -642,15 +698,24 @@ __global__ __launch_bounds__(512, 1) void sweep_superblock_kernel(SweepArgs a) {
   const SweepSmem<16> sm{Us, invd, codes8, Elds, upd};
   const int B = a.w;
   if (threadIdx.x < 256) {
-    for (int t = 0; t < a.nblk; ++t) {
+    auto block_args = [&](int t) {
       SweepArgs b = a;
       b.i = a.i + (int64_t)t * B;
       b.w = t + 1 < a.nblk ? B : a.wlast;
       b.E = a.E + (int64_t)t * B;
       b.Dblk = a.Dblk + (int64_t)t * LY::STRIDE;
       b.kpend = t * B;
-      if (t > 0) __syncthreads();  // B0
-      sweep_block_body<16, GMODE, false, true>(b, sm, t * B);
+      return b;
+    };
+    BlockLoads<16> pre;
+    SweepArgs b = block_args(0);
+    pre.load(b);
+    for (int t = 0; t < a.nblk; ++t) {
+      // (B0 of block t + 1 is taken inside block t's write-out, once its
+      // errors are in Elds)
+      const SweepArgs bn = block_args(t + 1 < a.nblk ? t + 1 : t);
+      sweep_block_body<16, GMODE, false, true>(b, sm, t * B, &pre, t + 1 < a.nblk ? &bn : nullptr);
+      b = bn;
     }
   } else {
     const int lane = threadIdx.x & 63, wq = (threadIdx.x >> 6) - 4;
@@ -661,7 +726,7 @@ __global__ __launch_bounds__(512, 1) void sweep_superblock_kernel(SweepArgs a) {
     for (int t = 0; t < a.nblk; ++t) {
       const int wt = t + 1 < a.nblk ? B : a.wlast;  // width of block t
       if (t > 0) {
-        __syncthreads();  // B0: block t - 1's errors are in Elds
+        lds_barrier();  // B0: block t - 1's errors are in Elds
         const PendingOps op(a, Elds, (t - 1) * B, a.i + (int64_t)t * B, wt);
         op.mul(0, bu[0], acc);
         if (nb > 1) op.mul(1, bu[1], acc);
@@ -671,7 +736,7 @@ __global__ __launch_bounds__(512, 1) void sweep_superblock_kernel(SweepArgs a) {
           for (int rr = 0; rr < 4; ++rr)
             upd[(4 * g16 + rr) * UPITCH + 16 * (2 * wq + q) + l16] = 16 * (2 * wq + q) + l16 < wt ? acc[q][rr] : 0.f;
       }
-      __syncthreads();  // B1
+      lds_barrier();  // B1
       acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (t + 1 < a.nblk) {
