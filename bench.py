@@ -671,17 +671,27 @@ def main():
     bench_layer(args)
 
 
-def trailing_schedule(m: int, n: int, B: int, group: int):
+def trailing_schedule(m: int, n: int, B: int, group: int, cus: int = 256):
     """Flops of the trailing update m n (n - B) split as gptq_quantize_layer
     runs it: (flops in the GEMM kernels, flops applied inside the sweep
-    kernel).  With B a multiple of 64 and groups no wider than a block the
-    blocks go in pairs: the second block of a pair takes the first one's
-    errors on its own columns inside the sweep, then GEMMs update the columns
-    after the pair (those of its 1024-column superblock at once, the rest
-    after the superblock with K = 1024; the same flops either way)."""
+    kernel).  With B a multiple of 64 and groups no wider than a block:
+    while the rows fit one 16-row workgroup per CU, one launch sweeps a whole
+    1024-column superblock, every block taking the superblock's earlier errors
+    inside the kernel, and a GEMM with K = 1024 updates the rest of the row
+    after each superblock; otherwise the blocks go in pairs: the second block
+    of a pair takes the first one's errors on its own columns inside the
+    sweep, then GEMMs update the columns after the pair (those of its
+    1024-column superblock at once, the rest after the superblock with
+    K = 1024; the same flops either way)."""
     look = B % 64 == 0 and (group <= 0 or group <= B) and n % 4 == 0
     gemm = in_sweep = 0.0
-    if look:
+    if look and -(-m // 16) <= cus:
+        for s0 in range(0, n, 1024):
+            s1 = min(s0 + 1024, n)
+            for i in range(s0, s1, B):
+                in_sweep += 2.0 * m * (i - s0) * min(B, s1 - i)
+            gemm += 2.0 * m * (s1 - s0) * (n - s1)
+    elif look:
         g0 = 0
         while g0 < n:
             w1 = min(B, n - g0)
@@ -821,7 +831,7 @@ def bench_layer(args):
     split = None
     try:
         Wk.copy_(W0)
-        split = kernel_ms(quant, {"sweep": ("sweep_block_kernel",),
+        split = kernel_ms(quant, {"sweep": ("sweep_block_kernel", "sweep_superblock_kernel"),
                                   "trailing_gemm": ("gemm_nn_dma_kernel", "gemm_nn_dma64_kernel", "gemm_f32_kernel", "gemm_split_reduce"),
                                   "other": ("to_f32", "diag_blocks", "row_params", "pack_kernel", "dequant",
                                             "zero_f32")})
@@ -840,7 +850,8 @@ def bench_layer(args):
 
     syrk_flop = float(n) * (n + 1) * T
     prep_flop = 4.0 * n ** 3 / 3
-    gemm_flop, in_sweep_flop = trailing_schedule(m, n, B, group)
+    gemm_flop, in_sweep_flop = trailing_schedule(m, n, B, group,
+                                                 torch.cuda.get_device_properties(dev).multi_processor_count)
     sweep_bytes = m * n * (4 + 4 + bits / 8) + 8.0 * m * G + 4.0 * n * B
     ph = {
         "syrk": _phase(phase["hessian"], syrk_flop, "TFLOP/s", PEAK_TF16, ATTAIN_TF16,
@@ -872,7 +883,8 @@ def bench_layer(args):
                                           "source": "bench.py --kernel peaks (HBM read stream)"},
                            "latency_floor_us": [round(n * c / 2.4e3, 1) for c in (20, 50)],
                            "work_note": "m n (4 + 4 + b/8) + 8 m G + 4 n B bytes: V read, E written, codes, "
-                                        "scales and zeros, the factor's diagonal blocks"}
+                                        "scales and zeros, the factor's diagonal blocks; the sweep kernels "
+                                        f"also apply {in_sweep_flop:.4g} flops of the trailing update on MFMA"}
         ph["quantize"]["other_ms"] = round(split["other"], 4)
     achieved = ph["syrk"]["achieved"]
     traffic = traffic_bytes(args.traffic) if args.workload == "attn" else None
