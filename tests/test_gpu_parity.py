@@ -93,9 +93,12 @@ def test_prepare_parity(n):
     Ug = U.cpu().numpy().astype(np.float64)
     assert np.all(np.tril(Ug, -1) == 0)
     rel = np.linalg.norm(Ug - U_ref) / np.linalg.norm(U_ref)
+    # element by element, each row against its own largest entry (measured
+    # at most 3.2e-6 for n <= 6000)
+    row_rel = np.max(np.max(np.abs(Ug - U_ref), axis=1) / np.max(np.abs(U_ref), axis=1))
     resid = np.linalg.norm(Ug.T @ Ug @ Hd - np.eye(n)) / np.sqrt(n)
-    say(f"  U rel err {rel:.3e}  residual {resid:.3e}")
-    assert rel <= 2e-4 and resid <= 2e-3
+    say(f"  U rel err {rel:.3e}  worst row element-wise {row_rel:.3e}  residual {resid:.3e}")
+    assert rel <= 2e-4 and row_rel <= 5e-5 and resid <= 2e-3
 
 
 def test_prepare_in_place_and_failures():
@@ -150,6 +153,8 @@ SWEEP_CASES = [
     (36, 640, 5, 32, 128, "bf16"),    # four groups per block, 5-bit codes straddling words
     (70, 1400, 4, 64, 64, "f16"),     # look-ahead path over a full and a partial 1024-column superblock
     (40, 2600, 3, 0, 128, "f32"),     # three superblocks, the last one ragged (a 40-column block)
+    (40, 4500, 4, 128, 128, "f16"),   # superblock launches: four full 1024-column superblocks and a ragged fifth
+    (24, 4224, 3, 0, 64, "bf16"),     # 64-column blocks: 16 per superblock launch, pending K up to 960
 ]
 
 

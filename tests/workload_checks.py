@@ -90,8 +90,13 @@ def run_job(workload: str, job_index: int, sample_rows: int = 1024, sample_cols:
         U_ref, inf = O.inverse_cholesky_upper(Hd)
         assert inf == 0
         out["u_rel"] = float(np.linalg.norm(Ug - U_ref) / np.linalg.norm(U_ref))
-        say(f"  U rel err vs oracle (from the GPU's H) {out['u_rel']:.3e}")
+        # element by element, each row against its own largest entry (the
+        # factor's rows span several orders of magnitude; measured at most
+        # 2.1e-5, at n = 11008)
+        out["u_row_rel"] = float(np.max(np.max(np.abs(Ug - U_ref), axis=1) / np.max(np.abs(U_ref), axis=1)))
+        say(f"  U rel err vs oracle (from the GPU's H) {out['u_rel']:.3e}, worst row, element-wise {out['u_row_rel']:.3e}")
         assert out["u_rel"] <= 1e-4
+        assert out["u_row_rel"] <= 2e-4
         del U_ref
     v = rng.standard_normal((n, 2))
     r = Hd @ (Ug.T @ (Ug @ v)) - v
