@@ -100,6 +100,10 @@ struct SweepArgs {
   // column, at this block's columns)
   int nblk;
   int wlast;
+  // superblock launches whose flush runs as three bf16 products: the errors
+  // as [E_hi | E_hi | E_lo] bf16 per row (leading dimension 3 SBW), written
+  // instead of E; null otherwise
+  uint16_t* Ecat;
 };
 
 // Lanes-per-row variants: 16 lanes (one DPP row) x 8 columns = 128 columns,
@@ -554,10 +558,25 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
   if (active) {
     // one branch on the output type for the whole row, not one per column
     const bool full = w == NSTEP;
+    if (SBM && a.Ecat) {
+      uint16_t* erow = a.Ecat + r * (3 * SBW) + ecol;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = lr + LPR * k;
-      if (full || c < w) a.E[r * ELD + c] = ek[k];
+      for (int k = 0; k < 8; ++k) {
+        const int c = lr + LPR * k;
+        if (full || c < w) {
+          const uint16_t hi = f32_to_bf16(ek[k]);
+          const uint16_t lo = f32_to_bf16(ek[k] - bf16_to_f32(hi));
+          erow[c] = hi;
+          erow[SBW + c] = hi;
+          erow[2 * SBW + c] = lo;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = lr + LPR * k;
+        if (full || c < w) a.E[r * ELD + c] = ek[k];
+      }
     }
     if (a.Wout) {
       if (a.wdt == 0) {
@@ -912,9 +931,17 @@ dim3 rows_grid(int64_t cols, int64_t rows) {
 inline int64_t dstride_for(int64_t B) { return B <= 32 ? BlockLayout<4>::STRIDE : BlockLayout<16>::STRIDE; }
 inline size_t dblk_bytes(int64_t n, int64_t B) { return (size_t)cdiv(n, B) * (size_t)dstride_for(B) * 4; }
 
+// Then, for the superblock path's flushes as bf16 products: the errors as
+// [E_hi | E_hi | E_lo] [m x 3 SBW] and the split, transposed factor rows
+// [n x 3 SBW], bf16.
+inline size_t x3_bytes(int64_t m, int64_t n) {
+  return align256((size_t)m * 3 * SBW * 2) + align256((size_t)n * 3 * SBW * 2);
+}
+
 size_t quantize_workspace_bytes(int64_t m, int64_t n, int64_t B) {
   if (m < 1 || n < 1 || B < 1) return 0;
-  return align256((size_t)m * n * 4) + align256((size_t)m * n) + align256((size_t)m * ELD * 4) + align256(dblk_bytes(n, B));
+  return align256((size_t)m * n * 4) + align256((size_t)m * n) + align256((size_t)m * ELD * 4) +
+         align256(dblk_bytes(n, B)) + x3_bytes(m, n);
 }
 
 hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, const float* U, int bits,
@@ -928,6 +955,10 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   float* E = (float*)p;
   p += align256((size_t)m * ELD * 4);
   float* Dblk = (float*)p;
+  p += align256(dblk_bytes(n, B));
+  uint16_t* Ecat = (uint16_t*)p;
+  p += align256((size_t)m * 3 * SBW * 2);
+  uint16_t* Bt = (uint16_t*)p;
   const int64_t dstride = dstride_for(B);
   // every block starts on a word boundary of the packed rows: the sweep packs its own codes
   const bool packed = (B * bits) % 32 == 0;
@@ -973,7 +1004,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
                          Z, G, i / group);
     SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, packed ? nullptr : Q8, packed ? qcodes : nullptr, words,
                 bits, write_dequant ? W : nullptr, dt, ldw, E + eoff, err_sq, Dblk + (i / B) * dstride,
-                E + epair, (int)(i - g0), U + g0 * n + i, 1, w};
+                E + epair, (int)(i - g0), U + g0 * n + i, 1, w, nullptr};
     if (B <= 32) launch_sweep<4, false>(a, gmode, st);
     else if (look) launch_sweep<16, true>(a, gmode, st);
     else launch_sweep<16, false>(a, gmode, st);
@@ -1002,12 +1033,16 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
     for (int64_t s0 = 0; s0 < n; s0 += SBW) {
       const int64_t s1 = std::min<int64_t>(s0 + SBW, n);
       const int nblk = (int)cdiv(s1 - s0, B);
+      // the flush past the superblock as three bf16 products (its errors
+      // written as [E_hi | E_hi | E_lo] by the sweep kernel)
       SweepArgs a{U, V, n, m, s0, (int)B, maxq, group, G, S, Z, packed ? nullptr : Q8, packed ? qcodes : nullptr,
                   words, bits, write_dequant ? W : nullptr, dt, ldw, E, err_sq, Dblk + (s0 / B) * dstride,
-                  nullptr, 0, U + s0 * n + s0, nblk, (int)(s1 - s0 - (int64_t)(nblk - 1) * B)};
+                  nullptr, 0, U + s0 * n + s0, nblk, (int)(s1 - s0 - (int64_t)(nblk - 1) * B),
+                  s1 < n ? Ecat : nullptr};
       launch_sweep_sb(a, gmode, st);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if ((e = flush(0, s0, (int)(s1 - s0), s1, n - s1)) != hipSuccess) return e;
+      if (s1 < n && (e = flush_x3(Ecat, 3 * SBW, U, n, s0, (int)(s1 - s0), s1, V, m, Bt, 3 * SBW, st)) != hipSuccess)
+        return e;
     }
   } else if (look) {
     // Look-ahead: LA blocks per flush.  Block t of a group first takes the
