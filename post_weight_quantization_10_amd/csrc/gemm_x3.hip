@@ -57,15 +57,18 @@ __global__ __launch_bounds__(256) void split_t_kernel(const float* U, int64_t n,
 }
 
 // C[M x N] (fp32, leading dimension ldc) -= A[M x K3] Bt[N x K3]^T, both bf16
-// and contiguous along K (leading dimensions lda, ldb), K3 a multiple of XK.
+// and contiguous along K (leading dimensions lda, ldb), K3 = 3 K with K a
+// multiple of XK.  A's three K-segments (hi, hi, lo) start aseg elements
+// apart in each row, so a stage never straddles two of them.
 // 128 x 128 tiles, four waves of 64 x 64 on v_mfma_f32_32x32x16_bf16 (lane l
 // supplies row / column l % 32 and k = 8 (l / 32) .. + 7 of a 16-deep step;
 // accumulator r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column
 // l % 32).  Stages of 64 k move global -> registers -> LDS, double buffered;
 // rows past M or N load the last valid row (never stored).
-__global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restrict__ A, int64_t lda,
-                                                         const uint16_t* __restrict__ Bt, int64_t ldb,
-                                                         float* __restrict__ C, int64_t ldc, int M, int N, int K3) {
+__global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t aseg,
+                                                         int K, const uint16_t* __restrict__ Bt, int64_t ldb,
+                                                         float* __restrict__ C, int64_t ldc, int M, int N) {
+  const int K3 = 3 * K;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][XT * XP];
   const int tN = (N + XT - 1) / XT;
   const int tm = blockIdx.x / tN, tn = blockIdx.x % tN;
@@ -87,9 +90,11 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
   }
   u32x4 ra[4], rb[4];
   auto gload = [&](int k0) {
+    const int seg = k0 / K;
+    const int64_t ak = seg * aseg + (k0 - seg * K);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      ra[e] = *(const u32x4*)(pa[e] + k0);
+      ra[e] = *(const u32x4*)(pa[e] + ak);
       rb[e] = *(const u32x4*)(pb[e] + k0);
     }
   };
@@ -150,21 +155,23 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
 
 }  // namespace
 
-// V[:, c0:n] -= Ecat[:, 0:3K] [U_hi | U_lo | U_hi]^T-of-rows [r0, r0 + K), for
-// m rows (V leading dimension n, Ecat leading dimension lde >= 3K); Bt is
-// scratch of (n - c0) x ldb bf16 with ldb >= 3K.
-hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, const float* U, int64_t n, int64_t r0, int K, int64_t c0,
-                    float* V, int64_t m, uint16_t* Bt, int64_t ldb, hipStream_t s) {
-  const int64_t N = n - c0;
+// V[:, c0:c0+N] -= E_cat U_cat for m rows (V leading dimension n): E_cat's
+// row r holds E_hi, E_hi, E_lo of the K errors at Ecat + r lde, + aseg,
+// + 2 aseg; U_cat is the hi / lo / hi split of U's rows [r0, r0 + K),
+// columns [c0, c0 + N), written transposed to the scratch Bt (N x ldb bf16,
+// ldb >= 3K).  K must be a multiple of 64.
+hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t aseg, const float* U, int64_t n, int64_t r0, int K,
+                    int64_t c0, int64_t N, float* V, int64_t m, uint16_t* Bt, int64_t ldb, hipStream_t s) {
   if (N <= 0 || m <= 0 || K <= 0) return hipSuccess;
-  if ((3 * K) % XK != 0 || lde < 3 * K || ldb < 3 * K || (lde % 8) != 0 || (ldb % 8) != 0 || m > INT32_MAX ||
-      N > INT32_MAX)
+  if (K % XK != 0 || aseg < K || lde < 2 * aseg + K || ldb < 3 * (int64_t)K || (lde % 8) != 0 || (aseg % 8) != 0 ||
+      (ldb % 8) != 0 || (((uintptr_t)Ecat) & 15) != 0 || (((uintptr_t)Bt) & 15) != 0 || m > INT32_MAX ||
+      N > INT32_MAX || c0 + N > n || r0 + K > n)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)cdiv(N, TT), (unsigned)cdiv(K, TT)), dim3(256), 0, s, U, n, r0, K,
                      c0, (int)N, Bt, ldb);
   const int64_t tiles = cdiv(m, XT) * cdiv(N, XT);
-  hipLaunchKernelGGL(gemm_x3_kernel, dim3((unsigned)tiles), dim3(256), 0, s, Ecat, lde, (const uint16_t*)Bt, ldb,
-                     V + c0, n, (int)m, (int)N, 3 * K);
+  hipLaunchKernelGGL(gemm_x3_kernel, dim3((unsigned)tiles), dim3(256), 0, s, Ecat, lde, aseg, K, (const uint16_t*)Bt,
+                     ldb, V + c0, n, (int)m, (int)N);
   return hipGetLastError();
 }
 

@@ -100,9 +100,10 @@ struct SweepArgs {
   // column, at this block's columns)
   int nblk;
   int wlast;
-  // superblock launches whose flush runs as three bf16 products: the errors
-  // as [E_hi | E_hi | E_lo] bf16 per row (leading dimension 3 SBW), written
-  // instead of E; null otherwise
+  // flushes as three bf16 products: the errors as E_hi, E_hi, E_lo bf16 in
+  // three segments SBW apart per row (leading dimension 3 SBW), at this
+  // block's column of its superblock (superblock launches: at the
+  // superblock's first column, and written instead of E); null otherwise
   uint16_t* Ecat;
 };
 
@@ -558,8 +559,8 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
   if (active) {
     // one branch on the output type for the whole row, not one per column
     const bool full = w == NSTEP;
-    if (SBM && a.Ecat) {
-      uint16_t* erow = a.Ecat + r * (3 * SBW) + ecol;
+    if (a.Ecat) {  // also keep E itself on the paired path, whose look-ahead reads it
+      uint16_t* erow = a.Ecat + r * (3 * SBW) + (SBM ? ecol : 0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int c = lr + LPR * k;
@@ -571,7 +572,8 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
           erow[2 * SBW + c] = lo;
         }
       }
-    } else {
+    }
+    if (!SBM || !a.Ecat) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int c = lr + LPR * k;
@@ -995,18 +997,29 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  const bool look = B % 64 == 0 && (group <= 0 || group <= B) && n % 4 == 0;
+  // on the look-ahead paths the flushes run as three bf16 products (the
+  // sweep kernels write the errors split into E_hi, E_hi, E_lo as well);
+  // a flush whose K is not a multiple of 64 (a short last block) stays fp32.
+  // Rows longer than X3_MAX_N stay fp32 too: every column takes the errors of
+  // all earlier superblocks, and at 49152 columns the products' error moved
+  // 0.11 % of the codes (99.89 % identical against 99.96 % in fp32), at
+  // 12288 columns and below it moves none beyond the near-tie band.
+  constexpr int64_t X3_MAX_N = 16384;
+  const bool x3 = look && n <= X3_MAX_N;
+
   // sweep one block [i, i + w) with its errors written at column eoff of E;
   // on the look-ahead path the kpend columns before it (from column g0, their
   // errors at column epair of E) are still to be applied to it
-  auto sweep_block = [&](int64_t i, int w, int eoff, bool look, int64_t g0, int epair) -> hipError_t {
+  auto sweep_block = [&](int64_t i, int w, int eoff, bool la, int64_t g0, int epair) -> hipError_t {
     if (group > B && i % group == 0)
       hipLaunchKernelGGL(row_params_kernel, dim3(prow), dim3(256), 0, st, (const float*)V, m, n, i, group, maxq, S,
                          Z, G, i / group);
     SweepArgs a{U, V, n, m, i, w, maxq, group, G, S, Z, packed ? nullptr : Q8, packed ? qcodes : nullptr, words,
                 bits, write_dequant ? W : nullptr, dt, ldw, E + eoff, err_sq, Dblk + (i / B) * dstride,
-                E + epair, (int)(i - g0), U + g0 * n + i, 1, w, nullptr};
+                E + epair, (int)(i - g0), U + g0 * n + i, 1, w, x3 && la ? Ecat + eoff : nullptr};
     if (B <= 32) launch_sweep<4, false>(a, gmode, st);
-    else if (look) launch_sweep<16, true>(a, gmode, st);
+    else if (la) launch_sweep<16, true>(a, gmode, st);
     else launch_sweep<16, false>(a, gmode, st);
     return hipGetLastError();
   };
@@ -1022,7 +1035,11 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
     return gemm_f32(g, false, false, st);
   };
   // (pending K = t B is a multiple of the 64-row chunks; rows of V 16-byte aligned)
-  const bool look = B % 64 == 0 && (group <= 0 || group <= B) && n % 4 == 0;
+  auto flushx = [&](int ec, int64_t r0, int K, int64_t c0, int64_t N) -> hipError_t {
+    if (N <= 0) return hipSuccess;
+    if (x3 && K % 64 == 0) return flush_x3(Ecat + ec, 3 * SBW, SBW, U, n, r0, K, c0, N, V, m, Bt, 3 * SBW, st);
+    return flush(ec, r0, K, c0, N);
+  };
   // Superblock launches while the rows fit the GPU in one round of one
   // workgroup (16 rows) per CU: each superblock of SBW columns is swept by one
   // launch (every block taking the errors of the superblock's earlier blocks
@@ -1041,7 +1058,8 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
                   s1 < n ? Ecat : nullptr};
       launch_sweep_sb(a, gmode, st);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (s1 < n && (e = flush_x3(Ecat, 3 * SBW, U, n, s0, (int)(s1 - s0), s1, V, m, Bt, 3 * SBW, st)) != hipSuccess)
+      if (s1 < n &&
+          (e = flush_x3(Ecat, 3 * SBW, SBW, U, n, s0, (int)(s1 - s0), s1, n - s1, V, m, Bt, 3 * SBW, st)) != hipSuccess)
         return e;
     }
   } else if (look) {
@@ -1064,10 +1082,10 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
           if ((e = sweep_block(i, w, (int)(i - s0), true, g0, (int)(g0 - s0))) != hipSuccess) return e;
           i += w;
         }
-        if ((e = flush((int)(g0 - s0), g0, (int)(i - g0), i, s1 - i)) != hipSuccess) return e;
+        if ((e = flushx((int)(g0 - s0), g0, (int)(i - g0), i, s1 - i)) != hipSuccess) return e;
         g0 = i;
       }
-      if ((e = flush(0, s0, (int)(s1 - s0), s1, n - s1)) != hipSuccess) return e;
+      if ((e = flushx(0, s0, (int)(s1 - s0), s1, n - s1)) != hipSuccess) return e;
     }
   } else {
     for (int64_t i = 0; i < n; i += B) {
