@@ -1,0 +1,82 @@
+"""Host-side model of every global access of the trailing products run as
+three bf16 products (csrc/gemm_x3.hip, csrc/sweep.hip): the transposing
+split of U's rows, the product's operand loads (rows past M or N clamped to
+the last valid row) and masked stores, and the sweep kernels' split-error
+writes, checked against the buffers quantize_layer carves from its workspace,
+for the tested and configured shapes.  (The kernels' index formulas are
+restated here; a change to them must be mirrored, which is the point.)"""
+import numpy as np
+import pytest
+
+SBW, XT, XK, TT = 1024, 128, 64, 64
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def flushes(m, n, B, superblock):
+    """(ec, r0, K, c0, N) of every flush that runs as bf16 products."""
+    out = []
+    for s0 in range(0, n, SBW):
+        s1 = min(s0 + SBW, n)
+        if not superblock:
+            g0 = s0
+            while g0 < s1:
+                i = g0
+                for _ in range(2):
+                    if i < s1:
+                        i += min(B, s1 - i)
+                if s1 - i > 0 and (i - g0) % 64 == 0:
+                    out.append((g0 - s0, g0, i - g0, i, s1 - i))
+                g0 = i
+        if s1 < n and (s1 - s0) % 64 == 0:
+            out.append((0, s0, s1 - s0, s1, n - s1))
+    return out
+
+
+def check(m, n, B, superblock):
+    lde = ldb = 3 * SBW
+    ecat, bt, vsz, usz = m * 3 * SBW, n * 3 * SBW, m * n, n * n
+    for ec, r0, K, c0, N in flushes(m, n, B, superblock):
+        assert K % XK == 0 and c0 + N <= n and r0 + K <= n
+        # split_t_kernel: reads U rows r0.., columns c0..; writes Bt rows j, columns k, K + k, 2K + k
+        i = np.arange(TT)[:, None]
+        jj = np.arange(TT)[None, :]
+        for bx in range(cdiv(N, TT)):
+            for by in range(cdiv(K, TT)):
+                ok = (by * TT + i < K) & (bx * TT + jj < N)
+                rd = (r0 + by * TT + i) * n + c0 + bx * TT + jj
+                assert rd[ok].min() >= 0 and rd[ok].max() < usz
+                wr = (bx * TT + jj) * ldb + by * TT + i + 2 * K
+                assert wr[ok].max() < bt
+        # gemm_x3_kernel loads: A row min(r, M-1), segment offsets 0, SBW, 2 SBW, 16 bytes each
+        last_a = (m - 1) * lde + ec + 2 * SBW + (K - XK) + 56 + 7
+        last_b = (N - 1) * ldb + (3 * K - XK) + 56 + 7
+        assert last_a < ecat and last_b < bt
+        # masked stores into V's columns c0.. (row < M, column < N)
+        assert (m - 1) * n + c0 + N - 1 < vsz
+    # split-error writes of the sweep kernels: row r, block column (in its superblock) + c, + SBW, + 2 SBW
+    for s0 in range(0, n, SBW):
+        s1 = min(s0 + SBW, n)
+        for i in range(s0, s1, B):
+            w = min(B, s1 - i)
+            assert (m - 1) * 3 * SBW + (i - s0) + w - 1 + 2 * SBW < ecat
+
+
+@pytest.mark.parametrize("m,n,B", [(130, 2048, 128), (70, 1400, 64), (40, 2600, 128), (40, 4500, 128),
+                                   (24, 4224, 64), (256, 1024, 128), (4096, 4096, 128), (4096, 11008, 128)])
+def test_superblock_path_in_bounds(m, n, B):
+    check(m, n, B, superblock=True)
+
+
+@pytest.mark.parametrize("m,n,B", [(33000, 2176, 128), (12288, 4096, 128), (22016, 4096, 128),
+                                   (49152, 12288, 128), (11008, 4096, 128), (300, 100, 64)])
+def test_paired_path_in_bounds(m, n, B):
+    check(m, n, B, superblock=False)
+
+
+def test_short_last_block_stays_fp32():
+    """A flush whose K is not a multiple of 64 is not run as bf16 products."""
+    fl = flushes(40, 1100, 100, superblock=False)
+    assert all(K % 64 == 0 for _, _, K, _, _ in fl)
