@@ -28,6 +28,8 @@ constexpr int XT = 128;         // output tile (rows and columns)
 constexpr int XK = 64;          // K per stage (bf16)
 constexpr int XP = XK + 8;      // LDS pitch of a stage row (bf16): 144 bytes
 constexpr int TT = 64;          // transpose tile
+constexpr int NXCD = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int GB = 8;           // tile rows per band of the tile order
 
 // Bt[j][k], Bt[j][K + k], Bt[j][2K + k] = hi, lo, hi of U[r0 + k][c0 + j]
 // for j < N, k < K (leading dimension ldb): 64 x 64 tiles through LDS, read
@@ -70,8 +72,16 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
                                                          float* __restrict__ C, int64_t ldc, int M, int N) {
   const int K3 = 3 * K;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][XT * XP];
-  const int tN = (N + XT - 1) / XT;
-  const int tm = blockIdx.x / tN, tn = blockIdx.x % tN;
+  const int tN = (N + XT - 1) / XT, tM = (M + XT - 1) / XT;
+  // Tile order: XCD x (workgroup x mod 8) takes tiles [x P, (x + 1) P) of an
+  // order that walks bands of GB tile rows column by column, so the
+  // workgroups resident on one XCD share a few row panels of A and column
+  // panels of Bt in its L2 instead of streaming all of Bt per tile row.
+  const int T = tM * tN, P = (T + NXCD - 1) / NXCD;
+  const int t = (blockIdx.x % NXCD) * P + blockIdx.x / NXCD;
+  if (t >= T) return;  // the grid is NXCD * P workgroups
+  const int band = t / (GB * tN), rows = min(GB, tM - band * GB), within = t - band * GB * tN;
+  const int tm = band * GB + within % rows, tn = within / rows;
   const int r0 = tm * XT, c0 = tn * XT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -170,8 +180,8 @@ hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t aseg, const float
   hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)cdiv(N, TT), (unsigned)cdiv(K, TT)), dim3(256), 0, s, U, n, r0, K,
                      c0, (int)N, Bt, ldb);
   const int64_t tiles = cdiv(m, XT) * cdiv(N, XT);
-  hipLaunchKernelGGL(gemm_x3_kernel, dim3((unsigned)tiles), dim3(256), 0, s, Ecat, lde, aseg, K, (const uint16_t*)Bt,
-                     ldb, V + c0, n, (int)m, (int)N);
+  hipLaunchKernelGGL(gemm_x3_kernel, dim3((unsigned)(NXCD * cdiv(tiles, NXCD))), dim3(256), 0, s, Ecat, lde, aseg, K,
+                     (const uint16_t*)Bt, ldb, V + c0, n, (int)m, (int)N);
   return hipGetLastError();
 }
 

@@ -80,3 +80,25 @@ def test_short_last_block_stays_fp32():
     """A flush whose K is not a multiple of 64 is not run as bf16 products."""
     fl = flushes(40, 1100, 100, superblock=False)
     assert all(K % 64 == 0 for _, _, K, _, _ in fl)
+
+
+def test_tile_order_is_a_bijection():
+    """gemm_x3_kernel's tile order (XCD x takes tiles [x P, (x + 1) P) of an
+    order walking bands of 8 tile rows column by column) covers every tile of
+    the grid exactly once, and workgroups past the tiles exit."""
+    for tM in range(1, 50):
+        for tN in range(1, 30):
+            T = tM * tN
+            P = cdiv(T, 8)
+            seen = set()
+            for b in range(8 * P):
+                t = (b % 8) * P + b // 8
+                if t >= T:
+                    continue
+                band = t // (8 * tN)
+                rows = min(8, tM - band * 8)
+                within = t - band * 8 * tN
+                tm, tn = band * 8 + within % rows, within // rows
+                assert 0 <= tm < tM and 0 <= tn < tN
+                seen.add((tm, tn))
+            assert len(seen) == T
