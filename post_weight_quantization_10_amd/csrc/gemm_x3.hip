@@ -12,11 +12,10 @@
 //   E U ~ E_hi U_hi + E_hi U_lo + E_lo U_hi,
 // every product accumulated in fp32: each term keeps about 16 bits of its
 // operands (the dropped E_lo U_lo and the rounding of the lo parts are about
-// 2^-16 of the term).  The three products are one bf16 product with
-// K' = 3K over the concatenations A = [E_hi | E_hi | E_lo] (rows of E,
-// written so by the superblock sweep kernel) and Bt = [U_hi | U_lo | U_hi]^T
-// (columns of U's rows r0.., transposed here so that both operands are
-// contiguous along K).
+// 2^-16 of the term).  E's rows hold [E_hi | E_lo] (written so by the
+// superblock sweep kernel); U's rows r0.. are split and transposed here into
+// Bt = [U_hi | U_lo]^T, so that both operands are contiguous along K.  Each
+// K stage loads the four panels once and runs the three products on them.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -31,7 +30,7 @@ constexpr int TT = 64;          // transpose tile
 constexpr int NXCD = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int GB = 8;           // tile rows per band of the tile order
 
-// Bt[j][k], Bt[j][K + k], Bt[j][2K + k] = hi, lo, hi of U[r0 + k][c0 + j]
+// Bt[j][k], Bt[j][K + k] = hi, lo of U[r0 + k][c0 + j]
 // for j < N, k < K (leading dimension ldb): 64 x 64 tiles through LDS, read
 // along U's rows, written along Bt's rows.
 __global__ __launch_bounds__(256) void split_t_kernel(const float* U, int64_t n, int64_t r0, int K, int64_t c0, int N,
@@ -53,25 +52,26 @@ __global__ __launch_bounds__(256) void split_t_kernel(const float* U, int64_t n,
       uint16_t* row = Bt + (int64_t)(j0 + jj) * ldb + k0 + i;
       row[0] = hi;
       row[K] = lo;
-      row[2 * K] = hi;
     }
   }
 }
 
-// C[M x N] (fp32, leading dimension ldc) -= A[M x K3] Bt[N x K3]^T, both bf16
-// and contiguous along K (leading dimensions lda, ldb), K3 = 3 K with K a
-// multiple of XK.  A's three K-segments (hi, hi, lo) start aseg elements
-// apart in each row, so a stage never straddles two of them.
+// C[M x N] (fp32, leading dimension ldc) -= A_hi Bt_hi^T + A_hi Bt_lo^T +
+// A_lo Bt_hi^T over K (a multiple of XK), all operands bf16 and contiguous
+// along K: row r of A_hi at A + r lda, of A_lo alo elements further; row j of
+// Bt_hi at Bt + j ldb, of Bt_lo blo elements further.
 // 128 x 128 tiles, four waves of 64 x 64 on v_mfma_f32_32x32x16_bf16 (lane l
 // supplies row / column l % 32 and k = 8 (l / 32) .. + 7 of a 16-deep step;
 // accumulator r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column
-// l % 32).  Stages of 64 k move global -> registers -> LDS, double buffered;
-// rows past M or N load the last valid row (never stored).
-__global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t aseg,
+// l % 32).  A stage of 64 k holds the four panels (72 KiB of LDS, two
+// workgroups per CU); the next stage's panels are loaded into registers while
+// the current one is multiplied, then stored between two barriers.  Rows past
+// M or N load the last valid row (never stored).
+__global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t alo,
                                                          int K, const uint16_t* __restrict__ Bt, int64_t ldb,
-                                                         float* __restrict__ C, int64_t ldc, int M, int N) {
-  const int K3 = 3 * K;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][XT * XP];
+                                                         int64_t blo, float* __restrict__ C, int64_t ldc, int M,
+                                                         int N) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4][XT * XP];  // A_hi, A_lo, Bt_hi, Bt_lo
   const int tN = (N + XT - 1) / XT, tM = (M + XT - 1) / XT;
   // Tile order: XCD x (workgroup x mod 8) takes tiles [x P, (x + 1) P) of an
   // order that walks bands of GB tile rows column by column, so the
@@ -86,8 +86,8 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
 
-  // loader: chunk q = tid + 256 e (e < 4) of each operand's stage is row
-  // q / 8, 16-byte piece q % 8 of that row's 64 k
+  // loader: chunk q = tid + 256 e (e < 4) of each panel's stage is row q / 8,
+  // 16-byte piece q % 8 of that row's 64 k
   const uint16_t* pa[4];
   const uint16_t* pb[4];
   int lo_[4];
@@ -98,21 +98,23 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
     pb[e] = Bt + (int64_t)min(c0 + row, N - 1) * ldb + 8 * c8;
     lo_[e] = row * XP + 8 * c8;
   }
-  u32x4 ra[4], rb[4];
+  u32x4 rah[4], ral[4], rbh[4], rbl[4];
   auto gload = [&](int k0) {
-    const int seg = k0 / K;
-    const int64_t ak = seg * aseg + (k0 - seg * K);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      ra[e] = *(const u32x4*)(pa[e] + ak);
-      rb[e] = *(const u32x4*)(pb[e] + k0);
+      rah[e] = *(const u32x4*)(pa[e] + k0);
+      ral[e] = *(const u32x4*)(pa[e] + alo + k0);
+      rbh[e] = *(const u32x4*)(pb[e] + k0);
+      rbl[e] = *(const u32x4*)(pb[e] + blo + k0);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&]() {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      *(u32x4*)(&lds[buf][0][lo_[e]]) = ra[e];
-      *(u32x4*)(&lds[buf][1][lo_[e]]) = rb[e];
+      *(u32x4*)(&lds[0][lo_[e]]) = rah[e];
+      *(u32x4*)(&lds[1][lo_[e]]) = ral[e];
+      *(u32x4*)(&lds[2][lo_[e]]) = rbh[e];
+      *(u32x4*)(&lds[3][lo_[e]]) = rbl[e];
     }
   };
 
@@ -122,33 +124,46 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
+  const int arow = (wr * 64 + (lane & 31)) * XP, brow = (wc * 64 + (lane & 31)) * XP;
   gload(0);
-  lstore(0);
+  lstore();
   __syncthreads();
-  int buf = 0;
-  for (int k0 = 0; k0 < K3; k0 += XK) {
-    const bool more = k0 + XK < K3;
+  for (int k0 = 0; k0 < K; k0 += XK) {
+    const bool more = k0 + XK < K;
     if (more) gload(k0 + XK);
-    const uint16_t* Ta = lds[buf][0];
-    const uint16_t* Tb = lds[buf][1];
 #pragma unroll
     for (int ks = 0; ks < XK / 16; ++ks) {
       const int kk = 16 * ks + 8 * (lane >> 5);
-      u32x4 av[2], bv[2];
+      bf16x8 ah[2], al[2], bh[2], bl[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) av[mb] = *(const u32x4*)(Ta + (wr * 64 + mb * 32 + (lane & 31)) * XP + kk);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) bv[nb] = *(const u32x4*)(Tb + (wc * 64 + nb * 32 + (lane & 31)) * XP + kk);
+      for (int h = 0; h < 2; ++h) {
+        ah[h] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lds[0][arow + 32 * h * XP + kk]));
+        al[h] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lds[1][arow + 32 * h * XP + kk]));
+        bh[h] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lds[2][brow + 32 * h * XP + kk]));
+        bl[h] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lds[3][brow + 32 * h * XP + kk]));
+      }
+      // four independent accumulators between two products into the same one
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[mb]),
-                                                               __builtin_bit_cast(bf16x8, bv[nb]), acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl[nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
     }
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    if (more) {
+      __syncthreads();  // every wave is done with this stage
+      lstore();
+      __syncthreads();  // the next stage is visible
+    }
   }
 
 #pragma unroll
@@ -165,23 +180,23 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
 
 }  // namespace
 
-// V[:, c0:c0+N] -= E_cat U_cat for m rows (V leading dimension n): E_cat's
-// row r holds E_hi, E_hi, E_lo of the K errors at Ecat + r lde, + aseg,
-// + 2 aseg; U_cat is the hi / lo / hi split of U's rows [r0, r0 + K),
-// columns [c0, c0 + N), written transposed to the scratch Bt (N x ldb bf16,
-// ldb >= 3K).  K must be a multiple of 64.
-hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t aseg, const float* U, int64_t n, int64_t r0, int K,
+// V[:, c0:c0+N] -= E U[r0:r0+K, c0:c0+N] for m rows (V leading dimension
+// n) as three bf16 products: row r of E holds E_hi at Ecat + r lde and E_lo
+// alo elements further; U's rows [r0, r0 + K), columns [c0, c0 + N) are split
+// into hi / lo and written transposed to the scratch Bt (N rows of ldb bf16,
+// ldb >= 2K: hi at 0, lo at K).  K must be a multiple of 64.
+hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t alo, const float* U, int64_t n, int64_t r0, int K,
                     int64_t c0, int64_t N, float* V, int64_t m, uint16_t* Bt, int64_t ldb, hipStream_t s) {
   if (N <= 0 || m <= 0 || K <= 0) return hipSuccess;
-  if (K % XK != 0 || aseg < K || lde < 2 * aseg + K || ldb < 3 * (int64_t)K || (lde % 8) != 0 || (aseg % 8) != 0 ||
+  if (K % XK != 0 || alo < K || lde < alo + K || ldb < 2 * (int64_t)K || (lde % 8) != 0 || (alo % 8) != 0 ||
       (ldb % 8) != 0 || (((uintptr_t)Ecat) & 15) != 0 || (((uintptr_t)Bt) & 15) != 0 || m > INT32_MAX ||
       N > INT32_MAX || c0 + N > n || r0 + K > n)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)cdiv(N, TT), (unsigned)cdiv(K, TT)), dim3(256), 0, s, U, n, r0, K,
                      c0, (int)N, Bt, ldb);
   const int64_t tiles = cdiv(m, XT) * cdiv(N, XT);
-  hipLaunchKernelGGL(gemm_x3_kernel, dim3((unsigned)(NXCD * cdiv(tiles, NXCD))), dim3(256), 0, s, Ecat, lde, aseg, K,
-                     (const uint16_t*)Bt, ldb, V + c0, n, (int)m, (int)N);
+  hipLaunchKernelGGL(gemm_x3_kernel, dim3((unsigned)(NXCD * cdiv(tiles, NXCD))), dim3(256), 0, s, Ecat, lde, alo, K,
+                     (const uint16_t*)Bt, ldb, (int64_t)K, V + c0, n, (int)m, (int)N);
   return hipGetLastError();
 }
 

@@ -48,10 +48,10 @@ hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s);
 int device_cus();
 
 // A trailing update V[:, c0:c0+N] -= E U[r0:r0+K, c0:c0+N] as three bf16
-// products (gemm_x3.hip): E given as E_hi, E_hi, E_lo segments aseg apart in
-// each row of Ecat, U split and transposed into the scratch Bt
-// (N x ldb bf16); K a multiple of 64.
-hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t aseg, const float* U, int64_t n, int64_t r0, int K,
+// products (gemm_x3.hip): row r of E given as E_hi at Ecat + r lde and E_lo
+// alo elements further, U split and transposed into the scratch Bt
+// (N x ldb bf16, ldb >= 2K); K a multiple of 64.
+hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t alo, const float* U, int64_t n, int64_t r0, int K,
                     int64_t c0, int64_t N, float* V, int64_t m, uint16_t* Bt, int64_t ldb, hipStream_t s);
 
 }  // namespace gptq

@@ -100,8 +100,8 @@ struct SweepArgs {
   // column, at this block's columns)
   int nblk;
   int wlast;
-  // flushes as three bf16 products: the errors as E_hi, E_hi, E_lo bf16 in
-  // three segments SBW apart per row (leading dimension 3 SBW), at this
+  // flushes as three bf16 products: the errors as E_hi, E_lo bf16 in two
+  // segments SBW apart per row (leading dimension 2 SBW), at this
   // block's column of its superblock (superblock launches: at the
   // superblock's first column, and written instead of E); null otherwise
   uint16_t* Ecat;
@@ -560,7 +560,7 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
     // one branch on the output type for the whole row, not one per column
     const bool full = w == NSTEP;
     if (a.Ecat) {  // also keep E itself on the paired path, whose look-ahead reads it
-      uint16_t* erow = a.Ecat + r * (3 * SBW) + (SBM ? ecol : 0);
+      uint16_t* erow = a.Ecat + r * (2 * SBW) + (SBM ? ecol : 0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int c = lr + LPR * k;
@@ -568,8 +568,7 @@ __device__ __forceinline__ void sweep_block_body(const SweepArgs& a, const Sweep
           const uint16_t hi = f32_to_bf16(ek[k]);
           const uint16_t lo = f32_to_bf16(ek[k] - bf16_to_f32(hi));
           erow[c] = hi;
-          erow[SBW + c] = hi;
-          erow[2 * SBW + c] = lo;
+          erow[SBW + c] = lo;
         }
       }
     }
@@ -934,10 +933,10 @@ inline int64_t dstride_for(int64_t B) { return B <= 32 ? BlockLayout<4>::STRIDE 
 inline size_t dblk_bytes(int64_t n, int64_t B) { return (size_t)cdiv(n, B) * (size_t)dstride_for(B) * 4; }
 
 // Then, for the superblock path's flushes as bf16 products: the errors as
-// [E_hi | E_hi | E_lo] [m x 3 SBW] and the split, transposed factor rows
-// [n x 3 SBW], bf16.
+// [E_hi | E_lo] [m x 2 SBW] and the split, transposed factor rows
+// [n x 2 SBW], bf16.
 inline size_t x3_bytes(int64_t m, int64_t n) {
-  return align256((size_t)m * 3 * SBW * 2) + align256((size_t)n * 3 * SBW * 2);
+  return align256((size_t)m * 2 * SBW * 2) + align256((size_t)n * 2 * SBW * 2);
 }
 
 size_t quantize_workspace_bytes(int64_t m, int64_t n, int64_t B) {
@@ -959,7 +958,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   float* Dblk = (float*)p;
   p += align256(dblk_bytes(n, B));
   uint16_t* Ecat = (uint16_t*)p;
-  p += align256((size_t)m * 3 * SBW * 2);
+  p += align256((size_t)m * 2 * SBW * 2);
   uint16_t* Bt = (uint16_t*)p;
   const int64_t dstride = dstride_for(B);
   // every block starts on a word boundary of the packed rows: the sweep packs its own codes
@@ -999,7 +998,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
 
   const bool look = B % 64 == 0 && (group <= 0 || group <= B) && n % 4 == 0;
   // on the look-ahead paths the flushes run as three bf16 products (the
-  // sweep kernels write the errors split into E_hi, E_hi, E_lo as well);
+  // sweep kernels write the errors split into E_hi and E_lo as well);
   // a flush whose K is not a multiple of 64 (a short last block) stays fp32.
   // Rows longer than X3_MAX_N stay fp32 too: every column takes the errors of
   // all earlier superblocks, and at 49152 columns the products' error moved
@@ -1037,7 +1036,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   // (pending K = t B is a multiple of the 64-row chunks; rows of V 16-byte aligned)
   auto flushx = [&](int ec, int64_t r0, int K, int64_t c0, int64_t N) -> hipError_t {
     if (N <= 0) return hipSuccess;
-    if (x3 && K % 64 == 0) return flush_x3(Ecat + ec, 3 * SBW, SBW, U, n, r0, K, c0, N, V, m, Bt, 3 * SBW, st);
+    if (x3 && K % 64 == 0) return flush_x3(Ecat + ec, 2 * SBW, SBW, U, n, r0, K, c0, N, V, m, Bt, 2 * SBW, st);
     return flush(ec, r0, K, c0, N);
   };
   // Superblock launches while the rows fit the GPU in one round of one
@@ -1051,7 +1050,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
       const int64_t s1 = std::min<int64_t>(s0 + SBW, n);
       const int nblk = (int)cdiv(s1 - s0, B);
       // the flush past the superblock as three bf16 products (its errors
-      // written as [E_hi | E_hi | E_lo] by the sweep kernel)
+      // written as [E_hi | E_lo] by the sweep kernel)
       SweepArgs a{U, V, n, m, s0, (int)B, maxq, group, G, S, Z, packed ? nullptr : Q8, packed ? qcodes : nullptr,
                   words, bits, write_dequant ? W : nullptr, dt, ldw, E, err_sq, Dblk + (s0 / B) * dstride,
                   nullptr, 0, U + s0 * n + s0, nblk, (int)(s1 - s0 - (int64_t)(nblk - 1) * B),
@@ -1059,7 +1058,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
       launch_sweep_sb(a, gmode, st);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (s1 < n &&
-          (e = flush_x3(Ecat, 3 * SBW, SBW, U, n, s0, (int)(s1 - s0), s1, n - s1, V, m, Bt, 3 * SBW, st)) != hipSuccess)
+          (e = flush_x3(Ecat, 2 * SBW, SBW, U, n, s0, (int)(s1 - s0), s1, n - s1, V, m, Bt, 2 * SBW, st)) != hipSuccess)
         return e;
     }
   } else if (look) {

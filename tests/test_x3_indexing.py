@@ -1,7 +1,7 @@
 """Host-side model of every global access of the trailing products run as
 three bf16 products (csrc/gemm_x3.hip, csrc/sweep.hip): the transposing
-split of U's rows, the product's operand loads (rows past M or N clamped to
-the last valid row) and masked stores, and the sweep kernels' split-error
+split of U's rows into hi and lo, the product's operand loads (rows past M or
+N clamped to the last valid row), its LDS panels and masked stores, and the sweep kernels' split-error
 writes, checked against the buffers quantize_layer carves from its workspace,
 for the tested and configured shapes.  (The kernels' index formulas are
 restated here; a change to them must be mirrored, which is the point.)"""
@@ -36,11 +36,12 @@ def flushes(m, n, B, superblock):
 
 
 def check(m, n, B, superblock):
-    lde = ldb = 3 * SBW
-    ecat, bt, vsz, usz = m * 3 * SBW, n * 3 * SBW, m * n, n * n
+    lde = ldb = 2 * SBW
+    ecat, bt, vsz, usz = m * 2 * SBW, n * 2 * SBW, m * n, n * n
     for ec, r0, K, c0, N in flushes(m, n, B, superblock):
         assert K % XK == 0 and c0 + N <= n and r0 + K <= n
-        # split_t_kernel: reads U rows r0.., columns c0..; writes Bt rows j, columns k, K + k, 2K + k
+        assert ldb >= 2 * K
+        # split_t_kernel: reads U rows r0.., columns c0..; writes Bt rows j, columns k and K + k
         i = np.arange(TT)[:, None]
         jj = np.arange(TT)[None, :]
         for bx in range(cdiv(N, TT)):
@@ -48,20 +49,39 @@ def check(m, n, B, superblock):
                 ok = (by * TT + i < K) & (bx * TT + jj < N)
                 rd = (r0 + by * TT + i) * n + c0 + bx * TT + jj
                 assert rd[ok].min() >= 0 and rd[ok].max() < usz
-                wr = (bx * TT + jj) * ldb + by * TT + i + 2 * K
+                wr = (bx * TT + jj) * ldb + by * TT + i + K
                 assert wr[ok].max() < bt
-        # gemm_x3_kernel loads: A row min(r, M-1), segment offsets 0, SBW, 2 SBW, 16 bytes each
-        last_a = (m - 1) * lde + ec + 2 * SBW + (K - XK) + 56 + 7
-        last_b = (N - 1) * ldb + (3 * K - XK) + 56 + 7
+        # gemm_x3_kernel loads: A row min(r, M-1) at ec (hi) and ec + SBW (lo),
+        # Bt row min(j, N-1) at 0 (hi) and K (lo), 16 bytes at k0 + 8 c8
+        last_a = (m - 1) * lde + ec + SBW + (K - XK) + 56 + 7
+        last_b = (N - 1) * ldb + K + (K - XK) + 56 + 7
         assert last_a < ecat and last_b < bt
+        assert ec + K <= SBW  # the hi segment does not run into the lo one
         # masked stores into V's columns c0.. (row < M, column < N)
         assert (m - 1) * n + c0 + N - 1 < vsz
-    # split-error writes of the sweep kernels: row r, block column (in its superblock) + c, + SBW, + 2 SBW
+    # split-error writes of the sweep kernels: row r, block column (in its superblock) + c, + SBW
     for s0 in range(0, n, SBW):
         s1 = min(s0 + SBW, n)
         for i in range(s0, s1, B):
             w = min(B, s1 - i)
-            assert (m - 1) * 3 * SBW + (i - s0) + w - 1 + 2 * SBW < ecat
+            assert (m - 1) * 2 * SBW + (i - s0) + w - 1 + SBW < ecat
+
+
+def test_lds_indexes_in_bounds():
+    """gemm_x3_kernel's four LDS panels of XT rows x XP bf16: the stores
+    (row q / 8, piece q % 8) and the fragment reads (row 64 wr + 32 h + l % 32,
+    k 16 ks + 8 (l / 32) .. + 7) stay inside a panel."""
+    XP = XK + 8
+    q = np.arange(1024)
+    st = (q >> 3) * XP + 8 * (q & 7) + 7
+    assert st.max() < XT * XP
+    lane = np.arange(64)
+    for wr in range(2):
+        for h in range(2):
+            for ks in range(XK // 16):
+                rd = (wr * 64 + (lane & 31)) * XP + 32 * h * XP + 16 * ks + 8 * (lane >> 5) + 7
+                assert rd.max() < XT * XP
+    assert 4 * XT * XP * 2 * 2 <= 160 * 1024  # two workgroups per CU
 
 
 @pytest.mark.parametrize("m,n,B", [(130, 2048, 128), (70, 1400, 64), (40, 2600, 128), (40, 4500, 128),
