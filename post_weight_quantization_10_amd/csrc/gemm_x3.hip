@@ -13,9 +13,10 @@
 // every product accumulated in fp32: each term keeps about 16 bits of its
 // operands (the dropped E_lo U_lo and the rounding of the lo parts are about
 // 2^-16 of the term).  E's rows hold [E_hi | E_lo] (written so by the
-// superblock sweep kernel); U's rows r0.. are split and transposed here into
-// Bt = [U_hi | U_lo]^T, so that both operands are contiguous along K.  Each
-// K stage loads the four panels once and runs the three products on them.
+// superblock sweep kernel); U is split and transposed once per layer into
+// Ut = [U_hi | U_lo]^T, so that both operands are contiguous along K, and
+// every flush reads its factor rows from there.  Each K stage loads the four
+// panels once and runs the three products on them.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -30,28 +31,31 @@ constexpr int TT = 64;          // transpose tile
 constexpr int NXCD = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int GB = 8;           // tile rows per band of the tile order
 
-// Bt[j][k], Bt[j][K + k] = hi, lo of U[r0 + k][c0 + j]
-// for j < N, k < K (leading dimension ldb): 64 x 64 tiles through LDS, read
-// along U's rows, written along Bt's rows.
-__global__ __launch_bounds__(256) void split_t_kernel(const float* U, int64_t n, int64_t r0, int K, int64_t c0, int N,
-                                                      uint16_t* Bt, int64_t ldb) {
+// Ut[j][k], Ut[j][n + k] = hi, lo of U[k][j] (rows of ldu bf16): 64 x 64
+// tiles through LDS, read along U's rows, written along Ut's rows.  A flush
+// reads only entries whose row k lies in an earlier granule (of gran
+// columns: the flushes' factor rows end at a granule boundary at or before
+// their first column), so every other tile is skipped.
+__global__ __launch_bounds__(256) void split_t_kernel(const float* U, int64_t n, uint16_t* Ut, int64_t ldu,
+                                                      int64_t gran) {
   __shared__ float t[TT][TT + 1];
-  const int j0 = blockIdx.x * TT, k0 = blockIdx.y * TT;
+  const int64_t j0 = (int64_t)blockIdx.x * TT, k0 = (int64_t)blockIdx.y * TT;
+  if (k0 / gran >= j0 / gran) return;
   const int tid = threadIdx.x;
   for (int e = tid; e < TT * TT; e += 256) {
-    const int i = e / TT, jj = e % TT;  // row k0 + i of the slice, column j0 + jj
-    t[i][jj] = (k0 + i < K && j0 + jj < N) ? U[(r0 + k0 + i) * n + c0 + j0 + jj] : 0.f;
+    const int i = e / TT, jj = e % TT;  // row k0 + i of U, column j0 + jj
+    t[i][jj] = (k0 + i < n && j0 + jj < n) ? U[(k0 + i) * n + j0 + jj] : 0.f;
   }
   __syncthreads();
   for (int e = tid; e < TT * TT; e += 256) {
     const int jj = e / TT, i = e % TT;
-    if (k0 + i < K && j0 + jj < N) {
+    if (k0 + i < n && j0 + jj < n) {
       const float u = t[i][jj];
       const uint16_t hi = f32_to_bf16(u);
       const uint16_t lo = f32_to_bf16(u - bf16_to_f32(hi));
-      uint16_t* row = Bt + (int64_t)(j0 + jj) * ldb + k0 + i;
+      uint16_t* row = Ut + (j0 + jj) * ldu + k0 + i;
       row[0] = hi;
-      row[K] = lo;
+      row[n] = lo;
     }
   }
 }
@@ -180,23 +184,36 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
 
 }  // namespace
 
-// V[:, c0:c0+N] -= E U[r0:r0+K, c0:c0+N] for m rows (V leading dimension
-// n) as three bf16 products: row r of E holds E_hi at Ecat + r lde and E_lo
-// alo elements further; U's rows [r0, r0 + K), columns [c0, c0 + N) are split
-// into hi / lo and written transposed to the scratch Bt (N rows of ldb bf16,
-// ldb >= 2K: hi at 0, lo at K).  K must be a multiple of 64.
-hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t alo, const float* U, int64_t n, int64_t r0, int K,
-                    int64_t c0, int64_t N, float* V, int64_t m, uint16_t* Bt, int64_t ldb, hipStream_t s) {
-  if (N <= 0 || m <= 0 || K <= 0) return hipSuccess;
-  if (K % XK != 0 || alo < K || lde < alo + K || ldb < 2 * (int64_t)K || (lde % 8) != 0 || (alo % 8) != 0 ||
-      (ldb % 8) != 0 || (((uintptr_t)Ecat) & 15) != 0 || (((uintptr_t)Bt) & 15) != 0 || m > INT32_MAX ||
-      N > INT32_MAX || c0 + N > n || r0 + K > n)
+// Ut (n rows of 2n bf16) = [U_hi | U_lo]^T of the n x n factor U, the part
+// above the diagonal blocks of gran columns (a multiple of 64) that the
+// flushes read; n a multiple of 4.
+hipError_t split_ut_x3(const float* U, int64_t n, uint16_t* Ut, int64_t gran, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4 != 0 || gran <= 0 || gran % TT != 0 || (((uintptr_t)Ut) & 15) != 0 || cdiv(n, TT) > INT32_MAX)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)cdiv(N, TT), (unsigned)cdiv(K, TT)), dim3(256), 0, s, U, n, r0, K,
-                     c0, (int)N, Bt, ldb);
+  hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)cdiv(n, TT), (unsigned)cdiv(n, TT)), dim3(256), 0, s, U, n, Ut,
+                     2 * n, gran);
+  return hipGetLastError();
+}
+
+// V[:, c0:c0+N] -= E U[r0:r0+K, c0:c0+N] for m rows (V leading dimension n)
+// as three bf16 products: row r of E holds E_hi at Ecat + r lde and E_lo alo
+// elements further; the factor comes split from split_ut_x3 (row j of Ut:
+// hi of U[:, j] at Ut + 2n j, lo n elements further), and the flush reads
+// only its rows [r0, r0 + K), which must end at a boundary of that split's
+// granules at or before its first column c0.  K and r0 must be multiples
+// of 64.
+hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t alo, const uint16_t* Ut, int64_t n, int64_t r0,
+                    int K, int64_t c0, int64_t N, float* V, int64_t m, hipStream_t s) {
+  if (N <= 0 || m <= 0 || K <= 0) return hipSuccess;
+  if (K % XK != 0 || r0 % XK != 0 || alo < K || lde < alo + K || (lde % 8) != 0 || (alo % 8) != 0 || n % 4 != 0 ||
+      (((uintptr_t)Ecat) & 15) != 0 || (((uintptr_t)Ut) & 15) != 0 || m > INT32_MAX || N > INT32_MAX ||
+      c0 + N > n || r0 + K > c0)
+    return hipErrorInvalidValue;
+  const int64_t ldu = 2 * n;
   const int64_t tiles = cdiv(m, XT) * cdiv(N, XT);
   hipLaunchKernelGGL(gemm_x3_kernel, dim3((unsigned)(NXCD * cdiv(tiles, NXCD))), dim3(256), 0, s, Ecat, lde, alo, K,
-                     (const uint16_t*)Bt, ldb, (int64_t)K, V + c0, n, (int)m, (int)N);
+                     Ut + c0 * ldu + r0, ldu, n, V + c0, n, (int)m, (int)N);
   return hipGetLastError();
 }
 

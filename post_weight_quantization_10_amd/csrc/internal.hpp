@@ -47,11 +47,17 @@ hipError_t gemm_f32(const GemmDesc& d, bool transA, bool transB, hipStream_t s);
 // Compute units of the current device (256 if the query fails), read once.
 int device_cus();
 
+// The factor split for the trailing updates as three bf16 products
+// (gemm_x3.hip): Ut (n rows of 2n bf16, 16-byte aligned) = [U_hi | U_lo]^T
+// above the diagonal blocks of gran columns (a multiple of 64); n a
+// multiple of 4.
+hipError_t split_ut_x3(const float* U, int64_t n, uint16_t* Ut, int64_t gran, hipStream_t s);
+
 // A trailing update V[:, c0:c0+N] -= E U[r0:r0+K, c0:c0+N] as three bf16
-// products (gemm_x3.hip): row r of E given as E_hi at Ecat + r lde and E_lo
-// alo elements further, U split and transposed into the scratch Bt
-// (N x ldb bf16, ldb >= 2K); K a multiple of 64.
-hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t alo, const float* U, int64_t n, int64_t r0, int K,
-                    int64_t c0, int64_t N, float* V, int64_t m, uint16_t* Bt, int64_t ldb, hipStream_t s);
+// products: row r of E given as E_hi at Ecat + r lde and E_lo alo elements
+// further, U as split by split_ut_x3 (rows [r0, r0 + K) ending at one of its
+// granule boundaries, at or before c0); K and r0 multiples of 64.
+hipError_t flush_x3(const uint16_t* Ecat, int64_t lde, int64_t alo, const uint16_t* Ut, int64_t n, int64_t r0,
+                    int K, int64_t c0, int64_t N, float* V, int64_t m, hipStream_t s);
 
 }  // namespace gptq

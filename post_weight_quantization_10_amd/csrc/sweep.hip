@@ -932,11 +932,16 @@ dim3 rows_grid(int64_t cols, int64_t rows) {
 inline int64_t dstride_for(int64_t B) { return B <= 32 ? BlockLayout<4>::STRIDE : BlockLayout<16>::STRIDE; }
 inline size_t dblk_bytes(int64_t n, int64_t B) { return (size_t)cdiv(n, B) * (size_t)dstride_for(B) * 4; }
 
-// Then, for the superblock path's flushes as bf16 products: the errors as
-// [E_hi | E_lo] [m x 2 SBW] and the split, transposed factor rows
-// [n x 2 SBW], bf16.
+// Rows up to X3_MAX_N columns run their trailing products as three bf16
+// products (the reason for the limit is given where quantize_layer decides).
+constexpr int64_t X3_MAX_N = 16384;
+
+// Then, for the flushes as bf16 products: the errors as [E_hi | E_lo]
+// [m x 2 SBW] and the factor split and transposed once, [U_hi | U_lo]^T
+// [n x 2n], bf16 (none past X3_MAX_N columns).
 inline size_t x3_bytes(int64_t m, int64_t n) {
-  return align256((size_t)m * 2 * SBW * 2) + align256((size_t)n * 2 * SBW * 2);
+  if (n > X3_MAX_N) return 0;
+  return align256((size_t)m * 2 * SBW * 2) + align256((size_t)n * 2 * n * 2);
 }
 
 size_t quantize_workspace_bytes(int64_t m, int64_t n, int64_t B) {
@@ -957,9 +962,9 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   p += align256((size_t)m * ELD * 4);
   float* Dblk = (float*)p;
   p += align256(dblk_bytes(n, B));
-  uint16_t* Ecat = (uint16_t*)p;
+  uint16_t* Ecat = (uint16_t*)p;  // Ecat and Ut only when n <= X3_MAX_N
   p += align256((size_t)m * 2 * SBW * 2);
-  uint16_t* Bt = (uint16_t*)p;
+  uint16_t* Ut = (uint16_t*)p;
   const int64_t dstride = dstride_for(B);
   // every block starts on a word boundary of the packed rows: the sweep packs its own codes
   const bool packed = (B * bits) % 32 == 0;
@@ -998,14 +1003,18 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
 
   const bool look = B % 64 == 0 && (group <= 0 || group <= B) && n % 4 == 0;
   // on the look-ahead paths the flushes run as three bf16 products (the
-  // sweep kernels write the errors split into E_hi and E_lo as well);
-  // a flush whose K is not a multiple of 64 (a short last block) stays fp32.
+  // sweep kernels write the errors split into E_hi and E_lo as well, and
+  // the factor is split once, here); a flush whose K is not a multiple of
+  // 64 (a short last block) stays fp32.
   // Rows longer than X3_MAX_N stay fp32 too: every column takes the errors of
   // all earlier superblocks, and at 49152 columns the products' error moved
   // 0.11 % of the codes (99.89 % identical against 99.96 % in fp32), at
   // 12288 columns and below it moves none beyond the near-tie band.
-  constexpr int64_t X3_MAX_N = 16384;
   const bool x3 = look && n <= X3_MAX_N;
+  // superblock launches (below) flush only past whole superblocks; the
+  // paired blocks flush past every 64-column multiple
+  const bool sb = look && cdiv(m, 16) <= device_cus();
+  if (x3 && (e = split_ut_x3(U, n, Ut, sb ? SBW : 64, st)) != hipSuccess) return e;
 
   // sweep one block [i, i + w) with its errors written at column eoff of E;
   // on the look-ahead path the kpend columns before it (from column g0, their
@@ -1036,7 +1045,7 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   // (pending K = t B is a multiple of the 64-row chunks; rows of V 16-byte aligned)
   auto flushx = [&](int ec, int64_t r0, int K, int64_t c0, int64_t N) -> hipError_t {
     if (N <= 0) return hipSuccess;
-    if (x3 && K % 64 == 0) return flush_x3(Ecat + ec, 2 * SBW, SBW, U, n, r0, K, c0, N, V, m, Bt, 2 * SBW, st);
+    if (x3 && K % 64 == 0) return flush_x3(Ecat + ec, 2 * SBW, SBW, Ut, n, r0, K, c0, N, V, m, st);
     return flush(ec, r0, K, c0, N);
   };
   // Superblock launches while the rows fit the GPU in one round of one
@@ -1044,22 +1053,20 @@ hipError_t quantize_layer(void* W, int dt, int64_t m, int64_t n, int64_t ldw, co
   // launch (every block taking the errors of the superblock's earlier blocks
   // inside the kernel), then one product brings the rest of the row up to
   // date.
-  const bool sb = look && cdiv(m, 16) <= device_cus();
   if (sb) {
     for (int64_t s0 = 0; s0 < n; s0 += SBW) {
       const int64_t s1 = std::min<int64_t>(s0 + SBW, n);
       const int nblk = (int)cdiv(s1 - s0, B);
-      // the flush past the superblock as three bf16 products (its errors
-      // written as [E_hi | E_lo] by the sweep kernel)
+      // the flush past the superblock: three bf16 products up to X3_MAX_N
+      // columns (its errors written as [E_hi | E_lo] by the sweep kernel
+      // instead of E), else fp32 from E
       SweepArgs a{U, V, n, m, s0, (int)B, maxq, group, G, S, Z, packed ? nullptr : Q8, packed ? qcodes : nullptr,
                   words, bits, write_dequant ? W : nullptr, dt, ldw, E, err_sq, Dblk + (s0 / B) * dstride,
                   nullptr, 0, U + s0 * n + s0, nblk, (int)(s1 - s0 - (int64_t)(nblk - 1) * B),
-                  s1 < n ? Ecat : nullptr};
+                  x3 && s1 < n ? Ecat : nullptr};
       launch_sweep_sb(a, gmode, st);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (s1 < n &&
-          (e = flush_x3(Ecat, 2 * SBW, SBW, U, n, s0, (int)(s1 - s0), s1, n - s1, V, m, Bt, 2 * SBW, st)) != hipSuccess)
-        return e;
+      if ((e = flushx(0, s0, (int)(s1 - s0), s1, n - s1)) != hipSuccess) return e;
     }
   } else if (look) {
     // Look-ahead: LA blocks per flush.  Block t of a group first takes the

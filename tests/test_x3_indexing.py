@@ -1,6 +1,7 @@
 """Host-side model of every global access of the trailing products run as
 three bf16 products (csrc/gemm_x3.hip, csrc/sweep.hip): the transposing
-split of U's rows into hi and lo, the product's operand loads (rows past M or
+split of the factor into hi and lo (once per layer, the part above the
+diagonal blocks), the product's operand loads (rows past M or
 N clamped to the last valid row), its LDS panels and masked stores, and the sweep kernels' split-error
 writes, checked against the buffers quantize_layer carves from its workspace,
 for the tested and configured shapes.  (The kernels' index formulas are
@@ -36,27 +37,41 @@ def flushes(m, n, B, superblock):
 
 
 def check(m, n, B, superblock):
-    lde = ldb = 2 * SBW
-    ecat, bt, vsz, usz = m * 2 * SBW, n * 2 * SBW, m * n, n * n
+    lde, ldu = 2 * SBW, 2 * n
+    ecat, ut, vsz, usz = m * 2 * SBW, n * 2 * n, m * n, n * n
+    assert n % 4 == 0 and ldu % 8 == 0
+    # split_t_kernel (once per layer): tile (j0, k0) skipped unless k0 lies
+    # in an earlier granule than j0 (granules of SBW columns on the
+    # superblock path, 64 on the paired one); reads U[k][j], writes Ut[j][k]
+    # (hi) and Ut[j][n + k] (lo)
+    gran = SBW if superblock else 64
+    written = set()
+    for bx in range(cdiv(n, TT)):
+        for by in range(cdiv(n, TT)):
+            j0, k0 = bx * TT, by * TT
+            if k0 // gran >= j0 // gran:
+                continue
+            written.add((bx, by))
+            kk = k0 + np.arange(TT)[:, None]
+            jj = j0 + np.arange(TT)[None, :]
+            ok = (kk < n) & (jj < n)
+            assert (kk * n + jj)[ok].max() < usz
+            assert (jj * ldu + kk + n)[ok].max() < ut
     for ec, r0, K, c0, N in flushes(m, n, B, superblock):
-        assert K % XK == 0 and c0 + N <= n and r0 + K <= n
-        assert ldb >= 2 * K
-        # split_t_kernel: reads U rows r0.., columns c0..; writes Bt rows j, columns k and K + k
-        i = np.arange(TT)[:, None]
-        jj = np.arange(TT)[None, :]
-        for bx in range(cdiv(N, TT)):
-            for by in range(cdiv(K, TT)):
-                ok = (by * TT + i < K) & (bx * TT + jj < N)
-                rd = (r0 + by * TT + i) * n + c0 + bx * TT + jj
-                assert rd[ok].min() >= 0 and rd[ok].max() < usz
-                wr = (bx * TT + jj) * ldb + by * TT + i + K
-                assert wr[ok].max() < bt
-        # gemm_x3_kernel loads: A row min(r, M-1) at ec (hi) and ec + SBW (lo),
-        # Bt row min(j, N-1) at 0 (hi) and K (lo), 16 bytes at k0 + 8 c8
+        assert K % XK == 0 and r0 % XK == 0 and c0 + N <= n and r0 + K <= c0
+        # gemm_x3_kernel loads: A row min(r, M-1) at ec (hi) and ec + SBW (lo);
+        # Bt = Ut + c0 ldu + r0: row min(j, N-1) at 0 (hi) and n (lo), 16
+        # bytes at k0 + 8 c8
         last_a = (m - 1) * lde + ec + SBW + (K - XK) + 56 + 7
-        last_b = (N - 1) * ldb + K + (K - XK) + 56 + 7
-        assert last_a < ecat and last_b < bt
+        last_b = (c0 + N - 1) * ldu + r0 + n + (K - XK) + 56 + 7
+        assert last_a < ecat and last_b < ut
         assert ec + K <= SBW  # the hi segment does not run into the lo one
+        # every Ut entry read (rows c0.., columns r0..r0+K-1) was written:
+        # the flush's factor rows end at a granule boundary at or before c0
+        assert (r0 + K) % gran == 0
+        for j in {c0, c0 + N - 1}:
+            for k in {r0, r0 + K - 1}:
+                assert (j // TT, k // TT) in written
         # masked stores into V's columns c0.. (row < M, column < N)
         assert (m - 1) * n + c0 + N - 1 < vsz
     # split-error writes of the sweep kernels: row r, block column (in its superblock) + c, + SBW
