@@ -1,5 +1,5 @@
-// The trailing update past a superblock, V[:, c0:] -= E U[r0:r0+K, c0:], as
-// three bf16 products on the 16-bit matrix cores with fp32 accumulation.
+// The sweep's lazy trailing updates, V[:, c0:c0+N] -= E U[r0:r0+K, c0:c0+N],
+// as three bf16 products on the 16-bit matrix cores with fp32 accumulation.
 //
 // "Part 3: Adaptive Rounding: GPTQ", 'Observation 2: Lazy Batch Updates' and
 // 'Algorithm GPTQ': after a batch of columns is swept, its errors are applied
@@ -13,7 +13,7 @@
 // every product accumulated in fp32: each term keeps about 16 bits of its
 // operands (the dropped E_lo U_lo and the rounding of the lo parts are about
 // 2^-16 of the term).  E's rows hold [E_hi | E_lo] (written so by the
-// superblock sweep kernel); U is split and transposed once per layer into
+// sweep kernels); U is split and transposed once per layer into
 // Ut = [U_hi | U_lo]^T, so that both operands are contiguous along K, and
 // every flush reads its factor rows from there.  Each K stage loads the four
 // panels once and runs the three products on them.
