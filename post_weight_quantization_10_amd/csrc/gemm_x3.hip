@@ -69,8 +69,9 @@ __global__ __launch_bounds__(256) void split_t_kernel(const float* U, int64_t n,
 // accumulator r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column
 // l % 32).  A stage of 64 k holds the four panels (72 KiB of LDS, two
 // workgroups per CU); the next stage's panels are loaded into registers while
-// the current one is multiplied, then stored between two barriers.  Rows past
-// M or N load the last valid row (never stored).
+// the current one is multiplied, then stored between two barriers, and C's
+// tile is loaded while the last stage is multiplied.  Rows past M or N load
+// the last valid row (never stored).
 __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t alo,
                                                          int K, const uint16_t* __restrict__ Bt, int64_t ldb,
                                                          int64_t blo, float* __restrict__ C, int64_t ldc, int M,
@@ -129,12 +130,7 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
     for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
   const int arow = (wr * 64 + (lane & 31)) * XP, brow = (wc * 64 + (lane & 31)) * XP;
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int k0 = 0; k0 < K; k0 += XK) {
-    const bool more = k0 + XK < K;
-    if (more) gload(k0 + XK);
+  auto stage = [&]() {
 #pragma unroll
     for (int ks = 0; ks < XK / 16; ++ks) {
       const int kk = 16 * ks + 8 * (lane >> 5);
@@ -163,12 +159,33 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
     }
-    if (more) {
-      __syncthreads();  // every wave is done with this stage
-      lstore();
-      __syncthreads();  // the next stage is visible
-    }
+  };
+
+  gload(0);
+  lstore();
+  __syncthreads();
+  for (int k0 = XK; k0 < K; k0 += XK) {
+    gload(k0);
+    stage();
+    __syncthreads();  // every wave is done with this stage
+    lstore();
+    __syncthreads();  // the next stage is visible
   }
+  // the last stage, with this lane's part of C (rows and columns past M or N
+  // read the last valid one, never stored) loaded ahead of its products, in
+  // the registers the stage loads no longer need
+  float cv[2][2][16];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float* colp = C + min(c0 + wc * 64 + nb * 32 + mfma32_col(lane), N - 1);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        cv[mb][nb][r] = colp[(int64_t)min(r0 + wr * 64 + mb * 32 + mfma32_row(r, lane), M - 1) * ldc];
+    }
+  __builtin_amdgcn_sched_barrier(0);  // every load issued before the stage's products
+  stage();
 
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -178,7 +195,7 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const uint16_t* __restr
       for (int r = 0; r < 16; ++r) {
         const int row = r0 + wr * 64 + mb * 32 + mfma32_row(r, lane);
         const int col = c0 + wc * 64 + nb * 32 + mfma32_col(lane);
-        if (row < M && col < N) C[(int64_t)row * ldc + col] -= acc[mb][nb][r];
+        if (row < M && col < N) C[(int64_t)row * ldc + col] = cv[mb][nb][r] - acc[mb][nb][r];
       }
 }
 
