@@ -230,6 +230,41 @@ def test_sweep_parity_large_rows_ragged_tiles():
     assert np.allclose(got, Wh, rtol=1e-3, atol=1e-3 * np.abs(Wh).max())
 
 
+def test_sweep_parity_superblock_long_rows_fp32_flushes():
+    """Rows longer than 16384 columns on the superblock path (40 rows, one
+    ragged workgroup; 16512 columns: sixteen full 1024-column superblocks and
+    a 128-column one): the flushes past each superblock stay fp32 from E.
+    An X-derived factor of this width is beyond the oracle's seconds, so the
+    factor is a seeded upper-triangular one shaped like an inverse Cholesky
+    factor (lognormal diagonal, off-diagonal entries 0.3 / sqrt(n) of their
+    row's diagonal); the algorithm takes any such U.  Codes, zero points and
+    scales are compared; the layer loss needs H and is left out."""
+    m, n, bits, group, block = 40, 16512, 4, 128, 128
+    say(f"[sweep, long rows] m={m} n={n} bits={bits} group={group} block={block} W=f16")
+    rng = np.random.default_rng(16512)
+    d = np.exp(0.3 * rng.standard_normal(n)).astype(np.float32)
+    U32 = rng.standard_normal((n, n), dtype=np.float32)
+    U32 *= np.float32(0.3 / np.sqrt(n))
+    U32 = np.triu(U32, 1)
+    U32 *= d[:, None]
+    U32[np.diag_indices(n)] = d
+    W = (0.02 * np.exp(0.5 * rng.standard_normal((m, 1))) * rng.standard_normal((m, n))).astype(np.float16)
+    Wt = to_dev(W, "f16")
+    res = pw.quantize_layer(Wt, torch.from_numpy(U32).to(DEV), bits, group, block, write_dequant=True)
+    torch.cuda.synchronize()
+    Wd = W.astype(np.float64)
+    U64 = U32.astype(np.float64)
+    del U32
+    ref = O.gptq_quantize(Wd, U64, bits, group, block)
+    q = unpack(res, n, bits)
+    sc = res["scales"].cpu().numpy()
+    z = res["zeros"].cpu().numpy()
+    rep = compare_codes(q, sc, z, ref, group)
+    say(f"  same {rep['same_frac']:.6f} diverged rows {rep['rows_diverged']} scale rel {rep['scale_rel_max']:.2e}")
+    assert_codes(rep, "sweep-long-rows")
+    follow_check(q, sc, z, Wd, U64, bits, group, block, "sweep-long-rows")
+
+
 def test_sweep_block_invariance_on_gpu():
     """B = 1, 32 and 128 give the same codes except at near-ties."""
     m, n, bits, group = 64, 384, 4, 128
