@@ -483,6 +483,29 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_dma64_kernel(GemmDesc d, int t
     }
   };
 
+  // this lane's 16 entries of C, fetched before the K loop when beta != 0
+  // (rows and columns past M or N read the last valid one, never stored):
+  // loaded one by one behind the store's bounds test they would be 16
+  // dependent memory round trips at the end.  They are issued before the
+  // first stage's copies, so the in-order vmcnt waits below also cover them.
+  const float alpha = d.alpha, beta = d.beta;
+  f32x4 cp[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) cp[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (beta != 0.f) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float* colp = C + min(c0 + 32 * wc + 16 * nb + l16, d.N - 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          cp[mb][nb][r] = colp[(int64_t)min(r0 + 32 * wr + 16 * mb + 4 * kq + r, d.M - 1) * d.ldc];
+      }
+  }
+
   // three-stage ring: stages st + 1 and st + 2 are in flight while st computes
   if (nst > 0) issue(0);
   if (nst > 1) issue(1);
@@ -493,7 +516,6 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_dma64_kernel(GemmDesc d, int t
     compute(stg + (st % SNS) * SSTAGE_F);
   }
 
-  const float alpha = d.alpha, beta = d.beta;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -502,9 +524,8 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_dma64_kernel(GemmDesc d, int t
       for (int r = 0; r < 4; ++r) {
         const int row = r0 + 32 * wr + 16 * mb + 4 * kq + r, col = c0 + 32 * wc + 16 * nb + l16;
         if (row < d.M && col < d.N) {
-          float* pc = C + (int64_t)row * d.ldc + col;
           const float v = alpha * acc[mb][nb][r];
-          *pc = (beta == 0.f) ? v : fmaf(beta, *pc, v);
+          C[(int64_t)row * d.ldc + col] = (beta == 0.f) ? v : fmaf(beta, cp[mb][nb][r], v);
         }
       }
 }
