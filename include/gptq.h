@@ -152,8 +152,13 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp, float* U,
  *   e = (v - what)/U[p][p];  later columns of the block v_j -= e U[p][j];
  * and the block's errors reach the later columns as V[:, i2:] -= E U[i:i2, i2:]
  * before those columns are swept (the library may apply the errors of two
- * consecutive blocks in one product; the result differs only in the order
- * of floating-point sums).
+ * consecutive blocks, or of a 1024-column superblock, in one product; the
+ * result differs only in the order of floating-point sums).  Working
+ * precision: V and E in float32; for rows of at most 16384 columns, when
+ * block_size is a multiple of 64 and groups fit inside a block, the
+ * products past a pair of blocks or a superblock take E and U split into
+ * bf16 hi and lo parts, E_hi U_hi + E_hi U_lo + E_lo U_hi accumulated in
+ * float32 (about 16 bits of every term); otherwise float32 products.
  *
  *   W          [m x n] weights, leading dimension ldw >= n, type w_dtype.
  *              Read; if write_dequant != 0, overwritten by what = s(q - z)
@@ -172,7 +177,8 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp, float* U,
  *   scales     [m x G] float32 out, zeros [m x G] int32 out, G = 1 per-row,
  *              else ceil(n / group_size).
  *   err_sq     optional [m] float32 out (NULL to skip): sum_p e_p^2 per row.
- *   workspace, ws_bytes: at least gptq_quantize_workspace_bytes(m, n, block_size).
+ *   workspace, ws_bytes: at least gptq_quantize_workspace_bytes(m, n, block_size)
+ *              (for n <= 16384 it includes 4 n^2 bytes for the split factor).
  * Errors: m < 1, n < 1, ldw < n, bits outside 2..8, block_size outside
  * 1..128, group/block not nesting, NULL required pointers, unknown dtype ->
  * GPTQ_ERR_INVALID_ARG; short workspace -> GPTQ_ERR_WORKSPACE.
