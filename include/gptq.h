@@ -155,8 +155,9 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp, float* U,
  * consecutive blocks, or of a 1024-column superblock, in one product; the
  * result differs only in the order of floating-point sums).  Working
  * precision: V and E in float32; for rows of at most 16384 columns, when
- * block_size is a multiple of 64 and groups fit inside a block, the
- * products past a pair of blocks or a superblock take E and U split into
+ * block_size is a multiple of 64, n a multiple of 4 and the groups fit
+ * inside a block (or scales are per row), the products past a pair of
+ * blocks or a superblock (K a multiple of 64) take E and U split into
  * bf16 hi and lo parts, E_hi U_hi + E_hi U_lo + E_lo U_hi accumulated in
  * float32 (about 16 bits of every term); otherwise float32 products.
  *
