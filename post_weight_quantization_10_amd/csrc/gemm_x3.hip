@@ -47,15 +47,22 @@ __global__ __launch_bounds__(256) void split_t_kernel(const float* U, int64_t n,
     t[i][jj] = (k0 + i < n && j0 + jj < n) ? U[(k0 + i) * n + j0 + jj] : 0.f;
   }
   __syncthreads();
-  for (int e = tid; e < TT * TT; e += 256) {
-    const int jj = e / TT, i = e % TT;
+  // four consecutive k per thread, 8-byte stores (n is a multiple of 4, so a
+  // run of four is inside or outside the matrix as a whole)
+  for (int e = tid; e < TT * TT / 4; e += 256) {
+    const int jj = e / (TT / 4), i = 4 * (e % (TT / 4));
     if (k0 + i < n && j0 + jj < n) {
-      const float u = t[i][jj];
-      const uint16_t hi = f32_to_bf16(u);
-      const uint16_t lo = f32_to_bf16(u - bf16_to_f32(hi));
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float u = t[i + r][jj];
+        const uint16_t h = f32_to_bf16(u);
+        hi[r] = h;
+        lo[r] = f32_to_bf16(u - bf16_to_f32(h));
+      }
       uint16_t* row = Ut + (j0 + jj) * ldu + k0 + i;
-      row[0] = hi;
-      row[n] = lo;
+      *(uint2*)row = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      *(uint2*)(row + n) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
     }
   }
 }
